@@ -1,0 +1,248 @@
+"""Workload recipes: the exact sequence of cache calls for each synthetic workload.
+
+A recipe is data: a list of operations over symbolic handle names.  The oracle
+and the HIP library each replay the same list with their own implementation.
+Every append, decode and verify draws its numbers from ``workloads.gen`` with a
+stream of its own.
+
+Operations:
+
+* ``("new", h)``                          -- empty root sequence named ``h``
+* ``("append", h, ntok, call)``           -- append ``ntok`` tokens; K values come from
+  stream ``(KIND_K, call)`` and V values from ``(KIND_V, call)``, each laid out
+  ``[layers][ntok][kv_heads][head_dim]``
+* ``("fork", h, n, [c0, ..., c(n-1)])``   -- n children of ``h``; ``h`` stays live
+* ``("release", h)``
+* ``("truncate", h, new_len)``
+* ``("decode", layer, [h...], qcall)``    -- one query per handle; Q from stream
+  ``(KIND_Q, qcall)``, laid out ``[n][q_heads][head_dim]``
+* ``("verify", layer, [h...], [nq...], qcall)`` -- the last ``nq[i]`` positions of each
+  handle are queries; Q laid out ``[sum nq][q_heads][head_dim]``
+
+The tree shapes follow the fork-based decoding strategies of the Dendrite
+article (ainews.cool, "technical deep dive" and its Table 1: width-4 fork
+search, multi-draft speculative decoding), the MCTS run of the Dendrite demo
+tape (branching 4, depth 12, head_dim 128) and the predict / verify /
+accept-or-rollback loop of the DSpark blog (second layer).  The KV shape of the
+bf16 workloads is Llama 3 8B's (32 query heads, 8 KV heads, head_dim 128), the
+model the article benchmarks.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import itertools
+from typing import List, Tuple
+
+from . import gen
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    dtype: str  # 'f32' | 'bf16'
+    layers: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    num_blocks: int
+    ops: List[tuple]
+    seed: int = 0
+    block_size: int = 16
+    # descriptive fields (no effect on replay)
+    description: str = ""
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def attend_ops(self):
+        return [op for op in self.ops if op[0] in ("decode", "verify")]
+
+
+class _Names:
+    def __init__(self):
+        self._c = itertools.count()
+
+    def __call__(self) -> int:
+        return next(self._c)
+
+
+def _blocks_for(ntok: int, bs: int) -> int:
+    return (ntok + bs - 1) // bs
+
+
+def fork_workload(name: str, *, dtype: str, layers: int, q_heads: int, kv_heads: int,
+                  head_dim: int, requests: int, prefix: int, width: int, branch_tokens: int,
+                  seed: int = 0, extra_blocks: int = 0, description: str = "") -> Workload:
+    """Per request: P = new; append(P, prefix); C = fork(P, width); release(P);
+    append(C[b], branch_tokens) for each b.  Then one decode over all branches."""
+    nm = _Names()
+    ops: List[tuple] = []
+    call = 0
+    leaves = []
+    for _ in range(requests):
+        p = nm()
+        ops.append(("new", p))
+        ops.append(("append", p, prefix, call)); call += 1
+        kids = [nm() for _ in range(width)]
+        ops.append(("fork", p, width, kids))
+        ops.append(("release", p))
+        for c in kids:
+            if branch_tokens > 0:
+                ops.append(("append", c, branch_tokens, call)); call += 1
+        leaves.extend(kids)
+    for layer in range(layers):
+        ops.append(("decode", layer, list(leaves), layer))
+    bs = 16
+    need = requests * (_blocks_for(prefix, bs) + width * _blocks_for(branch_tokens, bs))
+    return Workload(name, dtype, layers, q_heads, kv_heads, head_dim, need + extra_blocks, ops,
+                    seed=seed, description=description)
+
+
+def mcts_paths(seed: int, leaves: int, branching: int, depth: int) -> List[Tuple[int, ...]]:
+    """``leaves`` distinct uniformly random root-to-leaf paths (``depth`` draws from
+    ``[0, branching)`` each; a duplicate path is redrawn), in lexicographic order."""
+    if leaves > branching ** depth:
+        raise ValueError("more leaves than distinct paths")
+    stream = gen.stream_id(gen.KIND_SHAPE, 0)
+    seen = set()
+    counter = 0
+    while len(seen) < leaves:
+        path = []
+        for _ in range(depth):
+            path.append(gen.uniform_int(seed, stream, counter, branching))
+            counter += 1
+        seen.add(tuple(path))
+    return sorted(seen)
+
+
+def mcts_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_heads: int = 8,
+                  head_dim: int = 128, root_tokens: int = 2048, branching: int = 4,
+                  depth: int = 12, leaves: int = 256, node_tokens: int = 16, seed: int = 0,
+                  extra_blocks: int = 0, description: str = "") -> Workload:
+    """Root: append root_tokens.  Breadth-first by depth: each present node (in
+    lexicographic order) is forked into its present children and released, then
+    every child gets node_tokens appended (lexicographic order).  Every leaf then
+    decodes one query, leaves in lexicographic order."""
+    paths = mcts_paths(seed, leaves, branching, depth)
+    nm = _Names()
+    ops: List[tuple] = []
+    call = 0
+    root = nm()
+    ops.append(("new", root))
+    ops.append(("append", root, root_tokens, call)); call += 1
+    level = {(): root}
+    nodes = 0
+    for dpt in range(depth):
+        prefixes = sorted({p[: dpt + 1] for p in paths})
+        children_of = {}
+        for pre in prefixes:
+            children_of.setdefault(pre[:-1], []).append(pre)
+        nxt = {}
+        for parent in sorted(level):
+            kids = children_of.get(parent, [])
+            if not kids:
+                continue
+            names = [nm() for _ in kids]
+            ops.append(("fork", level[parent], len(kids), names))
+            ops.append(("release", level[parent]))
+            for pre, h in zip(kids, names):
+                nxt[pre] = h
+        for pre in sorted(nxt):
+            ops.append(("append", nxt[pre], node_tokens, call)); call += 1
+            nodes += 1
+        level = nxt
+    leaf_handles = [level[p] for p in paths]
+    ops.append(("decode", 0, leaf_handles, 0))
+    bs = 16
+    need = _blocks_for(root_tokens, bs) + nodes * _blocks_for(node_tokens, bs)
+    return Workload(name, dtype, 1, q_heads, kv_heads, head_dim, need + extra_blocks, ops,
+                    seed=seed, description=description)
+
+
+def verify_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_heads: int = 8,
+                    head_dim: int = 128, requests: int = 64, prefix: int = 2048, paths: int = 3,
+                    drafts: int = 8, seed: int = 0, accept: bool = True, extra_blocks: int = 0,
+                    description: str = "") -> Workload:
+    """Per request: P = new; append(P, prefix); C = fork(P, paths); release(P);
+    append(C[b], drafts).  One verify over every path with nq = drafts.  Then,
+    per request, path a ~ U{0..paths-1} and k ~ U{0..drafts} are drawn: the
+    accepted path is truncated to prefix + k and the others are released."""
+    nm = _Names()
+    ops: List[tuple] = []
+    call = 0
+    per_req = []
+    for _ in range(requests):
+        p = nm()
+        ops.append(("new", p))
+        ops.append(("append", p, prefix, call)); call += 1
+        kids = [nm() for _ in range(paths)]
+        ops.append(("fork", p, paths, kids))
+        ops.append(("release", p))
+        for c in kids:
+            ops.append(("append", c, drafts, call)); call += 1
+        per_req.append(kids)
+    allh = [h for kids in per_req for h in kids]
+    ops.append(("verify", 0, allh, [drafts] * len(allh), 0))
+    if accept:
+        for r, kids in enumerate(per_req):
+            st = gen.stream_id(gen.KIND_ACCEPT, r)
+            a = gen.uniform_int(seed, st, 0, paths)
+            k = gen.uniform_int(seed, st, 1, drafts + 1)
+            ops.append(("truncate", kids[a], prefix + k))
+            for b, c in enumerate(kids):
+                if b != a:
+                    ops.append(("release", c))
+    bs = 16
+    need = requests * (_blocks_for(prefix, bs) + paths * _blocks_for(drafts, bs))
+    return Workload(name, dtype, 1, q_heads, kv_heads, head_dim, need + extra_blocks, ops,
+                    seed=seed, description=description)
+
+
+# ---------------------------------------------------------------------------
+# The five standard workloads.
+
+def tiny_fork(seed: int = 0) -> Workload:
+    return fork_workload("tiny_fork", dtype="f32", layers=1, q_heads=4, kv_heads=4, head_dim=64,
+                         requests=1, prefix=256, width=4, branch_tokens=32, seed=seed,
+                         description="fp32, 1 layer, MHA 4/4, d=64; 256-token prefix forked "
+                                     "into 4 branches of 32 tokens; 4 decode queries")
+
+
+def llama_fork(seed: int = 0) -> Workload:
+    return fork_workload("llama_fork", dtype="bf16", layers=1, q_heads=32, kv_heads=8, head_dim=128,
+                         requests=32, prefix=4096, width=4, branch_tokens=64, seed=seed,
+                         description="bf16 GQA 32/8, d=128; 32 requests x (4096-token prefix "
+                                     "forked into 4 branches of 64 tokens); 128 decode queries")
+
+
+def mcts_tree(seed: int = 0) -> Workload:
+    return mcts_workload("mcts_tree", seed=seed,
+                         description="bf16 GQA 32/8, d=128; 2048-token root; union of 256 random "
+                                     "depth-12 paths of a branching-4 tree, 16 tokens per node; "
+                                     "256 leaf decode queries")
+
+
+def spec_verify(seed: int = 0) -> Workload:
+    return verify_workload("spec_verify", seed=seed,
+                           description="bf16 GQA 32/8, d=128; 64 requests x (2048-token prefix "
+                                       "forked into 3 draft paths of 8 tokens); verify 1536 draft "
+                                       "queries; accept/rollback by truncation")
+
+
+def full_depth(seed: int = 0) -> Workload:
+    return fork_workload("full_depth", dtype="bf16", layers=32, q_heads=32, kv_heads=8, head_dim=128,
+                         requests=64, prefix=8192, width=16, branch_tokens=256, seed=seed,
+                         description="bf16, 32 layers of Llama-3-8B KV shape; 64 requests x "
+                                     "(8192-token prefix forked into 16 branches of 256 tokens); "
+                                     "one decode step per branch over all layers")
+
+
+STANDARD = {
+    "tiny_fork": tiny_fork,
+    "llama_fork": llama_fork,
+    "mcts_tree": mcts_tree,
+    "spec_verify": spec_verify,
+    "full_depth": full_depth,
+}
