@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark: tree-attention decode over a forked, copy-on-write KV cache on one MI355X.
+
+A step is one ``tkv_attend_decode`` call (plan lookup, split-K partial
+attention kernel, merge kernel) over the Llama-3-8B-shaped fork workload: 32
+requests, each a 4096-token prefix forked into 4 branches of 64 tokens, one
+decode query per branch (128 queries x 32 heads, GQA 32/8, head_dim 128, bf16).
+The tree is built first (fork + append, untimed); K/V are resident in HBM
+before the timed region.  Consecutive steps rotate over ``--copies``
+independent copies of the workload (disjoint pools) so that no step finds the
+previous step's KV in L2 or the 256 MB Infinity Cache.
+
+Printed: one JSON line.  ``value`` is unique-KV GB/s: distinct (block, KV head)
+tiles the step must read, counted by valid token slots, K and V, divided by the
+wall time per step.  Also reported: branch-queries/s, the speculative-verify
+workload's verify tokens/s (64 requests x 3 draft paths x 8 drafts), the
+partial-attention kernel's roofline against 8 TB/s measured with HIP events,
+fork latency, and the CPU oracle timed on a sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def _unique_kv_bytes(lib, op, wl):
+    from tree_structured_copy_amd import tkv
+    info = tkv.tkv_plan_info_get(lib.c, lib.handles(op), op[3] if op[0] == "verify" else None)
+    return info, info["unique_tokens"] * wl.kv_heads * wl.head_dim * wl.elem_bytes * 2
+
+
+def _prepare(wl, copies):
+    import torch
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    from workloads import device as wdev
+    items = []
+    for _ in range(copies):
+        lib = LibReplay(wl, "cuda")
+        i = lib.build()
+        op = wl.ops[i]
+        rows = lib.nrows(op)
+        q = wdev.q_tensor(wl, op[-1], rows)
+        out = torch.empty((rows, wl.q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+        ws, need = lib.workspace(op)
+        seqs = tkv.seq_array(lib.handles(op))
+        nq = tkv.i32_array(op[3]) if op[0] == "verify" else None
+        items.append((lib, op, q, out, ws, need, seqs, nq))
+    torch.cuda.synchronize()
+    return items
+
+
+def _call(item, stream):
+    from tree_structured_copy_amd import tkv
+    lib, op, q, out, ws, need, seqs, nq = item
+    if nq is None:
+        tkv.tkv_attend_decode(lib.c, op[1], seqs, q, out, ws, need, stream)
+    else:
+        tkv.tkv_attend_verify(lib.c, op[1], seqs, nq, q, out, ws, need, stream)
+
+
+def _time_steps(items, steps, warmup):
+    import torch
+    from tree_structured_copy_amd import tkv
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(warmup):
+        _call(items[i % len(items)], stream)
+    torch.cuda.synchronize()
+    for it in items:
+        tkv.tkv_profile_read(it[0].c)
+        tkv.tkv_profile_enable(it[0].c, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        _call(items[i % len(items)], stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    part = merge = 0.0
+    calls = 0
+    for it in items:
+        p, m, n = tkv.tkv_profile_read(it[0].c)
+        tkv.tkv_profile_enable(it[0].c, False)
+        part += p
+        merge += m
+        calls += n
+    return (t1 - t0) / steps * 1e3, part / max(1, calls), merge / max(1, calls)
+
+
+def _fork_latency_ns():
+    """Median wall time of one tkv_fork(n=1) call through ctypes, for a prefix of
+    16 vs 65536 tokens (host-only cache).  ctypes adds its own ~1 us."""
+    from tree_structured_copy_amd import tkv
+    res = {}
+    for prefix in (16, 65536):
+        c = tkv.tkv_create(1, 32, 8, 128, prefix // 16 + 8, tkv.TKV_BF16)
+        s = tkv.tkv_seq_new(c)
+        tkv.tkv_append(c, s, prefix)
+        out = (tkv._U64 * 1)()
+        ts = []
+        for _ in range(20000):
+            t0 = time.perf_counter_ns()
+            tkv._lib.tkv_fork(c, s, 1, out)
+            ts.append(time.perf_counter_ns() - t0)
+            tkv._lib.tkv_release(c, out[0])
+        ts.sort()
+        res[str(prefix)] = ts[len(ts) // 2]
+        tkv.tkv_destroy(c)
+    return res
+
+
+def _cpu_baseline(requests: int, reps: int):
+    """The float64 oracle on the first ``requests`` requests of the fork workload:
+    materialise each branch's history and run textbook attention for all heads."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    from oracle import attention
+    from oracle.cache import ArraySource, MaterializedCache
+    from workloads import gen, recipes
+    import workloads
+    full = recipes.llama_fork()
+    wl = recipes.fork_workload("llama_fork_sample", dtype="bf16", layers=1, q_heads=32, kv_heads=8, head_dim=128,
+                               requests=requests, prefix=4096, width=4, branch_tokens=64, seed=full.seed)
+    # inputs generated up front (not timed)
+    arrays = {}
+    for op in wl.ops:
+        if op[0] == "append":
+            _, h, ntok, call = op
+            arrays[call] = (workloads.kv_values(wl, call, ntok, gen.KIND_K),
+                            workloads.kv_values(wl, call, ntok, gen.KIND_V))
+    dec = wl.attend_ops()[0]
+    Q = workloads.q_values(wl, dec[-1], len(dec[2])).astype(np.float64)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        mc = MaterializedCache()
+        names = {}
+        for op in wl.ops:
+            if op[0] == "new":
+                names[op[1]] = mc.seq_new()
+            elif op[0] == "append":
+                mc.append(names[op[1]], ArraySource(*arrays[op[3]]))
+            elif op[0] == "fork":
+                for n, c in zip(op[3], mc.fork(names[op[1]], op[2])):
+                    names[n] = c
+            elif op[0] == "release":
+                mc.release(names.pop(op[1]))
+        for r, h in enumerate(dec[2]):
+            kv = [mc.kv(names[h], 0, g) for g in range(wl.kv_heads)]
+            for hq in range(wl.q_heads):
+                K, V = kv[attention.kv_head_of(hq, wl.q_heads, wl.kv_heads)]
+                attention.attend_one(K, V, Q[r, hq])
+        times.append(time.perf_counter() - t0)
+    t = sorted(times)[len(times) // 2]
+    unique = requests * (4096 + 4 * 64) * wl.kv_heads * wl.head_dim * 2 * 2
+    return {"value": unique / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d of 32 requests of the fork workload (%d decode queries x 32 heads), median of %d "
+                      "runs of %.2f s" % (requests, 4 * requests, reps, t),
+            "branch_queries_per_s": 4 * requests / t}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-requests", type=int, default=8)
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the fork workload's requests are independent trees, so "
+              "more GPUs would shard requests with no communication; --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from workloads import recipes
+
+    torch.cuda.init()
+    wl = recipes.llama_fork()
+    items = _prepare(wl, args.copies)
+    op = items[0][1]
+    info, ubytes = _unique_kv_bytes(items[0][0], op, wl)
+    ms, part_ms, merge_ms = _time_steps(items, args.steps, args.warmup)
+    value = ubytes / (ms / 1e3) / 1e9
+    achieved = ubytes / (part_ms / 1e3) / 1e9 if part_ms > 0 else None
+    nq = len(op[2])
+    for it in items:
+        it[0].close()
+    del items
+    torch.cuda.empty_cache()
+
+    verify = None
+    if not args.no_verify:
+        vwl = recipes.spec_verify()
+        vitems = _prepare(vwl, args.copies)
+        vop = vitems[0][1]
+        vinfo, vbytes = _unique_kv_bytes(vitems[0][0], vop, vwl)
+        vms, vpart, vmerge = _time_steps(vitems, args.steps, args.warmup)
+        ntok = sum(vop[3])
+        verify = {"workload": "spec_verify", "verify_tokens_per_s": ntok / (vms / 1e3),
+                  "ms_per_step": vms, "unique_kv_GBps": vbytes / (vms / 1e3) / 1e9,
+                  "partial_kernel_ms": vpart, "merge_kernel_ms": vmerge,
+                  "partial_kernel_GBps": vbytes / (vpart / 1e3) / 1e9 if vpart > 0 else None}
+        for it in vitems:
+            it[0].close()
+        del vitems
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = _cpu_baseline(args.cpu_requests, args.cpu_reps)
+
+    line = {
+        "metric": "tree-attn decode unique-KV GB/s (% HBM peak) + branch-queries/s; verify tokens/s",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama_fork", "requests": 32, "prefix_tokens": 4096, "fork_width": 4,
+                   "branch_tokens": 64, "q_heads": 32, "kv_heads": 8, "head_dim": 128, "block_size": 16,
+                   "decode_queries": nq, "copies_rotated": args.copies},
+        "hbm_peak_frac": value / HBM_PEAK_GBS,
+        "branch_queries_per_s": nq / (ms / 1e3),
+        "unique_kv_bytes": ubytes,
+        "plan": info,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
+                     "kernel": "attn_partial_kernel<BF16,128,1,false>", "kernel_ms": part_ms,
+                     "merge_kernel_ms": merge_ms},
+        "verify": verify,
+        "fork_latency_ns_ctypes": _fork_latency_ns(),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path against the oracle, element by element (small sizes).
+
+Sizes are small enough for the float64 oracle to finish in seconds, yet span
+several 16-token blocks, several work items, ragged tails, unaligned forks,
+truncations, block reuse and both dtypes.  Tolerances: max-abs 1e-5 (fp32) and
+2e-3 (bf16 inputs, fp32 accumulation).
+"""
+
+import numpy as np
+import pytest
+
+from workloads import gen, recipes
+
+from _gpu_common import TOL, assert_close, need_gpu, run_both, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_fork_fp32_full():
+    wl = recipes.tiny_fork()
+    assert_close(run_both(wl), "f32")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("bf16", 8, 2, 64), ("f32", 4, 4, 64),
+                                            ("f32", 16, 2, 128)])
+def test_small_fork_ragged(dtype, hq, hkv, d):
+    wl = recipes.fork_workload("small_fork", dtype=dtype, layers=2, q_heads=hq, kv_heads=hkv, head_dim=d,
+                               requests=3, prefix=100, width=4, branch_tokens=7, seed=3)
+    assert_close(run_both(wl), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_verify(dtype):
+    wl = recipes.verify_workload("small_verify", dtype=dtype, q_heads=8, kv_heads=2, head_dim=128,
+                                 requests=3, prefix=37, paths=3, drafts=5, seed=5)
+    assert_close(run_both(wl), dtype)
+
+
+def test_small_mcts():
+    wl = recipes.mcts_workload("small_mcts", q_heads=32, kv_heads=8, head_dim=128, root_tokens=50,
+                               branching=3, depth=4, leaves=20, node_tokens=5, seed=7)
+    assert_close(run_both(wl), "bf16")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_sessions(seed):
+    dtype = "bf16" if seed % 2 == 0 else "f32"
+    hq, hkv, d = [(8, 2, 128), (4, 4, 64), (32, 8, 128), (16, 1, 64)][seed % 4]
+    wl = recipes.random_tree_workload("rand", seed=seed, dtype=dtype, q_heads=hq, kv_heads=hkv, head_dim=d,
+                                      layers=1 + seed % 2)
+    assert_close(run_both(wl), dtype)
+
+
+@pytest.mark.parametrize("opts", [{1: 1}, {1: 100000, 2: 1}, {3: 16}, {3: 32, 2: 2}])
+def test_chunking_and_grouping_options(opts):
+    """Split-K granularity and group size change only rounding."""
+    wl = recipes.fork_workload("opt_fork", dtype="bf16", layers=1, q_heads=32, kv_heads=8, head_dim=128,
+                               requests=2, prefix=300, width=6, branch_tokens=20, seed=11)
+    assert_close(run_both(wl, options=opts), "bf16")
+
+
+def test_many_queries_per_group_mha():
+    """MHA with 64 branches: one group of 64 rows (4 row tiles)."""
+    wl = recipes.fork_workload("mha64", dtype="bf16", layers=1, q_heads=4, kv_heads=4, head_dim=64,
+                               requests=1, prefix=70, width=64, branch_tokens=3, seed=13, extra_blocks=4)
+    assert_close(run_both(wl), "bf16")
+
+
+def test_gather_returns_appended_kv_exactly():
+    """tkv_gather reads back, in token order, exactly what the oracle's history holds."""
+    torch = need_gpu()
+    from oracle.replay import OracleReplay
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    for seed, dtype, hkv, d in [(21, "bf16", 2, 128), (22, "f32", 4, 64), (23, "bf16", 8, 64)]:
+        wl = recipes.random_tree_workload("gather", seed=seed, dtype=dtype, q_heads=hkv * 2, kv_heads=hkv,
+                                          head_dim=d, layers=2, verify=False)
+        say("gather seed %d %s" % (seed, dtype))
+        lib, orc = LibReplay(wl), OracleReplay(wl)
+        try:
+            for op in wl.ops:
+                lib.apply(op)
+                orc.apply(op)
+            for name in lib.h:
+                L = tkv.tkv_seq_len(lib.c, lib.h[name])
+                if L == 0:
+                    continue
+                for layer in range(wl.layers):
+                    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+                    ko = torch.empty((L, hkv, d), dtype=dt, device="cuda")
+                    vo = torch.empty_like(ko)
+                    tkv.tkv_gather(lib.c, lib.h[name], layer, ko, vo, torch.cuda.current_stream())
+                    torch.cuda.synchronize()
+                    for g in range(hkv):
+                        K, V = orc.mat.kv(orc.h_mat[name], layer, g)
+                        np.testing.assert_array_equal(ko[:, g].float().cpu().numpy(), K)
+                        np.testing.assert_array_equal(vo[:, g].float().cpu().numpy(), V)
+        finally:
+            lib.close()
+
+
+def test_single_token_is_exact_v():
+    """One key: softmax weight 1, so the output is the value itself."""
+    torch = need_gpu()
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    from workloads import device as wdev
+    wl = recipes.fork_workload("one", dtype="bf16", layers=1, q_heads=8, kv_heads=2, head_dim=128,
+                               requests=5, prefix=1, width=1, branch_tokens=0, seed=2)
+    lib = LibReplay(wl)
+    try:
+        lib.build()
+        op = wl.attend_ops()[0]
+        out = lib.attend(op)
+        for i, hname in enumerate(op[2]):
+            ko = torch.empty((1, 2, 128), dtype=torch.bfloat16, device="cuda")
+            vo = torch.empty_like(ko)
+            tkv.tkv_gather(lib.c, lib.h[hname], 0, ko, vo, torch.cuda.current_stream())
+            for h in range(8):
+                assert torch.equal(out[i, h], vo[0, h // 4].float())
+    finally:
+        lib.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fork_and_identical_siblings_invariance(dtype):
+    """Forking a branch does not change its output; siblings with identical K/V
+    give identical outputs; permuting the batch permutes the outputs.  Work is
+    regrouped between the calls, so only rounding may differ: fp32 within 1e-6,
+    bf16 within the bf16 tolerance (the softmax weights are rounded to bf16
+    relative to a running max that depends on the processing order)."""
+    torch = need_gpu()
+    from tree_structured_copy_amd import tkv
+    from workloads import device as wdev
+    tol = 1e-6 if dtype == "f32" else TOL["bf16"]
+    hq, hkv, d = 32, 8, 128
+    nb = 200
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kp = torch.empty(nb * hkv * 16 * d, dtype=tdt, device="cuda")
+    vp = torch.empty_like(kp)
+    c = tkv.tkv_create(1, hq, hkv, d, nb, tkv.TKV_BF16 if dtype == "bf16" else tkv.TKV_F32, kp, vp)
+    try:
+        wl = recipes.fork_workload("inv", dtype=dtype, layers=1, q_heads=hq, kv_heads=hkv, head_dim=d,
+                                   requests=1, prefix=1, width=1, branch_tokens=0)
+        s = tkv.tkv_seq_new(c)
+        k = wdev.kv_tensor(wl, 0, 517, gen.KIND_K)
+        v = wdev.kv_tensor(wl, 0, 517, gen.KIND_V)
+        tkv.tkv_append(c, s, 517, k, v, torch.cuda.current_stream())
+        q = wdev.q_tensor(wl, 0, 4)
+        out = torch.empty((1, hq, d), dtype=torch.float32, device="cuda")
+        ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+        tkv.tkv_attend_decode(c, 0, [s], q[:1], out, ws, ws.numel(), None)
+        before = out.clone()
+        kids = tkv.tkv_fork(c, s, 3)
+        k2 = wdev.kv_tensor(wl, 1, 9, gen.KIND_K)
+        v2 = wdev.kv_tensor(wl, 1, 9, gen.KIND_V)
+        for kid in kids[:2]:  # two siblings get identical tokens
+            tkv.tkv_append(c, kid, 9, k2, v2, torch.cuda.current_stream())
+        tkv.tkv_append(c, kids[2], 3, k2, v2, torch.cuda.current_stream())
+        qq = torch.cat([q[:1], q[1:2], q[1:2], q[2:3]])
+        out4 = torch.empty((4, hq, d), dtype=torch.float32, device="cuda")
+        seqs = [s] + kids
+        tkv.tkv_attend_decode(c, 0, seqs, qq, out4, ws, ws.numel(), None)
+        torch.cuda.synchronize()
+        assert float((out4[0] - before[0]).abs().max()) <= tol
+        assert float((out4[1] - out4[2]).abs().max()) <= tol
+        perm = [3, 1, 0, 2]
+        outp = torch.empty_like(out4)
+        tkv.tkv_attend_decode(c, 0, [seqs[i] for i in perm], qq[perm], outp, ws, ws.numel(), None)
+        torch.cuda.synchronize()
+        assert float((outp - out4[perm]).abs().max()) <= tol
+    finally:
+        tkv.tkv_destroy(c)
+
+
+def test_release_then_reuse_same_stream():
+    """A released block reused by a later append on the same stream: outputs still
+    match the oracle (the stream orders the reads and the overwrite)."""
+    wl = recipes.Workload("reuse", "bf16", 1, 8, 2, 128, 12, [
+        ("new", 0), ("append", 0, 100, 0), ("fork", 0, 2, [1, 2]), ("append", 1, 40, 1),
+        ("decode", 0, [1, 2], 0), ("release", 1), ("append", 2, 45, 2), ("decode", 0, [2, 0], 1),
+        ("release", 2), ("release", 0), ("new", 3), ("append", 3, 150, 3), ("decode", 0, [3], 2)])
+    assert_close(run_both(wl), "bf16")
+
+
+def test_workspace_and_argument_errors():
+    torch = need_gpu()
+    from tree_structured_copy_amd import tkv
+    kp = torch.empty(64 * 2 * 16 * 128, dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    c = tkv.tkv_create(1, 8, 2, 128, 64, tkv.TKV_BF16, kp, vp)
+    try:
+        s = tkv.tkv_seq_new(c)
+        k = torch.zeros((1, 700, 2, 128), dtype=torch.bfloat16, device="cuda")
+        tkv.tkv_append(c, s, 700, k, k, None)
+        kids = tkv.tkv_fork(c, s, 8)
+        q = torch.zeros((8, 8, 128), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((8, 8, 128), dtype=torch.float32, device="cuda")
+        tkv.tkv_set_option(c, tkv.TKV_OPT_TARGET_WGS, 100000)
+        need = tkv.tkv_workspace_size(c, kids)
+        assert need > 0
+        with pytest.raises(tkv.TkvError) as e:
+            tkv.tkv_attend_decode(c, 0, kids, q, out, None, 0, None)
+        assert e.value.code == tkv.TKV_E_WORKSPACE
+        with pytest.raises(tkv.TkvError) as e:
+            tkv.tkv_attend_decode(c, 1, kids, q, out, None, 0, None)
+        assert e.value.code == tkv.TKV_E_RANGE
+        with pytest.raises(tkv.TkvError) as e:
+            tkv.tkv_attend_decode(c, 0, kids, q.data_ptr() + 2, out, None, 0, None)
+        assert e.value.code == tkv.TKV_E_INVAL
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        tkv.tkv_attend_decode(c, 0, kids, q, out, ws, need, None)
+        torch.cuda.synchronize()
+        # q = 0 and K = V = 0: every output is exactly 0
+        assert float(out.abs().max()) == 0.0
+    finally:
+        tkv.tkv_destroy(c)

@@ -1,0 +1,354 @@
+"""The library's host core (C ABI, no GPU) against the oracle's flat allocator.
+
+A host-only cache (no pools) runs the real tree, allocator and planner;
+``tkv_append`` without K/V reserves slots only.  Block tables, lengths, sharer
+counts, free counts and error codes must equal the oracle's after every step.
+"""
+
+import itertools
+import json
+import os
+import random
+import re
+import time
+
+import pytest
+
+from oracle import allocator as A
+from workloads import recipes
+
+tkv = pytest.importorskip("tree_structured_copy_amd.tkv")
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+ERR = {"inval": tkv.TKV_E_INVAL, "nomem": tkv.TKV_E_NOMEM, "badseq": tkv.TKV_E_BADSEQ,
+       "shared": tkv.TKV_E_SHARED, "range": tkv.TKV_E_RANGE}
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "tkv.h")).read()
+    declared = set(re.findall(r"^\s*(?:int|const char\*|size_t)\s+(tkv_\w+)\s*\(", header, re.M))
+    assert declared, "no declarations parsed"
+    assert declared == set(tkv.EXPORTED)
+    for name in declared:
+        assert hasattr(tkv._lib, name)
+
+
+def host_cache(num_blocks, layers=1, hq=4, hkv=4, d=64):
+    return tkv.tkv_create(layers, hq, hkv, d, num_blocks, tkv.TKV_F32)
+
+
+class Pair:
+    """Library and oracle driven in lockstep over symbolic handle names."""
+
+    def __init__(self, num_blocks):
+        self.nb = num_blocks
+        self.c = host_cache(num_blocks)
+        self.o = A.FlatAllocator(num_blocks, 16)
+        self.lh, self.oh = {}, {}
+
+    def close(self):
+        tkv.tkv_destroy(self.c)
+
+    def step(self, op):
+        """Apply op to both; return (lib error name or None, oracle error name or None)."""
+        kind, name = op[0], op[1]
+        le = oe = None
+        try:
+            if kind == "new":
+                self.lh[name] = tkv.tkv_seq_new(self.c)
+            elif kind == "append":
+                tkv.tkv_append(self.c, self.lh.get(name, 0), op[2])
+            elif kind == "fork":
+                kids = tkv.tkv_fork(self.c, self.lh.get(name, 0), op[2])
+                for k, s in zip(op[3], kids):
+                    self.lh[k] = s
+            elif kind == "release":
+                tkv.tkv_release(self.c, self.lh.get(name, 0))
+                self.lh.pop(name, None)
+            elif kind == "truncate":
+                tkv.tkv_truncate(self.c, self.lh.get(name, 0), op[2])
+        except tkv.TkvError as e:
+            le = e.name
+        try:
+            if kind == "new":
+                self.oh[name] = self.o.seq_new()
+            elif kind == "append":
+                self.o.append(self.oh.get(name, -1), op[2])
+            elif kind == "fork":
+                kids = self.o.fork(self.oh.get(name, -1), op[2])
+                for k, s in zip(op[3], kids):
+                    self.oh[k] = s
+            elif kind == "release":
+                self.o.release(self.oh.get(name, -1))
+                self.oh.pop(name, None)
+            elif kind == "truncate":
+                self.o.truncate(self.oh.get(name, -1), op[2])
+        except A.OracleError as e:
+            oe = e.code
+        return le, oe
+
+    def compare(self):
+        assert set(self.lh) == set(self.oh)
+        for name in self.lh:
+            assert tkv.tkv_block_table(self.c, self.lh[name]) == self.o.table(self.oh[name]), name
+            assert tkv.tkv_seq_len(self.c, self.lh[name]) == self.o.length(self.oh[name])
+        assert tkv.tkv_num_free(self.c) == self.o.num_free()
+        assert tkv.tkv_block_refcounts(self.c, self.nb) == [self.o.sharers(b) for b in range(self.nb)]
+
+
+def test_walkthrough_scaled_to_block_16():
+    """The hand-derived block-size-4 walkthrough with every token count x4 runs
+    unchanged at block size 16."""
+    g = json.load(open(os.path.join(GOLD, "alloc_walkthrough.json")))
+    p = Pair(g["num_blocks"])
+    try:
+        for st in g["steps"]:
+            op = list(st["op"])
+            if op[0] in ("append", "truncate"):
+                op[2] *= 4
+            le, oe = p.step(op)
+            assert le == oe == st.get("error"), (op, le, oe)
+            want = {k: [(b, 4 * v) for b, v in t] for k, t in st["tables"].items()}
+            got = {k: tkv.tkv_block_table(p.c, s) for k, s in p.lh.items()}
+            assert got == want, op
+            assert tkv.tkv_num_free(p.c) == st["free"]
+            assert tkv.tkv_block_refcounts(p.c, g["num_blocks"]) == st["sharers"]
+            p.compare()
+    finally:
+        p.close()
+
+
+def _random_ops(seed, n_ops, nb):
+    rnd = random.Random(seed)
+    live, nxt, ops = [], 0, []
+    for _ in range(n_ops):
+        r = rnd.random()
+        if not live or r < 0.07:
+            ops.append(("new", nxt)); live.append(nxt); nxt += 1
+        elif r < 0.27:
+            h = rnd.choice(live); n = rnd.randint(1, 3)
+            kids = list(range(nxt, nxt + n)); nxt += n
+            ops.append(("fork", h, n, kids)); live += kids
+        elif r < 0.62:
+            ops.append(("append", rnd.choice(live), rnd.choice([1, 2, 5, 15, 16, 17, 31, 40, 64])))
+        elif r < 0.78:
+            h = rnd.choice(live); ops.append(("release", h)); live.remove(h)
+        elif r < 0.95:
+            ops.append(("truncate", rnd.choice(live), rnd.randint(0, 300)))
+        else:  # stale / bad arguments
+            ops.append(rnd.choice([("append", rnd.choice(live), 0), ("fork", rnd.choice(live), 0, []),
+                                   ("truncate", rnd.choice(live), -1), ("release", 10 ** 6)]))
+    return ops
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_differential(seed):
+    nb = 40
+    p = Pair(nb)
+    try:
+        for op in _random_ops(seed, 300, nb):
+            if op[0] == "truncate" and op[1] in p.oh:
+                L = p.o.length(p.oh[op[1]])
+                if op[2] > L and op[2] != -1:
+                    op = ("truncate", op[1], L if random.Random(op[2]).random() < 0.3 else op[2] % (L + 1))
+            le, oe = p.step(op)
+            assert le == oe, (op, le, oe)
+            p.compare()
+    finally:
+        p.close()
+
+
+def test_exhaustive_short_sequences():
+    """Every sequence of up to 4 moves over 3 handle names on a 4-block pool."""
+    moves = []
+    for h in range(3):
+        moves += [("append", h, 4), ("append", h, 20), ("fork", h, 1, None), ("fork", h, 2, None),
+                  ("release", h), ("truncate", h, 4), ("truncate", h, 0)]
+    count = 0
+    for length in range(1, 5):
+        for seq in itertools.product(moves, repeat=length):
+            p = Pair(4)
+            try:
+                p.step(("new", 0))
+                nxt = 1
+                for mv in seq:
+                    if mv[1] not in p.lh:
+                        continue
+                    if mv[0] == "fork":
+                        kids = list(range(nxt, nxt + mv[2])); nxt += mv[2]
+                        mv = ("fork", mv[1], mv[2], kids)
+                    if mv[0] == "truncate":
+                        L = p.o.length(p.oh[mv[1]])
+                        mv = ("truncate", mv[1], min(mv[2], L))
+                    le, oe = p.step(mv)
+                    assert le == oe, (seq, mv, le, oe)
+                p.compare()
+            finally:
+                p.close()
+            count += 1
+    assert count == sum(21 ** k for k in range(1, 5))
+
+
+@pytest.mark.parametrize("name", ["tiny_fork", "llama_fork", "mcts_tree", "spec_verify", "full_depth"])
+def test_standard_recipes_match_oracle(name):
+    wl = recipes.STANDARD[name]()
+    c = host_cache(wl.num_blocks, wl.layers, wl.q_heads, wl.kv_heads, wl.head_dim)
+    o = A.FlatAllocator(wl.num_blocks, 16)
+    lh, oh = {}, {}
+    try:
+        for op in wl.ops:
+            k = op[0]
+            if k == "new":
+                lh[op[1]] = tkv.tkv_seq_new(c); oh[op[1]] = o.seq_new()
+            elif k == "append":
+                tkv.tkv_append(c, lh[op[1]], op[2]); o.append(oh[op[1]], op[2])
+            elif k == "fork":
+                for n, s, t in zip(op[3], tkv.tkv_fork(c, lh[op[1]], op[2]), o.fork(oh[op[1]], op[2])):
+                    lh[n], oh[n] = s, t
+            elif k == "release":
+                tkv.tkv_release(c, lh.pop(op[1])); o.release(oh.pop(op[1]))
+            elif k == "truncate":
+                tkv.tkv_truncate(c, lh[op[1]], op[2]); o.truncate(oh[op[1]], op[2])
+            else:
+                for h in op[2]:
+                    assert tkv.tkv_block_table(c, lh[h]) == o.table(oh[h])
+                info = tkv.tkv_plan_info_get(c, [lh[h] for h in op[2]], op[3] if k == "verify" else None)
+                tabs = {b: v for h in op[2] for b, v in o.table(oh[h])}
+                assert info["unique_blocks"] == len(tabs)
+                assert info["unique_tokens"] == sum(tabs.values())
+        assert tkv.tkv_num_free(c) == o.num_free()
+        assert tkv.tkv_block_refcounts(c, wl.num_blocks) == [o.sharers(b) for b in range(wl.num_blocks)]
+    finally:
+        tkv.tkv_destroy(c)
+
+
+# ---------------------------------------------------------------------------
+# fork cost: O(1) in prefix length and depth
+
+def test_fork_touches_no_block():
+    c = host_cache(5000)
+    try:
+        s = tkv.tkv_seq_new(c)
+        tkv.tkv_append(c, s, 16 * 4000 + 5)
+        before = tkv.tkv_get_counters(c)
+        free = tkv.tkv_num_free(c)
+        kids = tkv.tkv_fork(c, s, 16)
+        after = tkv.tkv_get_counters(c)
+        assert tkv.tkv_num_free(c) == free
+        for k in ("blocks_taken", "blocks_freed", "block_ids_copied", "nodes_created"):
+            assert after[k] == before[k], k
+        assert all(tkv.tkv_block_table(c, k) == tkv.tkv_block_table(c, s) for k in kids[:2])
+    finally:
+        tkv.tkv_destroy(c)
+
+
+def _median_fork_ns(prefix_tokens, depth, reps=3000):
+    c = host_cache(prefix_tokens // 16 + depth + 8)
+    try:
+        s = tkv.tkv_seq_new(c)
+        tkv.tkv_append(c, s, prefix_tokens)
+        for _ in range(depth - 1):  # a chain of depth nodes
+            s2 = tkv.tkv_fork(c, s, 1)[0]
+            tkv.tkv_release(c, s)
+            s = s2
+            tkv.tkv_append(c, s, 1)
+        f = tkv._lib.tkv_fork
+        out = (tkv._U64 * 1)()
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter_ns()
+            f(c, s, 1, out)
+            times.append(time.perf_counter_ns() - t0)
+            tkv._lib.tkv_release(c, out[0])
+        times.sort()
+        return times[len(times) // 2]
+    finally:
+        tkv.tkv_destroy(c)
+
+
+def test_fork_latency_flat_in_prefix_and_depth():
+    base = _median_fork_ns(16, 1)
+    for prefix, depth in [(65536, 1), (16, 500), (65536, 500)]:
+        assert _median_fork_ns(prefix, depth) < 3 * base + 2000
+
+
+# ---------------------------------------------------------------------------
+# errors
+
+def test_error_codes_and_strong_guarantee():
+    c = host_cache(4)
+    try:
+        s = tkv.tkv_seq_new(c)
+        tkv.tkv_append(c, s, 40)  # 3 blocks
+        with pytest.raises(tkv.TkvError) as e:
+            tkv.tkv_append(c, s, 9 + 16)  # 8 slots left in the tail + needs 2 blocks, 1 free
+        assert e.value.code == tkv.TKV_E_NOMEM
+        assert tkv.tkv_seq_len(c, s) == 40 and tkv.tkv_num_free(c) == 1
+        for bad, code in [(lambda: tkv.tkv_fork(c, s, 0), tkv.TKV_E_INVAL),
+                          (lambda: tkv.tkv_append(c, s, 0), tkv.TKV_E_INVAL),
+                          (lambda: tkv.tkv_truncate(c, s, 41), tkv.TKV_E_RANGE),
+                          (lambda: tkv.tkv_release(c, s + 1), tkv.TKV_E_BADSEQ),
+                          (lambda: tkv.tkv_release(c, 0), tkv.TKV_E_BADSEQ),
+                          (lambda: tkv.tkv_attend_decode(c, 0, [s], 1, 1), tkv.TKV_E_NODEVICE),
+                          (lambda: tkv.tkv_gather(c, s, 0, 1, 1), tkv.TKV_E_NODEVICE),
+                          (lambda: tkv.tkv_set_option(c, tkv.TKV_OPT_MAX_ROWS, 8), tkv.TKV_E_RANGE)]:
+            with pytest.raises(tkv.TkvError) as e:
+                bad()
+            assert e.value.code == code
+        k = tkv.tkv_fork(c, s, 1)[0]
+        with pytest.raises(tkv.TkvError) as e:
+            tkv.tkv_truncate(c, k, 39)
+        assert e.value.code == tkv.TKV_E_SHARED
+        tkv.tkv_release(c, s)
+        with pytest.raises(tkv.TkvError) as e:
+            tkv.tkv_seq_len(c, s)
+        assert e.value.code == tkv.TKV_E_BADSEQ
+        e0 = tkv.tkv_seq_new(c)
+        with pytest.raises(tkv.TkvError) as e:
+            tkv.tkv_workspace_size(c, [e0])
+        assert e.value.code == tkv.TKV_E_EMPTY
+        with pytest.raises(tkv.TkvError) as e:
+            tkv.tkv_workspace_size(c, [k], [41])
+        assert e.value.code == tkv.TKV_E_RANGE
+    finally:
+        tkv.tkv_destroy(c)
+
+
+def test_bad_configs_rejected():
+    for args in [(0, 4, 4, 64, 10), (1, 4, 3, 64, 10), (1, 4, 4, 96, 10), (1, 4, 4, 64, 0)]:
+        with pytest.raises(tkv.TkvError) as e:
+            tkv.tkv_create(*args, tkv.TKV_F32)
+        assert e.value.code == tkv.TKV_E_INVAL
+    with pytest.raises(tkv.TkvError):
+        tkv.tkv_create(1, 4, 4, 64, 10, tkv.TKV_F32, k_pool=256, v_pool=None)
+
+
+def test_plan_shapes():
+    """Groups never mix independent trees and hold <= 64 rows; every query is in one group."""
+    wl = recipes.llama_fork()
+    c = host_cache(wl.num_blocks, 1, 32, 8, 128)
+    try:
+        h = {}
+        for op in wl.ops:
+            if op[0] == "new":
+                h[op[1]] = tkv.tkv_seq_new(c)
+            elif op[0] == "append":
+                tkv.tkv_append(c, h[op[1]], op[2])
+            elif op[0] == "fork":
+                for n, s in zip(op[3], tkv.tkv_fork(c, h[op[1]], op[2])):
+                    h[n] = s
+            elif op[0] == "release":
+                tkv.tkv_release(c, h.pop(op[1]))
+        seqs = [h[x] for x in wl.attend_ops()[0][2]]
+        info = tkv.tkv_plan_info_get(c, seqs)
+        assert info["groups"] == 32
+        assert info["unique_blocks"] == 32 * 272
+        assert info["block_entries"] == 32 * 272  # each block listed once
+        assert info["rows_per_tile_hist"][0] == info["items"]  # 16 rows per group -> 1 tile
+        before = tkv.tkv_get_counters(c)["plans_built"]
+        tkv.tkv_plan_info_get(c, seqs)
+        assert tkv.tkv_get_counters(c)["plans_built"] == before  # cached
+    finally:
+        tkv.tkv_destroy(c)

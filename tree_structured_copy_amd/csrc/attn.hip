@@ -1,0 +1,368 @@
+// Tree attention kernels for gfx950.
+//
+// Dendrite article (ainews.cool, "technical deep dive"): a branch's query
+// attends over the keys and values of its shared ancestor path and then of its
+// own leaf path.  The planner has cut the batch into groups of up to 64 rows
+// (rows = the group's queries x the query heads that share one KV head) and
+// lists each group's blocks once, with a mask of which queries see each block.
+//
+// One workgroup (4 waves) runs one work item (a run of a group's block list) for
+// one KV head.  Each wave takes every 4th block of the item and keeps, for all
+// of the group's rows, a flash-decoding state (running max m, sum l, output
+// accumulator) in registers:
+//   * a block's K tile arrives with four contiguous 1 KiB wave loads already in
+//     MFMA operand order (layout.h) and S^T = K Q^T for 16 tokens x 16 rows is a
+//     handful of MFMAs: every key is fetched from HBM once per group, however
+//     many sibling branches and GQA heads read it;
+//   * the S^T fragment a lane gets (4 tokens of one row) is exactly the operand
+//     P^T the P.V MFMA needs, so the softmax stays in registers;
+//   * the running max is rescaled lazily (only when it grows by more than 2^8,
+//     which bounds every weight by 2^8 and keeps fp32 sums exact enough).
+// At the end the 4 waves' states are merged through LDS; an item that covers its
+// whole group writes normalised outputs, otherwise it writes fp32 partials
+// (m, l, acc) and attn_merge combines them (log-sum-exp, exp2 domain).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace tkv {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kTau = 8.0f;
+
+template <class To, class From>
+__device__ inline To bitcast(const From& f) {
+  return __builtin_bit_cast(To, f);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// bf16 inputs: S^T via 16x16x32 bf16 MFMAs, O^T via 16x16x16 bf16 MFMAs.
+struct BF16 {
+  using elem = uint16_t;
+  template <int D>
+  struct Frag {
+    u32x4 v[D / 32];
+  };
+  template <int D>
+  __device__ static void load_tile(Frag<D>& f, const elem* tile, int lane) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(tile) + lane;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) f.v[i] = p[i * 64];
+  }
+  template <int D>
+  __device__ static void load_q(Frag<D>& f, const elem* row, int g) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) f.v[kk] = *reinterpret_cast<const u32x4*>(row + 32 * kk + 8 * g);
+  }
+  template <int D>
+  __device__ static void zero(Frag<D>& f) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) f.v[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  template <int D>
+  __device__ static f32x4 qk(const Frag<D>& k, const Frag<D>& q) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(k.v[kk]), bitcast<bf16x8>(q.v[kk]), s, 0, 0, 0);
+    return s;
+  }
+  // acc[dt] += V^T[16dt..16dt+15][4 tokens] . P^T; the weights are rounded to
+  // bf16 once and the same rounded values are summed into l.
+  template <int D>
+  __device__ static void pv(const Frag<D>& v, const float* p, f32x4* acc, float& l) {
+    const __bf16 b0 = static_cast<__bf16>(p[0]), b1 = static_cast<__bf16>(p[1]);
+    const __bf16 b2 = static_cast<__bf16>(p[2]), b3 = static_cast<__bf16>(p[3]);
+    l += (static_cast<float>(b0) + static_cast<float>(b1)) + (static_cast<float>(b2) + static_cast<float>(b3));
+    i16x4 pp;
+    pp[0] = bitcast<short>(b0);
+    pp[1] = bitcast<short>(b1);
+    pp[2] = bitcast<short>(b2);
+    pp[3] = bitcast<short>(b3);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u32x4 w = v.v[dt >> 1];
+      const u32x2 half = (dt & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y};
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<i16x4>(half), pp, acc[dt], 0, 0, 0);
+    }
+  }
+};
+
+// fp32 inputs: 16x16x4 fp32 MFMAs (full fp32 products and sums).
+struct F32 {
+  using elem = float;
+  template <int D>
+  struct Frag {
+    f32x4 v[D / 16];
+  };
+  template <int D>
+  __device__ static void load_tile(Frag<D>& f, const elem* tile, int lane) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(tile) + lane;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) f.v[i] = p[i * 64];
+  }
+  template <int D>
+  __device__ static void load_q(Frag<D>& f, const elem* row, int g) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) f.v[c] = *reinterpret_cast<const f32x4*>(row + 16 * c + 4 * g);
+  }
+  template <int D>
+  __device__ static void zero(Frag<D>& f) {
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) f.v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  template <int D>
+  __device__ static f32x4 qk(const Frag<D>& k, const Frag<D>& q) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_mfma_f32_16x16x4f32(k.v[c][j], q.v[c][j], s, 0, 0, 0);
+    return s;
+  }
+  template <int D>
+  __device__ static void pv(const Frag<D>& v, const float* p, f32x4* acc, float& l) {
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.v[dt][i], p[i], acc[dt], 0, 0, 0);
+  }
+};
+
+template <class P, int D, int T, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
+  using E = typename P::elem;
+  using F = typename P::template Frag<D>;
+  constexpr int NDT = D / 16;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  const int kvh = blockIdx.x % a.hkv;
+  const DevItem it = a.items[a.item0 + blockIdx.x / a.hkv];
+  const DevGroup gr = a.groups[it.group];
+  const int G = a.gsize;
+  const int nrows = gr.nq * G;
+  const uint64_t gmask = gr.nq >= 64 ? ~0ull : ((1ull << gr.nq) - 1);
+
+  F qf[T];
+  int qj[T], qlim[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int R = 16 * t + r;
+    if (R < nrows) {
+      const int j = R / G;
+      const int h = kvh * G + (R - j * G);
+      const int qi = a.gq[gr.q_begin + j];
+      P::load_q(qf[t], static_cast<const E*>(a.q) + (static_cast<size_t>(qi) * a.hq + h) * D, g);
+      qj[t] = j;
+      qlim[t] = CAUSAL ? a.gqpos[gr.q_begin + j] : 0;
+    } else {
+      P::zero(qf[t]);
+      qj[t] = 0;
+      qlim[t] = 0x7fffffff;
+    }
+  }
+
+  float m[T], l[T];
+  f32x4 acc[T][NDT];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    m[t] = kNegInf;
+    l[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const DevBlock* bl = a.blocks + it.blk_begin;
+  const int nb = it.blk_count;
+  const int nmine = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;
+  const size_t tile = 16 * D;
+  const size_t bstride = static_cast<size_t>(a.hkv) * tile;
+  const E* kb = static_cast<const E*>(a.kpool) + static_cast<size_t>(kvh) * tile;
+  const E* vb = static_cast<const E*>(a.vpool) + static_cast<size_t>(kvh) * tile;
+  const float sl2 = a.scale_log2;
+
+  auto process = [&](const F& kf, const F& vf, const DevBlock& e) {
+    const bool all_see = (e.mask & gmask) == gmask;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const f32x4 s = P::qk(kf, qf[t]);
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 4 * g + i;
+        bool ok = tok < e.valid;
+        if (!all_see) ok = ok && ((e.mask >> qj[t]) & 1ull);
+        if (CAUSAL) ok = ok && (e.pos + tok <= qlim[t]);
+        sc[i] = ok ? s[i] * sl2 : kNegInf;
+      }
+      float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float mn = fmaxf(m[t], bm);
+      if (__any(mn > m[t] + kTau)) {
+        const float alpha = (m[t] == kNegInf) ? 0.f : fast_exp2(m[t] - mn);
+        l[t] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[t][dt] *= alpha;
+        m[t] = mn;
+      }
+      const float mu = (m[t] == kNegInf) ? 0.f : m[t];
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - mu);
+      P::pv(vf, p, acc[t], l[t]);
+    }
+  };
+
+  if (nmine > 0) {
+    F kA, vA, kB, vB;
+    DevBlock eA = bl[wave], eB;
+    P::load_tile(kA, kb + static_cast<size_t>(eA.id) * bstride, lane);
+    P::load_tile(vA, vb + static_cast<size_t>(eA.id) * bstride, lane);
+    for (int k = 0; k < nmine; k += 2) {
+      const int k1 = min(k + 1, nmine - 1);
+      eB = bl[wave + k1 * kWaves];
+      P::load_tile(kB, kb + static_cast<size_t>(eB.id) * bstride, lane);
+      P::load_tile(vB, vb + static_cast<size_t>(eB.id) * bstride, lane);
+      process(kA, vA, eA);
+      if (k + 1 >= nmine) break;
+      const int k2 = min(k + 2, nmine - 1);
+      eA = bl[wave + k2 * kWaves];
+      P::load_tile(kA, kb + static_cast<size_t>(eA.id) * bstride, lane);
+      P::load_tile(vA, vb + static_cast<size_t>(eA.id) * bstride, lane);
+      process(kB, vB, eB);
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    l[t] += __shfl_xor(l[t], 16);
+    l[t] += __shfl_xor(l[t], 32);
+  }
+
+  // merge the four waves' states
+  __shared__ float s_m[kWaves][16];
+  __shared__ float s_l[kWaves][16];
+  __shared__ float s_acc[kWaves][D][17];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (16 * t >= nrows) break;
+    if (g == 0) {
+      s_m[wave][r] = m[t];
+      s_l[wave][r] = l[t];
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_acc[wave][16 * dt + 4 * g + i][r] = acc[t][dt][i];
+    __syncthreads();
+    for (int o = tid; o < 16 * D; o += 256) {
+      const int rr = o / D, d = o - rr * D;
+      const int R = 16 * t + rr;
+      if (R >= nrows) continue;
+      float M = s_m[0][rr];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][rr]);
+      float ls = 0.f, as = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = s_m[w][rr];
+        const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+        ls += s_l[w][rr] * f;
+        as += s_acc[w][d][rr] * f;
+      }
+      const int j = R / G;
+      const int h = kvh * G + (R - j * G);
+      if (it.part_base < 0) {
+        const int qi = a.gq[gr.q_begin + j];
+        a.out[(static_cast<size_t>(qi) * a.hq + h) * D + d] = as / ls;
+      } else {
+        const size_t slot = static_cast<size_t>(it.part_base) + static_cast<size_t>(j) * a.hq + h;
+        a.part_acc[slot * D + d] = as;
+        if (d == 0) {
+          a.part_ml[2 * slot] = M;
+          a.part_ml[2 * slot + 1] = ls;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void attn_merge_kernel(MergeArgs a) {
+  const int qh = blockIdx.x;
+  const int q = qh / a.hq, h = qh - q * a.hq;
+  const int d = threadIdx.x;
+  const DevMerge mg = a.merge[q];
+  if (mg.gi_count == 0) return;
+  float M = kNegInf;
+  for (int c = 0; c < mg.gi_count; ++c) {
+    const int item = a.group_items[mg.gi_begin + c];
+    const size_t slot = static_cast<size_t>(a.items[item].part_base) + static_cast<size_t>(mg.j) * a.hq + h;
+    M = fmaxf(M, a.part_ml[2 * slot]);
+  }
+  float ls = 0.f, as = 0.f;
+  for (int c = 0; c < mg.gi_count; ++c) {
+    const int item = a.group_items[mg.gi_begin + c];
+    const size_t slot = static_cast<size_t>(a.items[item].part_base) + static_cast<size_t>(mg.j) * a.hq + h;
+    const float mc = a.part_ml[2 * slot];
+    const float f = (mc == kNegInf) ? 0.f : fast_exp2(mc - M);
+    ls += a.part_ml[2 * slot + 1] * f;
+    as += a.part_acc[slot * D + d] * f;
+  }
+  a.out[(static_cast<size_t>(q) * a.hq + h) * D + d] = as / ls;
+}
+
+template <class P, int D, bool C>
+hipError_t launch_t(int tiles, const AttnArgs& args, int32_t n_items, hipStream_t s) {
+  const dim3 grid(n_items * args.hkv), block(256);
+  switch (tiles) {
+    case 1: hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, C>), grid, block, 0, s, args); break;
+    case 2: hipLaunchKernelGGL((attn_partial_kernel<P, D, 2, C>), grid, block, 0, s, args); break;
+    case 3: hipLaunchKernelGGL((attn_partial_kernel<P, D, 3, C>), grid, block, 0, s, args); break;
+    case 4: hipLaunchKernelGGL((attn_partial_kernel<P, D, 4, C>), grid, block, 0, s, args); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class P, int D>
+hipError_t launch_c(int tiles, bool causal, const AttnArgs& args, int32_t n_items, hipStream_t s) {
+  return causal ? launch_t<P, D, true>(tiles, args, n_items, s) : launch_t<P, D, false>(tiles, args, n_items, s);
+}
+
+}  // namespace
+
+hipError_t launch_attn_partial(int dtype, int head_dim, int tiles, bool causal, const AttnArgs& args,
+                               int32_t n_items, hipStream_t stream) {
+  if (n_items <= 0) return hipSuccess;
+  if (dtype == 1 && head_dim == 128) return launch_c<BF16, 128>(tiles, causal, args, n_items, stream);
+  if (dtype == 1 && head_dim == 64) return launch_c<BF16, 64>(tiles, causal, args, n_items, stream);
+  if (dtype == 0 && head_dim == 128) return launch_c<F32, 128>(tiles, causal, args, n_items, stream);
+  if (dtype == 0 && head_dim == 64) return launch_c<F32, 64>(tiles, causal, args, n_items, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_merge(int head_dim, const MergeArgs& args, hipStream_t stream) {
+  if (args.nq <= 0) return hipSuccess;
+  const dim3 grid(args.nq * args.hq);
+  if (head_dim == 128) hipLaunchKernelGGL((attn_merge_kernel<128>), grid, dim3(128), 0, stream, args);
+  else if (head_dim == 64) hipLaunchKernelGGL((attn_merge_kernel<64>), grid, dim3(64), 0, stream, args);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace tkv

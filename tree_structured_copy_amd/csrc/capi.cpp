@@ -1,0 +1,541 @@
+// The C ABI: argument checks, plan caching and upload, kernel launches.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <array>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kernels.h"
+#include "plan.h"
+#include "tkv.h"
+#include "tree.h"
+
+using namespace tkv;
+
+namespace {
+
+struct PlanSlot {
+  std::vector<tkv_seq> seqs;
+  std::vector<int32_t> nq;
+  bool verify = false;
+  uint64_t epoch = 0;
+  uint64_t opt_epoch = 0;
+  bool valid = false;
+  Plan plan;
+  void* dev = nullptr;
+  size_t dev_cap = 0;
+  bool uploaded = false;
+  uint64_t stamp = 0;
+};
+
+constexpr int kPlanSlots = 4;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct DeviceGuard {
+  int prev = -1;
+  int want;
+  explicit DeviceGuard(int dev) : want(dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != want) (void)hipSetDevice(want);
+  }
+  ~DeviceGuard() {
+    if (prev >= 0 && prev != want) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+struct tkv_cache {
+  tkv_config cfg{};
+  Tree tree;
+  int device = -1;
+  bool has_pools = false;
+  PlanOptions opt;
+  uint64_t opt_epoch = 1;
+  bool plan_cache = true;
+  PlanSlot slots[kPlanSlots];
+  uint64_t stamp = 0;
+  // pinned staging for plan uploads
+  void* pinned = nullptr;
+  size_t pinned_cap = 0;
+  hipEvent_t pinned_ev = nullptr;
+  bool pinned_busy = false;
+  // profiling
+  bool prof = false;
+  std::vector<std::array<hipEvent_t, 3>> prof_used;
+  std::vector<hipEvent_t> ev_pool;
+  int64_t prof_calls = 0;
+
+  explicit tkv_cache(const tkv_config& c) : cfg(c), tree(c.num_blocks) {}
+
+  size_t elem_bytes() const { return cfg.dtype == TKV_BF16 ? 2 : 4; }
+  size_t tile_elems() const { return 16 * static_cast<size_t>(cfg.head_dim); }
+  size_t layer_elems() const {
+    return static_cast<size_t>(cfg.num_blocks) * cfg.num_kv_heads * tile_elems();
+  }
+  const char* kpool_layer(int layer) const {
+    return static_cast<const char*>(cfg.k_pool) + layer * layer_elems() * elem_bytes();
+  }
+  const char* vpool_layer(int layer) const {
+    return static_cast<const char*>(cfg.v_pool) + layer * layer_elems() * elem_bytes();
+  }
+
+  hipEvent_t get_event() {
+    if (!ev_pool.empty()) {
+      hipEvent_t e = ev_pool.back();
+      ev_pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+namespace {
+
+int find_plan(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq, PlanSlot** out) {
+  const bool verify = nq != nullptr;
+  const uint64_t ep = c->tree.epoch();
+  if (c->plan_cache) {
+    for (auto& s : c->slots) {
+      if (!s.valid || s.epoch != ep || s.opt_epoch != c->opt_epoch || s.verify != verify) continue;
+      if (s.seqs.size() != static_cast<size_t>(nseq)) continue;
+      if (std::memcmp(s.seqs.data(), seqs, nseq * sizeof(tkv_seq))) continue;
+      if (verify && std::memcmp(s.nq.data(), nq, nseq * sizeof(int32_t))) continue;
+      s.stamp = ++c->stamp;
+      *out = &s;
+      return TKV_OK;
+    }
+  }
+  // build into the least recently used slot (a slot with stale contents first)
+  PlanSlot* victim = &c->slots[0];
+  for (auto& s : c->slots) {
+    const bool stale = !s.valid || s.epoch != ep || s.opt_epoch != c->opt_epoch;
+    const bool vstale = !victim->valid || victim->epoch != ep || victim->opt_epoch != c->opt_epoch;
+    if (stale && !vstale) victim = &s;
+    else if (stale == vstale && s.stamp < victim->stamp) victim = &s;
+  }
+  Plan p;
+  const int32_t gsize = c->cfg.num_q_heads / c->cfg.num_kv_heads;
+  if (int rc = build_plan(c->tree, seqs, nq, nseq, gsize, c->cfg.num_kv_heads, c->opt, &p)) return rc;
+  try {
+    victim->seqs.assign(seqs, seqs + nseq);
+    if (verify) victim->nq.assign(nq, nq + nseq);
+    else victim->nq.clear();
+  } catch (const std::bad_alloc&) {
+    victim->valid = false;
+    return TKV_E_NOMEM;
+  }
+  victim->plan = std::move(p);
+  victim->verify = verify;
+  victim->epoch = ep;
+  victim->opt_epoch = c->opt_epoch;
+  victim->valid = true;
+  victim->uploaded = false;
+  victim->stamp = ++c->stamp;
+  ++c->tree.counters.plans_built;
+  *out = victim;
+  return TKV_OK;
+}
+
+int upload_plan(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
+  if (s->uploaded) return TKV_OK;
+  const size_t bytes = std::max<size_t>(s->plan.bytes, 256);
+  if (s->dev_cap < bytes) {
+    if (s->dev) {
+      // the old buffer may still be read by queued kernels
+      if (hipStreamSynchronize(stream) != hipSuccess) return TKV_E_DEVICE;
+      (void)hipFree(s->dev);
+      s->dev = nullptr;
+      s->dev_cap = 0;
+    }
+    const size_t cap = align256(bytes + bytes / 4);
+    if (hipMalloc(&s->dev, cap) != hipSuccess) {
+      s->dev = nullptr;
+      return TKV_E_NOMEM;
+    }
+    s->dev_cap = cap;
+  }
+  if (c->pinned_busy) {
+    if (hipEventSynchronize(c->pinned_ev) != hipSuccess) return TKV_E_DEVICE;
+    c->pinned_busy = false;
+  }
+  if (c->pinned_cap < bytes) {
+    if (c->pinned) (void)hipHostFree(c->pinned);
+    c->pinned = nullptr;
+    c->pinned_cap = 0;
+    const size_t cap = align256(bytes + bytes / 4);
+    if (hipHostMalloc(&c->pinned, cap, hipHostMallocDefault) != hipSuccess) {
+      c->pinned = nullptr;
+      return TKV_E_NOMEM;
+    }
+    c->pinned_cap = cap;
+  }
+  if (!c->pinned_ev && hipEventCreateWithFlags(&c->pinned_ev, hipEventDisableTiming) != hipSuccess)
+    return TKV_E_DEVICE;
+  s->plan.serialise(c->pinned);
+  if (hipMemcpyAsync(s->dev, c->pinned, s->plan.bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return TKV_E_DEVICE;
+  if (hipEventRecord(c->pinned_ev, stream) != hipSuccess) return TKV_E_DEVICE;
+  c->pinned_busy = true;
+  s->uploaded = true;
+  ++c->tree.counters.plans_uploaded;
+  return TKV_OK;
+}
+
+size_t partial_bytes(const tkv_cache* c, const Plan& p) {
+  if (p.partial_slots == 0) return 0;
+  const size_t acc = align256(static_cast<size_t>(p.partial_slots) * c->cfg.head_dim * sizeof(float));
+  return acc + align256(static_cast<size_t>(p.partial_slots) * 2 * sizeof(float));
+}
+
+int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
+           const void* q, float* out, void* ws, size_t ws_bytes, void* stream_) {
+  if (!c) return TKV_E_INVAL;
+  if (!c->has_pools) return TKV_E_NODEVICE;
+  if (layer < 0 || layer >= c->cfg.num_layers) return TKV_E_RANGE;
+  if (!seqs || nseq < 1 || !q || !out) return TKV_E_INVAL;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(ws)) & 15)
+    return TKV_E_INVAL;
+  PlanSlot* s = nullptr;
+  if (int rc = find_plan(c, seqs, nq, nseq, &s)) return rc;
+  const Plan& P = s->plan;
+  const size_t need = partial_bytes(c, P);
+  if (need > 0 && (!ws || ws_bytes < need)) return TKV_E_WORKSPACE;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  DeviceGuard dg(c->device);
+  if (int rc = upload_plan(c, s, stream)) return rc;
+
+  const char* dev = static_cast<const char*>(s->dev);
+  AttnArgs a{};
+  a.kpool = c->kpool_layer(layer);
+  a.vpool = c->vpool_layer(layer);
+  a.q = q;
+  a.out = out;
+  a.items = reinterpret_cast<const DevItem*>(dev + P.off_items);
+  a.groups = reinterpret_cast<const DevGroup*>(dev + P.off_groups);
+  a.gq = reinterpret_cast<const int32_t*>(dev + P.off_gq);
+  a.gqpos = reinterpret_cast<const int32_t*>(dev + P.off_gqpos);
+  a.blocks = reinterpret_cast<const DevBlock*>(dev + P.off_blocks);
+  a.part_acc = static_cast<float*>(ws);
+  a.part_ml = P.partial_slots
+                  ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                             align256(static_cast<size_t>(P.partial_slots) * c->cfg.head_dim * 4))
+                  : nullptr;
+  a.hq = c->cfg.num_q_heads;
+  a.hkv = c->cfg.num_kv_heads;
+  a.gsize = a.hq / a.hkv;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(c->cfg.head_dim)));
+
+  std::array<hipEvent_t, 3> ev{nullptr, nullptr, nullptr};
+  if (c->prof) {
+    for (auto& e : ev) e = c->get_event();
+    if (ev[0] && ev[1] && ev[2]) (void)hipEventRecord(ev[0], stream);
+  }
+  for (int t = 1; t <= 4; ++t) {
+    const int32_t n = P.bucket_begin[t] - P.bucket_begin[t - 1];
+    if (n <= 0) continue;
+    a.item0 = P.bucket_begin[t - 1];
+    if (launch_attn_partial(c->cfg.dtype, c->cfg.head_dim, t, P.causal, a, n, stream) != hipSuccess)
+      return TKV_E_DEVICE;
+  }
+  if (c->prof && ev[1]) (void)hipEventRecord(ev[1], stream);
+  if (P.any_merge) {
+    MergeArgs m{};
+    m.items = a.items;
+    m.group_items = reinterpret_cast<const int32_t*>(dev + P.off_group_items);
+    m.merge = reinterpret_cast<const DevMerge*>(dev + P.off_merge);
+    m.part_acc = a.part_acc;
+    m.part_ml = a.part_ml;
+    m.out = out;
+    m.hq = a.hq;
+    m.nq = P.nqueries;
+    if (launch_attn_merge(c->cfg.head_dim, m, stream) != hipSuccess) return TKV_E_DEVICE;
+  }
+  if (c->prof) {
+    if (ev[0] && ev[1] && ev[2]) {
+      (void)hipEventRecord(ev[2], stream);
+      c->prof_used.push_back(ev);
+      ++c->prof_calls;
+    } else {
+      for (auto e : ev)
+        if (e) c->ev_pool.push_back(e);
+    }
+  }
+  return TKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tkv_strerror(int status) {
+  switch (status) {
+    case TKV_OK: return "ok";
+    case TKV_E_INVAL: return "invalid argument";
+    case TKV_E_NOMEM: return "out of blocks or memory";
+    case TKV_E_BADSEQ: return "stale or unknown sequence handle";
+    case TKV_E_SHARED: return "truncation would remove tokens shared with other branches";
+    case TKV_E_EMPTY: return "attention over an empty sequence";
+    case TKV_E_RANGE: return "value out of range";
+    case TKV_E_DEVICE: return "HIP call or kernel launch failed";
+    case TKV_E_WORKSPACE: return "workspace too small";
+    case TKV_E_NODEVICE: return "cache has no device pools";
+    default: return "unknown status";
+  }
+}
+
+int tkv_create(const tkv_config* cfg, tkv_cache** out) {
+  if (!cfg || !out) return TKV_E_INVAL;
+  const tkv_config& c = *cfg;
+  if (c.num_layers < 1 || c.num_q_heads < 1 || c.num_kv_heads < 1 || c.num_blocks < 1) return TKV_E_INVAL;
+  if (c.num_q_heads % c.num_kv_heads || c.num_q_heads / c.num_kv_heads > kMaxRows) return TKV_E_INVAL;
+  if (c.head_dim != 64 && c.head_dim != 128) return TKV_E_INVAL;
+  if (c.block_size != kBlock || c.reserved != 0) return TKV_E_INVAL;
+  if (c.dtype != TKV_F32 && c.dtype != TKV_BF16) return TKV_E_INVAL;
+  if ((c.k_pool == nullptr) != (c.v_pool == nullptr)) return TKV_E_INVAL;
+  if ((reinterpret_cast<uintptr_t>(c.k_pool) | reinterpret_cast<uintptr_t>(c.v_pool)) & 15) return TKV_E_INVAL;
+  tkv_cache* cache = nullptr;
+  try {
+    cache = new tkv_cache(c);
+  } catch (const std::bad_alloc&) {
+    return TKV_E_NOMEM;
+  }
+  cache->has_pools = c.k_pool != nullptr;
+  if (cache->has_pools && hipGetDevice(&cache->device) != hipSuccess) {
+    delete cache;
+    return TKV_E_DEVICE;
+  }
+  *out = cache;
+  return TKV_OK;
+}
+
+int tkv_destroy(tkv_cache* c) {
+  if (!c) return TKV_E_INVAL;
+  if (c->has_pools) {
+    DeviceGuard dg(c->device);
+    (void)hipDeviceSynchronize();
+    for (auto& s : c->slots)
+      if (s.dev) (void)hipFree(s.dev);
+    if (c->pinned) (void)hipHostFree(c->pinned);
+    if (c->pinned_ev) (void)hipEventDestroy(c->pinned_ev);
+    for (auto& t : c->prof_used)
+      for (auto e : t) (void)hipEventDestroy(e);
+    for (auto e : c->ev_pool) (void)hipEventDestroy(e);
+  }
+  delete c;
+  return TKV_OK;
+}
+
+int tkv_seq_new(tkv_cache* c, tkv_seq* out) { return c ? c->tree.seq_new(out) : TKV_E_INVAL; }
+
+int tkv_fork(tkv_cache* c, tkv_seq parent, int32_t n, tkv_seq* out_children) {
+  return c ? c->tree.fork(parent, n, out_children) : TKV_E_INVAL;
+}
+
+int tkv_release(tkv_cache* c, tkv_seq s) { return c ? c->tree.release(s) : TKV_E_INVAL; }
+
+int tkv_truncate(tkv_cache* c, tkv_seq s, int64_t new_len) {
+  return c ? c->tree.truncate(s, new_len) : TKV_E_INVAL;
+}
+
+int tkv_append(tkv_cache* c, tkv_seq s, int32_t ntok, const void* k, const void* v, void* stream_) {
+  if (!c) return TKV_E_INVAL;
+  if ((k == nullptr) != (v == nullptr)) return TKV_E_INVAL;
+  if (k && !c->has_pools) return TKV_E_NODEVICE;
+  if (k && ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)) return TKV_E_INVAL;
+  Placement pl;
+  if (int rc = c->tree.append(s, ntok, &pl)) return rc;
+  if (!k) return TKV_OK;
+  const bool made = c->tree.last_append_made_node();
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  DeviceGuard dg(c->device);
+  const int32_t nent = static_cast<int32_t>(pl.blocks.size());
+  for (int32_t e0 = 0; e0 < nent; e0 += kAppendMaxBlocks) {
+    AppendArgs a{};
+    a.src_k = k;
+    a.src_v = v;
+    a.kpool = c->cfg.k_pool;
+    a.vpool = c->cfg.v_pool;
+    a.layer_stride = static_cast<int64_t>(c->layer_elems());
+    a.ntok = ntok;
+    a.hkv = c->cfg.num_kv_heads;
+    a.nent = std::min(kAppendMaxBlocks, nent - e0);
+    a.s0 = e0 == 0 ? pl.first_slot : 0;
+    a.tok0 = e0 == 0 ? 0 : (16 - pl.first_slot) + (e0 - 1) * 16;
+    for (int32_t i = 0; i < a.nent; ++i) a.blk[i] = pl.blocks[e0 + i];
+    if (launch_append(c->cfg.dtype, c->cfg.head_dim, c->cfg.num_layers, a, stream) != hipSuccess) {
+      c->tree.undo_append(s, ntok, pl, made);
+      return TKV_E_DEVICE;
+    }
+  }
+  return TKV_OK;
+}
+
+int tkv_workspace_size(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq, size_t* bytes) {
+  if (!c || !bytes) return TKV_E_INVAL;
+  PlanSlot* s = nullptr;
+  if (int rc = find_plan(c, seqs, nq, nseq, &s)) return rc;
+  *bytes = partial_bytes(c, s->plan);
+  return TKV_OK;
+}
+
+int tkv_attend_decode(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t nseq, const void* q,
+                      float* out, void* ws, size_t ws_bytes, void* stream) {
+  return attend(c, layer, seqs, nullptr, nseq, q, out, ws, ws_bytes, stream);
+}
+
+int tkv_attend_verify(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
+                      const void* q, float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!nq) return TKV_E_INVAL;
+  return attend(c, layer, seqs, nq, nseq, q, out, ws, ws_bytes, stream);
+}
+
+int tkv_gather(tkv_cache* c, tkv_seq s, int32_t layer, void* k_out, void* v_out, void* stream_) {
+  if (!c) return TKV_E_INVAL;
+  if (!c->has_pools) return TKV_E_NODEVICE;
+  if (layer < 0 || layer >= c->cfg.num_layers) return TKV_E_RANGE;
+  if (!k_out || !v_out) return TKV_E_INVAL;
+  if ((reinterpret_cast<uintptr_t>(k_out) | reinterpret_cast<uintptr_t>(v_out)) & 15) return TKV_E_INVAL;
+  int32_t n = 0;
+  int rc = c->tree.block_table(s, nullptr, nullptr, 0, &n);
+  if (rc && rc != TKV_E_RANGE) return rc;
+  std::vector<int32_t> ids(n), valid(n);
+  if (n > 0 && (rc = c->tree.block_table(s, ids.data(), valid.data(), n, &n))) return rc;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  DeviceGuard dg(c->device);
+  int32_t pos = 0;
+  for (int32_t e0 = 0; e0 < n; e0 += kGatherMaxBlocks) {
+    GatherArgs a{};
+    a.kpool = c->kpool_layer(layer);
+    a.vpool = c->vpool_layer(layer);
+    a.k_out = k_out;
+    a.v_out = v_out;
+    a.hkv = c->cfg.num_kv_heads;
+    a.nent = std::min(kGatherMaxBlocks, n - e0);
+    for (int32_t i = 0; i < a.nent; ++i) {
+      a.blk[i] = ids[e0 + i];
+      a.valid[i] = valid[e0 + i];
+      a.pos[i] = pos;
+      pos += valid[e0 + i];
+    }
+    if (launch_gather(c->cfg.dtype, c->cfg.head_dim, a, stream) != hipSuccess) return TKV_E_DEVICE;
+  }
+  return TKV_OK;
+}
+
+int tkv_seq_len(const tkv_cache* c, tkv_seq s, int64_t* len) { return c ? c->tree.seq_len(s, len) : TKV_E_INVAL; }
+
+int tkv_block_table(const tkv_cache* c, tkv_seq s, int32_t* ids, int32_t* valid, int32_t cap, int32_t* n) {
+  return c ? c->tree.block_table(s, ids, valid, cap, n) : TKV_E_INVAL;
+}
+
+int tkv_block_refcount(const tkv_cache* c, int32_t block, int32_t* rc) {
+  return c ? c->tree.block_refcount(block, rc) : TKV_E_INVAL;
+}
+
+int tkv_block_refcounts(const tkv_cache* c, int32_t* rc) { return c ? c->tree.block_refcounts(rc) : TKV_E_INVAL; }
+
+int tkv_num_free(const tkv_cache* c, int32_t* n) {
+  if (!c || !n) return TKV_E_INVAL;
+  *n = c->tree.num_free();
+  return TKV_OK;
+}
+
+int tkv_get_counters(const tkv_cache* c, tkv_counters* out) {
+  if (!c || !out) return TKV_E_INVAL;
+  *out = c->tree.counters;
+  return TKV_OK;
+}
+
+int tkv_plan_info_get(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq, tkv_plan_info* out) {
+  if (!c || !out) return TKV_E_INVAL;
+  PlanSlot* s = nullptr;
+  if (int rc = find_plan(c, seqs, nq, nseq, &s)) return rc;
+  const Plan& P = s->plan;
+  tkv_plan_info info{};
+  info.groups = static_cast<int32_t>(P.groups.size());
+  info.items = static_cast<int32_t>(P.items.size());
+  info.block_entries = static_cast<int32_t>(P.blocks.size());
+  info.unique_blocks = P.unique_blocks;
+  info.unique_tokens = P.unique_tokens;
+  info.partial_slots = P.partial_slots;
+  for (int t = 1; t <= 4; ++t) info.rows_per_tile_hist[t - 1] = P.bucket_begin[t] - P.bucket_begin[t - 1];
+  *out = info;
+  return TKV_OK;
+}
+
+int tkv_set_option(tkv_cache* c, int32_t key, int64_t value) {
+  if (!c) return TKV_E_INVAL;
+  switch (key) {
+    case TKV_OPT_TARGET_WGS:
+      if (value < 1 || value > (1 << 24)) return TKV_E_RANGE;
+      c->opt.target_wgs = static_cast<int32_t>(value);
+      break;
+    case TKV_OPT_MIN_CHUNK:
+      if (value < 1 || value > (1 << 24)) return TKV_E_RANGE;
+      c->opt.min_chunk = static_cast<int32_t>(value);
+      break;
+    case TKV_OPT_MAX_ROWS:
+      if (value < 16 || value > kMaxRows) return TKV_E_RANGE;
+      c->opt.max_rows = static_cast<int32_t>(value);
+      break;
+    case TKV_OPT_PLAN_CACHE:
+      c->plan_cache = value != 0;
+      break;
+    default:
+      return TKV_E_INVAL;
+  }
+  ++c->opt_epoch;
+  return TKV_OK;
+}
+
+int tkv_get_option(const tkv_cache* c, int32_t key, int64_t* value) {
+  if (!c || !value) return TKV_E_INVAL;
+  switch (key) {
+    case TKV_OPT_TARGET_WGS: *value = c->opt.target_wgs; break;
+    case TKV_OPT_MIN_CHUNK: *value = c->opt.min_chunk; break;
+    case TKV_OPT_MAX_ROWS: *value = c->opt.max_rows; break;
+    case TKV_OPT_PLAN_CACHE: *value = c->plan_cache ? 1 : 0; break;
+    default: return TKV_E_INVAL;
+  }
+  return TKV_OK;
+}
+
+int tkv_profile_enable(tkv_cache* c, int32_t on) {
+  if (!c) return TKV_E_INVAL;
+  if (on && !c->has_pools) return TKV_E_NODEVICE;
+  c->prof = on != 0;
+  return TKV_OK;
+}
+
+int tkv_profile_read(tkv_cache* c, double* partial_ms, double* merge_ms, int64_t* calls) {
+  if (!c) return TKV_E_INVAL;
+  double pm = 0, mm = 0;
+  int rc = TKV_OK;
+  if (!c->prof_used.empty()) {
+    DeviceGuard dg(c->device);
+    for (auto& t : c->prof_used) {
+      float a = 0.f, b = 0.f;
+      if (hipEventSynchronize(t[2]) != hipSuccess || hipEventElapsedTime(&a, t[0], t[1]) != hipSuccess ||
+          hipEventElapsedTime(&b, t[1], t[2]) != hipSuccess)
+        rc = TKV_E_DEVICE;
+      pm += a;
+      mm += b;
+      for (auto e : t) c->ev_pool.push_back(e);
+    }
+  }
+  c->prof_used.clear();
+  if (partial_ms) *partial_ms = pm;
+  if (merge_ms) *merge_ms = mm;
+  if (calls) *calls = c->prof_calls;
+  c->prof_calls = 0;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,24 @@
+// Launchers for the HIP kernels (defined in attn.hip and kv.hip).
+#pragma once
+#include <hip/hip_runtime_api.h>
+
+#include "tkv_types.h"
+
+namespace tkv {
+
+// Partial attention over items [args.item0, args.item0 + n_items) whose groups
+// need `tiles` row tiles of 16; grid = n_items * Hkv workgroups of 256 threads.
+hipError_t launch_attn_partial(int dtype, int head_dim, int tiles, bool causal, const AttnArgs& args,
+                               int32_t n_items, hipStream_t stream);
+
+// Log-sum-exp merge of split-K partials into out; grid = nq * Hq.
+hipError_t launch_attn_merge(int head_dim, const MergeArgs& args, hipStream_t stream);
+
+// Scatter appended tokens into pool tiles; grid = nent x Hkv x layers.
+hipError_t launch_append(int dtype, int head_dim, int32_t layers, const AppendArgs& args,
+                         hipStream_t stream);
+
+// Copy a path's tiles back out in token order; grid = nent x Hkv.
+hipError_t launch_gather(int dtype, int head_dim, const GatherArgs& args, hipStream_t stream);
+
+}  // namespace tkv

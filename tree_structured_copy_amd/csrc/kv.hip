@@ -1,0 +1,165 @@
+// Append-scatter and gather kernels for the pool tiles.
+//
+// tkv_append writes each new token's K and V once into its block slot (DSpark
+// blog, third layer: each token's KV is computed once and reused).  One
+// workgroup builds one (block, KV head, layer) tile: it stages the new tokens'
+// rows in LDS with 16-byte loads, then writes the tile's 16-byte chunks in the
+// pool's element order (layout.h).  A block that this append opens is written
+// whole, with zeros in the slots no token fills yet, so no slot ever holds
+// uninitialised bits; a block that continues keeps its earlier slots.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+#include "layout.h"
+
+namespace tkv {
+namespace {
+
+template <int EB>
+struct Elem;
+template <>
+struct Elem<2> {
+  using T = uint16_t;
+};
+template <>
+struct Elem<4> {
+  using T = uint32_t;
+};
+
+template <int EB, int D>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  using L = Layout<EB>;
+  using E = typename Elem<EB>::T;
+  constexpr int PC = L::kPerChunk;
+  constexpr int NCH = 16 * D / PC;
+  constexpr int CPR = D / PC;  // chunks per token row
+  __shared__ __align__(16) E sk[16 * D];
+  __shared__ __align__(16) E sv[16 * D];
+
+  const int e = blockIdx.x, kvh = blockIdx.y, layer = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int slot_lo = (e == 0) ? a.s0 : 0;
+  const int src0 = (e == 0) ? a.tok0 : a.tok0 + (16 - a.s0) + (e - 1) * 16;
+  const int cnt = min(16 - slot_lo, a.ntok - src0);
+  const bool fresh = slot_lo == 0;
+  if (cnt <= 0) return;
+
+  const E* srck = static_cast<const E*>(a.src_k);
+  const E* srcv = static_cast<const E*>(a.src_v);
+  for (int idx = tid; idx < cnt * CPR; idx += 256) {
+    const int t = idx / CPR, c = idx - t * CPR;
+    const size_t so = ((static_cast<size_t>(layer) * a.ntok + src0 + t) * a.hkv + kvh) * D + c * PC;
+    const int lo = (slot_lo + t) * D + c * PC;
+    *reinterpret_cast<uint4*>(&sk[lo]) = *reinterpret_cast<const uint4*>(srck + so);
+    *reinterpret_cast<uint4*>(&sv[lo]) = *reinterpret_cast<const uint4*>(srcv + so);
+  }
+  __syncthreads();
+
+  const size_t base = static_cast<size_t>(layer) * a.layer_stride +
+                      (static_cast<size_t>(a.blk[e]) * a.hkv + kvh) * (16 * D);
+  uint4* kt = reinterpret_cast<uint4*>(static_cast<E*>(a.kpool) + base);
+  uint4* vt = reinterpret_cast<uint4*>(static_cast<E*>(a.vpool) + base);
+  const int hi = slot_lo + cnt;
+  for (int ch = tid; ch < NCH; ch += 256) {
+    // K: a chunk holds one token
+    {
+      int tok, d;
+      L::k_coord(ch, 0, tok, d);
+      const bool isnew = tok >= slot_lo && tok < hi;
+      if (isnew || fresh) {
+        E vals[PC];
+#pragma unroll
+        for (int el = 0; el < PC; ++el) {
+          L::k_coord(ch, el, tok, d);
+          vals[el] = isnew ? sk[tok * D + d] : E(0);
+        }
+        kt[ch] = *reinterpret_cast<uint4*>(vals);
+      }
+    }
+    // V: a chunk holds four consecutive tokens
+    {
+      bool anynew = false;
+#pragma unroll
+      for (int el = 0; el < PC; ++el) {
+        int tok, d;
+        L::v_coord(ch, el, tok, d);
+        anynew |= tok >= slot_lo && tok < hi;
+      }
+      if (anynew || fresh) {
+        E vals[PC];
+        if (!fresh) *reinterpret_cast<uint4*>(vals) = vt[ch];
+#pragma unroll
+        for (int el = 0; el < PC; ++el) {
+          int tok, d;
+          L::v_coord(ch, el, tok, d);
+          if (tok >= slot_lo && tok < hi) vals[el] = sv[tok * D + d];
+          else if (fresh) vals[el] = E(0);
+        }
+        vt[ch] = *reinterpret_cast<uint4*>(vals);
+      }
+    }
+  }
+}
+
+template <int EB, int D>
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+  using L = Layout<EB>;
+  using E = typename Elem<EB>::T;
+  constexpr int PC = L::kPerChunk;
+  constexpr int NCH = 16 * D / PC;
+  constexpr int CPR = D / PC;
+  __shared__ __align__(16) E sk[16 * D];
+  __shared__ __align__(16) E sv[16 * D];
+  const int e = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
+  const size_t base = (static_cast<size_t>(a.blk[e]) * a.hkv + kvh) * (16 * D);
+  const uint4* kt = reinterpret_cast<const uint4*>(static_cast<const E*>(a.kpool) + base);
+  const uint4* vt = reinterpret_cast<const uint4*>(static_cast<const E*>(a.vpool) + base);
+  for (int ch = tid; ch < NCH; ch += 256) {
+    E kv[PC], vv[PC];
+    *reinterpret_cast<uint4*>(kv) = kt[ch];
+    *reinterpret_cast<uint4*>(vv) = vt[ch];
+#pragma unroll
+    for (int el = 0; el < PC; ++el) {
+      int tok, d;
+      L::k_coord(ch, el, tok, d);
+      sk[tok * D + d] = kv[el];
+      L::v_coord(ch, el, tok, d);
+      sv[tok * D + d] = vv[el];
+    }
+  }
+  __syncthreads();
+  const int valid = a.valid[e], pos = a.pos[e];
+  E* ko = static_cast<E*>(a.k_out);
+  E* vo = static_cast<E*>(a.v_out);
+  for (int idx = tid; idx < valid * CPR; idx += 256) {
+    const int t = idx / CPR, c = idx - t * CPR;
+    const size_t oo = (static_cast<size_t>(pos + t) * a.hkv + kvh) * D + c * PC;
+    *reinterpret_cast<uint4*>(ko + oo) = *reinterpret_cast<const uint4*>(&sk[t * D + c * PC]);
+    *reinterpret_cast<uint4*>(vo + oo) = *reinterpret_cast<const uint4*>(&sv[t * D + c * PC]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(int dtype, int head_dim, int32_t layers, const AppendArgs& args,
+                         hipStream_t stream) {
+  const dim3 grid(args.nent, args.hkv, layers);
+  if (dtype == 1 && head_dim == 128) hipLaunchKernelGGL((append_kernel<2, 128>), grid, dim3(256), 0, stream, args);
+  else if (dtype == 1 && head_dim == 64) hipLaunchKernelGGL((append_kernel<2, 64>), grid, dim3(256), 0, stream, args);
+  else if (dtype == 0 && head_dim == 128) hipLaunchKernelGGL((append_kernel<4, 128>), grid, dim3(256), 0, stream, args);
+  else if (dtype == 0 && head_dim == 64) hipLaunchKernelGGL((append_kernel<4, 64>), grid, dim3(256), 0, stream, args);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(int dtype, int head_dim, const GatherArgs& args, hipStream_t stream) {
+  const dim3 grid(args.nent, args.hkv, 1);
+  if (dtype == 1 && head_dim == 128) hipLaunchKernelGGL((gather_kernel<2, 128>), grid, dim3(256), 0, stream, args);
+  else if (dtype == 1 && head_dim == 64) hipLaunchKernelGGL((gather_kernel<2, 64>), grid, dim3(256), 0, stream, args);
+  else if (dtype == 0 && head_dim == 128) hipLaunchKernelGGL((gather_kernel<4, 128>), grid, dim3(256), 0, stream, args);
+  else if (dtype == 0 && head_dim == 64) hipLaunchKernelGGL((gather_kernel<4, 64>), grid, dim3(256), 0, stream, args);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace tkv

@@ -1,0 +1,324 @@
+#include "plan.h"
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+namespace tkv {
+
+namespace {
+
+struct LNode {
+  int32_t node = -1;    // tree node id
+  int32_t parent = -1;  // local index
+  int32_t pre = 0;      // DFS preorder index
+  int32_t root = 0;     // index of its tree's root in the root list
+  int64_t qcount = 0;   // queries in the subtree
+  std::vector<int32_t> children;
+  std::vector<int32_t> handles;  // batch indices whose tip is this node
+};
+
+struct Query {
+  int32_t handle;  // batch index
+  int32_t global;  // global query index (row of q / out)
+  int32_t pos;     // absolute position
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+void Plan::layout() {
+  size_t o = 0;
+  off_items = o;        o = align256(o + items.size() * sizeof(DevItem));
+  off_groups = o;       o = align256(o + groups.size() * sizeof(DevGroup));
+  off_gq = o;           o = align256(o + gq.size() * sizeof(int32_t));
+  off_gqpos = o;        o = align256(o + gqpos.size() * sizeof(int32_t));
+  off_blocks = o;       o = align256(o + blocks.size() * sizeof(DevBlock));
+  off_group_items = o;  o = align256(o + group_items.size() * sizeof(int32_t));
+  off_merge = o;        o = align256(o + merge.size() * sizeof(DevMerge));
+  bytes = o;
+}
+
+void Plan::serialise(void* dst) const {
+  char* p = static_cast<char*>(dst);
+  std::memcpy(p + off_items, items.data(), items.size() * sizeof(DevItem));
+  std::memcpy(p + off_groups, groups.data(), groups.size() * sizeof(DevGroup));
+  std::memcpy(p + off_gq, gq.data(), gq.size() * sizeof(int32_t));
+  std::memcpy(p + off_gqpos, gqpos.data(), gqpos.size() * sizeof(int32_t));
+  std::memcpy(p + off_blocks, blocks.data(), blocks.size() * sizeof(DevBlock));
+  std::memcpy(p + off_group_items, group_items.data(), group_items.size() * sizeof(int32_t));
+  std::memcpy(p + off_merge, merge.data(), merge.size() * sizeof(DevMerge));
+}
+
+int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
+               int32_t q_per_kv, int32_t num_kv_heads, const PlanOptions& opt, Plan* out) {
+  if (!seqs || nseq < 1 || !out || q_per_kv < 1 || q_per_kv > kMaxRows) return TKV_E_INVAL;
+  try {
+    // 1. handles and queries
+    std::vector<int32_t> tip(nseq), qn(nseq), qbase(nseq);
+    std::vector<int64_t> len(nseq);
+    int64_t total_q = 0;
+    for (int32_t i = 0; i < nseq; ++i) {
+      if (int rc = tree.resolve(seqs[i], &tip[i])) return rc;
+      const Node& t = tree.node(tip[i]);
+      len[i] = t.base + t.ntok;
+      qn[i] = nq ? nq[i] : 1;
+      if (len[i] == 0) return TKV_E_EMPTY;
+      if (qn[i] < 1 || qn[i] > len[i] || len[i] > INT32_MAX) return TKV_E_RANGE;
+      qbase[i] = static_cast<int32_t>(total_q);
+      total_q += qn[i];
+      if (total_q > INT32_MAX / 4) return TKV_E_RANGE;
+    }
+
+    // 2. local tree over the union of the paths
+    std::vector<int32_t> loc(tree.node_capacity(), -1);
+    std::vector<LNode> ln;
+    for (int32_t i = 0; i < nseq; ++i) {
+      int32_t prev = -1;
+      for (int32_t id = tip[i]; id >= 0; id = tree.node(id).parent) {
+        if (loc[id] >= 0) {
+          if (prev >= 0) ln[prev].parent = loc[id];
+          break;
+        }
+        loc[id] = static_cast<int32_t>(ln.size());
+        ln.emplace_back();
+        ln.back().node = id;
+        if (prev >= 0) ln[prev].parent = loc[id];
+        prev = loc[id];
+      }
+      ln[loc[tip[i]]].handles.push_back(i);
+    }
+    const int32_t nl = static_cast<int32_t>(ln.size());
+    std::vector<int32_t> roots;
+    for (int32_t k = 0; k < nl; ++k) {
+      if (ln[k].parent >= 0) ln[ln[k].parent].children.push_back(k);
+      else roots.push_back(k);
+    }
+    auto by_node = [&](int32_t a, int32_t b) { return ln[a].node < ln[b].node; };
+    std::sort(roots.begin(), roots.end(), by_node);
+    for (auto& n : ln) std::sort(n.children.begin(), n.children.end(), by_node);
+
+    // subtree query counts, bottom-up by depth
+    {
+      std::vector<int32_t> order(nl);
+      for (int32_t k = 0; k < nl; ++k) order[k] = k;
+      std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+        return tree.node(ln[a].node).depth > tree.node(ln[b].node).depth;
+      });
+      for (int32_t k : order) {
+        for (int32_t h : ln[k].handles) ln[k].qcount += qn[h];
+        if (ln[k].parent >= 0) ln[ln[k].parent].qcount += ln[k].qcount;
+      }
+    }
+    // DFS preorder
+    {
+      int32_t pre = 0;
+      std::vector<int32_t> st;
+      for (size_t r = 0; r < roots.size(); ++r) {
+        st.push_back(roots[r]);
+        while (!st.empty()) {
+          const int32_t k = st.back();
+          st.pop_back();
+          ln[k].pre = pre++;
+          ln[k].root = static_cast<int32_t>(r);
+          for (auto it = ln[k].children.rbegin(); it != ln[k].children.rend(); ++it) st.push_back(*it);
+        }
+      }
+    }
+
+    // 3. groups: subtrees with <= qg queries become units; units of one tree are
+    //    packed in DFS order up to qg queries
+    const int32_t rows = std::max(16, std::min<int32_t>(opt.max_rows, kMaxRows));
+    const int32_t qg = std::max(1, std::min(64, rows / q_per_kv));
+    auto queries_of_handle = [&](int32_t h, std::vector<Query>& dst) {
+      for (int32_t k = 0; k < qn[h]; ++k)
+        dst.push_back({h, qbase[h] + k, static_cast<int32_t>(len[h] - qn[h] + k)});
+    };
+    std::vector<std::vector<Query>> group_q;
+    std::vector<int32_t> group_root;
+    {
+      std::vector<int32_t> st, sub;
+      for (size_t r = 0; r < roots.size(); ++r) {
+        std::vector<std::vector<Query>> units;
+        st.push_back(roots[r]);
+        while (!st.empty()) {
+          const int32_t k = st.back();
+          st.pop_back();
+          if (ln[k].qcount <= qg) {
+            std::vector<Query> u;
+            sub.push_back(k);
+            while (!sub.empty()) {
+              const int32_t s = sub.back();
+              sub.pop_back();
+              for (int32_t h : ln[s].handles) queries_of_handle(h, u);
+              for (auto it = ln[s].children.rbegin(); it != ln[s].children.rend(); ++it) sub.push_back(*it);
+            }
+            if (!u.empty()) units.push_back(std::move(u));
+          } else {
+            std::vector<Query> own;
+            for (int32_t h : ln[k].handles) queries_of_handle(h, own);
+            for (size_t a = 0; a < own.size(); a += qg)
+              units.emplace_back(own.begin() + a, own.begin() + std::min(own.size(), a + qg));
+            for (auto it = ln[k].children.rbegin(); it != ln[k].children.rend(); ++it) st.push_back(*it);
+          }
+        }
+        std::vector<Query> cur;
+        for (auto& u : units) {
+          if (!cur.empty() && cur.size() + u.size() > (size_t)qg) {
+            group_q.push_back(std::move(cur));
+            group_root.push_back(static_cast<int32_t>(r));
+            cur.clear();
+          }
+          cur.insert(cur.end(), u.begin(), u.end());
+        }
+        if (!cur.empty()) {
+          group_q.push_back(std::move(cur));
+          group_root.push_back(static_cast<int32_t>(r));
+        }
+      }
+    }
+    const int32_t ngroups = static_cast<int32_t>(group_q.size());
+
+    // 4. per-group block lists
+    Plan& P = *out;
+    P = Plan();
+    P.nqueries = static_cast<int32_t>(total_q);
+    P.causal = nq != nullptr;
+    P.groups.resize(ngroups);
+    std::vector<int32_t> gblk_begin(ngroups), gblk_count(ngroups);
+    std::vector<uint64_t> mask(nl, 0);
+    std::vector<int32_t> touched;
+    std::vector<int32_t> query_group(total_q), query_j(total_q);
+    for (int32_t gi = 0; gi < ngroups; ++gi) {
+      const auto& qs = group_q[gi];
+      P.groups[gi].q_begin = static_cast<int32_t>(P.gq.size());
+      P.groups[gi].nq = static_cast<int32_t>(qs.size());
+      touched.clear();
+      for (size_t j = 0; j < qs.size(); ++j) {
+        P.gq.push_back(qs[j].global);
+        P.gqpos.push_back(qs[j].pos);
+        query_group[qs[j].global] = gi;
+        query_j[qs[j].global] = static_cast<int32_t>(j);
+        for (int32_t k = loc[tip[qs[j].handle]]; k >= 0; k = ln[k].parent) {
+          if (!mask[k]) touched.push_back(k);
+          mask[k] |= 1ull << j;
+        }
+      }
+      std::sort(touched.begin(), touched.end(), [&](int32_t a, int32_t b) { return ln[a].pre < ln[b].pre; });
+      gblk_begin[gi] = static_cast<int32_t>(P.blocks.size());
+      for (int32_t k : touched) {
+        const Node& nd = tree.node(ln[k].node);
+        const int32_t nb = static_cast<int32_t>(nd.blocks.size());
+        for (int32_t b = 0; b < nb; ++b) {
+          DevBlock e;
+          e.id = nd.blocks[b];
+          e.pos = static_cast<int32_t>(nd.base + 16 * (int64_t)b);
+          e.valid = (b == nb - 1) ? nd.tail_valid() : 16;
+          e.pad = 0;
+          e.mask = mask[k];
+          P.blocks.push_back(e);
+        }
+        mask[k] = 0;
+      }
+      gblk_count[gi] = static_cast<int32_t>(P.blocks.size()) - gblk_begin[gi];
+    }
+
+    // 5. split-K chunking and items
+    int64_t total_entries = 0;
+    for (int32_t gi = 0; gi < ngroups; ++gi) total_entries += gblk_count[gi];
+    const int64_t tw = std::max<int32_t>(1, opt.target_wgs);
+    const int64_t chunk = std::max<int64_t>(std::max<int32_t>(1, opt.min_chunk),
+                                            (total_entries * num_kv_heads + tw - 1) / tw);
+    struct Tmp {
+      DevItem it;
+      int32_t tiles, root, chunk;
+    };
+    std::vector<Tmp> tmp;
+    std::vector<int32_t> gchunks(ngroups);
+    int64_t slots = 0;
+    for (int32_t gi = 0; gi < ngroups; ++gi) {
+      const int32_t nb = gblk_count[gi];
+      const int32_t nc = static_cast<int32_t>(std::max<int64_t>(1, (nb + chunk - 1) / chunk));
+      gchunks[gi] = nc;
+      const int32_t tiles = (P.groups[gi].nq * q_per_kv + 15) / 16;
+      int32_t at = 0;
+      for (int32_t c = 0; c < nc; ++c) {
+        const int32_t cnt = nb / nc + (c < nb % nc ? 1 : 0);
+        Tmp t;
+        t.it.group = gi;
+        t.it.blk_begin = gblk_begin[gi] + at;
+        t.it.blk_count = cnt;
+        if (nc == 1) {
+          t.it.part_base = -1;
+        } else {
+          t.it.part_base = static_cast<int32_t>(slots);
+          slots += static_cast<int64_t>(P.groups[gi].nq) * q_per_kv * num_kv_heads;
+          if (slots > INT32_MAX) return TKV_E_RANGE;
+        }
+        t.tiles = tiles;
+        t.root = group_root[gi];
+        t.chunk = c;
+        tmp.push_back(t);
+        at += cnt;
+      }
+    }
+    P.partial_slots = slots;
+    // order: by row-tile bucket, then items that read the same blocks next to each
+    // other (same tree, same chunk index), so the KV heads' workgroups of
+    // neighbouring items share L2
+    std::stable_sort(tmp.begin(), tmp.end(), [](const Tmp& a, const Tmp& b) {
+      if (a.tiles != b.tiles) return a.tiles < b.tiles;
+      if (a.root != b.root) return a.root < b.root;
+      if (a.chunk != b.chunk) return a.chunk < b.chunk;
+      return a.it.group < b.it.group;
+    });
+    P.items.resize(tmp.size());
+    for (int t = 0; t < 5; ++t) P.bucket_begin[t] = 0;
+    std::vector<std::vector<int32_t>> gitems(ngroups);
+    for (size_t k = 0; k < tmp.size(); ++k) {
+      P.items[k] = tmp[k].it;
+      gitems[tmp[k].it.group].push_back(static_cast<int32_t>(k));
+    }
+    for (int t = 1; t <= 4; ++t) {
+      int32_t cnt = 0;
+      for (const auto& x : tmp) cnt += (x.tiles <= t);
+      P.bucket_begin[t] = cnt;
+    }
+    std::vector<int32_t> gi_begin(ngroups);
+    for (int32_t gi = 0; gi < ngroups; ++gi) {
+      gi_begin[gi] = static_cast<int32_t>(P.group_items.size());
+      P.group_items.insert(P.group_items.end(), gitems[gi].begin(), gitems[gi].end());
+    }
+    P.merge.resize(total_q);
+    for (int64_t q = 0; q < total_q; ++q) {
+      const int32_t gi = query_group[q];
+      DevMerge m;
+      m.gi_begin = gi_begin[gi];
+      m.gi_count = gchunks[gi] > 1 ? gchunks[gi] : 0;
+      m.j = query_j[q];
+      m.pad = 0;
+      P.merge[q] = m;
+      if (m.gi_count) P.any_merge = true;
+    }
+
+    // statistics: distinct blocks read and their valid slots
+    {
+      std::vector<std::pair<int32_t, int32_t>> ids;
+      ids.reserve(P.blocks.size());
+      for (const auto& b : P.blocks) ids.push_back({b.id, b.valid});
+      std::sort(ids.begin(), ids.end());
+      ids.erase(std::unique(ids.begin(), ids.end(),
+                            [](const auto& a, const auto& b) { return a.first == b.first; }),
+                ids.end());
+      P.unique_blocks = static_cast<int32_t>(ids.size());
+      for (const auto& x : ids) P.unique_tokens += x.second;
+    }
+    P.layout();
+  } catch (const std::bad_alloc&) {
+    return TKV_E_NOMEM;
+  }
+  return TKV_OK;
+}
+
+}  // namespace tkv

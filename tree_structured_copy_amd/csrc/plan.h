@@ -1,0 +1,62 @@
+// Host planner: turns a batch of handles (and query counts) into the work list
+// the attention kernels run.
+//
+// The article (ainews.cool, "technical deep dive") has attention walk the tree,
+// reading K/V from the shared ancestor path and the branch's leaf path.  Reading
+// that literally per query would fetch a shared prefix once per branch and per
+// query head.  The planner instead:
+//   1. collects the union of the batch's paths as a tree of nodes;
+//   2. cuts it into groups of queries (at most kMaxRows rows = queries x heads per
+//      KV head) that lie close together in the tree, never mixing independent
+//      trees, so that one pass over a group's blocks serves all its rows;
+//   3. lists each group's blocks once (root first, in position order), with a
+//      mask of the group's queries that can see each block;
+//   4. splits long lists into work items (split-K), one workgroup per item and
+//      KV head, and records where each query's partial results go.
+#pragma once
+#include <stdint.h>
+
+#include <vector>
+
+#include "tkv_types.h"
+#include "tree.h"
+
+namespace tkv {
+
+struct PlanOptions {
+  int32_t target_wgs = 2048;
+  int32_t min_chunk = 16;
+  int32_t max_rows = kMaxRows;
+};
+
+struct Plan {
+  // items sorted by row-tile count; bucket t (1..4) = items [bucket_begin[t-1], bucket_begin[t])
+  std::vector<DevItem> items;
+  int32_t bucket_begin[5] = {0, 0, 0, 0, 0};
+  std::vector<DevGroup> groups;
+  std::vector<int32_t> gq;
+  std::vector<int32_t> gqpos;
+  std::vector<DevBlock> blocks;
+  std::vector<int32_t> group_items;
+  std::vector<DevMerge> merge;
+  int32_t nqueries = 0;
+  int64_t partial_slots = 0;  // records of (m, l, acc[D])
+  bool any_merge = false;
+  bool causal = false;
+  // statistics
+  int32_t unique_blocks = 0;
+  int64_t unique_tokens = 0;
+
+  // serialised layout (byte offsets into one device buffer)
+  size_t off_items = 0, off_groups = 0, off_gq = 0, off_gqpos = 0, off_blocks = 0,
+         off_group_items = 0, off_merge = 0, bytes = 0;
+  void layout();
+  void serialise(void* dst) const;
+};
+
+// Build the plan for a decode (nq == nullptr) or verify call.  Validates the
+// handles (TKV_E_BADSEQ), query counts (TKV_E_RANGE) and emptiness (TKV_E_EMPTY).
+int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
+               int32_t q_per_kv, int32_t num_kv_heads, const PlanOptions& opt, Plan* out);
+
+}  // namespace tkv

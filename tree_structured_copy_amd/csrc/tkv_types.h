@@ -1,0 +1,111 @@
+// Plain structs shared by the host planner and the HIP kernels.
+#pragma once
+#include <stdint.h>
+
+namespace tkv {
+
+constexpr int kBlock = 16;          // token slots per block
+constexpr int kMaxRows = 64;        // rows (queries x heads-per-kv-head) per group
+constexpr int kWaves = 4;           // waves per attention workgroup
+constexpr int kAppendMaxBlocks = 128;
+constexpr int kGatherMaxBlocks = 64;
+
+// One work item: a contiguous run of a group's block list, processed by one
+// workgroup per KV head.  part_base < 0: the item covers its group's whole list
+// and writes normalised outputs directly; otherwise it writes fp32 partial
+// records (m, l, acc) at slots part_base + j * Hq + h.
+struct DevItem {
+  int32_t group;
+  int32_t blk_begin;
+  int32_t blk_count;
+  int32_t part_base;
+};
+
+// A query group: up to kMaxRows rows that share one pass over the union of
+// their paths.  Its queries are gq[q_begin .. q_begin + nq).
+struct DevGroup {
+  int32_t q_begin;
+  int32_t nq;
+  int32_t pad0;
+  int32_t pad1;
+};
+
+// One block on a group's path list.  mask bit j = group query j can see the
+// block; pos = absolute position of slot 0; valid = slots in use.
+struct DevBlock {
+  int32_t id;
+  int32_t pos;
+  int32_t valid;
+  int32_t pad;
+  uint64_t mask;
+};
+
+// Per query: where its partial records are (items group_items[gi_begin ..
+// gi_begin + gi_count), query index j inside its group).  gi_count == 0: the
+// query's output was written directly.
+struct DevMerge {
+  int32_t gi_begin;
+  int32_t gi_count;
+  int32_t j;
+  int32_t pad;
+};
+
+struct AttnArgs {
+  const void* kpool;  // layer base
+  const void* vpool;
+  const void* q;
+  float* out;
+  const DevItem* items;
+  const DevGroup* groups;
+  const int32_t* gq;     // global query index per group slot
+  const int32_t* gqpos;  // absolute position limit per group slot
+  const DevBlock* blocks;
+  float* part_acc;       // [slots][D]
+  float* part_ml;        // [slots][2]
+  int32_t hq;
+  int32_t hkv;
+  int32_t gsize;         // Hq / Hkv
+  int32_t item0;         // first item of this launch
+  float scale_log2;      // log2(e) / sqrt(D)
+  int32_t pad;
+};
+
+struct MergeArgs {
+  const DevItem* items;
+  const int32_t* group_items;
+  const DevMerge* merge;
+  const float* part_acc;
+  const float* part_ml;
+  float* out;
+  int32_t hq;
+  int32_t nq;
+};
+
+struct AppendArgs {
+  const void* src_k;   // [L][ntok][Hkv][D]
+  const void* src_v;
+  void* kpool;         // pool base (layer 0)
+  void* vpool;
+  int64_t layer_stride;  // elements per layer of a pool
+  int32_t ntok;        // tokens in the source arrays
+  int32_t hkv;
+  int32_t nent;        // blocks in this launch
+  int32_t s0;          // first slot written in entry 0 (0 = entry 0 is a fresh block)
+  int32_t tok0;        // source token written into entry 0's slot s0
+  int32_t pad;
+  int32_t blk[kAppendMaxBlocks];
+};
+
+struct GatherArgs {
+  const void* kpool;   // layer base
+  const void* vpool;
+  void* k_out;         // [len][Hkv][D]
+  void* v_out;
+  int32_t hkv;
+  int32_t nent;
+  int32_t blk[kGatherMaxBlocks];
+  int32_t valid[kGatherMaxBlocks];
+  int32_t pos[kGatherMaxBlocks];
+};
+
+}  // namespace tkv

@@ -246,3 +246,64 @@ STANDARD = {
     "spec_verify": spec_verify,
     "full_depth": full_depth,
 }
+
+
+def random_tree_workload(name: str, *, seed: int, dtype: str = "bf16", q_heads: int = 8,
+                         kv_heads: int = 2, head_dim: int = 128, layers: int = 1, steps: int = 60,
+                         num_blocks: int = 400, max_append: int = 40, verify: bool = True) -> Workload:
+    """A random session of forks (at unaligned lengths), appends, truncations and
+    releases, ending with one decode over every live non-empty handle and, if
+    ``verify``, one verify over a subset.  Random choices come from stream
+    (KIND_SHAPE, 1000 + seed) so the recipe is reproducible.  Appends that would
+    not fit in ``num_blocks`` are skipped, so the recipe never fails."""
+    st = gen.stream_id(gen.KIND_SHAPE, 1000 + seed)
+    ctr = itertools.count()
+
+    def rnd(n):
+        return gen.uniform_int(seed, st, next(ctr), n)
+
+    nm = _Names()
+    ops: List[tuple] = []
+    call = 0
+    live = {}      # name -> length
+    frozen_at = {}  # name -> length below which its tokens are shared
+    own_blocks = {}  # name -> blocks held by its own node (rough bound for the budget)
+    used = 0
+    r = nm()
+    ops.append(("new", r)); live[r] = 0; frozen_at[r] = 0
+    for _ in range(steps):
+        names = sorted(live)
+        choice = rnd(10)
+        h = names[rnd(len(names))]
+        if choice < 4:
+            n = 1 + rnd(max_append)
+            need = (n + 15) // 16 + 1
+            if used + need > num_blocks - 2:
+                continue
+            ops.append(("append", h, n, call)); call += 1
+            live[h] += n
+            used += need
+        elif choice < 6 and len(live) < 24:
+            k = 1 + rnd(3)
+            kids = [nm() for _ in range(k)]
+            ops.append(("fork", h, k, kids))
+            frozen_at[h] = live[h]
+            for c in kids:
+                live[c] = live[h]; frozen_at[c] = live[h]
+        elif choice < 8 and live[h] > frozen_at[h]:
+            L = frozen_at[h] + rnd(live[h] - frozen_at[h] + 1)
+            ops.append(("truncate", h, L)); live[h] = L
+        elif len(live) > 2:
+            ops.append(("release", h)); del live[h]
+    nonempty = [h for h in sorted(live) if live[h] > 0]
+    if not nonempty:
+        ops.append(("append", r if r in live else sorted(live)[0], 5, call)); call += 1
+        nonempty = [r if r in live else sorted(live)[0]]
+    for layer in range(layers):
+        ops.append(("decode", layer, nonempty, 100 + layer))
+    if verify:
+        vs = nonempty[::2]
+        nqs = [1 + rnd(min(8, live[h])) for h in vs]
+        ops.append(("verify", 0, vs, nqs, 200))
+    return Workload(name, dtype, layers, q_heads, kv_heads, head_dim, num_blocks, ops, seed=seed,
+                    description="random fork/append/truncate/release session")
