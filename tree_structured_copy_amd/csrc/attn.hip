@@ -45,7 +45,19 @@ __device__ inline To bitcast(const From& f) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// bf16 inputs: S^T via 16x16x32 bf16 MFMAs, O^T via 16x16x16 bf16 MFMAs.
+// Wait states between an MFMA chain and the first VALU / accvgpr read of its
+// result.  For v_mfma_f32_16x16x4_f32 on gfx950 the compiler's hazard model
+// leaves too few (the last accumulator register was read before the final MFMA
+// had written it: measured as missing terms in one score element), so the
+// distance is enforced here: 24 wait states, more than the 19 that the longest
+// (16-pass) XDL result needs, with scheduling barriers so nothing moves across.
+__device__ inline void mfma_result_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// bf16 inputs: S^T and O^T via 16x16x32 bf16 MFMAs.
 struct BF16 {
   using elem = uint16_t;
   template <int D>
@@ -76,23 +88,25 @@ struct BF16 {
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(k.v[kk]), bitcast<bf16x8>(q.v[kk]), s, 0, 0, 0);
     return s;
   }
-  // acc[dt] += V^T[16dt..16dt+15][4 tokens] . P^T; the weights are rounded to
-  // bf16 once and the same rounded values are summed into l.
+  // acc[dt] += V^T[16dt..16dt+15][4 tokens] . P^T.  A weight p is split into
+  // bf16 hi = bf16(p) and lo = bf16(p - hi), so hi + lo carries p to about
+  // 2^-17 relative; one 16x16x32 MFMA per d-tile takes k = (4 tokens, hi) and
+  // (the same 4 tokens, lo), with the lane's V^T fragment given twice.
   template <int D>
   __device__ static void pv(const Frag<D>& v, const float* p, f32x4* acc, float& l) {
-    const __bf16 b0 = static_cast<__bf16>(p[0]), b1 = static_cast<__bf16>(p[1]);
-    const __bf16 b2 = static_cast<__bf16>(p[2]), b3 = static_cast<__bf16>(p[3]);
-    l += (static_cast<float>(b0) + static_cast<float>(b1)) + (static_cast<float>(b2) + static_cast<float>(b3));
-    i16x4 pp;
-    pp[0] = bitcast<short>(b0);
-    pp[1] = bitcast<short>(b1);
-    pp[2] = bitcast<short>(b2);
-    pp[3] = bitcast<short>(b3);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+    bf16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 hi = static_cast<__bf16>(p[i]);
+      pb[i] = hi;
+      pb[4 + i] = static_cast<__bf16>(p[i] - static_cast<float>(hi));
+    }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const u32x4 w = v.v[dt >> 1];
-      const u32x2 half = (dt & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y};
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<i16x4>(half), pp, acc[dt], 0, 0, 0);
+      const u32x4 a = (dt & 1) ? u32x4{w.z, w.w, w.z, w.w} : u32x4{w.x, w.y, w.x, w.y};
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(a), pb, acc[dt], 0, 0, 0);
     }
   }
 };
@@ -127,6 +141,7 @@ struct F32 {
     for (int c = 0; c < D / 16; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_mfma_f32_16x16x4f32(k.v[c][j], q.v[c][j], s, 0, 0, 0);
+    mfma_result_fence();
     return s;
   }
   template <int D>
@@ -246,6 +261,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     }
   }
 
+  mfma_result_fence();
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     l[t] += __shfl_xor(l[t], 16);
