@@ -68,22 +68,34 @@ def _call(item, stream):
         tkv.tkv_attend_verify(lib.c, op[1], seqs, nq, q, out, ws, need, stream)
 
 
-def _time_steps(items, steps, warmup):
+def _time_wall(items, steps, warmup):
+    """Wall time per step: K calls back to back, synchronised on both sides, no
+    profiling events in the stream."""
     import torch
-    from tree_structured_copy_amd import tkv
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(warmup):
         _call(items[i % len(items)], stream)
-    torch.cuda.synchronize()
-    for it in items:
-        tkv.tkv_profile_read(it[0].c)
-        tkv.tkv_profile_enable(it[0].c, True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         _call(items[i % len(items)], stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    return (t1 - t0) / steps * 1e3
+
+
+def _time_kernels(items, steps):
+    """Average device time of the partial-attention and merge kernels per call,
+    from HIP events the library records around them on the call's stream."""
+    import torch
+    from tree_structured_copy_amd import tkv
+    stream = torch.cuda.current_stream().cuda_stream
+    for it in items:
+        tkv.tkv_profile_read(it[0].c)
+        tkv.tkv_profile_enable(it[0].c, True)
+    for i in range(steps):
+        _call(items[i % len(items)], stream)
+    torch.cuda.synchronize()
     part = merge = 0.0
     calls = 0
     for it in items:
@@ -92,7 +104,21 @@ def _time_steps(items, steps, warmup):
         part += p
         merge += m
         calls += n
-    return (t1 - t0) / steps * 1e3, part / max(1, calls), merge / max(1, calls)
+    return part / max(1, calls), merge / max(1, calls)
+
+
+def _time_rebuild(items, steps):
+    """Wall time per step when every call rebuilds and uploads its plan (plan
+    cache off): the cost a caller pays when the tree changed since the last call."""
+    import torch
+    from tree_structured_copy_amd import tkv
+    for it in items:
+        tkv.tkv_set_option(it[0].c, tkv.TKV_OPT_PLAN_CACHE, 0)
+    ms = _time_wall(items, steps, 2)
+    for it in items:
+        tkv.tkv_set_option(it[0].c, tkv.TKV_OPT_PLAN_CACHE, 1)
+    torch.cuda.synchronize()
+    return ms
 
 
 def _fork_latency_ns():
@@ -179,7 +205,7 @@ def main():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-requests", type=int, default=8)
+    ap.add_argument("--cpu-requests", type=int, default=32)
     ap.add_argument("--cpu-reps", type=int, default=3)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -196,7 +222,9 @@ def main():
     items = _prepare(wl, args.copies)
     op = items[0][1]
     info, ubytes = _unique_kv_bytes(items[0][0], op, wl)
-    ms, part_ms, merge_ms = _time_steps(items, args.steps, args.warmup)
+    ms = _time_wall(items, args.steps, args.warmup)
+    part_ms, merge_ms = _time_kernels(items, args.steps)
+    rebuild_ms = _time_rebuild(items, max(5, args.steps // 5))
     value = ubytes / (ms / 1e3) / 1e9
     achieved = ubytes / (part_ms / 1e3) / 1e9 if part_ms > 0 else None
     nq = len(op[2])
@@ -211,7 +239,8 @@ def main():
         vitems = _prepare(vwl, args.copies)
         vop = vitems[0][1]
         vinfo, vbytes = _unique_kv_bytes(vitems[0][0], vop, vwl)
-        vms, vpart, vmerge = _time_steps(vitems, args.steps, args.warmup)
+        vms = _time_wall(vitems, args.steps, args.warmup)
+        vpart, vmerge = _time_kernels(vitems, args.steps)
         ntok = sum(vop[3])
         verify = {"workload": "spec_verify", "verify_tokens_per_s": ntok / (vms / 1e3),
                   "ms_per_step": vms, "unique_kv_GBps": vbytes / (vms / 1e3) / 1e9,
@@ -244,11 +273,12 @@ def main():
                    "decode_queries": nq, "copies_rotated": args.copies},
         "hbm_peak_frac": value / HBM_PEAK_GBS,
         "branch_queries_per_s": nq / (ms / 1e3),
+        "ms_per_step_plan_rebuild": rebuild_ms,
         "unique_kv_bytes": ubytes,
         "plan": info,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
-                     "kernel": "attn_partial_kernel<BF16,128,1,false>", "kernel_ms": part_ms,
+                     "kernel": "attn_partial_kernel<BF16,128,1,4,false>", "kernel_ms": part_ms,
                      "merge_kernel_ms": merge_ms},
         "verify": verify,
         "fork_latency_ns_ctypes": _fork_latency_ns(),

@@ -187,10 +187,11 @@ int tkv_plan_info_get(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int3
 
 /* ---- tuning knobs (keys) ---- */
 enum {
-  TKV_OPT_TARGET_WGS = 1,   /* workgroups an attention call aims for (default 2048) */
-  TKV_OPT_MIN_CHUNK = 2,    /* fewest blocks per work item (default 16) */
+  TKV_OPT_TARGET_WGS = 1,   /* workgroups an attention call aims for (default: the device's CU count) */
+  TKV_OPT_MIN_CHUNK = 2,    /* fewest blocks per work item (default 32) */
   TKV_OPT_MAX_ROWS = 3,     /* max rows (queries x Hq/Hkv) per group: 16..64 (default 64) */
-  TKV_OPT_PLAN_CACHE = 4    /* 1 = reuse uploaded plans while the tree is unchanged (default) */
+  TKV_OPT_PLAN_CACHE = 4,   /* 1 = reuse uploaded plans while the tree is unchanged (default) */
+  TKV_OPT_WAVES = 5         /* waves per attention workgroup: 4 or 8 (0 = default, 4) */
 };
 int tkv_set_option(tkv_cache* c, int32_t key, int64_t value);
 int tkv_get_option(const tkv_cache* c, int32_t key, int64_t* value);

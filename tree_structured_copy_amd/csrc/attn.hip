@@ -68,7 +68,7 @@ struct BF16 {
   __device__ static void load_tile(Frag<D>& f, const elem* tile, int lane) {
     const u32x4* p = reinterpret_cast<const u32x4*>(tile) + lane;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) f.v[i] = p[i * 64];
+    for (int i = 0; i < D / 32; ++i) f.v[i] = __builtin_nontemporal_load(p + i * 64);
   }
   template <int D>
   __device__ static void load_q(Frag<D>& f, const elem* row, int g) {
@@ -109,6 +109,31 @@ struct BF16 {
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(a), pb, acc[dt], 0, 0, 0);
     }
   }
+  // Two blocks at once: k = 4 tokens of block a and 4 of block b; one MFMA
+  // per d-tile for the hi parts of the weights and one for the lo parts.
+  template <int D>
+  __device__ static void pv2(const Frag<D>& va, const Frag<D>& vb, const float* p, f32x4* acc, float& l) {
+    l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    bf16x8 hi, lo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 h = static_cast<__bf16>(p[i]);
+      hi[i] = h;
+      lo[i] = static_cast<__bf16>(p[i] - static_cast<float>(h));
+    }
+    u32x4 av[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u32x4 wa = va.v[dt >> 1], wb = vb.v[dt >> 1];
+      av[dt] = (dt & 1) ? u32x4{wa.z, wa.w, wb.z, wb.w} : u32x4{wa.x, wa.y, wb.x, wb.y};
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[dt]), hi, acc[dt], 0, 0, 0);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[dt]), lo, acc[dt], 0, 0, 0);
+  }
 };
 
 // fp32 inputs: 16x16x4 fp32 MFMAs (full fp32 products and sums).
@@ -122,7 +147,7 @@ struct F32 {
   __device__ static void load_tile(Frag<D>& f, const elem* tile, int lane) {
     const f32x4* p = reinterpret_cast<const f32x4*>(tile) + lane;
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) f.v[i] = p[i * 64];
+    for (int i = 0; i < D / 16; ++i) f.v[i] = __builtin_nontemporal_load(p + i * 64);
   }
   template <int D>
   __device__ static void load_q(Frag<D>& f, const elem* row, int g) {
@@ -152,24 +177,107 @@ struct F32 {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.v[dt][i], p[i], acc[dt], 0, 0, 0);
   }
+  template <int D>
+  __device__ static void pv2(const Frag<D>& va, const Frag<D>& vb, const float* p, f32x4* acc, float& l) {
+    pv(va, p, acc, l);
+    pv(vb, p + 4, acc, l);
+  }
 };
 
-template <class P, int D, int T, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
+// Metadata of one super-block (two consecutive blocks of the item's list),
+// wave-uniform.  idb == ida and vb == 0 when the list has an odd tail.
+struct SBMeta {
+  int ida, idb;
+  int va, vb;
+  int pa, pb;
+  uint64_t ma, mb;
+};
+
+template <class P, int D, int T, int W, bool CAUSAL>
+__global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
   using E = typename P::elem;
   using F = typename P::template Frag<D>;
   constexpr int NDT = D / 16;
+  constexpr int NT = 64 * W;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
   const int kvh = blockIdx.x % a.hkv;
   const DevItem it = a.items[a.item0 + blockIdx.x / a.hkv];
+  const int nb = it.blk_count;
+  const int nsb = (nb + 1) >> 1;
+  // super-blocks of this wave: wave, wave + W, wave + 2W, ...
+  const int nmine = nsb > wave ? (nsb - wave + W - 1) / W : 0;
+  const DevBlock* bl = a.blocks + it.blk_begin;
+  const size_t tile = 16 * D;
+  const size_t bstride = static_cast<size_t>(a.hkv) * tile;
+  const E* kbase = static_cast<const E*>(a.kpool) + static_cast<size_t>(kvh) * tile;
+  const E* vbase = static_cast<const E*>(a.vpool) + static_cast<size_t>(kvh) * tile;
+
+  // Block-list entries of this wave, one per lane, 32 super-blocks per batch:
+  // lane j holds block 2 * (wave + W * (32 * batch + j / 2)) + j % 2.  Reading
+  // them with readlane keeps scalar-load latency out of the streaming loop.
+  int e_id = -1, e_valid = 0, e_pos = 0;
+  uint32_t e_mlo = 0, e_mhi = 0;
+  int cur_batch = -1;
+  auto load_entries = [&](int batch) {
+    const int sbk = 32 * batch + (lane >> 1);
+    const int b = 2 * (wave + W * sbk) + (lane & 1);
+    if (sbk < nmine && b < nb) {
+      const DevBlock e = bl[b];
+      e_id = e.id;
+      e_valid = e.valid;
+      e_pos = e.pos;
+      e_mlo = static_cast<uint32_t>(e.mask);
+      e_mhi = static_cast<uint32_t>(e.mask >> 32);
+    } else {
+      e_id = -1;
+      e_valid = 0;
+      e_pos = 0;
+      e_mlo = e_mhi = 0;
+    }
+    cur_batch = batch;
+  };
+  auto meta = [&](int k) {
+    if ((k >> 5) != cur_batch) load_entries(k >> 5);
+    const int ja = 2 * (k & 31), jb = ja + 1;
+    SBMeta m;
+    m.ida = __builtin_amdgcn_readlane(e_id, ja);
+    m.idb = __builtin_amdgcn_readlane(e_id, jb);
+    m.va = __builtin_amdgcn_readlane(e_valid, ja);
+    m.vb = __builtin_amdgcn_readlane(e_valid, jb);
+    m.pa = __builtin_amdgcn_readlane(e_pos, ja);
+    m.pb = __builtin_amdgcn_readlane(e_pos, jb);
+    m.ma = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(e_mhi, ja))) << 32) |
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(e_mlo, ja));
+    m.mb = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(e_mhi, jb))) << 32) |
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(e_mlo, jb));
+    if (m.idb < 0) {  // odd tail: reload block a, fully masked
+      m.idb = m.ida;
+      m.vb = 0;
+    }
+    return m;
+  };
+  auto load_sb = [&](F& ka, F& va, F& kb, F& vb, const SBMeta& m) {
+    P::load_tile(ka, kbase + static_cast<size_t>(m.ida) * bstride, lane);
+    P::load_tile(kb, kbase + static_cast<size_t>(m.idb) * bstride, lane);
+    P::load_tile(va, vbase + static_cast<size_t>(m.ida) * bstride, lane);
+    P::load_tile(vb, vbase + static_cast<size_t>(m.idb) * bstride, lane);
+  };
+
+  F kA0, vA0, kA1, vA1, kB0, vB0, kB1, vB1;
+  SBMeta mA, mB;
+  if (nmine > 0) {
+    mA = meta(0);
+    load_sb(kA0, vA0, kA1, vA1, mA);
+  }
+
+  // queries: row R = 16 t + r of the group is query R / G, head kvh * G + R % G
   const DevGroup gr = a.groups[it.group];
   const int G = a.gsize;
   const int nrows = gr.nq * G;
   const uint64_t gmask = gr.nq >= 64 ? ~0ull : ((1ull << gr.nq) - 1);
-
   F qf[T];
   int qj[T], qlim[T];
 #pragma unroll
@@ -198,31 +306,38 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  const DevBlock* bl = a.blocks + it.blk_begin;
-  const int nb = it.blk_count;
-  const int nmine = nb > wave ? (nb - wave + kWaves - 1) / kWaves : 0;
-  const size_t tile = 16 * D;
-  const size_t bstride = static_cast<size_t>(a.hkv) * tile;
-  const E* kb = static_cast<const E*>(a.kpool) + static_cast<size_t>(kvh) * tile;
-  const E* vb = static_cast<const E*>(a.vpool) + static_cast<size_t>(kvh) * tile;
   const float sl2 = a.scale_log2;
+  const int min_lim = gr.min_pos;
 
-  auto process = [&](const F& kf, const F& vf, const DevBlock& e) {
-    const bool all_see = (e.mask & gmask) == gmask;
+  auto process = [&](const F& ka, const F& va, const F& kb, const F& vb, const SBMeta& e) {
+    const bool see_a = (e.ma & gmask) == gmask, see_b = (e.mb & gmask) == gmask;
+    const bool need_mask = e.va < 16 || e.vb < 16 || !see_a || !see_b || (CAUSAL && e.pb + 15 > min_lim) ||
+                           (CAUSAL && e.pa + 15 > min_lim);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const f32x4 s = P::qk(kf, qf[t]);
-      float sc[4];
+      const f32x4 sa = P::qk(ka, qf[t]);
+      const f32x4 sb = P::qk(kb, qf[t]);
+      float sc[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = 4 * g + i;
-        bool ok = tok < e.valid;
-        if (!all_see) ok = ok && ((e.mask >> qj[t]) & 1ull);
-        if (CAUSAL) ok = ok && (e.pos + tok <= qlim[t]);
-        sc[i] = ok ? s[i] * sl2 : kNegInf;
+        sc[i] = sa[i] * sl2;
+        sc[4 + i] = sb[i] * sl2;
       }
-      float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      if (need_mask) {
+        const bool qa = ((e.ma >> qj[t]) & 1ull) != 0, qb = ((e.mb >> qj[t]) & 1ull) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 4 * g + i;
+          bool oka = tok < e.va && qa, okb = tok < e.vb && qb;
+          if (CAUSAL) {
+            oka = oka && (e.pa + tok <= qlim[t]);
+            okb = okb && (e.pb + tok <= qlim[t]);
+          }
+          if (!oka) sc[i] = kNegInf;
+          if (!okb) sc[4 + i] = kNegInf;
+        }
+      }
+      float bm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
       const float mn = fmaxf(m[t], bm);
@@ -234,30 +349,22 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         m[t] = mn;
       }
       const float mu = (m[t] == kNegInf) ? 0.f : m[t];
-      float p[4];
+      float p[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - mu);
-      P::pv(vf, p, acc[t], l[t]);
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(sc[i] - mu);
+      P::pv2(va, vb, p, acc[t], l[t]);
     }
   };
 
   if (nmine > 0) {
-    F kA, vA, kB, vB;
-    DevBlock eA = bl[wave], eB;
-    P::load_tile(kA, kb + static_cast<size_t>(eA.id) * bstride, lane);
-    P::load_tile(vA, vb + static_cast<size_t>(eA.id) * bstride, lane);
     for (int k = 0; k < nmine; k += 2) {
-      const int k1 = min(k + 1, nmine - 1);
-      eB = bl[wave + k1 * kWaves];
-      P::load_tile(kB, kb + static_cast<size_t>(eB.id) * bstride, lane);
-      P::load_tile(vB, vb + static_cast<size_t>(eB.id) * bstride, lane);
-      process(kA, vA, eA);
+      mB = meta(min(k + 1, nmine - 1));
+      load_sb(kB0, vB0, kB1, vB1, mB);
+      process(kA0, vA0, kA1, vA1, mA);
       if (k + 1 >= nmine) break;
-      const int k2 = min(k + 2, nmine - 1);
-      eA = bl[wave + k2 * kWaves];
-      P::load_tile(kA, kb + static_cast<size_t>(eA.id) * bstride, lane);
-      P::load_tile(vA, vb + static_cast<size_t>(eA.id) * bstride, lane);
-      process(kB, vB, eB);
+      mA = meta(min(k + 2, nmine - 1));
+      load_sb(kA0, vA0, kA1, vA1, mA);
+      process(kB0, vB0, kB1, vB1, mB);
     }
   }
 
@@ -268,10 +375,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     l[t] += __shfl_xor(l[t], 32);
   }
 
-  // merge the four waves' states
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
-  __shared__ float s_acc[kWaves][D][17];
+  // merge the W waves' states through LDS, one row tile at a time
+  __shared__ float s_m[W][16];
+  __shared__ float s_l[W][16];
+  __shared__ float s_acc[W][D][17];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     if (16 * t >= nrows) break;
@@ -284,16 +391,16 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_acc[wave][16 * dt + 4 * g + i][r] = acc[t][dt][i];
     __syncthreads();
-    for (int o = tid; o < 16 * D; o += 256) {
+    for (int o = tid; o < 16 * D; o += NT) {
       const int rr = o / D, d = o - rr * D;
       const int R = 16 * t + rr;
       if (R >= nrows) continue;
       float M = s_m[0][rr];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][rr]);
+      for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w][rr]);
       float ls = 0.f, as = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float mw = s_m[w][rr];
         const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
         ls += s_l[w][rr] * f;
@@ -342,33 +449,36 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(MergeArgs a) {
   a.out[(static_cast<size_t>(q) * a.hq + h) * D + d] = as / ls;
 }
 
-template <class P, int D, bool C>
+template <class P, int D, int W, bool C>
 hipError_t launch_t(int tiles, const AttnArgs& args, int32_t n_items, hipStream_t s) {
-  const dim3 grid(n_items * args.hkv), block(256);
+  const dim3 grid(n_items * args.hkv), block(64 * W);
   switch (tiles) {
-    case 1: hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, C>), grid, block, 0, s, args); break;
-    case 2: hipLaunchKernelGGL((attn_partial_kernel<P, D, 2, C>), grid, block, 0, s, args); break;
-    case 3: hipLaunchKernelGGL((attn_partial_kernel<P, D, 3, C>), grid, block, 0, s, args); break;
-    case 4: hipLaunchKernelGGL((attn_partial_kernel<P, D, 4, C>), grid, block, 0, s, args); break;
+    case 1: hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, W, C>), grid, block, 0, s, args); break;
+    case 2: hipLaunchKernelGGL((attn_partial_kernel<P, D, 2, W, C>), grid, block, 0, s, args); break;
+    case 3: hipLaunchKernelGGL((attn_partial_kernel<P, D, 3, W, C>), grid, block, 0, s, args); break;
+    case 4: hipLaunchKernelGGL((attn_partial_kernel<P, D, 4, W, C>), grid, block, 0, s, args); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <class P, int D>
-hipError_t launch_c(int tiles, bool causal, const AttnArgs& args, int32_t n_items, hipStream_t s) {
-  return causal ? launch_t<P, D, true>(tiles, args, n_items, s) : launch_t<P, D, false>(tiles, args, n_items, s);
+hipError_t launch_c(int tiles, int waves, bool causal, const AttnArgs& args, int32_t n_items, hipStream_t s) {
+  if (waves == 8)
+    return causal ? launch_t<P, D, 8, true>(tiles, args, n_items, s) : launch_t<P, D, 8, false>(tiles, args, n_items, s);
+  return causal ? launch_t<P, D, 4, true>(tiles, args, n_items, s) : launch_t<P, D, 4, false>(tiles, args, n_items, s);
 }
 
 }  // namespace
 
-hipError_t launch_attn_partial(int dtype, int head_dim, int tiles, bool causal, const AttnArgs& args,
+hipError_t launch_attn_partial(int dtype, int head_dim, int tiles, int waves, bool causal, const AttnArgs& args,
                                int32_t n_items, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
-  if (dtype == 1 && head_dim == 128) return launch_c<BF16, 128>(tiles, causal, args, n_items, stream);
-  if (dtype == 1 && head_dim == 64) return launch_c<BF16, 64>(tiles, causal, args, n_items, stream);
-  if (dtype == 0 && head_dim == 128) return launch_c<F32, 128>(tiles, causal, args, n_items, stream);
-  if (dtype == 0 && head_dim == 64) return launch_c<F32, 64>(tiles, causal, args, n_items, stream);
+  if (waves != 4 && waves != 8) return hipErrorInvalidValue;
+  if (dtype == 1 && head_dim == 128) return launch_c<BF16, 128>(tiles, waves, causal, args, n_items, stream);
+  if (dtype == 1 && head_dim == 64) return launch_c<BF16, 64>(tiles, waves, causal, args, n_items, stream);
+  if (dtype == 0 && head_dim == 128) return launch_c<F32, 128>(tiles, waves, causal, args, n_items, stream);
+  if (dtype == 0 && head_dim == 64) return launch_c<F32, 64>(tiles, waves, causal, args, n_items, stream);
   return hipErrorInvalidValue;
 }
 

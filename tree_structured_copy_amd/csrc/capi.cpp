@@ -57,6 +57,7 @@ struct tkv_cache {
   PlanOptions opt;
   uint64_t opt_epoch = 1;
   bool plan_cache = true;
+  int32_t waves = 0;
   PlanSlot slots[kPlanSlots];
   uint64_t stamp = 0;
   // pinned staging for plan uploads
@@ -241,7 +242,8 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     const int32_t n = P.bucket_begin[t] - P.bucket_begin[t - 1];
     if (n <= 0) continue;
     a.item0 = P.bucket_begin[t - 1];
-    if (launch_attn_partial(c->cfg.dtype, c->cfg.head_dim, t, P.causal, a, n, stream) != hipSuccess)
+    const int w = c->waves ? c->waves : 4;
+    if (launch_attn_partial(c->cfg.dtype, c->cfg.head_dim, t, w, P.causal, a, n, stream) != hipSuccess)
       return TKV_E_DEVICE;
   }
   if (c->prof && ev[1]) (void)hipEventRecord(ev[1], stream);
@@ -307,9 +309,14 @@ int tkv_create(const tkv_config* cfg, tkv_cache** out) {
     return TKV_E_NOMEM;
   }
   cache->has_pools = c.k_pool != nullptr;
-  if (cache->has_pools && hipGetDevice(&cache->device) != hipSuccess) {
-    delete cache;
-    return TKV_E_DEVICE;
+  if (cache->has_pools) {
+    int cus = 0;
+    if (hipGetDevice(&cache->device) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cache->device) != hipSuccess) {
+      delete cache;
+      return TKV_E_DEVICE;
+    }
+    if (cus > 0) cache->opt.target_wgs = cus;
   }
   *out = cache;
   return TKV_OK;
@@ -488,6 +495,10 @@ int tkv_set_option(tkv_cache* c, int32_t key, int64_t value) {
     case TKV_OPT_PLAN_CACHE:
       c->plan_cache = value != 0;
       break;
+    case TKV_OPT_WAVES:
+      if (value != 0 && value != 4 && value != 8) return TKV_E_RANGE;
+      c->waves = static_cast<int32_t>(value);
+      break;
     default:
       return TKV_E_INVAL;
   }
@@ -502,6 +513,7 @@ int tkv_get_option(const tkv_cache* c, int32_t key, int64_t* value) {
     case TKV_OPT_MIN_CHUNK: *value = c->opt.min_chunk; break;
     case TKV_OPT_MAX_ROWS: *value = c->opt.max_rows; break;
     case TKV_OPT_PLAN_CACHE: *value = c->plan_cache ? 1 : 0; break;
+    case TKV_OPT_WAVES: *value = c->waves; break;
     default: return TKV_E_INVAL;
   }
   return TKV_OK;

@@ -7,8 +7,9 @@
 namespace tkv {
 
 // Partial attention over items [args.item0, args.item0 + n_items) whose groups
-// need `tiles` row tiles of 16; grid = n_items * Hkv workgroups of 256 threads.
-hipError_t launch_attn_partial(int dtype, int head_dim, int tiles, bool causal, const AttnArgs& args,
+// need `tiles` row tiles of 16; grid = n_items * Hkv workgroups of 64 * waves
+// threads (waves = 4 or 8).
+hipError_t launch_attn_partial(int dtype, int head_dim, int tiles, int waves, bool causal, const AttnArgs& args,
                                int32_t n_items, hipStream_t stream);
 
 // Log-sum-exp merge of split-K partials into out; grid = nq * Hq.

@@ -194,6 +194,10 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       const auto& qs = group_q[gi];
       P.groups[gi].q_begin = static_cast<int32_t>(P.gq.size());
       P.groups[gi].nq = static_cast<int32_t>(qs.size());
+      int32_t min_pos = INT32_MAX;
+      for (const auto& qq : qs) min_pos = std::min(min_pos, qq.pos);
+      P.groups[gi].min_pos = min_pos;
+      P.groups[gi].pad1 = 0;
       touched.clear();
       for (size_t j = 0; j < qs.size(); ++j) {
         P.gq.push_back(qs[j].global);

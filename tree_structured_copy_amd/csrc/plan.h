@@ -24,8 +24,8 @@
 namespace tkv {
 
 struct PlanOptions {
-  int32_t target_wgs = 2048;
-  int32_t min_chunk = 16;
+  int32_t target_wgs = 256;
+  int32_t min_chunk = 32;
   int32_t max_rows = kMaxRows;
 };
 

@@ -6,7 +6,6 @@ namespace tkv {
 
 constexpr int kBlock = 16;          // token slots per block
 constexpr int kMaxRows = 64;        // rows (queries x heads-per-kv-head) per group
-constexpr int kWaves = 4;           // waves per attention workgroup
 constexpr int kAppendMaxBlocks = 128;
 constexpr int kGatherMaxBlocks = 64;
 
@@ -22,11 +21,12 @@ struct DevItem {
 };
 
 // A query group: up to kMaxRows rows that share one pass over the union of
-// their paths.  Its queries are gq[q_begin .. q_begin + nq).
+// their paths.  Its queries are gq[q_begin .. q_begin + nq); min_pos is the
+// smallest position limit among them (keys at or below it are visible to all).
 struct DevGroup {
   int32_t q_begin;
   int32_t nq;
-  int32_t pad0;
+  int32_t min_pos;
   int32_t pad1;
 };
 

@@ -35,6 +35,7 @@ TKV_OPT_TARGET_WGS = 1
 TKV_OPT_MIN_CHUNK = 2
 TKV_OPT_MAX_ROWS = 3
 TKV_OPT_PLAN_CACHE = 4
+TKV_OPT_WAVES = 5
 
 STATUS_NAMES = {
     TKV_E_INVAL: "inval", TKV_E_NOMEM: "nomem", TKV_E_BADSEQ: "badseq", TKV_E_SHARED: "shared",
@@ -72,6 +73,15 @@ class tkv_plan_info(ctypes.Structure):
 
 
 def _load():
+    # One process must hold one HIP runtime.  torch ships its own copy of
+    # libamdhip64 and loads it by a file name that does not match the soname
+    # this library links against, so if libtkv.so came first a second runtime
+    # would be loaded behind torch.  Loading torch first lets libtkv.so bind to
+    # torch's runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(_LIB_PATH):
         raise ImportError("libtkv.so is not built (run __graft_entry__.build() or "
                           "python -m tree_structured_copy_amd.build): %s" % _LIB_PATH)
