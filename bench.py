@@ -32,40 +32,68 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 
 
-def _unique_kv_bytes(lib, op, wl):
-    from tree_structured_copy_amd import tkv
-    info = tkv.tkv_plan_info_get(lib.c, lib.handles(op), op[3] if op[0] == "verify" else None)
-    return info, info["unique_tokens"] * wl.kv_heads * wl.head_dim * wl.elem_bytes * 2
+class _Copy:
+    """One independent instance of a workload on the GPU: its tree, and every
+    attend call of one step (one per layer for multi-layer workloads) with its
+    query, output and workspace buffers."""
+
+    def __init__(self, wl):
+        import torch
+        from tree_structured_copy_amd import tkv
+        from tree_structured_copy_amd.replay import LibReplay
+        from workloads import device as wdev
+        self.wl = wl
+        self.lib = LibReplay(wl, "cuda")
+        i = self.lib.build()
+        self.ops = []
+        while i < len(wl.ops) and wl.ops[i][0] in ("decode", "verify"):
+            self.ops.append(wl.ops[i])
+            i += 1
+        self.calls = []
+        need = 0
+        for op in self.ops:
+            rows = self.lib.nrows(op)
+            q = wdev.q_tensor(wl, op[-1], rows)
+            out = torch.empty((rows, wl.q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+            nq = tkv.i32_array(op[3]) if op[0] == "verify" else None
+            seqs = tkv.seq_array(self.lib.handles(op))
+            need = max(need, tkv.tkv_workspace_size(self.lib.c, seqs, nq))
+            self.calls.append((op[1], seqs, nq, q, out))
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        self.need = need
+
+    def step(self, stream):
+        from tree_structured_copy_amd import tkv
+        c = self.lib.c
+        for layer, seqs, nq, q, out in self.calls:
+            if nq is None:
+                tkv.tkv_attend_decode(c, layer, seqs, q, out, self.ws, self.need, stream)
+            else:
+                tkv.tkv_attend_verify(c, layer, seqs, nq, q, out, self.ws, self.need, stream)
+
+    def unique_bytes(self):
+        from tree_structured_copy_amd import tkv
+        wl = self.wl
+        total = 0
+        infos = []
+        for layer, seqs, nq, q, out in self.calls:
+            info = tkv.tkv_plan_info_get(self.lib.c, seqs, nq)
+            infos.append(info)
+            total += info["unique_tokens"] * wl.kv_heads * wl.head_dim * wl.elem_bytes * 2
+        return total, infos[0]
+
+    def queries(self):
+        return sum(out.shape[0] for _, _, _, _, out in self.calls)
+
+    def close(self):
+        self.lib.close()
 
 
 def _prepare(wl, copies):
     import torch
-    from tree_structured_copy_amd import tkv
-    from tree_structured_copy_amd.replay import LibReplay
-    from workloads import device as wdev
-    items = []
-    for _ in range(copies):
-        lib = LibReplay(wl, "cuda")
-        i = lib.build()
-        op = wl.ops[i]
-        rows = lib.nrows(op)
-        q = wdev.q_tensor(wl, op[-1], rows)
-        out = torch.empty((rows, wl.q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
-        ws, need = lib.workspace(op)
-        seqs = tkv.seq_array(lib.handles(op))
-        nq = tkv.i32_array(op[3]) if op[0] == "verify" else None
-        items.append((lib, op, q, out, ws, need, seqs, nq))
+    items = [_Copy(wl) for _ in range(copies)]
     torch.cuda.synchronize()
     return items
-
-
-def _call(item, stream):
-    from tree_structured_copy_amd import tkv
-    lib, op, q, out, ws, need, seqs, nq = item
-    if nq is None:
-        tkv.tkv_attend_decode(lib.c, op[1], seqs, q, out, ws, need, stream)
-    else:
-        tkv.tkv_attend_verify(lib.c, op[1], seqs, nq, q, out, ws, need, stream)
 
 
 def _time_wall(items, steps, warmup):
@@ -74,11 +102,11 @@ def _time_wall(items, steps, warmup):
     import torch
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(warmup):
-        _call(items[i % len(items)], stream)
+        items[i % len(items)].step(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        _call(items[i % len(items)], stream)
+        items[i % len(items)].step(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return (t1 - t0) / steps * 1e3
@@ -91,16 +119,16 @@ def _time_kernels(items, steps):
     from tree_structured_copy_amd import tkv
     stream = torch.cuda.current_stream().cuda_stream
     for it in items:
-        tkv.tkv_profile_read(it[0].c)
-        tkv.tkv_profile_enable(it[0].c, True)
+        tkv.tkv_profile_read(it.lib.c)
+        tkv.tkv_profile_enable(it.lib.c, True)
     for i in range(steps):
-        _call(items[i % len(items)], stream)
+        items[i % len(items)].step(stream)
     torch.cuda.synchronize()
     part = merge = 0.0
     calls = 0
     for it in items:
-        p, m, n = tkv.tkv_profile_read(it[0].c)
-        tkv.tkv_profile_enable(it[0].c, False)
+        p, m, n = tkv.tkv_profile_read(it.lib.c)
+        tkv.tkv_profile_enable(it.lib.c, False)
         part += p
         merge += m
         calls += n
@@ -113,10 +141,10 @@ def _time_rebuild(items, steps):
     import torch
     from tree_structured_copy_amd import tkv
     for it in items:
-        tkv.tkv_set_option(it[0].c, tkv.TKV_OPT_PLAN_CACHE, 0)
+        tkv.tkv_set_option(it.lib.c, tkv.TKV_OPT_PLAN_CACHE, 0)
     ms = _time_wall(items, steps, 2)
     for it in items:
-        tkv.tkv_set_option(it[0].c, tkv.TKV_OPT_PLAN_CACHE, 1)
+        tkv.tkv_set_option(it.lib.c, tkv.TKV_OPT_PLAN_CACHE, 1)
     torch.cuda.synchronize()
     return ms
 
@@ -197,6 +225,32 @@ def _cpu_baseline(requests: int, reps: int):
             "branch_queries_per_s": 4 * requests / t}
 
 
+def measure(name, copies, steps, warmup, rebuild=False):
+    """Wall time per step, kernel times and derived rates for one workload."""
+    import torch
+    from workloads import recipes
+    wl = recipes.STANDARD[name]()
+    items = _prepare(wl, copies)
+    ubytes, info = items[0].unique_bytes()
+    queries = items[0].queries()
+    ms = _time_wall(items, steps, warmup)
+    part_ms, merge_ms = _time_kernels(items, steps)
+    ncalls = len(items[0].calls)
+    res = {"workload": name, "ms_per_step": ms, "attend_calls_per_step": ncalls,
+           "unique_kv_bytes": ubytes, "unique_kv_GBps": ubytes / (ms / 1e3) / 1e9,
+           "queries_per_step": queries, "queries_per_s": queries / (ms / 1e3),
+           "partial_kernel_ms_per_call": part_ms, "merge_kernel_ms_per_call": merge_ms,
+           "partial_kernel_GBps": (ubytes / ncalls) / (part_ms / 1e3) / 1e9 if part_ms > 0 else None,
+           "plan": info, "copies_rotated": copies}
+    if rebuild:
+        res["ms_per_step_plan_rebuild"] = _time_rebuild(items, max(5, steps // 5))
+    for it in items:
+        it.close()
+    del items
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +259,7 @@ def main():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also measure the MCTS and 32-layer workloads")
     ap.add_argument("--cpu-requests", type=int, default=32)
     ap.add_argument("--cpu-reps", type=int, default=3)
     args = ap.parse_args()
@@ -215,41 +270,24 @@ def main():
         sys.exit(2)
 
     import torch
-    from workloads import recipes
-
     torch.cuda.init()
-    wl = recipes.llama_fork()
-    items = _prepare(wl, args.copies)
-    op = items[0][1]
-    info, ubytes = _unique_kv_bytes(items[0][0], op, wl)
-    ms = _time_wall(items, args.steps, args.warmup)
-    part_ms, merge_ms = _time_kernels(items, args.steps)
-    rebuild_ms = _time_rebuild(items, max(5, args.steps // 5))
-    value = ubytes / (ms / 1e3) / 1e9
-    achieved = ubytes / (part_ms / 1e3) / 1e9 if part_ms > 0 else None
-    nq = len(op[2])
-    for it in items:
-        it[0].close()
-    del items
-    torch.cuda.empty_cache()
+
+    main_res = measure("llama_fork", args.copies, args.steps, args.warmup, rebuild=True)
+    ms = main_res["ms_per_step"]
+    ubytes = main_res["unique_kv_bytes"]
+    value = main_res["unique_kv_GBps"]
+    achieved = main_res["partial_kernel_GBps"]
 
     verify = None
     if not args.no_verify:
-        vwl = recipes.spec_verify()
-        vitems = _prepare(vwl, args.copies)
-        vop = vitems[0][1]
-        vinfo, vbytes = _unique_kv_bytes(vitems[0][0], vop, vwl)
-        vms = _time_wall(vitems, args.steps, args.warmup)
-        vpart, vmerge = _time_kernels(vitems, args.steps)
-        ntok = sum(vop[3])
-        verify = {"workload": "spec_verify", "verify_tokens_per_s": ntok / (vms / 1e3),
-                  "ms_per_step": vms, "unique_kv_GBps": vbytes / (vms / 1e3) / 1e9,
-                  "partial_kernel_ms": vpart, "merge_kernel_ms": vmerge,
-                  "partial_kernel_GBps": vbytes / (vpart / 1e3) / 1e9 if vpart > 0 else None}
-        for it in vitems:
-            it[0].close()
-        del vitems
-        torch.cuda.empty_cache()
+        v = measure("spec_verify", args.copies, args.steps, args.warmup)
+        v["verify_tokens_per_s"] = v["queries_per_s"]
+        verify = v
+    others = {}
+    if args.all:
+        others["mcts_tree"] = measure("mcts_tree", args.copies, args.steps, args.warmup)
+        others["full_depth"] = measure("full_depth", 1, max(3, args.steps // 10), 1)
+        others["full_depth"]["branch_query_steps_per_s"] = 1024 / (others["full_depth"]["ms_per_step"] / 1e3)
 
     cpu = None
     if not args.no_cpu:
@@ -270,17 +308,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama_fork", "requests": 32, "prefix_tokens": 4096, "fork_width": 4,
                    "branch_tokens": 64, "q_heads": 32, "kv_heads": 8, "head_dim": 128, "block_size": 16,
-                   "decode_queries": nq, "copies_rotated": args.copies},
+                   "decode_queries": main_res["queries_per_step"], "copies_rotated": args.copies},
         "hbm_peak_frac": value / HBM_PEAK_GBS,
-        "branch_queries_per_s": nq / (ms / 1e3),
-        "ms_per_step_plan_rebuild": rebuild_ms,
+        "branch_queries_per_s": main_res["queries_per_s"],
+        "ms_per_step_plan_rebuild": main_res["ms_per_step_plan_rebuild"],
         "unique_kv_bytes": ubytes,
-        "plan": info,
+        "plan": main_res["plan"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
-                     "kernel": "attn_partial_kernel<BF16,128,1,4,false>", "kernel_ms": part_ms,
-                     "merge_kernel_ms": merge_ms},
+                     "kernel": "attn_partial_kernel<BF16,128,1,4,false>",
+                     "kernel_ms": main_res["partial_kernel_ms_per_call"],
+                     "merge_kernel_ms": main_res["merge_kernel_ms_per_call"]},
         "verify": verify,
+        "other_workloads": others or None,
         "fork_latency_ns_ctypes": _fork_latency_ns(),
         "cpu_baseline": cpu,
     }

@@ -180,7 +180,7 @@ typedef struct tkv_plan_info {
   int32_t unique_blocks;   /* distinct blocks the call reads */
   int64_t unique_tokens;   /* valid token slots in those blocks */
   int64_t partial_slots;   /* fp32 partial records in the workspace */
-  int32_t rows_per_tile_hist[4]; /* items whose groups need 1, 2, 3, 4 row tiles */
+  int32_t items_per_kernel[6]; /* items run by each kernel shape: groups of 1, 2, 3-4, 5-6, 7-8, 9-16 row tiles */
 } tkv_plan_info;
 int tkv_plan_info_get(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
                       tkv_plan_info* out);
@@ -189,7 +189,7 @@ int tkv_plan_info_get(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int3
 enum {
   TKV_OPT_TARGET_WGS = 1,   /* workgroups an attention call aims for (default: the device's CU count) */
   TKV_OPT_MIN_CHUNK = 2,    /* fewest blocks per work item (default 32) */
-  TKV_OPT_MAX_ROWS = 3,     /* max rows (queries x Hq/Hkv) per group: 16..64 (default 64) */
+  TKV_OPT_MAX_ROWS = 3,     /* max rows (queries x Hq/Hkv) per group: 16..256 (default 256) */
   TKV_OPT_PLAN_CACHE = 4,   /* 1 = reuse uploaded plans while the tree is unchanged (default) */
   TKV_OPT_WAVES = 5         /* waves per attention workgroup: 4 or 8 (0 = default, 4) */
 };

@@ -59,6 +59,32 @@ def test_chunking_and_grouping_options(opts):
     assert_close(run_both(wl, options=opts), "bf16")
 
 
+@pytest.mark.parametrize("max_rows,cls", [(16, 0), (32, 1), (64, 2), (96, 3), (128, 4), (256, 5)])
+@pytest.mark.parametrize("kind", ["decode", "verify"])
+def test_every_kernel_class(max_rows, cls, kind):
+    """Group size decides the kernel: 1-2 row tiles in registers (attn.hip), 3-16
+    row tiles with K/V staged in LDS (attn_rows.hip).  Each class against the oracle."""
+    if kind == "decode":
+        wl = recipes.fork_workload("classes", dtype="bf16", layers=1, q_heads=16, kv_heads=4, head_dim=128,
+                                   requests=2, prefix=333, width=40, branch_tokens=5, seed=17)
+    else:
+        wl = recipes.verify_workload("classes_v", dtype="bf16", q_heads=16, kv_heads=4, head_dim=128,
+                                     requests=2, prefix=333, paths=8, drafts=7, seed=19)
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    need_gpu()
+    lib = LibReplay(wl)
+    try:
+        tkv.tkv_set_option(lib.c, tkv.TKV_OPT_MAX_ROWS, max_rows)
+        i = lib.build()
+        op = wl.ops[i]
+        info = tkv.tkv_plan_info_get(lib.c, lib.handles(op), op[3] if op[0] == "verify" else None)
+        assert info["items_per_kernel"][cls] > 0, info
+    finally:
+        lib.close()
+    assert_close(run_both(wl, options={3: max_rows}), "bf16")
+
+
 def test_many_queries_per_group_mha():
     """MHA with 64 branches: one group of 64 rows (4 row tiles)."""
     wl = recipes.fork_workload("mha64", dtype="bf16", layers=1, q_heads=4, kv_heads=4, head_dim=64,

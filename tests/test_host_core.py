@@ -346,7 +346,7 @@ def test_plan_shapes():
         assert info["groups"] == 32
         assert info["unique_blocks"] == 32 * 272
         assert info["block_entries"] == 32 * 272  # each block listed once
-        assert info["rows_per_tile_hist"][0] == info["items"]  # 16 rows per group -> 1 tile
+        assert info["items_per_kernel"][0] == info["items"]  # 16 rows per group -> 1 tile
         before = tkv.tkv_get_counters(c)["plans_built"]
         tkv.tkv_plan_info_get(c, seqs)
         assert tkv.tkv_get_counters(c)["plans_built"] == before  # cached

@@ -30,10 +30,13 @@ if not os.path.exists(CXX):
 
 DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The attention kernels never produce NaN (masked scores are -inf and every
+# exp / rescale guards the -inf - -inf case), so max() needs no NaN canonicalisation.
+ATTN_FLAGS = ["-fno-honor-nans"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
               "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]
 
-LIB_SOURCES = ["tree.cpp", "plan.cpp", "capi.cpp", "attn.hip", "kv.hip"]
+LIB_SOURCES = ["tree.cpp", "plan.cpp", "capi.cpp", "attn.hip", "attn_rows.hip", "kv.hip"]
 
 
 def _run(cmd, verbose):
@@ -50,7 +53,8 @@ def _run(cmd, verbose):
 
 def _compile(src: str, obj: str, verbose: bool):
     if src.endswith(".hip"):
-        cmd = [HIPCC] + DEVICE_FLAGS + ["-I" + INCLUDE, "-I" + CSRC, "-c", src, "-o", obj]
+        extra = ATTN_FLAGS if os.path.basename(src).startswith("attn") else []
+        cmd = [HIPCC] + DEVICE_FLAGS + extra + ["-I" + INCLUDE, "-I" + CSRC, "-c", src, "-o", obj]
     else:
         cmd = [CXX] + HOST_FLAGS + ["-I" + INCLUDE, "-I" + CSRC, "-c", src, "-o", obj]
     _run(cmd, verbose)

@@ -24,174 +24,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_common.h"
 #include "kernels.h"
 
 namespace tkv {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kNegInf = -__builtin_inff();
-constexpr float kTau = 8.0f;
-
-template <class To, class From>
-__device__ inline To bitcast(const From& f) {
-  return __builtin_bit_cast(To, f);
-}
-
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Wait states between an MFMA chain and the first VALU / accvgpr read of its
-// result.  For v_mfma_f32_16x16x4_f32 on gfx950 the compiler's hazard model
-// leaves too few (the last accumulator register was read before the final MFMA
-// had written it: measured as missing terms in one score element), so the
-// distance is enforced here: 24 wait states, more than the 19 that the longest
-// (16-pass) XDL result needs, with scheduling barriers so nothing moves across.
-__device__ inline void mfma_result_fence() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// bf16 inputs: S^T and O^T via 16x16x32 bf16 MFMAs.
-struct BF16 {
-  using elem = uint16_t;
-  template <int D>
-  struct Frag {
-    u32x4 v[D / 32];
-  };
-  template <int D>
-  __device__ static void load_tile(Frag<D>& f, const elem* tile, int lane) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(tile) + lane;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) f.v[i] = __builtin_nontemporal_load(p + i * 64);
-  }
-  template <int D>
-  __device__ static void load_q(Frag<D>& f, const elem* row, int g) {
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) f.v[kk] = *reinterpret_cast<const u32x4*>(row + 32 * kk + 8 * g);
-  }
-  template <int D>
-  __device__ static void zero(Frag<D>& f) {
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) f.v[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-  template <int D>
-  __device__ static f32x4 qk(const Frag<D>& k, const Frag<D>& q) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(k.v[kk]), bitcast<bf16x8>(q.v[kk]), s, 0, 0, 0);
-    return s;
-  }
-  // acc[dt] += V^T[16dt..16dt+15][4 tokens] . P^T.  A weight p is split into
-  // bf16 hi = bf16(p) and lo = bf16(p - hi), so hi + lo carries p to about
-  // 2^-17 relative; one 16x16x32 MFMA per d-tile takes k = (4 tokens, hi) and
-  // (the same 4 tokens, lo), with the lane's V^T fragment given twice.
-  template <int D>
-  __device__ static void pv(const Frag<D>& v, const float* p, f32x4* acc, float& l) {
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    bf16x8 pb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const __bf16 hi = static_cast<__bf16>(p[i]);
-      pb[i] = hi;
-      pb[4 + i] = static_cast<__bf16>(p[i] - static_cast<float>(hi));
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x4 w = v.v[dt >> 1];
-      const u32x4 a = (dt & 1) ? u32x4{w.z, w.w, w.z, w.w} : u32x4{w.x, w.y, w.x, w.y};
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(a), pb, acc[dt], 0, 0, 0);
-    }
-  }
-  // Two blocks at once: k = 4 tokens of block a and 4 of block b; one MFMA
-  // per d-tile for the hi parts of the weights and one for the lo parts.
-  template <int D>
-  __device__ static void pv2(const Frag<D>& va, const Frag<D>& vb, const float* p, f32x4* acc, float& l) {
-    l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    bf16x8 hi, lo;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 h = static_cast<__bf16>(p[i]);
-      hi[i] = h;
-      lo[i] = static_cast<__bf16>(p[i] - static_cast<float>(h));
-    }
-    u32x4 av[D / 16];
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x4 wa = va.v[dt >> 1], wb = vb.v[dt >> 1];
-      av[dt] = (dt & 1) ? u32x4{wa.z, wa.w, wb.z, wb.w} : u32x4{wa.x, wa.y, wb.x, wb.y};
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[dt]), hi, acc[dt], 0, 0, 0);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[dt]), lo, acc[dt], 0, 0, 0);
-  }
-};
-
-// fp32 inputs: 16x16x4 fp32 MFMAs (full fp32 products and sums).
-struct F32 {
-  using elem = float;
-  template <int D>
-  struct Frag {
-    f32x4 v[D / 16];
-  };
-  template <int D>
-  __device__ static void load_tile(Frag<D>& f, const elem* tile, int lane) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(tile) + lane;
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) f.v[i] = __builtin_nontemporal_load(p + i * 64);
-  }
-  template <int D>
-  __device__ static void load_q(Frag<D>& f, const elem* row, int g) {
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) f.v[c] = *reinterpret_cast<const f32x4*>(row + 16 * c + 4 * g);
-  }
-  template <int D>
-  __device__ static void zero(Frag<D>& f) {
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) f.v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  template <int D>
-  __device__ static f32x4 qk(const Frag<D>& k, const Frag<D>& q) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_mfma_f32_16x16x4f32(k.v[c][j], q.v[c][j], s, 0, 0, 0);
-    mfma_result_fence();
-    return s;
-  }
-  template <int D>
-  __device__ static void pv(const Frag<D>& v, const float* p, f32x4* acc, float& l) {
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.v[dt][i], p[i], acc[dt], 0, 0, 0);
-  }
-  template <int D>
-  __device__ static void pv2(const Frag<D>& va, const Frag<D>& vb, const float* p, f32x4* acc, float& l) {
-    pv(va, p, acc, l);
-    pv(vb, p + 4, acc, l);
-  }
-};
-
-// Metadata of one super-block (two consecutive blocks of the item's list),
-// wave-uniform.  idb == ida and vb == 0 when the list has an odd tail.
-struct SBMeta {
-  int ida, idb;
-  int va, vb;
-  int pa, pb;
-  uint64_t ma, mb;
-};
+using namespace attn;
 
 template <class P, int D, int T, int W, bool CAUSAL>
 __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
@@ -307,6 +146,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
     for (int dt = 0; dt < NDT; ++dt) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float sl2 = a.scale_log2;
+  const float tau_raw = kTau / sl2;  // the lazy-rescale threshold in raw score units
   const int min_lim = gr.min_pos;
 
   auto process = [&](const F& ka, const F& va, const F& kb, const F& vb, const SBMeta& e) {
@@ -320,8 +160,8 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
       float sc[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sc[i] = sa[i] * sl2;
-        sc[4 + i] = sb[i] * sl2;
+        sc[i] = sa[i];
+        sc[4 + i] = sb[i];
       }
       if (need_mask) {
         const bool qa = ((e.ma >> qj[t]) & 1ull) != 0, qb = ((e.mb >> qj[t]) & 1ull) != 0;
@@ -340,18 +180,19 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
       float bm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
+      // m is kept in raw score units; exponents are (s - m) * log2(e) / sqrt(D)
       const float mn = fmaxf(m[t], bm);
-      if (__any(mn > m[t] + kTau)) {
-        const float alpha = (m[t] == kNegInf) ? 0.f : fast_exp2(m[t] - mn);
+      if (__any(mn > m[t] + tau_raw)) {
+        const float alpha = (m[t] == kNegInf) ? 0.f : fast_exp2((m[t] - mn) * sl2);
         l[t] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) acc[t][dt] *= alpha;
         m[t] = mn;
       }
-      const float mu = (m[t] == kNegInf) ? 0.f : m[t];
+      const float mc = (m[t] == kNegInf) ? 0.f : m[t] * sl2;
       float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(sc[i] - mu);
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(sc[i], sl2, -mc));
       P::pv2(va, vb, p, acc[t], l[t]);
     }
   };
@@ -402,7 +243,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
       for (int w = 0; w < W; ++w) {
         const float mw = s_m[w][rr];
-        const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+        const float f = (mw == kNegInf) ? 0.f : fast_exp2((mw - M) * sl2);
         ls += s_l[w][rr] * f;
         as += s_acc[w][d][rr] * f;
       }
@@ -442,7 +283,7 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(MergeArgs a) {
     const int item = a.group_items[mg.gi_begin + c];
     const size_t slot = static_cast<size_t>(a.items[item].part_base) + static_cast<size_t>(mg.j) * a.hq + h;
     const float mc = a.part_ml[2 * slot];
-    const float f = (mc == kNegInf) ? 0.f : fast_exp2(mc - M);
+    const float f = (mc == kNegInf) ? 0.f : fast_exp2((mc - M) * a.scale_log2);
     ls += a.part_ml[2 * slot + 1] * f;
     as += a.part_acc[slot * D + d] * f;
   }

@@ -238,13 +238,18 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     for (auto& e : ev) e = c->get_event();
     if (ev[0] && ev[1] && ev[2]) (void)hipEventRecord(ev[0], stream);
   }
-  for (int t = 1; t <= 4; ++t) {
-    const int32_t n = P.bucket_begin[t] - P.bucket_begin[t - 1];
+  for (int cls = 0; cls < kKernelClasses; ++cls) {
+    const int32_t n = P.bucket_begin[cls + 1] - P.bucket_begin[cls];
     if (n <= 0) continue;
-    a.item0 = P.bucket_begin[t - 1];
-    const int w = c->waves ? c->waves : 4;
-    if (launch_attn_partial(c->cfg.dtype, c->cfg.head_dim, t, w, P.causal, a, n, stream) != hipSuccess)
-      return TKV_E_DEVICE;
+    a.item0 = P.bucket_begin[cls];
+    hipError_t e;
+    if (cls < 2) {
+      const int w = c->waves ? c->waves : 4;
+      e = launch_attn_partial(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], w, P.causal, a, n, stream);
+    } else {
+      e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], P.causal, a, n, stream);
+    }
+    if (e != hipSuccess) return TKV_E_DEVICE;
   }
   if (c->prof && ev[1]) (void)hipEventRecord(ev[1], stream);
   if (P.any_merge) {
@@ -257,6 +262,7 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     m.out = out;
     m.hq = a.hq;
     m.nq = P.nqueries;
+    m.scale_log2 = a.scale_log2;
     if (launch_attn_merge(c->cfg.head_dim, m, stream) != hipSuccess) return TKV_E_DEVICE;
   }
   if (c->prof) {
@@ -472,7 +478,7 @@ int tkv_plan_info_get(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int3
   info.unique_blocks = P.unique_blocks;
   info.unique_tokens = P.unique_tokens;
   info.partial_slots = P.partial_slots;
-  for (int t = 1; t <= 4; ++t) info.rows_per_tile_hist[t - 1] = P.bucket_begin[t] - P.bucket_begin[t - 1];
+  for (int cls = 0; cls < kKernelClasses; ++cls) info.items_per_kernel[cls] = P.bucket_begin[cls + 1] - P.bucket_begin[cls];
   *out = info;
   return TKV_OK;
 }

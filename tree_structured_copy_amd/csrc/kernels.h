@@ -12,6 +12,11 @@ namespace tkv {
 hipError_t launch_attn_partial(int dtype, int head_dim, int tiles, int waves, bool causal, const AttnArgs& args,
                                int32_t n_items, hipStream_t stream);
 
+// Partial attention for groups of 3..16 row tiles with K/V staged in LDS;
+// grid = n_items * Hkv workgroups (4 or 8 waves by tile count).
+hipError_t launch_attn_rows(int dtype, int head_dim, int tiles, bool causal, const AttnArgs& args, int32_t n_items,
+                            hipStream_t stream);
+
 // Log-sum-exp merge of split-K partials into out; grid = nq * Hq.
 hipError_t launch_attn_merge(int head_dim, const MergeArgs& args, hipStream_t stream);
 

@@ -130,7 +130,7 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     // 3. groups: subtrees with <= qg queries become units; units of one tree are
     //    packed in DFS order up to qg queries
     const int32_t rows = std::max(16, std::min<int32_t>(opt.max_rows, kMaxRows));
-    const int32_t qg = std::max(1, std::min(64, rows / q_per_kv));
+    const int32_t qg = std::max(1, std::min(kMaxGroupQueries, rows / q_per_kv));
     auto queries_of_handle = [&](int32_t h, std::vector<Query>& dst) {
       for (int32_t k = 0; k < qn[h]; ++k)
         dst.push_back({h, qbase[h] + k, static_cast<int32_t>(len[h] - qn[h] + k)});
@@ -232,8 +232,9 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     int64_t total_entries = 0;
     for (int32_t gi = 0; gi < ngroups; ++gi) total_entries += gblk_count[gi];
     const int64_t tw = std::max<int32_t>(1, opt.target_wgs);
-    const int64_t chunk = std::max<int64_t>(std::max<int32_t>(1, opt.min_chunk),
-                                            (total_entries * num_kv_heads + tw - 1) / tw);
+    const int64_t chunk = std::min<int64_t>(kRowsMaxItemBlocks,
+                                            std::max<int64_t>(std::max<int32_t>(1, opt.min_chunk),
+                                                              (total_entries * num_kv_heads + tw - 1) / tw));
     struct Tmp {
       DevItem it;
       int32_t tiles, root, chunk;
@@ -245,7 +246,7 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       const int32_t nb = gblk_count[gi];
       const int32_t nc = static_cast<int32_t>(std::max<int64_t>(1, (nb + chunk - 1) / chunk));
       gchunks[gi] = nc;
-      const int32_t tiles = (P.groups[gi].nq * q_per_kv + 15) / 16;
+      const int32_t tiles = kernel_class((P.groups[gi].nq * q_per_kv + 15) / 16);
       int32_t at = 0;
       for (int32_t c = 0; c < nc; ++c) {
         const int32_t cnt = nb / nc + (c < nb % nc ? 1 : 0);
@@ -278,16 +279,16 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       return a.it.group < b.it.group;
     });
     P.items.resize(tmp.size());
-    for (int t = 0; t < 5; ++t) P.bucket_begin[t] = 0;
+    for (int t = 0; t <= kKernelClasses; ++t) P.bucket_begin[t] = 0;
     std::vector<std::vector<int32_t>> gitems(ngroups);
     for (size_t k = 0; k < tmp.size(); ++k) {
       P.items[k] = tmp[k].it;
       gitems[tmp[k].it.group].push_back(static_cast<int32_t>(k));
     }
-    for (int t = 1; t <= 4; ++t) {
+    for (int c = 0; c < kKernelClasses; ++c) {
       int32_t cnt = 0;
-      for (const auto& x : tmp) cnt += (x.tiles <= t);
-      P.bucket_begin[t] = cnt;
+      for (const auto& x : tmp) cnt += (x.tiles <= c);
+      P.bucket_begin[c + 1] = cnt;
     }
     std::vector<int32_t> gi_begin(ngroups);
     for (int32_t gi = 0; gi < ngroups; ++gi) {

@@ -30,9 +30,11 @@ struct PlanOptions {
 };
 
 struct Plan {
-  // items sorted by row-tile count; bucket t (1..4) = items [bucket_begin[t-1], bucket_begin[t])
+  // Items sorted by kernel class (kernel_class() of their group's row tiles);
+  // class c = items [bucket_begin[c], bucket_begin[c + 1]).
   std::vector<DevItem> items;
-  int32_t bucket_begin[5] = {0, 0, 0, 0, 0};
+  int32_t bucket_begin[kKernelClasses + 1] = {0, 0, 0, 0, 0, 0, 0};
+  int32_t bucket_tiles[kKernelClasses] = {1, 2, 4, 6, 8, 16};
   std::vector<DevGroup> groups;
   std::vector<int32_t> gq;
   std::vector<int32_t> gqpos;
@@ -53,6 +55,14 @@ struct Plan {
   void layout();
   void serialise(void* dst) const;
 };
+
+// Which kernel runs a group of `tiles` row tiles of 16: 0, 1 = attn.hip with 1
+// or 2 tiles in every wave's registers (waves split the blocks); 2..5 =
+// attn_rows.hip with the K/V staged in LDS and up to 4, 6, 8, 16 tiles spread
+// over the waves.
+inline int kernel_class(int tiles) {
+  return tiles <= 1 ? 0 : tiles == 2 ? 1 : tiles <= 4 ? 2 : tiles <= 6 ? 3 : tiles <= 8 ? 4 : 5;
+}
 
 // Build the plan for a decode (nq == nullptr) or verify call.  Validates the
 // handles (TKV_E_BADSEQ), query counts (TKV_E_RANGE) and emptiness (TKV_E_EMPTY).

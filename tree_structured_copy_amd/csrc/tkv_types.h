@@ -5,7 +5,10 @@
 namespace tkv {
 
 constexpr int kBlock = 16;          // token slots per block
-constexpr int kMaxRows = 64;        // rows (queries x heads-per-kv-head) per group
+constexpr int kMaxRows = 256;       // rows (queries x heads-per-kv-head) per group
+constexpr int kMaxGroupQueries = 64; // one bit per query in a block's visibility mask
+constexpr int kKernelClasses = 6;   // A1, A2 (attn.hip), B4, B6, B8, B16 (attn_rows.hip)
+constexpr int kRowsMaxItemBlocks = 512;  // longest block list of one attn_rows.hip work item (12 KiB of LDS)
 constexpr int kAppendMaxBlocks = 128;
 constexpr int kGatherMaxBlocks = 64;
 
@@ -60,8 +63,8 @@ struct AttnArgs {
   const int32_t* gq;     // global query index per group slot
   const int32_t* gqpos;  // absolute position limit per group slot
   const DevBlock* blocks;
-  float* part_acc;       // [slots][D]
-  float* part_ml;        // [slots][2]
+  float* part_acc;       // [slots][D] unnormalised sums of exp2((s - m) * scale_log2) V
+  float* part_ml;        // [slots][2]: running max m (raw score units) and sum l
   int32_t hq;
   int32_t hkv;
   int32_t gsize;         // Hq / Hkv
@@ -79,6 +82,8 @@ struct MergeArgs {
   float* out;
   int32_t hq;
   int32_t nq;
+  float scale_log2;    // partial maxima are raw scores: weights are exp2((m - M) * scale_log2)
+  int32_t pad;
 };
 
 struct AppendArgs {

@@ -69,7 +69,7 @@ class tkv_plan_info(ctypes.Structure):
     _fields_ = [("groups", ctypes.c_int32), ("items", ctypes.c_int32),
                 ("block_entries", ctypes.c_int32), ("unique_blocks", ctypes.c_int32),
                 ("unique_tokens", ctypes.c_int64), ("partial_slots", ctypes.c_int64),
-                ("rows_per_tile_hist", ctypes.c_int32 * 4)]
+                ("items_per_kernel", ctypes.c_int32 * 6)]
 
 
 def _load():
@@ -284,8 +284,8 @@ def tkv_plan_info_get(c, seqs, nq=None) -> dict:
     na = i32_array(nq) if nq is not None else None
     x = tkv_plan_info()
     _check(_lib.tkv_plan_info_get(c, sa, na, len(sa), ctypes.byref(x)), "tkv_plan_info_get")
-    d = {f: getattr(x, f) for f, _ in tkv_plan_info._fields_ if f != "rows_per_tile_hist"}
-    d["rows_per_tile_hist"] = list(x.rows_per_tile_hist)
+    d = {f: getattr(x, f) for f, _ in tkv_plan_info._fields_ if f != "items_per_kernel"}
+    d["items_per_kernel"] = list(x.items_per_kernel)
     return d
 
 
