@@ -85,6 +85,26 @@ def test_every_kernel_class(max_rows, cls, kind):
     assert_close(run_both(wl, options={3: max_rows}), "bf16")
 
 
+@pytest.mark.parametrize("dtype,hkv,d", [("bf16", 3, 128), ("bf16", 2, 64), ("f32", 2, 64), ("f32", 2, 128)])
+def test_six_tile_shapes(dtype, hkv, d):
+    """Groups of 6 row tiles run two KV heads per workgroup where the head count
+    is even (and fp32 fragments fit), else one: each variant against the oracle."""
+    wl = recipes.verify_workload("six", dtype=dtype, q_heads=4 * hkv, kv_heads=hkv, head_dim=d,
+                                 requests=3, prefix=200, paths=3, drafts=8, seed=31 + hkv + d)
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    need_gpu()
+    lib = LibReplay(wl)
+    try:
+        i = lib.build()
+        op = wl.ops[i]
+        info = tkv.tkv_plan_info_get(lib.c, lib.handles(op), op[3])
+        assert info["items_per_kernel"][3] > 0, info
+    finally:
+        lib.close()
+    assert_close(run_both(wl), dtype)
+
+
 def test_many_queries_per_group_mha():
     """MHA with 64 branches: one group of 64 rows (4 row tiles)."""
     wl = recipes.fork_workload("mha64", dtype="bf16", layers=1, q_heads=4, kv_heads=4, head_dim=64,

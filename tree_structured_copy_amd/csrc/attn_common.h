@@ -25,6 +25,37 @@ __device__ inline To bitcast(const From& f) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS reads by byte address (the address of a __shared__ object plus an offset).
+template <class T>
+__device__ inline T lds_ld(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) T*)(addr);
+}
+// The same read kept apart from its neighbours: the compiler neither merges it
+// with an adjacent read nor reorders it across another volatile LDS read.
+template <class T>
+__device__ inline T lds_ld_sep(uint32_t addr) {
+  return *(const volatile __attribute__((address_space(3))) T*)(addr);
+}
+
+// Split 8 fp32 weights into bf16 hi = bf16(p) (round to nearest even) and
+// lo = bf16(p - hi): hi + lo carries p to about 2^-17 relative.  Packed
+// conversions, and the fp32 value of each hi recovered by a shift or a mask.
+__device__ inline void split_hi_lo(const float* p, bf16x8& hi, bf16x8& lo) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  u32x4 h, w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x2 pj = {p[2 * j], p[2 * j + 1]};
+    const uint32_t hj = bitcast<uint32_t>(__builtin_convertvector(pj, bf16x2));
+    const f32x2 rem = {pj.x - bitcast<float>(hj << 16), pj.y - bitcast<float>(hj & 0xffff0000u)};
+    h[j] = hj;
+    w[j] = bitcast<uint32_t>(__builtin_convertvector(rem, bf16x2));
+  }
+  hi = bitcast<bf16x8>(h);
+  lo = bitcast<bf16x8>(w);
+}
+
 // Wait states between an MFMA chain and the first VALU / accvgpr read of its
 // result.  For v_mfma_f32_16x16x4_f32 on gfx950 the compiler's hazard model
 // leaves too few (the last accumulator register was read before the final MFMA
@@ -51,10 +82,9 @@ struct BF16 {
     for (int i = 0; i < D / 32; ++i) f.v[i] = __builtin_nontemporal_load(p + i * 64);
   }
   template <int D>
-  __device__ static void load_tile_lds(Frag<D>& f, const char* lds_tile, int lane) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(lds_tile) + lane;
+  __device__ static void load_tile_lds(Frag<D>& f, uint32_t tile_addr, int lane) {
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) f.v[i] = p[i * 64];
+    for (int i = 0; i < D / 32; ++i) f.v[i] = lds_ld<u32x4>(tile_addr + (i * 64 + lane) * 16);
   }
   template <int D>
   __device__ static void load_q(Frag<D>& f, const elem* row, int g) {
@@ -102,12 +132,7 @@ struct BF16 {
   __device__ static void pv2_av(const u32x4* av, const float* p, f32x4* acc, float& l) {
     l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     bf16x8 hi, lo;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 h = static_cast<__bf16>(p[i]);
-      hi[i] = h;
-      lo[i] = static_cast<__bf16>(p[i] - static_cast<float>(h));
-    }
+    split_hi_lo(p, hi, lo);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[dt]), hi, acc[dt], 0, 0, 0);
@@ -118,12 +143,18 @@ struct BF16 {
   // The A operands of pv2_av for d-tile dt, read straight from two staged V
   // tiles in LDS: 8 bytes of block a and 8 bytes of block b per lane.
   template <int D>
-  __device__ static void lds_av(u32x4* av, const char* va_tile, const char* vb_tile, int lane) {
+  // The V tile of block b follows that of block a in LDS.
+  __device__ static void lds_av(u32x4* av, uint32_t va_addr, int lane) {
+    constexpr uint32_t kTileBytes = 16 * D * 2;
+    uint32_t base = va_addr + lane * 16;
+    asm volatile("" : "+v"(base));  // one address register; the rest are offsets
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const int off = ((dt >> 1) * 64 + lane) * 16 + (dt & 1) * 8;
-      const u32x2 x = *reinterpret_cast<const u32x2*>(va_tile + off);
-      const u32x2 y = *reinterpret_cast<const u32x2*>(vb_tile + off);
+      const uint32_t off = (dt >> 1) * 1024 + (dt & 1) * 8;
+      // two separate 8-byte reads that land in the halves of av[dt]; merged into
+      // one 16-byte read (adjacent d-tiles) they would cost register moves
+      const u32x2 x = lds_ld_sep<u32x2>(base + off);
+      const u32x2 y = lds_ld_sep<u32x2>(base + kTileBytes + off);
       av[dt] = u32x4{x.x, x.y, y.x, y.y};
     }
   }
@@ -131,12 +162,7 @@ struct BF16 {
   __device__ static void pv2(const Frag<D>& va, const Frag<D>& vb, const float* p, f32x4* acc, float& l) {
     l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     bf16x8 hi, lo;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 h = static_cast<__bf16>(p[i]);
-      hi[i] = h;
-      lo[i] = static_cast<__bf16>(p[i] - static_cast<float>(h));
-    }
+    split_hi_lo(p, hi, lo);
     u32x4 av[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
@@ -166,10 +192,9 @@ struct F32 {
     for (int i = 0; i < D / 16; ++i) f.v[i] = __builtin_nontemporal_load(p + i * 64);
   }
   template <int D>
-  __device__ static void load_tile_lds(Frag<D>& f, const char* lds_tile, int lane) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(lds_tile) + lane;
+  __device__ static void load_tile_lds(Frag<D>& f, uint32_t tile_addr, int lane) {
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) f.v[i] = p[i * 64];
+    for (int i = 0; i < D / 16; ++i) f.v[i] = lds_ld<f32x4>(tile_addr + (i * 64 + lane) * 16);
   }
   template <int D>
   __device__ static void load_q(Frag<D>& f, const elem* row, int g) {

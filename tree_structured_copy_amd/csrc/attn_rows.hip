@@ -35,10 +35,11 @@ __device__ inline uint32_t lds_byte_addr(const void* p) {
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
 }
 
-// One wave-load: lane i copies 16 bytes from src (its own address) to LDS byte
-// address dst + 16 i.  dst must be wave-uniform.
-__device__ inline void dma16(const void* src, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(dst) : "memory", "m0");
+// One wave-load: lane i copies the 16 bytes at sbase + voff (voff its own) to
+// LDS byte address dst + 16 i.  sbase and dst must be wave-uniform.
+__device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(dst)
+               : "memory", "m0");
 }
 
 template <int N>
@@ -46,84 +47,102 @@ __device__ inline void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// s_waitcnt vmcnt(n) for a wave-uniform n (an immediate must be spelled out).
-template <int N = 0>
-__device__ inline void wait_vm_dyn(int n) {
-  if constexpr (N < 48) {
-    if (n <= N) {
-      wait_vm<N>();
-      return;
-    }
-    wait_vm_dyn<N + 1>(n);
-  } else {
-    wait_vm<0>();
-  }
+__device__ inline const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Workgroups per CU a shape is built for: two at one tile per wave, else one.
-// Two workgroups hide each other's latency; one workgroup gets the deeper ring.
-template <int TPW, int W>
+// Wave-loads per loading wave: the smallest divisor of a super-block's loads
+// that W waves can cover.  Waves [0, loads / LPW) load LPW each and the rest
+// none, so every loading wave waits for the same count.
+template <int LOADS, int W>
+constexpr int rows_loads_per_wave() {
+  int d = 1;
+  while (d * W < LOADS || LOADS % d != 0) ++d;
+  return d;
+}
+
+// Workgroups per CU a shape is built for: two at one tile per wave (fp32 at
+// d = 128 excepted: its fragments need more registers), else one.  Two
+// workgroups hide each other's latency; one workgroup gets the deeper ring.
+template <class P, int D, int TPW, int HPW>
 constexpr int rows_wgs_per_cu() {
-  return TPW == 1 ? 2 : 1;
+  return (TPW == 1 && HPW == 1 && (kIsBF16<P> || D <= 64)) ? 2 : 1;
 }
-// Waves per SIMD the register budget must allow.  The dispatcher places each
-// workgroup's waves starting from the first SIMD, so two 6-wave workgroups can
-// put 4 waves on one SIMD: shapes with more than 4 waves need 128 VGPRs.
-template <int TPW, int W>
+// Waves per SIMD the register budget must allow for that many workgroups.
+template <class P, int D, int TPW, int W, int HPW>
 constexpr int rows_min_waves() {
-  return rows_wgs_per_cu<TPW, W>() == 1 ? 1 : (W > 4 ? 4 : 2);
+  return (rows_wgs_per_cu<P, D, TPW, HPW>() * W * HPW + 3) / 4;
 }
 
-template <class P, int D, int TPW, int W, int NS, bool CAUSAL>
-__global__ __launch_bounds__(64 * W, (rows_min_waves<TPW, W>())) void attn_rows_kernel(AttnArgs a) {
+// W waves per KV head; HPW KV heads per workgroup (the same item's block list
+// for heads kvh0 .. kvh0 + HPW - 1: a group's heads see identical blocks).
+template <class P, int D, int TPW, int W, int HPW, int NS, bool CAUSAL>
+__global__ __launch_bounds__(64 * W * HPW, (rows_min_waves<P, D, TPW, W, HPW>())) void attn_rows_kernel(AttnArgs a) {
   using E = typename P::elem;
   using F = typename P::template Frag<D>;
   constexpr int NDT = D / 16;
   constexpr int TILE_BYTES = 16 * D * static_cast<int>(sizeof(E));
   constexpr int LPT = TILE_BYTES / 1024;  // wave-loads per tile
-  constexpr int SB_LOADS = 4 * LPT;       // K a, K b, V a, V b
-  constexpr int LPW_MAX = (SB_LOADS + W - 1) / W;  // wave-loads per wave per super-block
+  constexpr int HEAD_LOADS = 4 * LPT;     // K a, K b, V a, V b of one head
+  constexpr int SB_LOADS = HPW * HEAD_LOADS;
+  constexpr int LPW = rows_loads_per_wave<SB_LOADS, W * HPW>();
+  constexpr int LOADERS = SB_LOADS / LPW;
   constexpr int STAGE = SB_LOADS * 1024;
+  static_assert(NS >= 2 && (NS - 2) * LPW < 64, "ring depth");
   __shared__ __attribute__((aligned(1024))) char ring[NS * STAGE];
   __shared__ DevBlock ents[kRowsMaxItemBlocks];  // the item's block list
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hsel = wave / W;     // which of the workgroup's heads this wave serves
+  const int lw = wave - hsel * W;  // the wave's index among that head's waves
   const int g = lane >> 4, r = lane & 15;
-  const int kvh = blockIdx.x % a.hkv;
-  const DevItem it = a.items[a.item0 + blockIdx.x / a.hkv];
+  const int hgroups = a.hkv / HPW;
+  const int kvh0 = (blockIdx.x % hgroups) * HPW;
+  const int kvh = kvh0 + hsel;
+  const DevItem it = a.items[a.item0 + blockIdx.x / hgroups];
   const int nb = it.blk_count;
   const int nsb = (nb + 1) >> 1;
   const DevBlock* bl = a.blocks + it.blk_begin;
   const size_t tile_elems = 16 * D;
-  const size_t bstride = static_cast<size_t>(a.hkv) * tile_elems;
-  const char* kbase = reinterpret_cast<const char*>(static_cast<const E*>(a.kpool) + kvh * tile_elems);
-  const char* vbase = reinterpret_cast<const char*>(static_cast<const E*>(a.vpool) + kvh * tile_elems);
+  const size_t bstride_bytes = static_cast<size_t>(a.hkv) * tile_elems * sizeof(E);
+  const char* kbase = uniform_ptr(reinterpret_cast<const char*>(static_cast<const E*>(a.kpool) + kvh0 * tile_elems));
+  const char* vbase = uniform_ptr(reinterpret_cast<const char*>(static_cast<const E*>(a.vpool) + kvh0 * tile_elems));
   const uint32_t ring_base = __builtin_amdgcn_readfirstlane(lds_byte_addr(ring));
 
-  // the item's block list, staged once: the loader and every wave read block ids,
-  // valid counts, positions and masks from here without touching global memory
-  for (int k = tid; k < nb; k += 64 * W) ents[k] = bl[k];
+  // the item's block list, staged once; waves read it 64 entries at a time
+  // (lane k holds entry base + k) and take each super-block's fields with
+  // v_readlane, so no LDS round trip sits on the per-super-block path
+  for (int k = tid; k < nb; k += 64 * W * HPW) ents[k] = bl[k];
   __syncthreads();
 
-  // Issue this wave's share of super-block s's loads into ring slot `slot`.
-  auto issue = [&](int s, int slot) {
-    const int ida = __builtin_amdgcn_readfirstlane(ents[2 * s].id);
-    const int idb = (2 * s + 1 < nb) ? __builtin_amdgcn_readfirstlane(ents[2 * s + 1].id) : ida;
+  // Issue this wave's share of super-block sp's loads into ring slot `slot`.
+  int ib_base = -64, ib_id = 0;  // ids of blocks [ib_base, ib_base + 64), one per lane
+  auto issue = [&](int sp, int slot) {
+    if (wave >= LOADERS) return;
+    const int b0 = 2 * sp;
+    if (b0 >= ib_base + 64) {
+      ib_base = b0;
+      ib_id = (b0 + lane < nb) ? ents[b0 + lane].id : 0;
+    }
+    const int ida = __builtin_amdgcn_readlane(ib_id, b0 - ib_base);
+    const int idb = (b0 + 1 < nb) ? __builtin_amdgcn_readlane(ib_id, b0 + 1 - ib_base) : ida;
 #pragma unroll
-    for (int k = 0; k < LPW_MAX; ++k) {
-      const int i = wave + W * k;
-      if (i >= SB_LOADS) break;
-      const int t = i / LPT, part = i - t * LPT;
-      const int id = (t & 1) ? idb : ida;
-      const char* base = (t & 2) ? vbase : kbase;
-      const char* src = base + (static_cast<size_t>(id) * bstride) * sizeof(E) + part * 1024 + lane * 16;
-      dma16(src, ring_base + slot * STAGE + i * 1024);
+    for (int k = 0; k < LPW; ++k) {
+      const int i = wave * LPW + k;  // LDS slot i * 1024: head i / HEAD_LOADS, then K a, K b, V a, V b
+      const int hh = i / HEAD_LOADS, j = i - hh * HEAD_LOADS;
+      const int t = j / LPT, part = j - t * LPT;
+      const char* src = ((t & 2) ? vbase : kbase) + static_cast<size_t>((t & 1) ? idb : ida) * bstride_bytes +
+                        hh * TILE_BYTES;
+      dma16(src, part * 1024 + lane * 16, ring_base + slot * STAGE + i * 1024);
     }
   };
 
-  // rows of this wave: tiles wave, wave + W, ...
+  // rows of this wave: tiles lw, lw + W, ... of head kvh
   const DevGroup gr = a.groups[it.group];
   const int G = a.gsize;
   const int nrows = gr.nq * G;
@@ -133,7 +152,7 @@ __global__ __launch_bounds__(64 * W, (rows_min_waves<TPW, W>())) void attn_rows_
   uint64_t my_q = 0;  // group queries with a row in this wave's tiles
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int tile = wave + W * t;
+    const int tile = lw + W * t;
     const int R = 16 * tile + r;
     if (16 * tile < nrows) {
       const int j0 = (16 * tile) / G, j1 = min(nrows - 1, 16 * tile + 15) / G;
@@ -164,7 +183,7 @@ __global__ __launch_bounds__(64 * W, (rows_min_waves<TPW, W>())) void attn_rows_
   const float sl2 = a.scale_log2;
   const float tau_raw = kTau / sl2;  // the lazy-rescale threshold in raw score units
   const int min_lim = gr.min_pos;
-  const bool active = 16 * wave < nrows;
+  const bool active = 16 * lw < nrows;
 
   // Every load the compiler can see (queries, group data, the block list) is
   // complete here, and it knows it, so it places no vmcnt waits of its own in
@@ -172,44 +191,50 @@ __global__ __launch_bounds__(64 * W, (rows_min_waves<TPW, W>())) void attn_rows_
   // the ring on every iteration.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (nsb > 0) {
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue(min(s, nsb - 1), s);
-  }
+  for (int sp = 0; sp < NS - 1; ++sp)
+    if (sp < nsb) issue(sp, sp);
 
-  // this wave's share of a super-block's loads (waves below SB_LOADS % W take one more)
-  const int my_loads = (SB_LOADS - wave + W - 1) / W;
-  const int ring_wait = (NS - 2) * my_loads;
+  // fields of blocks [cb_base, cb_base + 64), one per lane (zero past the list)
+  int cb_base = -64, cb_valid = 0, cb_pos = 0;
+  uint32_t cb_mlo = 0, cb_mhi = 0;
   for (int s = 0; s < nsb; ++s) {
-    if constexpr (SB_LOADS % W == 0) wait_vm<(NS - 2) * (SB_LOADS / W)>();
-    else wait_vm_dyn(ring_wait);
+    // super-block s has landed once this wave's loads of it are done (the
+    // later NS - 2 super-blocks may still be in flight) and every wave has
+    // passed the barrier; the barrier also frees slot (s - 1) % NS for reuse
+    if (s + NS - 1 <= nsb) wait_vm<(NS - 2) * LPW>();
+    else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    issue(min(s + NS - 1, nsb - 1), (s + NS - 1) % NS);
+    if (s + NS - 1 < nsb) issue(s + NS - 1, (s + NS - 1) % NS);
 
-    // metadata of super-block s
-    const int ba = 2 * s, bbk = 2 * s + 1;
+    const int b0 = 2 * s;
+    if (b0 >= cb_base + 64) {
+      cb_base = b0;
+      const int k = b0 + lane;
+      cb_valid = 0;
+      cb_pos = 0;
+      cb_mlo = cb_mhi = 0;
+      if (k < nb) {
+        const DevBlock e = ents[k];
+        cb_valid = e.valid;
+        cb_pos = e.pos;
+        cb_mlo = static_cast<uint32_t>(e.mask);
+        cb_mhi = static_cast<uint32_t>(e.mask >> 32);
+      }
+    }
+    const int la = b0 - cb_base;
     SBMeta e;
-    e.va = __builtin_amdgcn_readfirstlane(ents[ba].valid);
-    e.pa = __builtin_amdgcn_readfirstlane(ents[ba].pos);
-    {
-      const uint64_t mk = ents[ba].mask;
-      e.ma = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(mk >> 32))) << 32) |
-             static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(mk)));
-    }
-    if (bbk < nb) {
-      e.vb = __builtin_amdgcn_readfirstlane(ents[bbk].valid);
-      e.pb = __builtin_amdgcn_readfirstlane(ents[bbk].pos);
-      const uint64_t mk = ents[bbk].mask;
-      e.mb = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(mk >> 32))) << 32) |
-             static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(mk)));
-    } else {
-      e.vb = 0;
-      e.pb = e.pa;
-      e.mb = 0;
-    }
+    e.va = __builtin_amdgcn_readlane(cb_valid, la);
+    e.pa = __builtin_amdgcn_readlane(cb_pos, la);
+    e.ma = (static_cast<uint64_t>(__builtin_amdgcn_readlane(cb_mhi, la)) << 32) |
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(cb_mlo, la));
+    e.vb = __builtin_amdgcn_readlane(cb_valid, la + 1);
+    e.pb = __builtin_amdgcn_readlane(cb_pos, la + 1);
+    e.mb = (static_cast<uint64_t>(__builtin_amdgcn_readlane(cb_mhi, la + 1)) << 32) |
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(cb_mlo, la + 1));
     if (!active || ((e.ma | e.mb) & my_q) == 0) continue;
 
-    const char* st = ring + (s % NS) * STAGE;
+    const uint32_t st = ring_base + (s % NS) * STAGE + hsel * 4 * TILE_BYTES;
     F ka, kb, va, vb;
     P::load_tile_lds(ka, st + 0 * TILE_BYTES, lane);
     P::load_tile_lds(kb, st + 1 * TILE_BYTES, lane);
@@ -217,28 +242,29 @@ __global__ __launch_bounds__(64 * W, (rows_min_waves<TPW, W>())) void attn_rows_
     const bool see_a = (e.ma & gmask) == gmask, see_b = (e.mb & gmask) == gmask;
     const bool need_mask = e.va < 16 || e.vb < 16 || !see_a || !see_b ||
                            (CAUSAL && (e.pa + 15 > min_lim || e.pb + 15 > min_lim));
+    // all of this wave's scores first (the K fragments then die), V after
+    float sc[TPW][8];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      if (16 * (wave + W * t) >= nrows) break;
+      if (16 * (lw + W * t) >= nrows) break;
       const f32x4 sa = P::qk(ka, qf[t]);
       const f32x4 sb = P::qk(kb, qf[t]);
-      if (t == 0) {
-        // V fragments are read only once the K fragments are consumed, so the two
-        // are never live together (one tile per wave then fits 128 VGPRs)
-        if constexpr (TPW == 1) __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kIsBF16<P>) {
-          P::template lds_av<D>(av, st + 2 * TILE_BYTES, st + 3 * TILE_BYTES, lane);
-        } else {
-          P::load_tile_lds(va, st + 2 * TILE_BYTES, lane);
-          P::load_tile_lds(vb, st + 3 * TILE_BYTES, lane);
-        }
-      }
-      float sc[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sc[i] = sa[i];
-        sc[4 + i] = sb[i];
+        sc[t][i] = sa[i];
+        sc[t][4 + i] = sb[i];
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kIsBF16<P>) {
+      P::template lds_av<D>(av, st + 2 * TILE_BYTES, lane);
+    } else {
+      P::load_tile_lds(va, st + 2 * TILE_BYTES, lane);
+      P::load_tile_lds(vb, st + 3 * TILE_BYTES, lane);
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      if (16 * (lw + W * t) >= nrows) break;
       if (need_mask) {
         const bool qa = ((e.ma >> qj[t]) & 1ull) != 0, qb = ((e.mb >> qj[t]) & 1ull) != 0;
 #pragma unroll
@@ -249,26 +275,30 @@ __global__ __launch_bounds__(64 * W, (rows_min_waves<TPW, W>())) void attn_rows_
             oka = oka && (e.pa + tok <= qlim[t]);
             okb = okb && (e.pb + tok <= qlim[t]);
           }
-          if (!oka) sc[i] = kNegInf;
-          if (!okb) sc[4 + i] = kNegInf;
+          if (!oka) sc[t][i] = kNegInf;
+          if (!okb) sc[t][4 + i] = kNegInf;
         }
       }
-      float bm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      // m is kept in raw score units; exponents are (s - m) * log2(e) / sqrt(D)
-      const float mn = fmaxf(m[t], bm);
-      if (__any(mn > m[t] + tau_raw)) {
+      // Lazy rescale: the row maximum is only formed (across the 4 lanes that
+      // share a row) when some score of the wave exceeds its row's m by tau;
+      // otherwise m stays and every weight is at most 2^tau.
+      const float* x = sc[t];
+      const float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      if (__any(bm > m[t] + tau_raw)) {
+        float rm = fmaxf(bm, __shfl_xor(bm, 16));
+        rm = fmaxf(rm, __shfl_xor(rm, 32));
+        const float mn = fmaxf(m[t], rm);
         const float alpha = (m[t] == kNegInf) ? 0.f : fast_exp2((m[t] - mn) * sl2);
         l[t] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) acc[t][dt] *= alpha;
         m[t] = mn;
       }
+      // m is kept in raw score units; exponents are (s - m) * log2(e) / sqrt(D)
       const float mc = (m[t] == kNegInf) ? 0.f : m[t] * sl2;
       float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(sc[i], sl2, -mc));
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], sl2, -mc));
       if constexpr (kIsBF16<P>) P::template pv2_av<D>(av, p, acc[t], l[t]);
       else P::pv2(va, vb, p, acc[t], l[t]);
     }
@@ -280,7 +310,7 @@ __global__ __launch_bounds__(64 * W, (rows_min_waves<TPW, W>())) void attn_rows_
   // write this wave's rows: lane (g, r) holds O^T[16 dt + 4 g + i][row r]
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int tile = wave + W * t;
+    const int tile = lw + W * t;
     if (16 * tile >= nrows) break;
     float lt = l[t];
     lt += __shfl_xor(lt, 16);
@@ -309,29 +339,35 @@ __global__ __launch_bounds__(64 * W, (rows_min_waves<TPW, W>())) void attn_rows_
   }
 }
 
-// Ring depth: as many super-blocks as fit in 64 KiB (two workgroups per CU) or
-// 128 KiB (one), at most 8; with the 12 KiB block list either fits the CU's
-// 160 KiB of LDS.
-template <class P, int D, int WGS>
+// Ring depth: as many super-blocks (of all the workgroup's heads) as fit in
+// 64 KiB (two workgroups per CU) or 128 KiB (one), at most 8; with the 12 KiB
+// block list either fits the CU's 160 KiB of LDS.
+template <class P, int D, int HPW, int WGS>
 constexpr int ring_stages() {
-  constexpr int stage = 4 * 16 * D * static_cast<int>(sizeof(typename P::elem));
+  constexpr int stage = HPW * 4 * 16 * D * static_cast<int>(sizeof(typename P::elem));
   constexpr int budget = (WGS == 2 ? 64 : 128) * 1024;
   return (budget / stage) < 8 ? (budget / stage) : 8;
 }
 
-template <class P, int D, int TPW, int W, bool C>
+template <class P, int D, int TPW, int W, int HPW, bool C>
 hipError_t launch_one(const AttnArgs& args, int32_t n_items, hipStream_t s) {
-  constexpr int NS = ring_stages<P, D, rows_wgs_per_cu<TPW, W>()>();
-  hipLaunchKernelGGL((attn_rows_kernel<P, D, TPW, W, NS, C>), dim3(n_items * args.hkv), dim3(64 * W), 0, s, args);
+  constexpr int NS = ring_stages<P, D, HPW, rows_wgs_per_cu<P, D, TPW, HPW>()>();
+  hipLaunchKernelGGL((attn_rows_kernel<P, D, TPW, W, HPW, NS, C>), dim3(n_items * (args.hkv / HPW)),
+                     dim3(64 * W * HPW), 0, s, args);
   return hipGetLastError();
 }
 
 template <class P, int D, bool C>
 hipError_t launch_shape(int tiles, const AttnArgs& args, int32_t n_items, hipStream_t s) {
-  if (tiles <= 4) return launch_one<P, D, 1, 4, C>(args, n_items, s);
-  if (tiles <= 6) return launch_one<P, D, 1, 6, C>(args, n_items, s);
-  if (tiles <= 8) return launch_one<P, D, 1, 8, C>(args, n_items, s);
-  if (tiles <= 16) return launch_one<P, D, 2, 8, C>(args, n_items, s);
+  if (tiles <= 4) return launch_one<P, D, 1, 4, 1, C>(args, n_items, s);
+  // six tiles: two heads per workgroup, so that its 12 waves spread evenly
+  // over the CU's four SIMDs (a 6-wave workgroup puts 2, 2, 1, 1 on them)
+  if (tiles <= 6) {
+    if (args.hkv % 2 == 0 && (kIsBF16<P> || D <= 64)) return launch_one<P, D, 1, 6, 2, C>(args, n_items, s);
+    return launch_one<P, D, 1, 6, 1, C>(args, n_items, s);
+  }
+  if (tiles <= 8) return launch_one<P, D, 1, 8, 1, C>(args, n_items, s);
+  if (tiles <= 16) return launch_one<P, D, 2, 8, 1, C>(args, n_items, s);
   return hipErrorInvalidValue;
 }
 
