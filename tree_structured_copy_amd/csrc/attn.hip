@@ -98,18 +98,20 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
     }
     return m;
   };
-  auto load_sb = [&](F& ka, F& va, F& kb, F& vb, const SBMeta& m) {
+  using VP = typename P::template VPair<D>;
+  auto load_sb = [&](F& ka, F& kb, VP& v, const SBMeta& m) {
     P::load_tile(ka, kbase + static_cast<size_t>(m.ida) * bstride, lane);
     P::load_tile(kb, kbase + static_cast<size_t>(m.idb) * bstride, lane);
-    P::load_tile(va, vbase + static_cast<size_t>(m.ida) * bstride, lane);
-    P::load_tile(vb, vbase + static_cast<size_t>(m.idb) * bstride, lane);
+    P::load_vpair(v, vbase + static_cast<size_t>(m.ida) * bstride, vbase + static_cast<size_t>(m.idb) * bstride,
+                  lane);
   };
 
-  F kA0, vA0, kA1, vA1, kB0, vB0, kB1, vB1;
+  F kA0, kA1, kB0, kB1;
+  VP vA, vB;
   SBMeta mA, mB;
   if (nmine > 0) {
     mA = meta(0);
-    load_sb(kA0, vA0, kA1, vA1, mA);
+    load_sb(kA0, kA1, vA, mA);
   }
 
   // queries: row R = 16 t + r of the group is query R / G, head kvh * G + R % G
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
   const float tau_raw = kTau / sl2;  // the lazy-rescale threshold in raw score units
   const int min_lim = gr.min_pos;
 
-  auto process = [&](const F& ka, const F& va, const F& kb, const F& vb, const SBMeta& e) {
+  auto process = [&](const F& ka, const F& kb, const VP& v, const SBMeta& e) {
     const bool see_a = (e.ma & gmask) == gmask, see_b = (e.mb & gmask) == gmask;
     const bool need_mask = e.va < 16 || e.vb < 16 || !see_a || !see_b || (CAUSAL && e.pb + 15 > min_lim) ||
                            (CAUSAL && e.pa + 15 > min_lim);
@@ -177,12 +179,15 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
           if (!okb) sc[4 + i] = kNegInf;
         }
       }
-      float bm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      // m is kept in raw score units; exponents are (s - m) * log2(e) / sqrt(D)
-      const float mn = fmaxf(m[t], bm);
-      if (__any(mn > m[t] + tau_raw)) {
+      // Lazy rescale: the row maximum is only formed (across the 4 lanes that
+      // share a row) when some score of the wave exceeds its row's m by tau;
+      // otherwise m stays and every weight is at most 2^tau.
+      const float bm =
+          fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      if (__any(bm > m[t] + tau_raw)) {
+        float rm = fmaxf(bm, __shfl_xor(bm, 16));
+        rm = fmaxf(rm, __shfl_xor(rm, 32));
+        const float mn = fmaxf(m[t], rm);
         const float alpha = (m[t] == kNegInf) ? 0.f : fast_exp2((m[t] - mn) * sl2);
         l[t] *= alpha;
 #pragma unroll
@@ -193,19 +198,19 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(sc[i], sl2, -mc));
-      P::pv2(va, vb, p, acc[t], l[t]);
+      P::pv(v, p, acc[t], l[t]);
     }
   };
 
   if (nmine > 0) {
     for (int k = 0; k < nmine; k += 2) {
       mB = meta(min(k + 1, nmine - 1));
-      load_sb(kB0, vB0, kB1, vB1, mB);
-      process(kA0, vA0, kA1, vA1, mA);
+      load_sb(kB0, kB1, vB, mB);
+      process(kA0, kA1, vA, mA);
       if (k + 1 >= nmine) break;
       mA = meta(min(k + 2, nmine - 1));
-      load_sb(kA0, vA0, kA1, vA1, mA);
-      process(kB0, vB0, kB1, vB1, mB);
+      load_sb(kA0, kA1, vA, mA);
+      process(kB0, kB1, vB, mB);
     }
   }
 
@@ -296,18 +301,27 @@ hipError_t launch_t(int tiles, const AttnArgs& args, int32_t n_items, hipStream_
   switch (tiles) {
     case 1: hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, W, C>), grid, block, 0, s, args); break;
     case 2: hipLaunchKernelGGL((attn_partial_kernel<P, D, 2, W, C>), grid, block, 0, s, args); break;
-    case 3: hipLaunchKernelGGL((attn_partial_kernel<P, D, 3, W, C>), grid, block, 0, s, args); break;
-    case 4: hipLaunchKernelGGL((attn_partial_kernel<P, D, 4, W, C>), grid, block, 0, s, args); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// Eight waves only at one tile and not for fp32 at d = 128 (more fragments per
+// wave than eight waves leave registers for).
+template <class P, int D, bool C>
+hipError_t launch_w(int tiles, int waves, const AttnArgs& args, int32_t n_items, hipStream_t s) {
+  if constexpr (kIsBF16<P> || D <= 64) {
+    if (waves == 8 && tiles == 1) {
+      hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, 8, C>), dim3(n_items * args.hkv), dim3(64 * 8), 0, s, args);
+      return hipGetLastError();
+    }
+  }
+  return launch_t<P, D, 4, C>(tiles, args, n_items, s);
+}
+
 template <class P, int D>
 hipError_t launch_c(int tiles, int waves, bool causal, const AttnArgs& args, int32_t n_items, hipStream_t s) {
-  if (waves == 8)
-    return causal ? launch_t<P, D, 8, true>(tiles, args, n_items, s) : launch_t<P, D, 8, false>(tiles, args, n_items, s);
-  return causal ? launch_t<P, D, 4, true>(tiles, args, n_items, s) : launch_t<P, D, 4, false>(tiles, args, n_items, s);
+  return causal ? launch_w<P, D, true>(tiles, waves, args, n_items, s) : launch_w<P, D, false>(tiles, waves, args, n_items, s);
 }
 
 }  // namespace

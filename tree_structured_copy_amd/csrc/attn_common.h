@@ -68,6 +68,47 @@ __device__ inline void mfma_result_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// ---- direct-to-LDS loads (global_load_lds_dwordx4) -------------------------
+//
+// The loads are issued from inline asm so that the waits are ours: the compiler
+// would otherwise wait for every outstanding LDS DMA at each barrier.  The
+// kernels that use them keep every compiler-visible global load out of their
+// loops, so vmcnt counts only these loads there.
+
+__device__ inline uint32_t lds_byte_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// One wave-load: lane i copies the 16 bytes at sbase + voff (voff its own) to
+// LDS byte address dst + 16 i.  sbase and dst must be wave-uniform.
+__device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(dst)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ inline void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ inline const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Wave-loads per loading wave: the smallest divisor of a super-block's loads
+// that W waves can cover.  Waves [0, loads / LPW) load LPW each and the rest
+// none, so every loading wave waits for the same count.
+template <int LOADS, int W>
+constexpr int rows_loads_per_wave() {
+  int d = 1;
+  while (d * W < LOADS || LOADS % d != 0) ++d;
+  return d;
+}
+
 // bf16 inputs: S^T and O^T via 16x16x32 bf16 MFMAs.
 struct BF16 {
   using elem = uint16_t;
@@ -104,77 +145,55 @@ struct BF16 {
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(k.v[kk]), bitcast<bf16x8>(q.v[kk]), s, 0, 0, 0);
     return s;
   }
-  // acc[dt] += V^T[16dt..16dt+15][4 tokens] . P^T.  A weight p is split into
-  // bf16 hi = bf16(p) and lo = bf16(p - hi), so hi + lo carries p to about
-  // 2^-17 relative; one 16x16x32 MFMA per d-tile takes k = (4 tokens, hi) and
-  // (the same 4 tokens, lo), with the lane's V^T fragment given twice.
+  // The V side of one super-block: vp.av[dt] is the A operand of the P.V MFMA
+  // for d-tile dt, V^T[16 dt + dl][4 tokens of block a, 4 tokens of block b]
+  // for lane (g, dl): one 8-byte unit of each block's V tile (the pool keeps
+  // unit dt*64 + lane of a tile at byte 8 (dt*64 + lane), layout.h), so both
+  // halves load straight into place and every wave load is one contiguous
+  // 512-byte run.
   template <int D>
-  __device__ static void pv(const Frag<D>& v, const float* p, f32x4* acc, float& l) {
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    bf16x8 pb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const __bf16 hi = static_cast<__bf16>(p[i]);
-      pb[i] = hi;
-      pb[4 + i] = static_cast<__bf16>(p[i] - static_cast<float>(hi));
-    }
+  struct VPair {
+    u32x4 av[D / 16];
+  };
+  template <int D>
+  __device__ static void load_vpair(VPair<D>& v, const elem* va_tile, const elem* vb_tile, int lane) {
+    const u32x2* pa = reinterpret_cast<const u32x2*>(va_tile) + lane;
+    const u32x2* pb = reinterpret_cast<const u32x2*>(vb_tile) + lane;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x4 w = v.v[dt >> 1];
-      const u32x4 a = (dt & 1) ? u32x4{w.z, w.w, w.z, w.w} : u32x4{w.x, w.y, w.x, w.y};
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(a), pb, acc[dt], 0, 0, 0);
+      const u32x2 x = __builtin_nontemporal_load(pa + dt * 64);
+      const u32x2 y = __builtin_nontemporal_load(pb + dt * 64);
+      v.av[dt] = u32x4{x.x, x.y, y.x, y.y};
     }
   }
-  // Two blocks at once: k = 4 tokens of block a and 4 of block b; one MFMA
-  // per d-tile for the hi parts of the weights and one for the lo parts.  The
-  // P.V A operands are given ready-made (av[dt] = V^T fragments of a and b).
+  // The same from two staged V tiles in LDS (block b's right after block a's).
   template <int D>
-  __device__ static void pv2_av(const u32x4* av, const float* p, f32x4* acc, float& l) {
-    l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    bf16x8 hi, lo;
-    split_hi_lo(p, hi, lo);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[dt]), hi, acc[dt], 0, 0, 0);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[dt]), lo, acc[dt], 0, 0, 0);
-  }
-  // The A operands of pv2_av for d-tile dt, read straight from two staged V
-  // tiles in LDS: 8 bytes of block a and 8 bytes of block b per lane.
-  template <int D>
-  // The V tile of block b follows that of block a in LDS.
-  __device__ static void lds_av(u32x4* av, uint32_t va_addr, int lane) {
+  __device__ static void lds_vpair(VPair<D>& v, uint32_t va_addr, int lane) {
     constexpr uint32_t kTileBytes = 16 * D * 2;
-    uint32_t base = va_addr + lane * 16;
+    uint32_t base = va_addr + lane * 8;
     asm volatile("" : "+v"(base));  // one address register; the rest are offsets
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const uint32_t off = (dt >> 1) * 1024 + (dt & 1) * 8;
-      // two separate 8-byte reads that land in the halves of av[dt]; merged into
-      // one 16-byte read (adjacent d-tiles) they would cost register moves
-      const u32x2 x = lds_ld_sep<u32x2>(base + off);
-      const u32x2 y = lds_ld_sep<u32x2>(base + kTileBytes + off);
-      av[dt] = u32x4{x.x, x.y, y.x, y.y};
+      // separate reads (never merged with a neighbour) into the halves of av[dt]
+      const u32x2 x = lds_ld_sep<u32x2>(base + dt * 512);
+      const u32x2 y = lds_ld_sep<u32x2>(base + kTileBytes + dt * 512);
+      v.av[dt] = u32x4{x.x, x.y, y.x, y.y};
     }
   }
+  // acc[dt] += V^T . P^T over the super-block's 8 tokens per lane group.  A
+  // weight p is split into bf16 hi + lo (split_hi_lo); one MFMA per d-tile
+  // takes the hi parts, one the lo parts, with the same A operand.
   template <int D>
-  __device__ static void pv2(const Frag<D>& va, const Frag<D>& vb, const float* p, f32x4* acc, float& l) {
+  __device__ static void pv(const VPair<D>& v, const float* p, f32x4* acc, float& l) {
     l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     bf16x8 hi, lo;
     split_hi_lo(p, hi, lo);
-    u32x4 av[D / 16];
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x4 wa = va.v[dt >> 1], wb = vb.v[dt >> 1];
-      av[dt] = (dt & 1) ? u32x4{wa.z, wa.w, wb.z, wb.w} : u32x4{wa.x, wa.y, wb.x, wb.y};
-    }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[dt]), hi, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(v.av[dt]), hi, acc[dt], 0, 0, 0);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(av[dt]), lo, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(v.av[dt]), lo, acc[dt], 0, 0, 0);
   }
 };
 
@@ -216,18 +235,32 @@ struct F32 {
     mfma_result_fence();
     return s;
   }
+  // The V side of one super-block: the two V tiles in fragment order.
   template <int D>
-  __device__ static void pv(const Frag<D>& v, const float* p, f32x4* acc, float& l) {
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.v[dt][i], p[i], acc[dt], 0, 0, 0);
+  struct VPair {
+    Frag<D> a, b;
+  };
+  template <int D>
+  __device__ static void load_vpair(VPair<D>& v, const elem* va_tile, const elem* vb_tile, int lane) {
+    load_tile(v.a, va_tile, lane);
+    load_tile(v.b, vb_tile, lane);
   }
   template <int D>
-  __device__ static void pv2(const Frag<D>& va, const Frag<D>& vb, const float* p, f32x4* acc, float& l) {
-    pv(va, p, acc, l);
-    pv(vb, p + 4, acc, l);
+  __device__ static void lds_vpair(VPair<D>& v, uint32_t va_addr, int lane) {
+    load_tile_lds(v.a, va_addr, lane);
+    load_tile_lds(v.b, va_addr + 16 * D * 4, lane);
+  }
+  template <int D>
+  __device__ static void pv(const VPair<D>& v, const float* p, f32x4* acc, float& l) {
+    l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.a.v[dt][i], p[i], acc[dt], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(v.b.v[dt][i], p[4 + i], acc[dt], 0, 0, 0);
+    }
   }
 };
 

@@ -30,57 +30,15 @@ namespace {
 
 using namespace attn;
 
-__device__ inline uint32_t lds_byte_addr(const void* p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
-}
-
-// One wave-load: lane i copies the 16 bytes at sbase + voff (voff its own) to
-// LDS byte address dst + 16 i.  sbase and dst must be wave-uniform.
-__device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(dst)
-               : "memory", "m0");
-}
-
-template <int N>
-__device__ inline void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ inline const char* uniform_ptr(const char* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-// Wave-loads per loading wave: the smallest divisor of a super-block's loads
-// that W waves can cover.  Waves [0, loads / LPW) load LPW each and the rest
-// none, so every loading wave waits for the same count.
-template <int LOADS, int W>
-constexpr int rows_loads_per_wave() {
-  int d = 1;
-  while (d * W < LOADS || LOADS % d != 0) ++d;
-  return d;
-}
-
-// Workgroups per CU a shape is built for: two at one tile per wave (fp32 at
-// d = 128 excepted: its fragments need more registers), else one.  Two
-// workgroups hide each other's latency; one workgroup gets the deeper ring.
-template <class P, int D, int TPW, int HPW>
-constexpr int rows_wgs_per_cu() {
-  return (TPW == 1 && HPW == 1 && (kIsBF16<P> || D <= 64)) ? 2 : 1;
-}
-// Waves per SIMD the register budget must allow for that many workgroups.
-template <class P, int D, int TPW, int W, int HPW>
-constexpr int rows_min_waves() {
-  return (rows_wgs_per_cu<P, D, TPW, HPW>() * W * HPW + 3) / 4;
-}
-
-// W waves per KV head; HPW KV heads per workgroup (the same item's block list
-// for heads kvh0 .. kvh0 + HPW - 1: a group's heads see identical blocks).
-template <class P, int D, int TPW, int W, int HPW, int NS, bool CAUSAL>
-__global__ __launch_bounds__(64 * W * HPW, (rows_min_waves<P, D, TPW, W, HPW>())) void attn_rows_kernel(AttnArgs a) {
+// TPW row tiles per wave; W waves per KV head; HPW KV heads per workgroup (the
+// same item's block list for heads kvh0 .. kvh0 + HPW - 1: a group's heads see
+// identical blocks); NS ring slots of one super-block (of every head).
+// EARLY: a slot is refilled as soon as every wave has read its fragments (a
+// second barrier per super-block), so all NS slots are in flight during the
+// math; otherwise the refill waits for the next super-block's barrier and NS - 1
+// are.  MINW: waves per SIMD the register budget must allow.
+template <class P, int D, int TPW, int W, int HPW, int NS, bool EARLY, int MINW, bool CAUSAL>
+__global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs a) {
   using E = typename P::elem;
   using F = typename P::template Frag<D>;
   constexpr int NDT = D / 16;
@@ -91,9 +49,11 @@ __global__ __launch_bounds__(64 * W * HPW, (rows_min_waves<P, D, TPW, W, HPW>())
   constexpr int LPW = rows_loads_per_wave<SB_LOADS, W * HPW>();
   constexpr int LOADERS = SB_LOADS / LPW;
   constexpr int STAGE = SB_LOADS * 1024;
-  static_assert(NS >= 2 && (NS - 2) * LPW < 64, "ring depth");
+  static_assert(NS >= 2 && (NS - 1) * LPW < 64, "ring depth");
   __shared__ __attribute__((aligned(1024))) char ring[NS * STAGE];
-  __shared__ DevBlock ents[kRowsMaxItemBlocks];  // the item's block list
+  // the item's block list: a.max_blocks entries, sized at launch
+  extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
+  DevBlock* ents = reinterpret_cast<DevBlock*>(dyn_smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -191,8 +151,9 @@ __global__ __launch_bounds__(64 * W * HPW, (rows_min_waves<P, D, TPW, W, HPW>())
   // the ring on every iteration.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  constexpr int AHEAD = EARLY ? NS : NS - 1;  // super-blocks issued before the first is read
 #pragma unroll
-  for (int sp = 0; sp < NS - 1; ++sp)
+  for (int sp = 0; sp < AHEAD; ++sp)
     if (sp < nsb) issue(sp, sp);
 
   // fields of blocks [cb_base, cb_base + 64), one per lane (zero past the list)
@@ -200,12 +161,14 @@ __global__ __launch_bounds__(64 * W * HPW, (rows_min_waves<P, D, TPW, W, HPW>())
   uint32_t cb_mlo = 0, cb_mhi = 0;
   for (int s = 0; s < nsb; ++s) {
     // super-block s has landed once this wave's loads of it are done (the
-    // later NS - 2 super-blocks may still be in flight) and every wave has
-    // passed the barrier; the barrier also frees slot (s - 1) % NS for reuse
-    if (s + NS - 1 <= nsb) wait_vm<(NS - 2) * LPW>();
+    // later AHEAD - 1 super-blocks may still be in flight) and every wave has
+    // passed the barrier; without EARLY the barrier also frees slot (s - 1) % NS
+    if (s + AHEAD <= nsb) wait_vm<(AHEAD - 1) * LPW>();
     else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    if (s + NS - 1 < nsb) issue(s + NS - 1, (s + NS - 1) % NS);
+    if constexpr (!EARLY) {
+      if (s + NS - 1 < nsb) issue(s + NS - 1, (s + NS - 1) % NS);
+    }
 
     const int b0 = 2 * s;
     if (b0 >= cb_base + 64) {
@@ -232,13 +195,24 @@ __global__ __launch_bounds__(64 * W * HPW, (rows_min_waves<P, D, TPW, W, HPW>())
     e.pb = __builtin_amdgcn_readlane(cb_pos, la + 1);
     e.mb = (static_cast<uint64_t>(__builtin_amdgcn_readlane(cb_mhi, la + 1)) << 32) |
            static_cast<uint32_t>(__builtin_amdgcn_readlane(cb_mlo, la + 1));
-    if (!active || ((e.ma | e.mb) & my_q) == 0) continue;
+    // refill slot s % NS with super-block s + NS once every wave is done with it
+    auto refill_early = [&]() {
+      if constexpr (EARLY) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        if (s + NS < nsb) issue(s + NS, s % NS);
+      }
+    };
+    if (!active || ((e.ma | e.mb) & my_q) == 0) {
+      refill_early();
+      continue;
+    }
 
     const uint32_t st = ring_base + (s % NS) * STAGE + hsel * 4 * TILE_BYTES;
-    F ka, kb, va, vb;
+    F ka, kb;
+    typename P::template VPair<D> vp;
     P::load_tile_lds(ka, st + 0 * TILE_BYTES, lane);
     P::load_tile_lds(kb, st + 1 * TILE_BYTES, lane);
-    [[maybe_unused]] u32x4 av[NDT];
     const bool see_a = (e.ma & gmask) == gmask, see_b = (e.mb & gmask) == gmask;
     const bool need_mask = e.va < 16 || e.vb < 16 || !see_a || !see_b ||
                            (CAUSAL && (e.pa + 15 > min_lim || e.pb + 15 > min_lim));
@@ -246,7 +220,8 @@ __global__ __launch_bounds__(64 * W * HPW, (rows_min_waves<P, D, TPW, W, HPW>())
     float sc[TPW][8];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      if (16 * (lw + W * t) >= nrows) break;
+      // every tile of the wave runs (a tile past the group's rows has zero
+      // queries and is never written): no per-tile branches to keep values across
       const f32x4 sa = P::qk(ka, qf[t]);
       const f32x4 sb = P::qk(kb, qf[t]);
 #pragma unroll
@@ -256,15 +231,12 @@ __global__ __launch_bounds__(64 * W * HPW, (rows_min_waves<P, D, TPW, W, HPW>())
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kIsBF16<P>) {
-      P::template lds_av<D>(av, st + 2 * TILE_BYTES, lane);
-    } else {
-      P::load_tile_lds(va, st + 2 * TILE_BYTES, lane);
-      P::load_tile_lds(vb, st + 3 * TILE_BYTES, lane);
-    }
+    P::template lds_vpair<D>(vp, st + 2 * TILE_BYTES, lane);
+    refill_early();
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      if (16 * (lw + W * t) >= nrows) break;
+      // every tile of the wave runs (a tile past the group's rows has zero
+      // queries and is never written): no per-tile branches to keep values across
       if (need_mask) {
         const bool qa = ((e.ma >> qj[t]) & 1ull) != 0, qb = ((e.mb >> qj[t]) & 1ull) != 0;
 #pragma unroll
@@ -299,8 +271,8 @@ __global__ __launch_bounds__(64 * W * HPW, (rows_min_waves<P, D, TPW, W, HPW>())
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], sl2, -mc));
-      if constexpr (kIsBF16<P>) P::template pv2_av<D>(av, p, acc[t], l[t]);
-      else P::pv2(va, vb, p, acc[t], l[t]);
+      P::pv(vp, p, acc[t], l[t]);
+      if constexpr (TPW > 1) __builtin_amdgcn_sched_barrier(0);  // one tile's weights live at a time
     }
   }
   // every DMA this wave issued must land before the workgroup's LDS is released
@@ -339,35 +311,47 @@ __global__ __launch_bounds__(64 * W * HPW, (rows_min_waves<P, D, TPW, W, HPW>())
   }
 }
 
-// Ring depth: as many super-blocks (of all the workgroup's heads) as fit in
-// 64 KiB (two workgroups per CU) or 128 KiB (one), at most 8; with the 12 KiB
-// block list either fits the CU's 160 KiB of LDS.
-template <class P, int D, int HPW, int WGS>
-constexpr int ring_stages() {
+// Ring slots: as many super-blocks (of all the workgroup's heads) as fit in
+// the LDS budget, at most 8.
+template <class P, int D, int HPW, int BUDGET_KB>
+constexpr int ring_slots() {
   constexpr int stage = HPW * 4 * 16 * D * static_cast<int>(sizeof(typename P::elem));
-  constexpr int budget = (WGS == 2 ? 64 : 128) * 1024;
-  return (budget / stage) < 8 ? (budget / stage) : 8;
+  return (BUDGET_KB * 1024 / stage) < 8 ? (BUDGET_KB * 1024 / stage) : 8;
 }
 
-template <class P, int D, int TPW, int W, int HPW, bool C>
+template <class P, int D, int TPW, int W, int HPW, int NS, bool EARLY, int MINW, bool C>
 hipError_t launch_one(const AttnArgs& args, int32_t n_items, hipStream_t s) {
-  constexpr int NS = ring_stages<P, D, HPW, rows_wgs_per_cu<P, D, TPW, HPW>()>();
-  hipLaunchKernelGGL((attn_rows_kernel<P, D, TPW, W, HPW, NS, C>), dim3(n_items * (args.hkv / HPW)),
-                     dim3(64 * W * HPW), 0, s, args);
+  const size_t ents_bytes = sizeof(DevBlock) * static_cast<size_t>(args.max_blocks > 0 ? args.max_blocks : 1);
+  hipLaunchKernelGGL((attn_rows_kernel<P, D, TPW, W, HPW, NS, EARLY, MINW, C>), dim3(n_items * (args.hkv / HPW)),
+                     dim3(64 * W * HPW), ents_bytes, s, args);
   return hipGetLastError();
 }
 
+// Shapes by row tiles.  Two workgroups per CU (64 KiB rings) hide each other's
+// latency; one workgroup (128 KiB) gets the deeper ring; fp32 at d = 128 needs
+// the registers of one workgroup per CU.
 template <class P, int D, bool C>
 hipError_t launch_shape(int tiles, const AttnArgs& args, int32_t n_items, hipStream_t s) {
-  if (tiles <= 4) return launch_one<P, D, 1, 4, 1, C>(args, n_items, s);
-  // six tiles: two heads per workgroup, so that its 12 waves spread evenly
-  // over the CU's four SIMDs (a 6-wave workgroup puts 2, 2, 1, 1 on them)
-  if (tiles <= 6) {
-    if (args.hkv % 2 == 0 && (kIsBF16<P> || D <= 64)) return launch_one<P, D, 1, 6, 2, C>(args, n_items, s);
-    return launch_one<P, D, 1, 6, 1, C>(args, n_items, s);
+  constexpr bool kSmall = kIsBF16<P> || D <= 64;
+  if (tiles <= 4) {
+    if constexpr (kSmall) return launch_one<P, D, 1, 4, 1, ring_slots<P, D, 1, 64>(), false, 2, C>(args, n_items, s);
+    else return launch_one<P, D, 1, 4, 1, ring_slots<P, D, 1, 128>(), false, 1, C>(args, n_items, s);
   }
-  if (tiles <= 8) return launch_one<P, D, 1, 8, 1, C>(args, n_items, s);
-  if (tiles <= 16) return launch_one<P, D, 2, 8, 1, C>(args, n_items, s);
+  if (tiles <= 6) {
+    // two heads per workgroup where the head count allows, so that its 12 waves
+    // spread evenly over the CU's four SIMDs (6 waves would sit 2, 2, 1, 1)
+    if constexpr (kSmall) {
+      if (args.hkv % 2 == 0) return launch_one<P, D, 1, 6, 2, ring_slots<P, D, 2, 128>(), false, 3, C>(args, n_items, s);
+      return launch_one<P, D, 1, 6, 1, ring_slots<P, D, 1, 64>(), false, 3, C>(args, n_items, s);
+    } else {
+      return launch_one<P, D, 1, 6, 1, ring_slots<P, D, 1, 128>(), false, 2, C>(args, n_items, s);
+    }
+  }
+  if (tiles <= 8) {
+    if constexpr (kSmall) return launch_one<P, D, 1, 8, 1, ring_slots<P, D, 1, 64>(), false, 4, C>(args, n_items, s);
+    else return launch_one<P, D, 1, 8, 1, ring_slots<P, D, 1, 128>(), false, 2, C>(args, n_items, s);
+  }
+  if (tiles <= 16) return launch_one<P, D, 2, 8, 1, ring_slots<P, D, 1, 128>(), false, 2, C>(args, n_items, s);
   return hipErrorInvalidValue;
 }
 

@@ -242,6 +242,7 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     const int32_t n = P.bucket_begin[cls + 1] - P.bucket_begin[cls];
     if (n <= 0) continue;
     a.item0 = P.bucket_begin[cls];
+    a.max_blocks = P.bucket_max_blocks[cls];
     hipError_t e;
     if (cls < 2) {
       const int w = c->waves ? c->waves : 4;

@@ -9,9 +9,11 @@
 //   K chunk c*16 + n, element e   = K[token n][d = 8c + e]            (c < D/8)
 //     -> load i gives lane (g, n) K[n][32i + 8g + 0..7]: the A operand of a
 //        16x16x32 MFMA computing S^T = K Q^T (rows = tokens).
-//   V chunk p*64 + g*16 + dl, element e = 4h + i = V[token 4g + i][d = 32p + 16h + dl]
-//     -> load p gives lane (g, dl) V^T[d][tokens 4g..4g+3] for d = 32p + dl and
-//        32p + 16 + dl: two A operands of 16x16x16 MFMAs computing O^T += V^T P^T.
+//   V is kept in 8-byte units (half a chunk): unit u = dt*64 + g*16 + dl, element
+//   i = V[token 4g + i][d = 16dt + dl]; chunk ch holds units 2ch and 2ch + 1
+//     -> 8-byte load dt of lane (g, dl) reads unit dt*64 + L: V^T[d][tokens
+//        4g..4g+3] for d = 16dt + dl, half of the A operand of the 16x16x32 MFMA
+//        computing O^T += V^T P^T (the other half comes from the next block).
 // fp32 (4 elements per chunk):
 //   K chunk c*64 + g*16 + n, element e = K[token n][d = 16c + 4g + e]   (c < D/16)
 //   V chunk t*64 + g*16 + dl, element e = V[token 4g + e][d = 16t + dl]  (t < D/16)
@@ -30,9 +32,10 @@ struct Layout<2> {
     d = 8 * (ch >> 4) + e;
   }
   __device__ static inline void v_coord(int ch, int e, int& tok, int& d) {
-    const int p = ch >> 6, g = (ch >> 4) & 3, dl = ch & 15;
+    const int u = 2 * ch + (e >> 2);
+    const int dt = u >> 6, g = (u >> 4) & 3, dl = u & 15;
     tok = 4 * g + (e & 3);
-    d = 32 * p + 16 * (e >> 2) + dl;
+    d = 16 * dt + dl;
   }
 };
 

@@ -289,7 +289,9 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       int32_t cnt = 0;
       for (const auto& x : tmp) cnt += (x.tiles <= c);
       P.bucket_begin[c + 1] = cnt;
+      P.bucket_max_blocks[c] = 0;
     }
+    for (const auto& x : tmp) P.bucket_max_blocks[x.tiles] = std::max(P.bucket_max_blocks[x.tiles], x.it.blk_count);
     std::vector<int32_t> gi_begin(ngroups);
     for (int32_t gi = 0; gi < ngroups; ++gi) {
       gi_begin[gi] = static_cast<int32_t>(P.group_items.size());

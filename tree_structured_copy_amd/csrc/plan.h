@@ -35,6 +35,7 @@ struct Plan {
   std::vector<DevItem> items;
   int32_t bucket_begin[kKernelClasses + 1] = {0, 0, 0, 0, 0, 0, 0};
   int32_t bucket_tiles[kKernelClasses] = {1, 2, 4, 6, 8, 16};
+  int32_t bucket_max_blocks[kKernelClasses] = {0, 0, 0, 0, 0, 0};  // longest item of each class
   std::vector<DevGroup> groups;
   std::vector<int32_t> gq;
   std::vector<int32_t> gqpos;

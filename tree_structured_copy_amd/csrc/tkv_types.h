@@ -70,7 +70,7 @@ struct AttnArgs {
   int32_t gsize;         // Hq / Hkv
   int32_t item0;         // first item of this launch
   float scale_log2;      // log2(e) / sqrt(D)
-  int32_t pad;
+  int32_t max_blocks;    // the longest block list among this launch's items
 };
 
 struct MergeArgs {
