@@ -31,6 +31,35 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
+# HBM bytes per launch of the decode kernel on llama_fork, from two rocprofv3
+# --pmc passes (FETCH_SIZE, then WRITE_SIZE) over `bench.py --counters`, each
+# scaled by the factor that makes the same counter read a plain 1 GiB copy
+# right.  Valid only for the kernel sources they were taken on (sha256 below);
+# after any change to them the bench line reports traffic as null.
+TRAFFIC_RECORD = {
+    "sources_sha256": "bbf0386494959869ce7444cddc8612fc0cbafe2098719708ce97f1d79a9a1245",
+    "fetch_kib_per_launch": 286771, "fetch_factor": 1.9999,   # 1 GiB read reads as 524309 KiB
+    "write_kib_per_launch": 3690, "write_factor": 1.0,        # 1 GiB written reads as 1048576 KiB
+    "hbm_bytes_per_launch": 587282525 + 3778816,
+}
+
+
+def _kernel_sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tree_structured_copy_amd", "csrc")
+    for f in ("attn.hip", "attn_common.h", "layout.h", "tkv_types.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _recorded_traffic():
+    rec = TRAFFIC_RECORD
+    if not rec or rec.get("sources_sha256") != _kernel_sources_sha():
+        return None
+    return rec["hbm_bytes_per_launch"]
+
 
 class _Copy:
     """One independent instance of a workload on the GPU: its tree, and every
@@ -251,6 +280,29 @@ def measure(name, copies, steps, warmup, rebuild=False):
     return res
 
 
+def _counters_run(copies):
+    """What the traffic figures are taken on: 3 launches of a plain streaming
+    kernel over a 1 GiB buffer (dst = 2 * src: 1 GiB read + 1 GiB written per
+    launch), then 8 decode calls on the fork workload, rotating over `copies`
+    independent copies."""
+    import torch
+    from workloads import recipes
+    n = 1 << 30
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 2, out=dst)
+    torch.cuda.synchronize()
+    items = _prepare(recipes.llama_fork(), copies)
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(8):
+        items[i % len(items)].step(stream)
+    torch.cuda.synchronize()
+    ubytes, _ = items[0].unique_bytes()
+    print(json.dumps({"counters_run": True, "copy_bytes": n, "copy_launches": 3, "decode_calls": 8,
+                      "unique_kv_bytes_per_call": ubytes, "sources_sha256": _kernel_sources_sha()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,6 +314,9 @@ def main():
     ap.add_argument("--all", action="store_true", help="also measure the MCTS and 32-layer workloads")
     ap.add_argument("--cpu-requests", type=int, default=32)
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--counters", action="store_true",
+                    help="a short run for rocprofv3 --pmc passes: a plain 1 GiB copy (the counters' "
+                         "calibration), then decode calls on the fork workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the fork workload's requests are independent trees, so "
@@ -271,6 +326,10 @@ def main():
 
     import torch
     torch.cuda.init()
+
+    if args.counters:
+        _counters_run(args.copies)
+        return
 
     main_res = measure("llama_fork", args.copies, args.steps, args.warmup, rebuild=True)
     ms = main_res["ms_per_step"]
@@ -315,7 +374,7 @@ def main():
         "unique_kv_bytes": ubytes,
         "plan": main_res["plan"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": None,
+                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": _recorded_traffic(),
                      "kernel": "attn_partial_kernel<BF16,128,1,4,false>",
                      "kernel_ms": main_res["partial_kernel_ms_per_call"],
                      "merge_kernel_ms": main_res["merge_kernel_ms_per_call"]},
