@@ -306,8 +306,10 @@ def _counters_run(copies):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the clock ramps up from idle over the first tens of milliseconds of load:
+    # 300 warm-up steps (about 30 ms at these shapes) reach its steady state
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
