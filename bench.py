@@ -200,6 +200,23 @@ def _fork_latency_ns():
     return res
 
 
+def _fork_sweep_ns():
+    """Fork latency from the host-only C++ benchmark built beside the library
+    (tree_structured_copy_amd/fork_bench): median ns per tkv_fork(n) over
+    prefix 16..65536 tokens and path depth 1..500 nodes, no ctypes in between."""
+    import subprocess
+    exe = os.path.join(ROOT, "tree_structured_copy_amd", "fork_bench")
+    if not os.path.exists(exe):
+        return None
+    out = subprocess.run([exe, "400"], capture_output=True, text=True, timeout=120, check=True).stdout
+    grid = json.loads(out)
+    summary = {}
+    for n in (1, 4, 16):
+        vals = [v for k, v in grid.items() if k.endswith(":%d" % n)]
+        summary["n=%d" % n] = {"min": min(vals), "max": max(vals), "median": sorted(vals)[len(vals) // 2]}
+    return {"summary": summary, "grid_prefix_depth_n": grid}
+
+
 def _cpu_baseline(requests: int, reps: int):
     """The float64 oracle on the first ``requests`` requests of the fork workload:
     materialise each branch's history and run textbook attention for all heads."""
@@ -382,6 +399,7 @@ def main():
                      "merge_kernel_ms": main_res["merge_kernel_ms_per_call"]},
         "verify": verify,
         "other_workloads": others or None,
+        "fork_latency_ns": _fork_sweep_ns(),
         "fork_latency_ns_ctypes": _fork_latency_ns(),
         "cpu_baseline": cpu,
     }

@@ -268,6 +268,21 @@ def _median_fork_ns(prefix_tokens, depth, reps=3000):
         tkv.tkv_destroy(c)
 
 
+def test_fork_bench_flat_over_prefix_and_depth():
+    """The C++ fork benchmark: per n, the slowest (prefix, depth) point is within
+    3x (+50 ns) of the fastest, over prefix 16..65536 tokens and depth 1..500."""
+    import json
+    import subprocess
+    exe = os.path.join(ROOT, "tree_structured_copy_amd", "fork_bench")
+    if not os.path.exists(exe):
+        pytest.skip("fork_bench not built")
+    grid = json.loads(subprocess.run([exe, "100"], capture_output=True, text=True, timeout=120, check=True).stdout)
+    assert len(grid) >= 40
+    for n in (1, 4, 16):
+        vals = [v for k, v in grid.items() if k.endswith(":%d" % n)]
+        assert max(vals) < 3 * min(vals) + 50, (n, min(vals), max(vals))
+
+
 def test_fork_latency_flat_in_prefix_and_depth():
     base = _median_fork_ns(16, 1)
     for prefix, depth in [(65536, 1), (16, 500), (65536, 500)]:

@@ -84,7 +84,12 @@ def build(verbose: bool = False, jobs: int = 8) -> dict:
     genlib = os.path.join(ROOT, "workloads", "libtkvgen.so")
     _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, gen_obj, "-o", genlib + ".tmp"], verbose)
     os.replace(genlib + ".tmp", genlib)
-    return {"libtkv": lib, "libtkvgen": genlib}
+    # host-only fork-latency benchmark, linked against the library it measures
+    fb = os.path.join(HERE, "fork_bench")
+    _run([CXX, "-O2", "-std=c++17", "-I" + INCLUDE, os.path.join(HERE, "fork_bench.cpp"), "-L" + HERE, "-ltkv",
+          "-Wl,-rpath,$ORIGIN", "-o", fb + ".tmp"], verbose)
+    os.replace(fb + ".tmp", fb)
+    return {"libtkv": lib, "libtkvgen": genlib, "fork_bench": fb}
 
 
 if __name__ == "__main__":
