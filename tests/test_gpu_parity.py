@@ -42,6 +42,35 @@ def test_small_mcts():
     assert_close(run_both(wl), "bf16")
 
 
+@pytest.mark.parametrize("cascade,dtype,hq,hkv,d", [(1, "bf16", 8, 2, 128), (0, "bf16", 8, 2, 128),
+                                                      (1, "f32", 4, 1, 64), (1, "bf16", 16, 8, 64)])
+def test_mcts_cascade(cascade, dtype, hq, hkv, d):
+    """64 leaves of a branching-4 tree: groups of 16 row tiles whose deep nodes
+    are private to one leaf.  With the cascade on, those nodes go to one-tile
+    subgroups and every query merges its records from both; off, one group
+    reads everything.  Both against the oracle on every row."""
+    wl = recipes.mcts_workload("mcts_cascade", dtype=dtype, q_heads=hq, kv_heads=hkv, head_dim=d, root_tokens=70,
+                               branching=4, depth=5, leaves=64, node_tokens=9, seed=41 + cascade)
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    need_gpu()
+    lib = LibReplay(wl)
+    try:
+        tkv.tkv_set_option(lib.c, tkv.TKV_OPT_CASCADE, cascade)
+        i = lib.build()
+        op = wl.ops[i]
+        info = tkv.tkv_plan_info_get(lib.c, lib.handles(op), None)
+        say("plan %s" % info)
+        ipk = info["items_per_kernel"]
+        if cascade:
+            assert ipk[0] > 0 and sum(ipk[4:]) > 0, info
+        else:
+            assert ipk[0] == 0, info
+    finally:
+        lib.close()
+    assert_close(run_both(wl, options={6: cascade}), dtype)
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_random_sessions(seed):
     dtype = "bf16" if seed % 2 == 0 else "f32"

@@ -65,6 +65,12 @@ struct tkv_cache {
   size_t pinned_cap = 0;
   hipEvent_t pinned_ev = nullptr;
   bool pinned_busy = false;
+  // side streams (default priority) on which the kernel classes of one call
+  // after the first run concurrently, forked from and joined back to the
+  // caller's stream with events
+  hipStream_t aux[kKernelClasses - 1] = {};
+  hipEvent_t fork_ev = nullptr;
+  hipEvent_t join_ev[kKernelClasses - 1] = {};
   // profiling
   bool prof = false;
   std::vector<std::array<hipEvent_t, 3>> prof_used;
@@ -238,25 +244,45 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     for (auto& e : ev) e = c->get_event();
     if (ev[0] && ev[1] && ev[2]) (void)hipEventRecord(ev[0], stream);
   }
-  for (int cls = 0; cls < kKernelClasses; ++cls) {
+  // kernel classes of this call: the first runs on the caller's stream, every
+  // further one on a side stream, all at once
+  int classes[kKernelClasses];
+  int ncls = 0;
+  for (int cls = 0; cls < kKernelClasses; ++cls)
+    if (P.bucket_begin[cls + 1] > P.bucket_begin[cls]) classes[ncls++] = cls;
+  if (ncls > 1) {
+    if (!c->fork_ev && hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming) != hipSuccess) return TKV_E_DEVICE;
+    for (int k = 0; k < ncls - 1; ++k) {
+      if (!c->aux[k] && hipStreamCreateWithFlags(&c->aux[k], hipStreamNonBlocking) != hipSuccess) return TKV_E_DEVICE;
+      if (!c->join_ev[k] && hipEventCreateWithFlags(&c->join_ev[k], hipEventDisableTiming) != hipSuccess)
+        return TKV_E_DEVICE;
+    }
+    if (hipEventRecord(c->fork_ev, stream) != hipSuccess) return TKV_E_DEVICE;
+  }
+  for (int k = 0; k < ncls; ++k) {
+    const int cls = classes[k];
     const int32_t n = P.bucket_begin[cls + 1] - P.bucket_begin[cls];
-    if (n <= 0) continue;
+    hipStream_t st = k == 0 ? stream : c->aux[k - 1];
+    if (k > 0 && hipStreamWaitEvent(st, c->fork_ev, 0) != hipSuccess) return TKV_E_DEVICE;
     a.item0 = P.bucket_begin[cls];
     a.max_blocks = P.bucket_max_blocks[cls];
     hipError_t e;
     if (cls < 2) {
       const int w = c->waves ? c->waves : 4;
-      e = launch_attn_partial(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], w, P.causal, a, n, stream);
+      e = launch_attn_partial(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], w, P.causal, a, n, st);
     } else {
-      e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], P.causal, a, n, stream);
+      e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], P.causal, a, n, st);
     }
     if (e != hipSuccess) return TKV_E_DEVICE;
+    if (k > 0 && hipEventRecord(c->join_ev[k - 1], st) != hipSuccess) return TKV_E_DEVICE;
   }
+  for (int k = 1; k < ncls; ++k)
+    if (hipStreamWaitEvent(stream, c->join_ev[k - 1], 0) != hipSuccess) return TKV_E_DEVICE;
   if (c->prof && ev[1]) (void)hipEventRecord(ev[1], stream);
   if (P.any_merge) {
     MergeArgs m{};
     m.items = a.items;
-    m.group_items = reinterpret_cast<const int32_t*>(dev + P.off_group_items);
+    m.parts = reinterpret_cast<const DevPart*>(dev + P.off_parts);
     m.merge = reinterpret_cast<const DevMerge*>(dev + P.off_merge);
     m.part_acc = a.part_acc;
     m.part_ml = a.part_ml;
@@ -341,6 +367,11 @@ int tkv_destroy(tkv_cache* c) {
     for (auto& t : c->prof_used)
       for (auto e : t) (void)hipEventDestroy(e);
     for (auto e : c->ev_pool) (void)hipEventDestroy(e);
+    for (auto& st : c->aux)
+      if (st) (void)hipStreamDestroy(st);
+    for (auto& e : c->join_ev)
+      if (e) (void)hipEventDestroy(e);
+    if (c->fork_ev) (void)hipEventDestroy(c->fork_ev);
   }
   delete c;
   return TKV_OK;
@@ -506,6 +537,10 @@ int tkv_set_option(tkv_cache* c, int32_t key, int64_t value) {
       if (value != 0 && value != 4 && value != 8) return TKV_E_RANGE;
       c->waves = static_cast<int32_t>(value);
       break;
+    case TKV_OPT_CASCADE:
+      if (value != 0 && value != 1) return TKV_E_RANGE;
+      c->opt.cascade = static_cast<int32_t>(value);
+      break;
     default:
       return TKV_E_INVAL;
   }
@@ -521,6 +556,7 @@ int tkv_get_option(const tkv_cache* c, int32_t key, int64_t* value) {
     case TKV_OPT_MAX_ROWS: *value = c->opt.max_rows; break;
     case TKV_OPT_PLAN_CACHE: *value = c->plan_cache ? 1 : 0; break;
     case TKV_OPT_WAVES: *value = c->waves; break;
+    case TKV_OPT_CASCADE: *value = c->opt.cascade; break;
     default: return TKV_E_INVAL;
   }
   return TKV_OK;

@@ -17,7 +17,8 @@ hipError_t launch_attn_partial(int dtype, int head_dim, int tiles, int waves, bo
 hipError_t launch_attn_rows(int dtype, int head_dim, int tiles, bool causal, const AttnArgs& args, int32_t n_items,
                             hipStream_t stream);
 
-// Log-sum-exp merge of split-K partials into out; grid = nq * Hq.
+// Log-sum-exp merge of each query's partial records into out; one wave per
+// (query, query head), four per workgroup.
 hipError_t launch_attn_merge(int head_dim, const MergeArgs& args, hipStream_t stream);
 
 // Scatter appended tokens into pool tiles; grid = nent x Hkv x layers.

@@ -35,7 +35,7 @@ void Plan::layout() {
   off_gq = o;           o = align256(o + gq.size() * sizeof(int32_t));
   off_gqpos = o;        o = align256(o + gqpos.size() * sizeof(int32_t));
   off_blocks = o;       o = align256(o + blocks.size() * sizeof(DevBlock));
-  off_group_items = o;  o = align256(o + group_items.size() * sizeof(int32_t));
+  off_parts = o;        o = align256(o + parts.size() * sizeof(DevPart));
   off_merge = o;        o = align256(o + merge.size() * sizeof(DevMerge));
   bytes = o;
 }
@@ -47,7 +47,7 @@ void Plan::serialise(void* dst) const {
   std::memcpy(p + off_gq, gq.data(), gq.size() * sizeof(int32_t));
   std::memcpy(p + off_gqpos, gqpos.data(), gqpos.size() * sizeof(int32_t));
   std::memcpy(p + off_blocks, blocks.data(), blocks.size() * sizeof(DevBlock));
-  std::memcpy(p + off_group_items, group_items.data(), group_items.size() * sizeof(int32_t));
+  std::memcpy(p + off_parts, parts.data(), parts.size() * sizeof(DevPart));
   std::memcpy(p + off_merge, merge.data(), merge.size() * sizeof(DevMerge));
 }
 
@@ -178,83 +178,137 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
         }
       }
     }
-    const int32_t ngroups = static_cast<int32_t>(group_q.size());
 
-    // 4. per-group block lists
+    // 4. per-group block lists.  A large group (8+ row tiles) whose blocks are
+    //    partly narrow -- seen only by queries that one row tile holds, as the
+    //    deep, private nodes of a search tree are -- keeps its widely shared
+    //    blocks and hands each narrow node to a one-tile subgroup of its
+    //    queries: a large group costs row-tile work on every block it reads,
+    //    a one-tile group about its memory time.  A query then has partial
+    //    records in both groups, merged afterwards.
     Plan& P = *out;
     P = Plan();
     P.nqueries = static_cast<int32_t>(total_q);
     P.causal = nq != nullptr;
-    P.groups.resize(ngroups);
-    std::vector<int32_t> gblk_begin(ngroups), gblk_count(ngroups);
+    struct GroupOut {
+      int32_t blk_begin, blk_count, root;
+      bool partials;  // its queries have records in another group too
+    };
+    std::vector<GroupOut> gout;
+    std::vector<std::vector<std::pair<int32_t, int32_t>>> qmem(total_q);  // (group, j)
     std::vector<uint64_t> mask(nl, 0);
     std::vector<int32_t> touched;
-    std::vector<int32_t> query_group(total_q), query_j(total_q);
-    for (int32_t gi = 0; gi < ngroups; ++gi) {
-      const auto& qs = group_q[gi];
-      P.groups[gi].q_begin = static_cast<int32_t>(P.gq.size());
-      P.groups[gi].nq = static_cast<int32_t>(qs.size());
-      int32_t min_pos = INT32_MAX;
-      for (const auto& qq : qs) min_pos = std::min(min_pos, qq.pos);
-      P.groups[gi].min_pos = min_pos;
-      P.groups[gi].pad1 = 0;
-      touched.clear();
-      for (size_t j = 0; j < qs.size(); ++j) {
+    const int32_t sub = std::max(1, 16 / q_per_kv);  // queries of a one-tile subgroup
+    auto emit_group = [&](const Query* qs, int32_t n, int32_t root, bool partials) {
+      const int32_t gi = static_cast<int32_t>(P.groups.size());
+      DevGroup g;
+      g.q_begin = static_cast<int32_t>(P.gq.size());
+      g.nq = n;
+      g.min_pos = INT32_MAX;
+      g.pad1 = 0;
+      for (int32_t j = 0; j < n; ++j) {
         P.gq.push_back(qs[j].global);
         P.gqpos.push_back(qs[j].pos);
-        query_group[qs[j].global] = gi;
-        query_j[qs[j].global] = static_cast<int32_t>(j);
+        g.min_pos = std::min(g.min_pos, qs[j].pos);
+        qmem[qs[j].global].push_back({gi, j});
+      }
+      P.groups.push_back(g);
+      gout.push_back({static_cast<int32_t>(P.blocks.size()), 0, root, partials});
+      return gi;
+    };
+    auto emit_node = [&](int32_t k, uint64_t m) {
+      const Node& nd = tree.node(ln[k].node);
+      const int32_t nb = static_cast<int32_t>(nd.blocks.size());
+      for (int32_t b = 0; b < nb; ++b) {
+        DevBlock e;
+        e.id = nd.blocks[b];
+        e.pos = static_cast<int32_t>(nd.base + 16 * (int64_t)b);
+        e.valid = (b == nb - 1) ? nd.tail_valid() : 16;
+        e.pad = 0;
+        e.mask = m;
+        P.blocks.push_back(e);
+      }
+    };
+    auto close_group = [&]() { gout.back().blk_count = static_cast<int32_t>(P.blocks.size()) - gout.back().blk_begin; };
+    // the subgroup a node's queries fit in, or -1
+    auto narrow = [&](uint64_t m) {
+      const int32_t lo = __builtin_ctzll(m), hi = 63 - __builtin_clzll(m);
+      return lo / sub == hi / sub ? lo / sub : -1;
+    };
+    for (size_t g0 = 0; g0 < group_q.size(); ++g0) {
+      const auto& qs = group_q[g0];
+      const int32_t n = static_cast<int32_t>(qs.size());
+      touched.clear();
+      for (int32_t j = 0; j < n; ++j)
         for (int32_t k = loc[tip[qs[j].handle]]; k >= 0; k = ln[k].parent) {
           if (!mask[k]) touched.push_back(k);
           mask[k] |= 1ull << j;
         }
-      }
       std::sort(touched.begin(), touched.end(), [&](int32_t a, int32_t b) { return ln[a].pre < ln[b].pre; });
-      gblk_begin[gi] = static_cast<int32_t>(P.blocks.size());
-      for (int32_t k : touched) {
-        const Node& nd = tree.node(ln[k].node);
-        const int32_t nb = static_cast<int32_t>(nd.blocks.size());
-        for (int32_t b = 0; b < nb; ++b) {
-          DevBlock e;
-          e.id = nd.blocks[b];
-          e.pos = static_cast<int32_t>(nd.base + 16 * (int64_t)b);
-          e.valid = (b == nb - 1) ? nd.tail_valid() : 16;
-          e.pad = 0;
-          e.mask = mask[k];
-          P.blocks.push_back(e);
+      bool cascade = false;
+      if (opt.cascade && (n * q_per_kv + 15) / 16 >= 8 && n > sub) {
+        int64_t all = 0, thin = 0;
+        for (int32_t k : touched) {
+          const int64_t nb = static_cast<int64_t>(tree.node(ln[k].node).blocks.size());
+          all += nb;
+          if (narrow(mask[k]) >= 0) thin += nb;
         }
-        mask[k] = 0;
+        cascade = thin * 8 >= all && thin > 0;
       }
-      gblk_count[gi] = static_cast<int32_t>(P.blocks.size()) - gblk_begin[gi];
+      emit_group(qs.data(), n, group_root[g0], cascade);
+      for (int32_t k : touched)
+        if (!cascade || narrow(mask[k]) < 0) emit_node(k, mask[k]);
+      close_group();
+      if (cascade) {
+        for (int32_t t = 0; t * sub < n; ++t) {
+          bool any = false;
+          for (int32_t k : touched) any |= narrow(mask[k]) == t;
+          if (!any) continue;
+          emit_group(qs.data() + t * sub, std::min(sub, n - t * sub), group_root[g0], true);
+          for (int32_t k : touched)
+            if (narrow(mask[k]) == t) emit_node(k, mask[k] >> (t * sub));
+          close_group();
+        }
+      }
+      for (int32_t k : touched) mask[k] = 0;
     }
+    const int32_t ngroups = static_cast<int32_t>(P.groups.size());
 
-    // 5. split-K chunking and items
-    int64_t total_entries = 0;
-    for (int32_t gi = 0; gi < ngroups; ++gi) total_entries += gblk_count[gi];
+    // 5. split-K chunking and items.  A super-block costs a register-tile
+    //    workgroup (1-2 row tiles) about its memory time; an LDS-staged
+    //    workgroup (3+ tiles) pays a barrier and its waves' latency chain on
+    //    every super-block, about four times as long.  A group's chunk is the
+    //    per-workgroup share of the call's weighted work divided by its weight,
+    //    so that every workgroup of every class ends at about the same time.
+    auto weight = [&](int32_t gi) -> int64_t { return (P.groups[gi].nq * q_per_kv + 15) / 16 <= 2 ? 1 : 4; };
+    int64_t work = 0;
+    for (int32_t gi = 0; gi < ngroups; ++gi) work += gout[gi].blk_count * weight(gi);
     const int64_t tw = std::max<int32_t>(1, opt.target_wgs);
-    const int64_t chunk = std::min<int64_t>(kRowsMaxItemBlocks,
-                                            std::max<int64_t>(std::max<int32_t>(1, opt.min_chunk),
-                                                              (total_entries * num_kv_heads + tw - 1) / tw));
+    const int64_t unit = (work * num_kv_heads + tw - 1) / tw;  // weighted blocks per workgroup
+    auto chunk_of = [&](int32_t gi) {
+      return std::min<int64_t>(kRowsMaxItemBlocks, std::max<int64_t>(std::max<int32_t>(1, opt.min_chunk),
+                                                                     (unit + weight(gi) - 1) / weight(gi)));
+    };
     struct Tmp {
       DevItem it;
       int32_t tiles, root, chunk;
     };
     std::vector<Tmp> tmp;
-    std::vector<int32_t> gchunks(ngroups);
     int64_t slots = 0;
     for (int32_t gi = 0; gi < ngroups; ++gi) {
-      const int32_t nb = gblk_count[gi];
+      const int32_t nb = gout[gi].blk_count;
+      if (nb == 0) continue;
+      const int64_t chunk = chunk_of(gi);
       const int32_t nc = static_cast<int32_t>(std::max<int64_t>(1, (nb + chunk - 1) / chunk));
-      gchunks[gi] = nc;
       const int32_t tiles = kernel_class((P.groups[gi].nq * q_per_kv + 15) / 16);
       int32_t at = 0;
       for (int32_t c = 0; c < nc; ++c) {
         const int32_t cnt = nb / nc + (c < nb % nc ? 1 : 0);
         Tmp t;
         t.it.group = gi;
-        t.it.blk_begin = gblk_begin[gi] + at;
+        t.it.blk_begin = gout[gi].blk_begin + at;
         t.it.blk_count = cnt;
-        if (nc == 1) {
+        if (nc == 1 && !gout[gi].partials) {
           t.it.part_base = -1;
         } else {
           t.it.part_base = static_cast<int32_t>(slots);
@@ -262,7 +316,7 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
           if (slots > INT32_MAX) return TKV_E_RANGE;
         }
         t.tiles = tiles;
-        t.root = group_root[gi];
+        t.root = gout[gi].root;
         t.chunk = c;
         tmp.push_back(t);
         at += cnt;
@@ -292,21 +346,24 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       P.bucket_max_blocks[c] = 0;
     }
     for (const auto& x : tmp) P.bucket_max_blocks[x.tiles] = std::max(P.bucket_max_blocks[x.tiles], x.it.blk_count);
-    std::vector<int32_t> gi_begin(ngroups);
-    for (int32_t gi = 0; gi < ngroups; ++gi) {
-      gi_begin[gi] = static_cast<int32_t>(P.group_items.size());
-      P.group_items.insert(P.group_items.end(), gitems[gi].begin(), gitems[gi].end());
-    }
+    // merge records: every partial of a query, in the order its groups were made
     P.merge.resize(total_q);
     for (int64_t q = 0; q < total_q; ++q) {
-      const int32_t gi = query_group[q];
       DevMerge m;
-      m.gi_begin = gi_begin[gi];
-      m.gi_count = gchunks[gi] > 1 ? gchunks[gi] : 0;
-      m.j = query_j[q];
-      m.pad = 0;
+      m.p_begin = static_cast<int32_t>(P.parts.size());
+      int32_t direct = 0;
+      for (const auto& gj : qmem[q])
+        for (int32_t item : gitems[gj.first]) {
+          if (P.items[item].part_base < 0) {
+            ++direct;
+            continue;
+          }
+          P.parts.push_back({item, gj.second});
+        }
+      m.p_count = static_cast<int32_t>(P.parts.size()) - m.p_begin;
+      if (direct + m.p_count == 0 || (direct > 0 && (direct > 1 || m.p_count > 0))) return TKV_E_INVAL;
       P.merge[q] = m;
-      if (m.gi_count) P.any_merge = true;
+      if (m.p_count) P.any_merge = true;
     }
 
     // statistics: distinct blocks read and their valid slots

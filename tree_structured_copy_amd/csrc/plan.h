@@ -27,6 +27,7 @@ struct PlanOptions {
   int32_t target_wgs = 256;
   int32_t min_chunk = 32;
   int32_t max_rows = kMaxRows;
+  int32_t cascade = 1;  // split narrow blocks of large groups into one-tile subgroups
 };
 
 struct Plan {
@@ -40,7 +41,7 @@ struct Plan {
   std::vector<int32_t> gq;
   std::vector<int32_t> gqpos;
   std::vector<DevBlock> blocks;
-  std::vector<int32_t> group_items;
+  std::vector<DevPart> parts;
   std::vector<DevMerge> merge;
   int32_t nqueries = 0;
   int64_t partial_slots = 0;  // records of (m, l, acc[D])
@@ -52,7 +53,7 @@ struct Plan {
 
   // serialised layout (byte offsets into one device buffer)
   size_t off_items = 0, off_groups = 0, off_gq = 0, off_gqpos = 0, off_blocks = 0,
-         off_group_items = 0, off_merge = 0, bytes = 0;
+         off_parts = 0, off_merge = 0, bytes = 0;
   void layout();
   void serialise(void* dst) const;
 };

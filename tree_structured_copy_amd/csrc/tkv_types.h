@@ -43,14 +43,17 @@ struct DevBlock {
   uint64_t mask;
 };
 
-// Per query: where its partial records are (items group_items[gi_begin ..
-// gi_begin + gi_count), query index j inside its group).  gi_count == 0: the
-// query's output was written directly.
-struct DevMerge {
-  int32_t gi_begin;
-  int32_t gi_count;
+// One partial record of a query: work item `item` wrote it at slot
+// items[item].part_base + j * Hq + head (j = the query's index in that item's
+// group).  A query's records are parts[p_begin .. p_begin + p_count) of its
+// DevMerge; p_count == 0: its output was written directly.
+struct DevPart {
+  int32_t item;
   int32_t j;
-  int32_t pad;
+};
+struct DevMerge {
+  int32_t p_begin;
+  int32_t p_count;
 };
 
 struct AttnArgs {
@@ -75,7 +78,7 @@ struct AttnArgs {
 
 struct MergeArgs {
   const DevItem* items;
-  const int32_t* group_items;
+  const DevPart* parts;
   const DevMerge* merge;
   const float* part_acc;
   const float* part_ml;
