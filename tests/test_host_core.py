@@ -308,7 +308,9 @@ def test_error_codes_and_strong_guarantee():
                           (lambda: tkv.tkv_release(c, 0), tkv.TKV_E_BADSEQ),
                           (lambda: tkv.tkv_attend_decode(c, 0, [s], 1, 1), tkv.TKV_E_NODEVICE),
                           (lambda: tkv.tkv_gather(c, s, 0, 1, 1), tkv.TKV_E_NODEVICE),
-                          (lambda: tkv.tkv_set_option(c, tkv.TKV_OPT_MAX_ROWS, 8), tkv.TKV_E_RANGE)]:
+                          (lambda: tkv.tkv_set_option(c, tkv.TKV_OPT_MAX_ROWS, 8), tkv.TKV_E_RANGE),
+                          (lambda: tkv.tkv_set_option(c, tkv.TKV_OPT_CASCADE, 2), tkv.TKV_E_RANGE),
+                          (lambda: tkv.tkv_set_option(c, 99, 1), tkv.TKV_E_INVAL)]:
             with pytest.raises(tkv.TkvError) as e:
                 bad()
             assert e.value.code == code
@@ -367,3 +369,48 @@ def test_plan_shapes():
         assert tkv.tkv_get_counters(c)["plans_built"] == before  # cached
     finally:
         tkv.tkv_destroy(c)
+
+
+def _host_plan(wl, opts=()):
+    c = host_cache(wl.num_blocks, wl.layers, wl.q_heads, wl.kv_heads, wl.head_dim)
+    try:
+        for k, v in opts:
+            tkv.tkv_set_option(c, k, v)
+        h = {}
+        for op in wl.ops:
+            if op[0] == "new":
+                h[op[1]] = tkv.tkv_seq_new(c)
+            elif op[0] == "append":
+                tkv.tkv_append(c, h[op[1]], op[2])
+            elif op[0] == "fork":
+                for n, s in zip(op[3], tkv.tkv_fork(c, h[op[1]], op[2])):
+                    h[n] = s
+            elif op[0] == "release":
+                tkv.tkv_release(c, h.pop(op[1]))
+            elif op[0] == "truncate":
+                tkv.tkv_truncate(c, h[op[1]], op[2])
+            elif op[0] in ("decode", "verify"):
+                nq = op[3] if op[0] == "verify" else None
+                return tkv.tkv_plan_info_get(c, [h[x] for x in op[2]], nq)
+    finally:
+        tkv.tkv_destroy(c)
+
+
+def test_plan_cascade_shapes():
+    """The search tree's large groups hand their private (one-leaf) nodes to
+    one-tile subgroups: more groups, the same block entries (nothing is listed
+    twice more than before), one-tile items; the fork and verify workloads,
+    whose groups are small or whose blocks are all wide, are unchanged."""
+    wl = recipes.mcts_tree()
+    on = _host_plan(wl, [(tkv.TKV_OPT_TARGET_WGS, 256)])
+    off = _host_plan(wl, [(tkv.TKV_OPT_TARGET_WGS, 256), (tkv.TKV_OPT_CASCADE, 0)])
+    assert on["block_entries"] == off["block_entries"]
+    assert on["unique_blocks"] == off["unique_blocks"]
+    assert on["groups"] > off["groups"]
+    assert on["items_per_kernel"][0] > 0 and off["items_per_kernel"][0] == 0
+    for name in ("llama_fork", "spec_verify"):
+        w = recipes.STANDARD[name]()
+        a = _host_plan(w, [(tkv.TKV_OPT_TARGET_WGS, 256)])
+        b = _host_plan(w, [(tkv.TKV_OPT_TARGET_WGS, 256), (tkv.TKV_OPT_CASCADE, 0)])
+        assert a == b, name
+        assert a["partial_slots"] == 0
