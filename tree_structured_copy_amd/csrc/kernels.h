@@ -1,4 +1,4 @@
-// Launchers for the HIP kernels (defined in attn.hip and kv.hip).
+// Launchers for the HIP kernels (attn.hip, attn_rows.hip, attn_merge.hip, kv.hip).
 #pragma once
 #include <hip/hip_runtime_api.h>
 
