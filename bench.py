@@ -297,11 +297,11 @@ def measure(name, copies, steps, warmup, rebuild=False):
     return res
 
 
-def _counters_run(copies):
+def _counters_run(copies, workload="llama_fork"):
     """What the traffic figures are taken on: 3 launches of a plain streaming
     kernel over a 1 GiB buffer (dst = 2 * src: 1 GiB read + 1 GiB written per
-    launch), then 8 decode calls on the fork workload, rotating over `copies`
-    independent copies."""
+    launch), then 8 steps of the workload (by default the fork workload's decode
+    call), rotating over `copies` independent copies."""
     import torch
     from workloads import recipes
     n = 1 << 30
@@ -310,14 +310,15 @@ def _counters_run(copies):
     for _ in range(3):
         torch.mul(src, 2, out=dst)
     torch.cuda.synchronize()
-    items = _prepare(recipes.llama_fork(), copies)
+    items = _prepare(recipes.STANDARD[workload](), copies)
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(8):
         items[i % len(items)].step(stream)
     torch.cuda.synchronize()
     ubytes, _ = items[0].unique_bytes()
-    print(json.dumps({"counters_run": True, "copy_bytes": n, "copy_launches": 3, "decode_calls": 8,
-                      "unique_kv_bytes_per_call": ubytes, "sources_sha256": _kernel_sources_sha()}), flush=True)
+    print(json.dumps({"counters_run": True, "workload": workload, "copy_bytes": n, "copy_launches": 3,
+                      "steps": 8, "unique_kv_bytes_per_call": ubytes, "sources_sha256": _kernel_sources_sha()}),
+          flush=True)
 
 
 def main():
@@ -334,8 +335,10 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=32)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--counters", action="store_true",
-                    help="a short run for rocprofv3 --pmc passes: a plain 1 GiB copy (the counters' "
-                         "calibration), then decode calls on the fork workload")
+                    help="a short run for rocprofv3 --pmc passes: a plain 1 GiB streaming kernel (the "
+                         "counters' calibration), then 8 steps of --counters-workload")
+    ap.add_argument("--counters-workload", default="llama_fork",
+                    help="workload of the --counters run (llama_fork, spec_verify, mcts_tree, ...)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the fork workload's requests are independent trees, so "
@@ -347,7 +350,7 @@ def main():
     torch.cuda.init()
 
     if args.counters:
-        _counters_run(args.copies)
+        _counters_run(args.copies, args.counters_workload)
         return
 
     main_res = measure("llama_fork", args.copies, args.steps, args.warmup, rebuild=True)
