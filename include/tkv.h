@@ -130,9 +130,10 @@ int tkv_workspace_size(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int
  * ws: device scratch of at least tkv_workspace_size() bytes (may be NULL if that is 0),
  * owned by the call until the stream passes it.  A handle may appear more than once.
  * Ordering: the call's work is ordered on `stream`; when its plan holds several kernel
- * classes, the library forks them onto side streams of its own (default priority) with
- * an event and joins them back before the merge, so everything the call does is
- * complete once `stream` passes the point where the call was made.
+ * classes, they run one after another on `stream`, or at once on side streams of the
+ * library's own (default priority) forked from and joined back to `stream` with events
+ * (TKV_OPT_CONCURRENT), so everything the call does is complete once `stream` passes
+ * the point where the call was made.
  * TKV_E_EMPTY if a handle has no tokens. */
 int tkv_attend_decode(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t nseq,
                       const void* q, float* out, void* ws, size_t ws_bytes, void* stream);
@@ -196,8 +197,11 @@ enum {
   TKV_OPT_MAX_ROWS = 3,     /* max rows (queries x Hq/Hkv) per group: 16..256 (default 256) */
   TKV_OPT_PLAN_CACHE = 4,   /* 1 = reuse uploaded plans while the tree is unchanged (default) */
   TKV_OPT_WAVES = 5,        /* waves per attention workgroup: 4 or 8 (0 = default, 4) */
-  TKV_OPT_CASCADE = 6       /* 1 = a group of 8+ row tiles hands blocks that only one row tile's
+  TKV_OPT_CASCADE = 6,      /* 1 = a group of 8+ row tiles hands blocks that only one row tile's
                                queries see to one-tile subgroups, merged after (default); 0 = off */
+  TKV_OPT_CONCURRENT = 7    /* how a call's kernel classes run: 0 = one after another on the call's
+                               stream; 1 = at once, on side streams of the library's own forked from
+                               and joined back to the call's stream (default) */
 };
 int tkv_set_option(tkv_cache* c, int32_t key, int64_t value);
 int tkv_get_option(const tkv_cache* c, int32_t key, int64_t* value);

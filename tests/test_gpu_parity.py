@@ -71,6 +71,17 @@ def test_mcts_cascade(cascade, dtype, hq, hkv, d):
     assert_close(run_both(wl, options={6: cascade}), dtype)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_concurrent_modes(mode):
+    """The kernel classes of one call run one after another (0) or on side
+    streams (1): the same outputs against the oracle in both modes, on a plan
+    with one-tile, 8-tile and 16-tile items and a merge."""
+    from tree_structured_copy_amd import tkv
+    wl = recipes.mcts_workload("mcts_modes", dtype="bf16", q_heads=8, kv_heads=2, head_dim=128, root_tokens=70,
+                               branching=4, depth=5, leaves=64, node_tokens=9, seed=43)
+    assert_close(run_both(wl, options={tkv.TKV_OPT_CONCURRENT: mode}), "bf16")
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_random_sessions(seed):
     dtype = "bf16" if seed % 2 == 0 else "f32"

@@ -310,6 +310,8 @@ def test_error_codes_and_strong_guarantee():
                           (lambda: tkv.tkv_gather(c, s, 0, 1, 1), tkv.TKV_E_NODEVICE),
                           (lambda: tkv.tkv_set_option(c, tkv.TKV_OPT_MAX_ROWS, 8), tkv.TKV_E_RANGE),
                           (lambda: tkv.tkv_set_option(c, tkv.TKV_OPT_CASCADE, 2), tkv.TKV_E_RANGE),
+                          (lambda: tkv.tkv_set_option(c, tkv.TKV_OPT_CONCURRENT, 2), tkv.TKV_E_RANGE),
+                          (lambda: tkv.tkv_set_option(c, tkv.TKV_OPT_CONCURRENT, -1), tkv.TKV_E_RANGE),
                           (lambda: tkv.tkv_set_option(c, 99, 1), tkv.TKV_E_INVAL)]:
             with pytest.raises(tkv.TkvError) as e:
                 bad()

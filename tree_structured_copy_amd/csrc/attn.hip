@@ -60,22 +60,19 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
   int e_id = -1, e_valid = 0, e_pos = 0;
   uint32_t e_mlo = 0, e_mhi = 0;
   int cur_batch = -1;
+  // (the entry is selected by value and stored once: branches that each store
+  // the fields let the compiler merge their last stores through a selected
+  // pointer, which puts these registers on the stack)
   auto load_entries = [&](int batch) {
     const int sbk = 32 * batch + (lane >> 1);
     const int b = 2 * (wave + W * sbk) + (lane & 1);
-    if (sbk < nmine && b < nb) {
-      const DevBlock e = bl[b];
-      e_id = e.id;
-      e_valid = e.valid;
-      e_pos = e.pos;
-      e_mlo = static_cast<uint32_t>(e.mask);
-      e_mhi = static_cast<uint32_t>(e.mask >> 32);
-    } else {
-      e_id = -1;
-      e_valid = 0;
-      e_pos = 0;
-      e_mlo = e_mhi = 0;
-    }
+    DevBlock e{-1, 0, 0, 0, 0};
+    if (sbk < nmine && b < nb) e = bl[b];
+    e_id = e.id;
+    e_valid = e.valid;
+    e_pos = e.pos;
+    e_mlo = static_cast<uint32_t>(e.mask);
+    e_mhi = static_cast<uint32_t>(e.mask >> 32);
     cur_batch = batch;
   };
   auto meta = [&](int k) {

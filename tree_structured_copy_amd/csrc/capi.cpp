@@ -58,6 +58,7 @@ struct tkv_cache {
   uint64_t opt_epoch = 1;
   bool plan_cache = true;
   int32_t waves = 0;
+  int32_t concurrent = 1;  // TKV_OPT_CONCURRENT
   PlanSlot slots[kPlanSlots];
   uint64_t stamp = 0;
   // pinned staging for plan uploads
@@ -244,13 +245,16 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     for (auto& e : ev) e = c->get_event();
     if (ev[0] && ev[1] && ev[2]) (void)hipEventRecord(ev[0], stream);
   }
-  // kernel classes of this call: the first runs on the caller's stream, every
-  // further one on a side stream, all at once
+  // The kernel classes of this call, run by c->concurrent: 0 = one after
+  // another on the caller's stream; 1 = the first on the caller's stream, each
+  // further one on a side stream forked from it with an event and joined back
+  // before the merge.
   int classes[kKernelClasses];
   int ncls = 0;
   for (int cls = 0; cls < kKernelClasses; ++cls)
     if (P.bucket_begin[cls + 1] > P.bucket_begin[cls]) classes[ncls++] = cls;
-  if (ncls > 1) {
+  const bool side = c->concurrent == 1 && ncls > 1;
+  if (side) {
     if (!c->fork_ev && hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming) != hipSuccess) return TKV_E_DEVICE;
     for (int k = 0; k < ncls - 1; ++k) {
       if (!c->aux[k] && hipStreamCreateWithFlags(&c->aux[k], hipStreamNonBlocking) != hipSuccess) return TKV_E_DEVICE;
@@ -262,8 +266,8 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   for (int k = 0; k < ncls; ++k) {
     const int cls = classes[k];
     const int32_t n = P.bucket_begin[cls + 1] - P.bucket_begin[cls];
-    hipStream_t st = k == 0 ? stream : c->aux[k - 1];
-    if (k > 0 && hipStreamWaitEvent(st, c->fork_ev, 0) != hipSuccess) return TKV_E_DEVICE;
+    hipStream_t st = side && k > 0 ? c->aux[k - 1] : stream;
+    if (st != stream && hipStreamWaitEvent(st, c->fork_ev, 0) != hipSuccess) return TKV_E_DEVICE;
     a.item0 = P.bucket_begin[cls];
     a.max_blocks = P.bucket_max_blocks[cls];
     hipError_t e;
@@ -274,10 +278,11 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
       e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], P.causal, a, n, st);
     }
     if (e != hipSuccess) return TKV_E_DEVICE;
-    if (k > 0 && hipEventRecord(c->join_ev[k - 1], st) != hipSuccess) return TKV_E_DEVICE;
+    if (st != stream && hipEventRecord(c->join_ev[k - 1], st) != hipSuccess) return TKV_E_DEVICE;
   }
-  for (int k = 1; k < ncls; ++k)
-    if (hipStreamWaitEvent(stream, c->join_ev[k - 1], 0) != hipSuccess) return TKV_E_DEVICE;
+  if (side)
+    for (int k = 1; k < ncls; ++k)
+      if (hipStreamWaitEvent(stream, c->join_ev[k - 1], 0) != hipSuccess) return TKV_E_DEVICE;
   if (c->prof && ev[1]) (void)hipEventRecord(ev[1], stream);
   if (P.any_merge) {
     MergeArgs m{};
@@ -541,6 +546,10 @@ int tkv_set_option(tkv_cache* c, int32_t key, int64_t value) {
       if (value != 0 && value != 1) return TKV_E_RANGE;
       c->opt.cascade = static_cast<int32_t>(value);
       break;
+    case TKV_OPT_CONCURRENT:
+      if (value != 0 && value != 1) return TKV_E_RANGE;
+      c->concurrent = static_cast<int32_t>(value);
+      break;
     default:
       return TKV_E_INVAL;
   }
@@ -557,6 +566,7 @@ int tkv_get_option(const tkv_cache* c, int32_t key, int64_t* value) {
     case TKV_OPT_PLAN_CACHE: *value = c->plan_cache ? 1 : 0; break;
     case TKV_OPT_WAVES: *value = c->waves; break;
     case TKV_OPT_CASCADE: *value = c->opt.cascade; break;
+    case TKV_OPT_CONCURRENT: *value = c->concurrent; break;
     default: return TKV_E_INVAL;
   }
   return TKV_OK;

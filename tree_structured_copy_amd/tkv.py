@@ -37,6 +37,7 @@ TKV_OPT_MAX_ROWS = 3
 TKV_OPT_PLAN_CACHE = 4
 TKV_OPT_WAVES = 5
 TKV_OPT_CASCADE = 6
+TKV_OPT_CONCURRENT = 7
 
 STATUS_NAMES = {
     TKV_E_INVAL: "inval", TKV_E_NOMEM: "nomem", TKV_E_BADSEQ: "badseq", TKV_E_SHARED: "shared",
