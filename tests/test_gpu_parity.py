@@ -82,6 +82,18 @@ def test_concurrent_modes(mode):
     assert_close(run_both(wl, options={tkv.TKV_OPT_CONCURRENT: mode}), "bf16")
 
 
+@pytest.mark.parametrize("waves", [2, 4, 8])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_register_kernel_waves(waves, dtype, d):
+    """The one- and two-tile kernel with 2, 4 or 8 waves splitting a group's
+    super-blocks (the library keeps 4 where a shape has no 2- or 8-wave form):
+    the same results against the oracle."""
+    from tree_structured_copy_amd import tkv
+    wl = recipes.fork_workload("waves", dtype=dtype, layers=1, q_heads=8, kv_heads=2, head_dim=d,
+                               requests=3, prefix=333, width=5, branch_tokens=21, seed=47)
+    assert_close(run_both(wl, options={tkv.TKV_OPT_WAVES: waves}), dtype)
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_random_sessions(seed):
     dtype = "bf16" if seed % 2 == 0 else "f32"
@@ -283,6 +295,7 @@ def test_workspace_and_argument_errors():
         q = torch.zeros((8, 8, 128), dtype=torch.bfloat16, device="cuda")
         out = torch.empty((8, 8, 128), dtype=torch.float32, device="cuda")
         tkv.tkv_set_option(c, tkv.TKV_OPT_TARGET_WGS, 100000)
+        tkv.tkv_set_option(c, tkv.TKV_OPT_MIN_CHUNK, 1)
         need = tkv.tkv_workspace_size(c, kids)
         assert need > 0
         with pytest.raises(tkv.TkvError) as e:

@@ -288,6 +288,10 @@ hipError_t launch_w(int tiles, int waves, const AttnArgs& args, int32_t n_items,
       return hipGetLastError();
     }
   }
+  if (waves == 2 && tiles == 1) {
+    hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, 2, C>), dim3(n_items * args.hkv), dim3(64 * 2), 0, s, args);
+    return hipGetLastError();
+  }
   return launch_t<P, D, 4, C>(tiles, args, n_items, s);
 }
 
@@ -301,7 +305,7 @@ hipError_t launch_c(int tiles, int waves, bool causal, const AttnArgs& args, int
 hipError_t launch_attn_partial(int dtype, int head_dim, int tiles, int waves, bool causal, const AttnArgs& args,
                                int32_t n_items, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
-  if (waves != 4 && waves != 8) return hipErrorInvalidValue;
+  if (waves != 2 && waves != 4 && waves != 8) return hipErrorInvalidValue;
   if (dtype == 1 && head_dim == 128) return launch_c<BF16, 128>(tiles, waves, causal, args, n_items, stream);
   if (dtype == 1 && head_dim == 64) return launch_c<BF16, 64>(tiles, waves, causal, args, n_items, stream);
   if (dtype == 0 && head_dim == 128) return launch_c<F32, 128>(tiles, waves, causal, args, n_items, stream);

@@ -74,14 +74,19 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
   const char* vbase = uniform_ptr(reinterpret_cast<const char*>(static_cast<const E*>(a.vpool) + kvh0 * tile_elems));
   const uint32_t ring_base = __builtin_amdgcn_readfirstlane(lds_byte_addr(ring));
 
-  // the item's block list, staged once; waves read it 64 entries at a time
-  // (lane k holds entry base + k) and take each super-block's fields with
-  // v_readlane, so no LDS round trip sits on the per-super-block path
-  for (int k = tid; k < nb; k += 64 * W * HPW) ents[k] = bl[k];
-  __syncthreads();
+  const DevGroup gr = a.groups[it.group];
+  const int G = a.gsize;
+  const int nrows = gr.nq * G;
 
   // Issue this wave's share of super-block sp's loads into ring slot `slot`.
-  int ib_base = -64, ib_id = 0;  // ids of blocks [ib_base, ib_base + 64), one per lane
+  // The ids of the first 64 blocks come straight from global memory, so the
+  // ring's first super-blocks are in flight before the block list and the
+  // queries are staged; later batches come from the staged list.
+  int ib_base = 0, ib_id = lane < nb ? bl[lane].id : 0;  // ids of blocks [ib_base, ib_base + 64), one per lane
+  // one wait for the ids, on every path, before the first ring load: a wait
+  // the compiler placed at each (conditional) issue below would also drain
+  // the super-blocks issued before it
+  __builtin_amdgcn_s_waitcnt(0);
   auto issue = [&](int sp, int slot) {
     if (wave >= LOADERS) return;
     const int b0 = 2 * sp;
@@ -102,13 +107,18 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
     }
   };
 
-  // rows of this wave: tiles lw, lw + W, ... of head kvh
-  const DevGroup gr = a.groups[it.group];
-  const int G = a.gsize;
-  const int nrows = gr.nq * G;
+  // The ring's first super-blocks.  Compiler-visible loads issued after them
+  // make the compiler wait for them too where it waits for its own (the count
+  // is in issue order); everything visible is complete before the loop below.
+  constexpr int AHEAD = EARLY ? NS : NS - 1;  // super-blocks issued before the first is read
+#pragma unroll
+  for (int sp = 0; sp < AHEAD; ++sp)
+    if (sp < nsb) issue(sp, sp);
+
+  // rows of this wave: tiles lw, lw + W, ... of head kvh; their query
+  // indices load beside the block list
   const uint64_t gmask = gr.nq >= 64 ? ~0ull : ((1ull << gr.nq) - 1);
-  F qf[TPW];
-  int qj[TPW], qlim[TPW];
+  int qi[TPW], qj[TPW], qlim[TPW];
   uint64_t my_q = 0;  // group queries with a row in this wave's tiles
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
@@ -120,15 +130,30 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
     }
     if (R < nrows) {
       const int j = R / G;
-      const int h = kvh * G + (R - j * G);
-      const int qi = a.gq[gr.q_begin + j];
-      P::load_q(qf[t], static_cast<const E*>(a.q) + (static_cast<size_t>(qi) * a.hq + h) * D, g);
+      qi[t] = a.gq[gr.q_begin + j];
       qj[t] = j;
       qlim[t] = CAUSAL ? a.gqpos[gr.q_begin + j] : 0;
     } else {
-      P::zero(qf[t]);
+      qi[t] = -1;
       qj[t] = 0;
       qlim[t] = 0x7fffffff;
+    }
+  }
+
+  // the item's block list, staged once; waves read it 64 entries at a time
+  // (lane k holds entry base + k) and take each super-block's fields with
+  // v_readlane, so no LDS round trip sits on the per-super-block path
+  for (int k = tid; k < nb; k += 64 * W * HPW) ents[k] = bl[k];
+
+  F qf[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    if (qi[t] >= 0) {
+      const int R = 16 * (lw + W * t) + r;
+      const int h = kvh * G + (R - qj[t] * G);
+      P::load_q(qf[t], static_cast<const E*>(a.q) + (static_cast<size_t>(qi[t]) * a.hq + h) * D, g);
+    } else {
+      P::zero(qf[t]);
     }
   }
   float m[TPW], l[TPW];
@@ -151,10 +176,6 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
   // the ring on every iteration.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  constexpr int AHEAD = EARLY ? NS : NS - 1;  // super-blocks issued before the first is read
-#pragma unroll
-  for (int sp = 0; sp < AHEAD; ++sp)
-    if (sp < nsb) issue(sp, sp);
 
   // fields of blocks [cb_base, cb_base + 64), one per lane (zero past the list)
   int cb_base = -64, cb_valid = 0, cb_pos = 0;
@@ -351,7 +372,10 @@ hipError_t launch_shape(int tiles, const AttnArgs& args, int32_t n_items, hipStr
     if constexpr (kSmall) return launch_one<P, D, 1, 8, 1, ring_slots<P, D, 1, 64>(), false, 4, C>(args, n_items, s);
     else return launch_one<P, D, 1, 8, 1, ring_slots<P, D, 1, 128>(), false, 2, C>(args, n_items, s);
   }
-  if (tiles <= 16) return launch_one<P, D, 2, 8, 1, ring_slots<P, D, 1, 128>(), false, 2, C>(args, n_items, s);
+  if (tiles <= 16) {
+    if constexpr (kSmall) return launch_one<P, D, 1, 16, 1, ring_slots<P, D, 1, 128>(), false, 4, C>(args, n_items, s);
+    else return launch_one<P, D, 2, 8, 1, ring_slots<P, D, 1, 128>(), false, 2, C>(args, n_items, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -58,7 +58,7 @@ struct tkv_cache {
   uint64_t opt_epoch = 1;
   bool plan_cache = true;
   int32_t waves = 0;
-  int32_t concurrent = 1;  // TKV_OPT_CONCURRENT
+  int32_t concurrent = 0;  // TKV_OPT_CONCURRENT
   PlanSlot slots[kPlanSlots];
   uint64_t stamp = 0;
   // pinned staging for plan uploads
@@ -539,7 +539,7 @@ int tkv_set_option(tkv_cache* c, int32_t key, int64_t value) {
       c->plan_cache = value != 0;
       break;
     case TKV_OPT_WAVES:
-      if (value != 0 && value != 4 && value != 8) return TKV_E_RANGE;
+      if (value != 0 && value != 2 && value != 4 && value != 8) return TKV_E_RANGE;
       c->waves = static_cast<int32_t>(value);
       break;
     case TKV_OPT_CASCADE:

@@ -274,20 +274,44 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     }
     const int32_t ngroups = static_cast<int32_t>(P.groups.size());
 
-    // 5. split-K chunking and items.  A super-block costs a register-tile
-    //    workgroup (1-2 row tiles) about its memory time; an LDS-staged
-    //    workgroup (3+ tiles) pays a barrier and its waves' latency chain on
-    //    every super-block, about four times as long.  A group's chunk is the
-    //    per-workgroup share of the call's weighted work divided by its weight,
-    //    so that every workgroup of every class ends at about the same time.
-    auto weight = [&](int32_t gi) -> int64_t { return (P.groups[gi].nq * q_per_kv + 15) / 16 <= 2 ? 1 : 4; };
-    int64_t work = 0;
-    for (int32_t gi = 0; gi < ngroups; ++gi) work += gout[gi].blk_count * weight(gi);
-    const int64_t tw = std::max<int32_t>(1, opt.target_wgs);
-    const int64_t unit = (work * num_kv_heads + tw - 1) / tw;  // weighted blocks per workgroup
-    auto chunk_of = [&](int32_t gi) {
-      return std::min<int64_t>(kRowsMaxItemBlocks, std::max<int64_t>(std::max<int32_t>(1, opt.min_chunk),
-                                                                     (unit + weight(gi) - 1) / weight(gi)));
+    // 5. split-K chunking and items.  The kernel classes of a call do not
+    //    share the GPU well (a class's workgroups take whole CUs' registers or
+    //    LDS, and side-stream joins cost more than the overlap gains), so each
+    //    class is cut to fill the GPU on its own: about target_wgs / Hkv items,
+    //    shared among its groups in proportion to their blocks, rounded down
+    //    so that one round of workgroups holds them all.  A chunk stays long
+    //    next to its partial record: at least min_chunk blocks for the
+    //    register-tile classes, whose time is their memory time, and a quarter
+    //    of that for the LDS-staged classes (3+ row tiles), whose time per
+    //    block is several times longer; and at most kRowsMaxItemBlocks.
+    //    An LDS-staged class whose work (blocks x row tiles) is smaller than
+    //    that of the largest LDS-staged class present runs in that class's
+    //    kernel instead (its extra waves idle): one launch and one ramp fewer.
+    std::vector<int8_t> gclass(ngroups);
+    int64_t class_work[kKernelClasses] = {0, 0, 0, 0, 0, 0};
+    for (int32_t gi = 0; gi < ngroups; ++gi) {
+      const int32_t tiles = (P.groups[gi].nq * q_per_kv + 15) / 16;
+      gclass[gi] = static_cast<int8_t>(kernel_class(tiles));
+      class_work[gclass[gi]] += static_cast<int64_t>(gout[gi].blk_count) * tiles;
+    }
+    int top = -1;
+    for (int c = 2; c < kKernelClasses; ++c)
+      if (class_work[c] > 0) top = c;
+    if (top > 2)
+      for (int32_t gi = 0; gi < ngroups; ++gi)
+        if (gclass[gi] >= 2 && gclass[gi] < top && class_work[gclass[gi]] < class_work[top]) gclass[gi] = top;
+    int64_t class_blocks[kKernelClasses] = {0, 0, 0, 0, 0, 0};
+    auto class_of = [&](int32_t gi) { return static_cast<int>(gclass[gi]); };
+    for (int32_t gi = 0; gi < ngroups; ++gi) class_blocks[class_of(gi)] += gout[gi].blk_count;
+    const int64_t class_items = std::max<int64_t>(1, std::max<int32_t>(1, opt.target_wgs) / num_kv_heads);
+    auto chunks_of = [&](int32_t gi) -> int32_t {
+      const int cls = class_of(gi);
+      const int64_t nb = gout[gi].blk_count;
+      const int64_t floor = std::max<int32_t>(1, cls < 2 ? opt.min_chunk : opt.min_chunk / 4);
+      int64_t nc = nb * class_items / class_blocks[cls];
+      nc = std::min(nc, nb / floor);
+      nc = std::max<int64_t>(nc, (nb + kRowsMaxItemBlocks - 1) / kRowsMaxItemBlocks);
+      return static_cast<int32_t>(std::max<int64_t>(nc, 1));
     };
     struct Tmp {
       DevItem it;
@@ -298,9 +322,8 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     for (int32_t gi = 0; gi < ngroups; ++gi) {
       const int32_t nb = gout[gi].blk_count;
       if (nb == 0) continue;
-      const int64_t chunk = chunk_of(gi);
-      const int32_t nc = static_cast<int32_t>(std::max<int64_t>(1, (nb + chunk - 1) / chunk));
-      const int32_t tiles = kernel_class((P.groups[gi].nq * q_per_kv + 15) / 16);
+      const int32_t nc = chunks_of(gi);
+      const int32_t tiles = class_of(gi);
       int32_t at = 0;
       for (int32_t c = 0; c < nc; ++c) {
         const int32_t cnt = nb / nc + (c < nb % nc ? 1 : 0);
