@@ -37,10 +37,10 @@ HBM_PEAK_GBS = 8000.0
 # right.  Valid only for the kernel sources they were taken on (sha256 below);
 # after any change to them the bench line reports traffic as null.
 TRAFFIC_RECORD = {
-    "sources_sha256": "e6f20cf9ccfd5e94a8d3441943e540d472ecaf9cc240009716a51dd0d6c22c0d",
-    "fetch_kib_per_launch": 286816, "fetch_factor": 1.9999,   # 1 GiB read reads as 524309 KiB
-    "write_kib_per_launch": 3690, "write_factor": 1.0,        # 1 GiB written reads as 1048576 KiB
-    "hbm_bytes_per_launch": 587374681 + 3778496,
+    "sources_sha256": "40fba51ea4c5cdae885df4bf6c5464a1b1676f48bf3f9e4b03053fd15e977b2d",
+    "fetch_kib_per_launch": 281765, "fetch_factor": 1.9999,   # 1 GiB read reads as 524309 KiB
+    "write_kib_per_launch": 2048, "write_factor": 1.0,        # 1 GiB written reads as 1048576 KiB
+    "hbm_bytes_per_launch": 577031479 + 2097152,
 }
 
 
@@ -397,7 +397,7 @@ def main():
         "plan": main_res["plan"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": _recorded_traffic(),
-                     "kernel": "attn_partial_kernel<BF16,128,1,4,false>",
+                     "kernel": "attn_partial_kernel<BF16,128,1,2,false>",
                      "kernel_ms": main_res["partial_kernel_ms_per_call"],
                      "merge_kernel_ms": main_res["merge_kernel_ms_per_call"]},
         "verify": verify,

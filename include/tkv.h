@@ -196,7 +196,7 @@ enum {
   TKV_OPT_MIN_CHUNK = 2,    /* fewest blocks per work item (default 32) */
   TKV_OPT_MAX_ROWS = 3,     /* max rows (queries x Hq/Hkv) per group: 16..256 (default 256) */
   TKV_OPT_PLAN_CACHE = 4,   /* 1 = reuse uploaded plans while the tree is unchanged (default) */
-  TKV_OPT_WAVES = 5,        /* waves per attention workgroup: 2, 4 or 8 (0 = default, 4) */
+  TKV_OPT_WAVES = 5,        /* waves per one/two-tile workgroup: 2, 4 or 8 (0 = by launch size) */
   TKV_OPT_CASCADE = 6,      /* 1 = a group of 8+ row tiles hands blocks that only one row tile's
                                queries see to one-tile subgroups, merged after (default); 0 = off */
   TKV_OPT_CONCURRENT = 7    /* how a call's kernel classes run: 0 = one after another on the call's

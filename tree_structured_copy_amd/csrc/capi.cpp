@@ -58,6 +58,7 @@ struct tkv_cache {
   uint64_t opt_epoch = 1;
   bool plan_cache = true;
   int32_t waves = 0;
+  int32_t cus = 256;  // compute units of the device (set at create when pools are given)
   int32_t concurrent = 0;  // TKV_OPT_CONCURRENT
   PlanSlot slots[kPlanSlots];
   uint64_t stamp = 0;
@@ -272,7 +273,10 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     a.max_blocks = P.bucket_max_blocks[cls];
     hipError_t e;
     if (cls < 2) {
-      const int w = c->waves ? c->waves : 4;
+      // One tile with no more workgroups than CUs: two waves, i.e. two long
+      // streams of loads per CU, which HBM serves faster than four shorter
+      // ones; otherwise four, which a CU holds two workgroups of.
+      const int w = c->waves ? c->waves : (cls == 0 && static_cast<int64_t>(n) * c->cfg.num_kv_heads <= c->cus ? 2 : 4);
       e = launch_attn_partial(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], w, P.causal, a, n, st);
     } else {
       e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], P.causal, a, n, st);
@@ -354,7 +358,7 @@ int tkv_create(const tkv_config* cfg, tkv_cache** out) {
       delete cache;
       return TKV_E_DEVICE;
     }
-    if (cus > 0) cache->opt.target_wgs = cus;
+    if (cus > 0) cache->opt.target_wgs = cache->cus = cus;
   }
   *out = cache;
   return TKV_OK;

@@ -346,11 +346,14 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       }
     }
     P.partial_slots = slots;
-    // order: by row-tile bucket, then items that read the same blocks next to each
-    // other (same tree, same chunk index), so the KV heads' workgroups of
-    // neighbouring items share L2
+    // order: by kernel class; longest items first, so that when a class has
+    // more workgroups than the GPU holds at once the ones that start late are
+    // short; then items that read the same blocks next to each other (same
+    // tree, same chunk index), so the KV heads' workgroups of neighbouring
+    // items share L2
     std::stable_sort(tmp.begin(), tmp.end(), [](const Tmp& a, const Tmp& b) {
       if (a.tiles != b.tiles) return a.tiles < b.tiles;
+      if (a.it.blk_count != b.it.blk_count) return a.it.blk_count > b.it.blk_count;
       if (a.root != b.root) return a.root < b.root;
       if (a.chunk != b.chunk) return a.chunk < b.chunk;
       return a.it.group < b.it.group;
