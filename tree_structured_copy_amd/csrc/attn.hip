@@ -112,10 +112,9 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
   }
 
   // queries: row R = 16 t + r of the group is query R / G, head kvh * G + R % G
-  const DevGroup gr = a.groups[it.group];
   const int G = a.gsize;
-  const int nrows = gr.nq * G;
-  const uint64_t gmask = gr.nq >= 64 ? ~0ull : ((1ull << gr.nq) - 1);
+  const int nrows = it.nq * G;
+  const uint64_t gmask = it.nq >= 64 ? ~0ull : ((1ull << it.nq) - 1);
   F qf[T];
   int qj[T], qlim[T];
 #pragma unroll
@@ -124,10 +123,10 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
     if (R < nrows) {
       const int j = R / G;
       const int h = kvh * G + (R - j * G);
-      const int qi = a.gq[gr.q_begin + j];
+      const int qi = a.gq[it.q_begin + j];
       P::load_q(qf[t], static_cast<const E*>(a.q) + (static_cast<size_t>(qi) * a.hq + h) * D, g);
       qj[t] = j;
-      qlim[t] = CAUSAL ? a.gqpos[gr.q_begin + j] : 0;
+      qlim[t] = CAUSAL ? a.gqpos[it.q_begin + j] : 0;
     } else {
       P::zero(qf[t]);
       qj[t] = 0;
@@ -146,7 +145,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
   }
   const float sl2 = a.scale_log2;
   const float tau_raw = kTau / sl2;  // the lazy-rescale threshold in raw score units
-  const int min_lim = gr.min_pos;
+  const int min_lim = it.min_pos;
 
   auto process = [&](const F& ka, const F& kb, const VP& v, const SBMeta& e) {
     const bool see_a = (e.ma & gmask) == gmask, see_b = (e.mb & gmask) == gmask;
@@ -252,7 +251,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
       const int j = R / G;
       const int h = kvh * G + (R - j * G);
       if (it.part_base < 0) {
-        const int qi = a.gq[gr.q_begin + j];
+        const int qi = a.gq[it.q_begin + j];
         a.out[(static_cast<size_t>(qi) * a.hq + h) * D + d] = as / ls;
       } else {
         const size_t slot = static_cast<size_t>(it.part_base) + static_cast<size_t>(j) * a.hq + h;

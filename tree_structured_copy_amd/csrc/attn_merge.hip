@@ -35,8 +35,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   for (int c0 = 0; c0 < mg.p_count; c0 += 64) {
     const int c = c0 + lane;
     if (c < mg.p_count) {
-      const DevPart pt = a.parts[mg.p_begin + c];
-      const int slot = a.items[pt.item].part_base + pt.j * a.hq + h;
+      const int slot = a.parts[mg.p_begin + c].slot0 + h;
       M = fmaxf(M, a.part_ml[2 * slot]);
     }
   }
@@ -51,8 +50,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
     int slot = 0;
     float f = 0.f;
     if (c < mg.p_count) {
-      const DevPart pt = a.parts[mg.p_begin + c];
-      slot = a.items[pt.item].part_base + pt.j * a.hq + h;
+      slot = a.parts[mg.p_begin + c].slot0 + h;
       const float mc = a.part_ml[2 * slot];
       f = (mc == kNegInf) ? 0.f : fast_exp2((mc - M) * sl2);
       ls += a.part_ml[2 * slot + 1] * f;

@@ -74,9 +74,8 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
   const char* vbase = uniform_ptr(reinterpret_cast<const char*>(static_cast<const E*>(a.vpool) + kvh0 * tile_elems));
   const uint32_t ring_base = __builtin_amdgcn_readfirstlane(lds_byte_addr(ring));
 
-  const DevGroup gr = a.groups[it.group];
   const int G = a.gsize;
-  const int nrows = gr.nq * G;
+  const int nrows = it.nq * G;
 
   // Issue this wave's share of super-block sp's loads into ring slot `slot`.
   // The ids of the first 64 blocks come straight from global memory, so the
@@ -117,7 +116,7 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
 
   // rows of this wave: tiles lw, lw + W, ... of head kvh; their query
   // indices load beside the block list
-  const uint64_t gmask = gr.nq >= 64 ? ~0ull : ((1ull << gr.nq) - 1);
+  const uint64_t gmask = it.nq >= 64 ? ~0ull : ((1ull << it.nq) - 1);
   int qi[TPW], qj[TPW], qlim[TPW];
   uint64_t my_q = 0;  // group queries with a row in this wave's tiles
 #pragma unroll
@@ -130,9 +129,9 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
     }
     if (R < nrows) {
       const int j = R / G;
-      qi[t] = a.gq[gr.q_begin + j];
+      qi[t] = a.gq[it.q_begin + j];
       qj[t] = j;
-      qlim[t] = CAUSAL ? a.gqpos[gr.q_begin + j] : 0;
+      qlim[t] = CAUSAL ? a.gqpos[it.q_begin + j] : 0;
     } else {
       qi[t] = -1;
       qj[t] = 0;
@@ -167,7 +166,7 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
   }
   const float sl2 = a.scale_log2;
   const float tau_raw = kTau / sl2;  // the lazy-rescale threshold in raw score units
-  const int min_lim = gr.min_pos;
+  const int min_lim = it.min_pos;
   const bool active = 16 * lw < nrows;
 
   // Every load the compiler can see (queries, group data, the block list) is
@@ -313,7 +312,7 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
     const int j = R / G;
     const int h = kvh * G + (R - j * G);
     if (it.part_base < 0) {
-      const int qi = a.gq[gr.q_begin + j];
+      const int qi = a.gq[it.q_begin + j];
       float* o = a.out + (static_cast<size_t>(qi) * a.hq + h) * D;
       const float inv = 1.f / lt;
 #pragma unroll

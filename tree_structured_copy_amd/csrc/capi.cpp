@@ -227,7 +227,6 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   a.q = q;
   a.out = out;
   a.items = reinterpret_cast<const DevItem*>(dev + P.off_items);
-  a.groups = reinterpret_cast<const DevGroup*>(dev + P.off_groups);
   a.gq = reinterpret_cast<const int32_t*>(dev + P.off_gq);
   a.gqpos = reinterpret_cast<const int32_t*>(dev + P.off_gqpos);
   a.blocks = reinterpret_cast<const DevBlock*>(dev + P.off_blocks);
@@ -290,7 +289,6 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   if (c->prof && ev[1]) (void)hipEventRecord(ev[1], stream);
   if (P.any_merge) {
     MergeArgs m{};
-    m.items = a.items;
     m.parts = reinterpret_cast<const DevPart*>(dev + P.off_parts);
     m.merge = reinterpret_cast<const DevMerge*>(dev + P.off_merge);
     m.part_acc = a.part_acc;

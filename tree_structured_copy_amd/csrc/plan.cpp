@@ -31,7 +31,6 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 void Plan::layout() {
   size_t o = 0;
   off_items = o;        o = align256(o + items.size() * sizeof(DevItem));
-  off_groups = o;       o = align256(o + groups.size() * sizeof(DevGroup));
   off_gq = o;           o = align256(o + gq.size() * sizeof(int32_t));
   off_gqpos = o;        o = align256(o + gqpos.size() * sizeof(int32_t));
   off_blocks = o;       o = align256(o + blocks.size() * sizeof(DevBlock));
@@ -43,7 +42,6 @@ void Plan::layout() {
 void Plan::serialise(void* dst) const {
   char* p = static_cast<char*>(dst);
   std::memcpy(p + off_items, items.data(), items.size() * sizeof(DevItem));
-  std::memcpy(p + off_groups, groups.data(), groups.size() * sizeof(DevGroup));
   std::memcpy(p + off_gq, gq.data(), gq.size() * sizeof(int32_t));
   std::memcpy(p + off_gqpos, gqpos.data(), gqpos.size() * sizeof(int32_t));
   std::memcpy(p + off_blocks, blocks.data(), blocks.size() * sizeof(DevBlock));
@@ -331,6 +329,10 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
         t.it.group = gi;
         t.it.blk_begin = gout[gi].blk_begin + at;
         t.it.blk_count = cnt;
+        t.it.q_begin = P.groups[gi].q_begin;
+        t.it.nq = P.groups[gi].nq;
+        t.it.min_pos = P.groups[gi].min_pos;
+        t.it.pad = 0;
         if (nc == 1 && !gout[gi].partials) {
           t.it.part_base = -1;
         } else {
@@ -384,7 +386,7 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
             ++direct;
             continue;
           }
-          P.parts.push_back({item, gj.second});
+          P.parts.push_back({P.items[item].part_base + gj.second * q_per_kv * num_kv_heads, item});
         }
       m.p_count = static_cast<int32_t>(P.parts.size()) - m.p_begin;
       if (direct + m.p_count == 0 || (direct > 0 && (direct > 1 || m.p_count > 0))) return TKV_E_INVAL;

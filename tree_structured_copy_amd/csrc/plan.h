@@ -52,7 +52,7 @@ struct Plan {
   int64_t unique_tokens = 0;
 
   // serialised layout (byte offsets into one device buffer)
-  size_t off_items = 0, off_groups = 0, off_gq = 0, off_gqpos = 0, off_blocks = 0,
+  size_t off_items = 0, off_gq = 0, off_gqpos = 0, off_blocks = 0,
          off_parts = 0, off_merge = 0, bytes = 0;
   void layout();
   void serialise(void* dst) const;

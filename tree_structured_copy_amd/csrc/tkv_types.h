@@ -12,25 +12,32 @@ constexpr int kRowsMaxItemBlocks = 512;  // longest block list of one attn_rows.
 constexpr int kAppendMaxBlocks = 128;
 constexpr int kGatherMaxBlocks = 64;
 
-// One work item: a contiguous run of a group's block list, processed by one
-// workgroup per KV head.  part_base < 0: the item covers its group's whole list
-// and writes normalised outputs directly; otherwise it writes fp32 partial
-// records (m, l, acc) at slots part_base + j * Hq + h.
-struct DevItem {
-  int32_t group;
-  int32_t blk_begin;
-  int32_t blk_count;
-  int32_t part_base;
-};
-
 // A query group: up to kMaxRows rows that share one pass over the union of
 // their paths.  Its queries are gq[q_begin .. q_begin + nq); min_pos is the
 // smallest position limit among them (keys at or below it are visible to all).
+// (Host side: every work item carries its group's fields.)
 struct DevGroup {
   int32_t q_begin;
   int32_t nq;
   int32_t min_pos;
   int32_t pad1;
+};
+
+// One work item: a contiguous run of a group's block list, processed by one
+// workgroup per KV head, with its group's query range and position limit (so
+// a workgroup needs no group record before it can load its queries).
+// part_base < 0: the item covers its group's whole list and writes normalised
+// outputs directly; otherwise it writes fp32 partial records (m, l, acc) at
+// slots part_base + j * Hq + h.
+struct DevItem {
+  int32_t group;
+  int32_t blk_begin;
+  int32_t blk_count;
+  int32_t part_base;
+  int32_t q_begin;
+  int32_t nq;
+  int32_t min_pos;
+  int32_t pad;
 };
 
 // One block on a group's path list.  mask bit j = group query j can see the
@@ -43,13 +50,14 @@ struct DevBlock {
   uint64_t mask;
 };
 
-// One partial record of a query: work item `item` wrote it at slot
-// items[item].part_base + j * Hq + head (j = the query's index in that item's
-// group).  A query's records are parts[p_begin .. p_begin + p_count) of its
-// DevMerge; p_count == 0: its output was written directly.
+// One partial record of a query: the work item that wrote it put query head h
+// at slot slot0 + h (slot0 = the item's part_base + j * Hq, j = the query's
+// index in the item's group).  A query's records are parts[p_begin ..
+// p_begin + p_count) of its DevMerge; p_count == 0: its output was written
+// directly.
 struct DevPart {
-  int32_t item;
-  int32_t j;
+  int32_t slot0;
+  int32_t item;  // for checks and statistics; the merge does not read it
 };
 struct DevMerge {
   int32_t p_begin;
@@ -62,7 +70,6 @@ struct AttnArgs {
   const void* q;
   float* out;
   const DevItem* items;
-  const DevGroup* groups;
   const int32_t* gq;     // global query index per group slot
   const int32_t* gqpos;  // absolute position limit per group slot
   const DevBlock* blocks;
@@ -77,7 +84,6 @@ struct AttnArgs {
 };
 
 struct MergeArgs {
-  const DevItem* items;
   const DevPart* parts;
   const DevMerge* merge;
   const float* part_acc;
