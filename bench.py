@@ -339,6 +339,9 @@ def main():
                          "counters' calibration), then 8 steps of --counters-workload")
     ap.add_argument("--counters-workload", default="llama_fork",
                     help="workload of the --counters run (llama_fork, spec_verify, mcts_tree, ...)")
+    ap.add_argument("--only", default=None,
+                    help="measure just this workload (mcts_tree, spec_verify, full_depth, llama_fork) and print "
+                         "its figures as one JSON line: a short run for a kernel trace of that workload alone")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the fork workload's requests are independent trees, so "
@@ -351,6 +354,12 @@ def main():
 
     if args.counters:
         _counters_run(args.copies, args.counters_workload)
+        return
+    if args.only:
+        copies = 1 if args.only == "full_depth" else args.copies
+        steps, warmup = (max(3, args.steps // 10), 1) if args.only == "full_depth" else (args.steps, args.warmup)
+        res = measure(args.only, copies, steps, warmup)
+        print(json.dumps({"only": args.only, "steps": steps, "warmup": warmup, **res}), flush=True)
         return
 
     main_res = measure("llama_fork", args.copies, args.steps, args.warmup, rebuild=True)

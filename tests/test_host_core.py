@@ -416,3 +416,36 @@ def test_plan_cascade_shapes():
         b = _host_plan(w, [(tkv.TKV_OPT_TARGET_WGS, 256), (tkv.TKV_OPT_CASCADE, 0)])
         assert a == b, name
         assert a["partial_slots"] == 0
+
+
+def test_plan_classes_fill_one_round():
+    """Each kernel class is cut to fill the GPU on its own, in one round of
+    workgroups: the shared groups of the search tree become 30 items (240
+    workgroups for 256 CUs); groups that already give one workgroup per CU,
+    or that cannot be cut below the chunk floor, are left whole; the 32-layer
+    workload's 768-block lists split in two at the 512-block item limit."""
+    expect = {"llama_fork": [32, 0, 0, 0, 0, 0], "spec_verify": [0, 0, 0, 64, 0, 0],
+              "full_depth": [0, 0, 128, 0, 0, 0]}
+    for name, ipk in expect.items():
+        info = _host_plan(recipes.STANDARD[name](), [(tkv.TKV_OPT_TARGET_WGS, 256)])
+        assert info["items_per_kernel"] == ipk, (name, info)
+    info = _host_plan(recipes.mcts_tree(), [(tkv.TKV_OPT_TARGET_WGS, 256)])
+    ipk = info["items_per_kernel"]
+    assert ipk[0] == 65 and ipk[5] == 30 and sum(ipk[1:5]) == 0, info
+    assert ipk[5] * 8 <= 256
+    # twice the workgroups asked for: the shared groups are cut about twice as
+    # fine, still within one round
+    info2 = _host_plan(recipes.mcts_tree(), [(tkv.TKV_OPT_TARGET_WGS, 512)])
+    assert 2 * ipk[5] <= info2["items_per_kernel"][5] and info2["items_per_kernel"][5] * 8 <= 512, info2
+
+
+def test_plan_small_lds_class_joins_the_largest():
+    """An LDS-staged class with less work than the largest one present runs in
+    the largest one's kernel: the search tree's one 8-tile group (30 queries)
+    joins its 16-tile groups; a workload with only 8-tile groups keeps them."""
+    on = _host_plan(recipes.mcts_tree(), [(tkv.TKV_OPT_TARGET_WGS, 256)])
+    assert on["items_per_kernel"][4] == 0 and on["items_per_kernel"][5] > 0
+    wl = recipes.fork_workload("eight", dtype="bf16", layers=1, q_heads=32, kv_heads=8, head_dim=128,
+                               requests=2, prefix=300, width=30, branch_tokens=5, seed=3)
+    info = _host_plan(wl, [(tkv.TKV_OPT_TARGET_WGS, 256)])
+    assert info["items_per_kernel"][4] > 0 and info["items_per_kernel"][5] == 0, info
