@@ -35,3 +35,27 @@ def test_standard_workload_sampled(name, per_op):
     s = _sampler(per_op)
     s.heads = wl.q_heads
     assert_close(run_both(wl, sample=s), wl.dtype)
+
+
+@pytest.mark.parametrize("case", ["long_decode", "long_verify", "wide_batch", "gqa8_tree"])
+def test_extreme_shapes_sampled(case):
+    """Shapes beyond the standard workloads, sampled against the oracle:
+    a 40 000-token shared prefix (2500 blocks, cut into many split-K chunks
+    and merged); verification over a 30 000-token prefix; 1500 independent
+    sequences in one call (1500 groups, 12 000 workgroups); a search tree at
+    8 query heads per KV head (cascade subgroups of 2 queries)."""
+    if case == "long_decode":
+        wl = recipes.fork_workload("long_decode", dtype="bf16", layers=1, q_heads=8, kv_heads=2, head_dim=128,
+                                   requests=1, prefix=40000, width=3, branch_tokens=17, seed=51)
+    elif case == "long_verify":
+        wl = recipes.verify_workload("long_verify", dtype="bf16", q_heads=8, kv_heads=2, head_dim=128,
+                                     requests=2, prefix=30000, paths=3, drafts=8, seed=52)
+    elif case == "wide_batch":
+        wl = recipes.fork_workload("wide_batch", dtype="bf16", layers=1, q_heads=32, kv_heads=8, head_dim=128,
+                                   requests=1500, prefix=40, width=1, branch_tokens=3, seed=53)
+    else:
+        wl = recipes.mcts_workload("gqa8_tree", dtype="bf16", q_heads=32, kv_heads=4, head_dim=128,
+                                   root_tokens=300, branching=4, depth=5, leaves=128, node_tokens=16, seed=54)
+    s = _sampler(64, seed=3)
+    s.heads = wl.q_heads
+    assert_close(run_both(wl, sample=s), wl.dtype)
