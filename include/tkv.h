@@ -67,7 +67,7 @@ typedef struct tkv_config {
   int32_t num_kv_heads; /* >= 1; Hq/Hkv <= 64 */
   int32_t head_dim;     /* 64 or 128 */
   int32_t block_size;   /* must be 16 */
-  int32_t num_blocks;   /* blocks per layer in each pool, >= 1 */
+  int32_t num_blocks;   /* blocks per layer in each pool, 1 .. 2^27 */
   int32_t dtype;        /* tkv_dtype of K, V and Q */
   int32_t reserved;     /* must be 0 */
   /* Caller-owned device pools, each num_layers * num_blocks * num_kv_heads * 16 *

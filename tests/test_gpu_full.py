@@ -59,3 +59,20 @@ def test_extreme_shapes_sampled(case):
     s = _sampler(64, seed=3)
     s.heads = wl.q_heads
     assert_close(run_both(wl, sample=s), wl.dtype)
+
+
+@pytest.mark.parametrize("kind", ["decode", "verify"])
+def test_longest_lds_staged_item(kind):
+    """One LDS-staged work item of about 1000 blocks (the block list kernel B
+    stages is at most 1024 entries, 16 KiB): with a workgroup target of 2 the
+    planner leaves each group whole.  Sampled against the oracle."""
+    from tree_structured_copy_amd import tkv
+    if kind == "decode":
+        wl = recipes.fork_workload("long_item", dtype="bf16", layers=1, q_heads=8, kv_heads=2, head_dim=128,
+                                   requests=1, prefix=16000, width=12, branch_tokens=9, seed=61)
+    else:
+        wl = recipes.verify_workload("long_item_v", dtype="bf16", q_heads=8, kv_heads=2, head_dim=128,
+                                     requests=1, prefix=16000, paths=3, drafts=8, seed=62)
+    s = _sampler(64, seed=5)
+    s.heads = wl.q_heads
+    assert_close(run_both(wl, sample=s, options={tkv.TKV_OPT_TARGET_WGS: 2}), wl.dtype)

@@ -422,10 +422,10 @@ def test_plan_classes_fill_one_round():
     """Each kernel class is cut to fill the GPU on its own, in one round of
     workgroups: the shared groups of the search tree become 30 items (240
     workgroups for 256 CUs); groups that already give one workgroup per CU,
-    or that cannot be cut below the chunk floor, are left whole; the 32-layer
-    workload's 768-block lists split in two at the 512-block item limit."""
+    or that cannot be cut below the chunk floor, are left whole (the 32-layer
+    workload's 768-block lists fit one item each)."""
     expect = {"llama_fork": [32, 0, 0, 0, 0, 0], "spec_verify": [0, 0, 0, 64, 0, 0],
-              "full_depth": [0, 0, 128, 0, 0, 0]}
+              "full_depth": [0, 0, 64, 0, 0, 0]}
     for name, ipk in expect.items():
         info = _host_plan(recipes.STANDARD[name](), [(tkv.TKV_OPT_TARGET_WGS, 256)])
         assert info["items_per_kernel"] == ipk, (name, info)

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_common.h"
 #include "kernels.h"
 
@@ -16,14 +18,18 @@ namespace {
 
 using namespace attn;
 
-// Log-sum-exp merge: one wave per (query, query head).  Lane c first takes
-// partial c's record (slot, m, l), the wave forms the common maximum M, and
-// then every lane accumulates its D/64 output elements over the partials,
-// each weighted by exp2((m_c - M) * scale_log2); the sum of the weighted l_c
-// normalises.
+// Log-sum-exp merge: one wave per (query, query head).  Lane c takes partial
+// c's record (slot, m, l), the wave forms the common maximum M, and then every
+// lane accumulates its D/64 output elements over the partials, each weighted
+// by exp2((m_c - M) * scale_log2); the sum of the weighted l_c normalises.
+// The first 64 records' fields stay in registers between the two passes (most
+// queries have fewer), and the acc rows are loaded kBatch at a time before any
+// is used, so a wave waits for one round trip per batch, not per record.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   constexpr int PER = D / 64;  // output elements per lane
+  constexpr int kBatch = 8;
+  using VT = typename std::conditional<PER == 2, float2, float>::type;
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= a.nq * a.hq) return;
@@ -31,13 +37,17 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   const DevMerge mg = a.merge[q];
   if (mg.p_count == 0) return;
   const float sl2 = a.scale_log2;
-  float M = kNegInf;
-  for (int c0 = 0; c0 < mg.p_count; c0 += 64) {
+  int slot_r = 0;
+  float m_r = kNegInf, l_r = 0.f;
+  if (lane < mg.p_count) {
+    slot_r = a.parts[mg.p_begin + lane].slot0 + h;
+    m_r = a.part_ml[2 * slot_r];
+    l_r = a.part_ml[2 * slot_r + 1];
+  }
+  float M = m_r;
+  for (int c0 = 64; c0 < mg.p_count; c0 += 64) {
     const int c = c0 + lane;
-    if (c < mg.p_count) {
-      const int slot = a.parts[mg.p_begin + c].slot0 + h;
-      M = fmaxf(M, a.part_ml[2 * slot]);
-    }
+    if (c < mg.p_count) M = fmaxf(M, a.part_ml[2 * (a.parts[mg.p_begin + c].slot0 + h)]);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
@@ -47,25 +57,42 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   for (int c0 = 0; c0 < mg.p_count; c0 += 64) {
     const int c = c0 + lane;
-    int slot = 0;
-    float f = 0.f;
-    if (c < mg.p_count) {
-      slot = a.parts[mg.p_begin + c].slot0 + h;
-      const float mc = a.part_ml[2 * slot];
-      f = (mc == kNegInf) ? 0.f : fast_exp2((mc - M) * sl2);
-      ls += a.part_ml[2 * slot + 1] * f;
+    int slot = slot_r;
+    float mc = m_r, lc = l_r;
+    if (c0 > 0) {
+      slot = 0;
+      mc = kNegInf;
+      lc = 0.f;
+      if (c < mg.p_count) {
+        slot = a.parts[mg.p_begin + c].slot0 + h;
+        mc = a.part_ml[2 * slot];
+        lc = a.part_ml[2 * slot + 1];
+      }
     }
+    const float f = (mc == kNegInf) ? 0.f : fast_exp2((mc - M) * sl2);
+    ls += lc * f;
     const int cnt = min(64, mg.p_count - c0);
-    for (int k = 0; k < cnt; ++k) {
-      const int sk = __builtin_amdgcn_readlane(slot, k);
-      const float fk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), k));
-      const float* src = a.part_acc + static_cast<size_t>(sk) * D + lane * PER;
-      if constexpr (PER == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(src);
-        acc[0] += v.x * fk;
-        acc[1] += v.y * fk;
-      } else {
-        acc[0] += src[0] * fk;
+    for (int k0 = 0; k0 < cnt; k0 += kBatch) {
+      VT v[kBatch];
+      float fk[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        // past the end: the last record again, with weight 0 (no branch, so
+        // the batch's loads all issue before the first wait)
+        const int k = min(k0 + u, cnt - 1);
+        const int sk = __builtin_amdgcn_readlane(slot, k);
+        const float fu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), k));
+        fk[u] = (k0 + u < cnt) ? fu : 0.f;
+        v[u] = *reinterpret_cast<const VT*>(a.part_acc + static_cast<size_t>(sk) * D + lane * PER);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if constexpr (PER == 2) {
+          acc[0] += v[u].x * fk[u];
+          acc[1] += v[u].y * fk[u];
+        } else {
+          acc[0] += v[u] * fk[u];
+        }
       }
     }
   }

@@ -37,6 +37,17 @@ using namespace attn;
 // second barrier per super-block), so all NS slots are in flight during the
 // math; otherwise the refill waits for the next super-block's barrier and NS - 1
 // are.  MINW: waves per SIMD the register budget must allow.
+// An item's block list as staged in LDS: 16 bytes a block, the valid count
+// sharing the id's word (ids are below kMaxPoolBlocks = 2^27), so the longest
+// item (kRowsMaxItemBlocks) takes 16 KiB and two 64 KiB-ring workgroups still
+// fit a CU's 160 KiB.
+struct StagedBlock {
+  uint32_t id_valid;  // id | valid << 27
+  int32_t pos;
+  uint64_t mask;
+};
+constexpr uint32_t kStagedIdMask = (1u << 27) - 1;
+
 template <class P, int D, int TPW, int W, int HPW, int NS, bool EARLY, int MINW, bool CAUSAL>
 __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs a) {
   using E = typename P::elem;
@@ -53,7 +64,7 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
   __shared__ __attribute__((aligned(1024))) char ring[NS * STAGE];
   // the item's block list: a.max_blocks entries, sized at launch
   extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
-  DevBlock* ents = reinterpret_cast<DevBlock*>(dyn_smem);
+  StagedBlock* ents = reinterpret_cast<StagedBlock*>(dyn_smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -91,7 +102,7 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
     const int b0 = 2 * sp;
     if (b0 >= ib_base + 64) {
       ib_base = b0;
-      ib_id = (b0 + lane < nb) ? ents[b0 + lane].id : 0;
+      ib_id = (b0 + lane < nb) ? static_cast<int>(ents[b0 + lane].id_valid & kStagedIdMask) : 0;
     }
     const int ida = __builtin_amdgcn_readlane(ib_id, b0 - ib_base);
     const int idb = (b0 + 1 < nb) ? __builtin_amdgcn_readlane(ib_id, b0 + 1 - ib_base) : ida;
@@ -142,7 +153,10 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
   // the item's block list, staged once; waves read it 64 entries at a time
   // (lane k holds entry base + k) and take each super-block's fields with
   // v_readlane, so no LDS round trip sits on the per-super-block path
-  for (int k = tid; k < nb; k += 64 * W * HPW) ents[k] = bl[k];
+  for (int k = tid; k < nb; k += 64 * W * HPW) {
+    const DevBlock e = bl[k];
+    ents[k] = StagedBlock{static_cast<uint32_t>(e.id) | (static_cast<uint32_t>(e.valid) << 27), e.pos, e.mask};
+  }
 
   F qf[TPW];
 #pragma unroll
@@ -194,16 +208,13 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
     if (b0 >= cb_base + 64) {
       cb_base = b0;
       const int k = b0 + lane;
-      cb_valid = 0;
-      cb_pos = 0;
-      cb_mlo = cb_mhi = 0;
-      if (k < nb) {
-        const DevBlock e = ents[k];
-        cb_valid = e.valid;
-        cb_pos = e.pos;
-        cb_mlo = static_cast<uint32_t>(e.mask);
-        cb_mhi = static_cast<uint32_t>(e.mask >> 32);
-      }
+      // selected by value, stored once (see the same refill in attn.hip)
+      StagedBlock e{0, 0, 0};
+      if (k < nb) e = ents[k];
+      cb_valid = static_cast<int>(e.id_valid >> 27);
+      cb_pos = e.pos;
+      cb_mlo = static_cast<uint32_t>(e.mask);
+      cb_mhi = static_cast<uint32_t>(e.mask >> 32);
     }
     const int la = b0 - cb_base;
     SBMeta e;
@@ -341,7 +352,7 @@ constexpr int ring_slots() {
 
 template <class P, int D, int TPW, int W, int HPW, int NS, bool EARLY, int MINW, bool C>
 hipError_t launch_one(const AttnArgs& args, int32_t n_items, hipStream_t s) {
-  const size_t ents_bytes = sizeof(DevBlock) * static_cast<size_t>(args.max_blocks > 0 ? args.max_blocks : 1);
+  const size_t ents_bytes = sizeof(StagedBlock) * static_cast<size_t>(args.max_blocks > 0 ? args.max_blocks : 1);
   hipLaunchKernelGGL((attn_rows_kernel<P, D, TPW, W, HPW, NS, EARLY, MINW, C>), dim3(n_items * (args.hkv / HPW)),
                      dim3(64 * W * HPW), ents_bytes, s, args);
   return hipGetLastError();

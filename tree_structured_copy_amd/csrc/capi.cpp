@@ -335,7 +335,9 @@ const char* tkv_strerror(int status) {
 int tkv_create(const tkv_config* cfg, tkv_cache** out) {
   if (!cfg || !out) return TKV_E_INVAL;
   const tkv_config& c = *cfg;
-  if (c.num_layers < 1 || c.num_q_heads < 1 || c.num_kv_heads < 1 || c.num_blocks < 1) return TKV_E_INVAL;
+  if (c.num_layers < 1 || c.num_q_heads < 1 || c.num_kv_heads < 1 || c.num_blocks < 1 ||
+      c.num_blocks > kMaxPoolBlocks)
+    return TKV_E_INVAL;
   if (c.num_q_heads % c.num_kv_heads || c.num_q_heads / c.num_kv_heads > kMaxRows) return TKV_E_INVAL;
   if (c.head_dim != 64 && c.head_dim != 128) return TKV_E_INVAL;
   if (c.block_size != kBlock || c.reserved != 0) return TKV_E_INVAL;

@@ -8,7 +8,8 @@ constexpr int kBlock = 16;          // token slots per block
 constexpr int kMaxRows = 256;       // rows (queries x heads-per-kv-head) per group
 constexpr int kMaxGroupQueries = 64; // one bit per query in a block's visibility mask
 constexpr int kKernelClasses = 6;   // A1, A2 (attn.hip), B4, B6, B8, B16 (attn_rows.hip)
-constexpr int kRowsMaxItemBlocks = 512;  // longest block list of one attn_rows.hip work item (12 KiB of LDS)
+constexpr int kRowsMaxItemBlocks = 1024;  // longest block list of one attn_rows.hip work item (16 KiB of LDS)
+constexpr int kMaxPoolBlocks = 1 << 27;   // block ids fit 27 bits (attn_rows.hip packs the valid count beside them)
 constexpr int kAppendMaxBlocks = 128;
 constexpr int kGatherMaxBlocks = 64;
 
