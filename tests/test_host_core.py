@@ -336,7 +336,8 @@ def test_error_codes_and_strong_guarantee():
 
 
 def test_bad_configs_rejected():
-    for args in [(0, 4, 4, 64, 10), (1, 4, 3, 64, 10), (1, 4, 4, 96, 10), (1, 4, 4, 64, 0)]:
+    # block ids must fit 27 bits: 2^27 blocks is the largest pool
+    for args in [(0, 4, 4, 64, 10), (1, 4, 3, 64, 10), (1, 4, 4, 96, 10), (1, 4, 4, 64, 0), (1, 4, 4, 64, (1 << 27) + 1)]:
         with pytest.raises(tkv.TkvError) as e:
             tkv.tkv_create(*args, tkv.TKV_F32)
         assert e.value.code == tkv.TKV_E_INVAL
