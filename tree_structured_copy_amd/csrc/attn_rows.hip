@@ -358,51 +358,69 @@ hipError_t launch_one(const AttnArgs& args, int32_t n_items, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Shapes by row tiles.  Two workgroups per CU (64 KiB rings) hide each other's
-// latency; one workgroup (128 KiB) gets the deeper ring; fp32 at d = 128 needs
-// the registers of one workgroup per CU.
+// Ring depth that keeps about 16 KiB of each workgroup's loads in flight
+// beside the stage being read.  HBM serves these scattered tile streams best
+// with about two 16 KiB stages in flight per CU: deeper rings measured slower
+// (a 32-layer decode layer ran at 6.2 TB/s with four 16 KiB slots and two
+// workgroups per CU, 6.8-7.0 TB/s with two).
+template <class P, int D, int HPW>
+constexpr int shallow_slots() {
+  constexpr int stage = HPW * 4 * 16 * D * static_cast<int>(sizeof(typename P::elem));
+  return 1 + (16384 / stage > 1 ? 16384 / stage : 1);
+}
+
+// Shapes by row tiles.  Up to 4 tiles: 4 waves and a 64 KiB ring, so two
+// workgroups fit a CU; with no more workgroups than CUs the ring is filled
+// deeper, as one workgroup then has the CU's loads in flight alone.  fp32 at
+// d = 128 needs the registers of one workgroup per CU.
 template <class P, int D, bool C>
-hipError_t launch_shape(int tiles, const AttnArgs& args, int32_t n_items, hipStream_t s) {
+hipError_t launch_shape(int tiles, const AttnArgs& args, int32_t n_items, hipStream_t s, int cus) {
   constexpr bool kSmall = kIsBF16<P> || D <= 64;
   if (tiles <= 4) {
-    if constexpr (kSmall) return launch_one<P, D, 1, 4, 1, ring_slots<P, D, 1, 64>(), false, 2, C>(args, n_items, s);
-    else return launch_one<P, D, 1, 4, 1, ring_slots<P, D, 1, 128>(), false, 1, C>(args, n_items, s);
+    if constexpr (kSmall) {
+      if (static_cast<int64_t>(n_items) * args.hkv > cus)
+        return launch_one<P, D, 1, 4, 1, shallow_slots<P, D, 1>(), false, 2, C>(args, n_items, s);
+      return launch_one<P, D, 1, 4, 1, ring_slots<P, D, 1, 64>(), false, 2, C>(args, n_items, s);
+    } else {
+      return launch_one<P, D, 1, 4, 1, ring_slots<P, D, 1, 128>(), false, 1, C>(args, n_items, s);
+    }
   }
   if (tiles <= 6) {
     // two heads per workgroup where the head count allows, so that its 12 waves
     // spread evenly over the CU's four SIMDs (6 waves would sit 2, 2, 1, 1)
     if constexpr (kSmall) {
-      if (args.hkv % 2 == 0) return launch_one<P, D, 1, 6, 2, ring_slots<P, D, 2, 128>(), false, 3, C>(args, n_items, s);
-      return launch_one<P, D, 1, 6, 1, ring_slots<P, D, 1, 64>(), false, 3, C>(args, n_items, s);
+      if (args.hkv % 2 == 0) return launch_one<P, D, 1, 6, 2, shallow_slots<P, D, 2>(), false, 3, C>(args, n_items, s);
+      return launch_one<P, D, 1, 6, 1, shallow_slots<P, D, 1>(), false, 3, C>(args, n_items, s);
     } else {
       return launch_one<P, D, 1, 6, 1, ring_slots<P, D, 1, 128>(), false, 2, C>(args, n_items, s);
     }
   }
   if (tiles <= 8) {
-    if constexpr (kSmall) return launch_one<P, D, 1, 8, 1, ring_slots<P, D, 1, 64>(), false, 4, C>(args, n_items, s);
+    if constexpr (kSmall) return launch_one<P, D, 1, 8, 1, shallow_slots<P, D, 1>(), false, 4, C>(args, n_items, s);
     else return launch_one<P, D, 1, 8, 1, ring_slots<P, D, 1, 128>(), false, 2, C>(args, n_items, s);
   }
   if (tiles <= 16) {
-    if constexpr (kSmall) return launch_one<P, D, 1, 16, 1, ring_slots<P, D, 1, 128>(), false, 4, C>(args, n_items, s);
+    if constexpr (kSmall) return launch_one<P, D, 1, 16, 1, shallow_slots<P, D, 1>(), false, 4, C>(args, n_items, s);
     else return launch_one<P, D, 2, 8, 1, ring_slots<P, D, 1, 128>(), false, 2, C>(args, n_items, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <class P, int D>
-hipError_t launch_c(int tiles, bool causal, const AttnArgs& args, int32_t n_items, hipStream_t s) {
-  return causal ? launch_shape<P, D, true>(tiles, args, n_items, s) : launch_shape<P, D, false>(tiles, args, n_items, s);
+hipError_t launch_c(int tiles, bool causal, const AttnArgs& args, int32_t n_items, hipStream_t s, int cus) {
+  return causal ? launch_shape<P, D, true>(tiles, args, n_items, s, cus)
+                : launch_shape<P, D, false>(tiles, args, n_items, s, cus);
 }
 
 }  // namespace
 
 hipError_t launch_attn_rows(int dtype, int head_dim, int tiles, bool causal, const AttnArgs& args, int32_t n_items,
-                            hipStream_t stream) {
+                            hipStream_t stream, int cus) {
   if (n_items <= 0) return hipSuccess;
-  if (dtype == 1 && head_dim == 128) return launch_c<BF16, 128>(tiles, causal, args, n_items, stream);
-  if (dtype == 1 && head_dim == 64) return launch_c<BF16, 64>(tiles, causal, args, n_items, stream);
-  if (dtype == 0 && head_dim == 128) return launch_c<F32, 128>(tiles, causal, args, n_items, stream);
-  if (dtype == 0 && head_dim == 64) return launch_c<F32, 64>(tiles, causal, args, n_items, stream);
+  if (dtype == 1 && head_dim == 128) return launch_c<BF16, 128>(tiles, causal, args, n_items, stream, cus);
+  if (dtype == 1 && head_dim == 64) return launch_c<BF16, 64>(tiles, causal, args, n_items, stream, cus);
+  if (dtype == 0 && head_dim == 128) return launch_c<F32, 128>(tiles, causal, args, n_items, stream, cus);
+  if (dtype == 0 && head_dim == 64) return launch_c<F32, 64>(tiles, causal, args, n_items, stream, cus);
   return hipErrorInvalidValue;
 }
 

@@ -278,7 +278,7 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
       const int w = c->waves ? c->waves : (cls == 0 && static_cast<int64_t>(n) * c->cfg.num_kv_heads <= c->cus ? 2 : 4);
       e = launch_attn_partial(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], w, P.causal, a, n, st);
     } else {
-      e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], P.causal, a, n, st);
+      e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], P.causal, a, n, st, c->cus);
     }
     if (e != hipSuccess) return TKV_E_DEVICE;
     if (st != stream && hipEventRecord(c->join_ev[k - 1], st) != hipSuccess) return TKV_E_DEVICE;

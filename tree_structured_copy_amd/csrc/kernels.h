@@ -13,9 +13,10 @@ hipError_t launch_attn_partial(int dtype, int head_dim, int tiles, int waves, bo
                                int32_t n_items, hipStream_t stream);
 
 // Partial attention for groups of 3..16 row tiles with K/V staged in LDS;
-// grid = n_items * Hkv workgroups (4 or 8 waves by tile count).
+// grid = n_items * Hkv / (heads per workgroup) workgroups.  cus = the device's
+// compute units (the ring depth depends on workgroups per CU).
 hipError_t launch_attn_rows(int dtype, int head_dim, int tiles, bool causal, const AttnArgs& args, int32_t n_items,
-                            hipStream_t stream);
+                            hipStream_t stream, int cus);
 
 // Log-sum-exp merge of each query's partial records into out; one wave per
 // (query, query head), four per workgroup.
