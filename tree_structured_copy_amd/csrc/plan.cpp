@@ -372,8 +372,12 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       for (const auto& x : tmp) cnt += (x.tiles <= c);
       P.bucket_begin[c + 1] = cnt;
       P.bucket_max_blocks[c] = 0;
+      P.bucket_blocks[c] = 0;
     }
-    for (const auto& x : tmp) P.bucket_max_blocks[x.tiles] = std::max(P.bucket_max_blocks[x.tiles], x.it.blk_count);
+    for (const auto& x : tmp) {
+      P.bucket_max_blocks[x.tiles] = std::max(P.bucket_max_blocks[x.tiles], x.it.blk_count);
+      P.bucket_blocks[x.tiles] += x.it.blk_count;
+    }
     // merge records: every partial of a query, in the order its groups were made
     P.merge.resize(total_q);
     for (int64_t q = 0; q < total_q; ++q) {

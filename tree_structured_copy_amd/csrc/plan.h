@@ -37,6 +37,7 @@ struct Plan {
   int32_t bucket_begin[kKernelClasses + 1] = {0, 0, 0, 0, 0, 0, 0};
   int32_t bucket_tiles[kKernelClasses] = {1, 2, 4, 6, 8, 16};
   int32_t bucket_max_blocks[kKernelClasses] = {0, 0, 0, 0, 0, 0};  // longest item of each class
+  int64_t bucket_blocks[kKernelClasses] = {0, 0, 0, 0, 0, 0};      // blocks of all items of each class
   std::vector<DevGroup> groups;
   std::vector<int32_t> gq;
   std::vector<int32_t> gqpos;
