@@ -271,15 +271,17 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     a.item0 = P.bucket_begin[cls];
     a.max_blocks = P.bucket_max_blocks[cls];
     hipError_t e;
-    if (cls < 2) {
-      // One tile: two waves, i.e. few long streams of loads per CU, which HBM
-      // serves faster than more, shorter ones -- when the launch has no more
-      // workgroups than CUs, or when its items are long (64+ blocks on
-      // average); short items in large launches keep four waves, whose
-      // shorter per-wave chains finish them sooner.
-      const int64_t wgs = static_cast<int64_t>(n) * c->cfg.num_kv_heads;
-      const bool two = cls == 0 && (wgs <= c->cus || P.bucket_blocks[cls] >= 64LL * n);
-      const int w = c->waves ? c->waves : (two ? 2 : 4);
+    const int64_t wgs = static_cast<int64_t>(n) * c->cfg.num_kv_heads;
+    if (cls == 0 && !c->waves && wgs > c->cus && P.bucket_blocks[cls] < 64LL * n) {
+      // One tile, more workgroups than CUs, short items (a search tree's
+      // private nodes): the LDS-staged kernel's 4-tile shape, whose shallow
+      // ring with two workgroups per CU streams these faster than the
+      // register kernel
+      e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, 1, P.causal, a, n, st, c->cus);
+    } else if (cls < 2) {
+      // One tile otherwise: two waves, i.e. few long streams of loads per CU,
+      // which HBM serves faster than more, shorter ones; two tiles: four.
+      const int w = c->waves ? c->waves : (cls == 0 ? 2 : 4);
       e = launch_attn_partial(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], w, P.causal, a, n, st);
     } else {
       e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], P.causal, a, n, st, c->cus);
