@@ -37,13 +37,15 @@ def test_standard_workload_sampled(name, per_op):
     assert_close(run_both(wl, sample=s), wl.dtype)
 
 
-@pytest.mark.parametrize("case", ["long_decode", "long_verify", "wide_batch", "gqa8_tree"])
+@pytest.mark.parametrize("case", ["long_decode", "long_verify", "wide_batch", "gqa8_tree", "wide_batch_f32",
+                                  "wide_batch_d64"])
 def test_extreme_shapes_sampled(case):
     """Shapes beyond the standard workloads, sampled against the oracle:
     a 40 000-token shared prefix (2500 blocks, cut into many split-K chunks
     and merged); verification over a 30 000-token prefix; 1500 independent
     sequences in one call (1500 groups, 12 000 workgroups); a search tree at
-    8 query heads per KV head (cascade subgroups of 2 queries)."""
+    8 query heads per KV head (cascade subgroups of 2 queries); wide batches
+    at fp32 and at d = 64."""
     if case == "long_decode":
         wl = recipes.fork_workload("long_decode", dtype="bf16", layers=1, q_heads=8, kv_heads=2, head_dim=128,
                                    requests=1, prefix=40000, width=3, branch_tokens=17, seed=51)
@@ -53,6 +55,14 @@ def test_extreme_shapes_sampled(case):
     elif case == "wide_batch":
         wl = recipes.fork_workload("wide_batch", dtype="bf16", layers=1, q_heads=32, kv_heads=8, head_dim=128,
                                    requests=1500, prefix=40, width=1, branch_tokens=3, seed=53)
+    elif case == "wide_batch_f32":
+        # one-tile groups, more workgroups than CUs, short items: the LDS-staged
+        # kernel's 4-tile shape at fp32
+        wl = recipes.fork_workload("wide_batch_f32", dtype="f32", layers=1, q_heads=16, kv_heads=4, head_dim=128,
+                                   requests=600, prefix=70, width=1, branch_tokens=5, seed=55)
+    elif case == "wide_batch_d64":
+        wl = recipes.fork_workload("wide_batch_d64", dtype="bf16", layers=1, q_heads=16, kv_heads=4, head_dim=64,
+                                   requests=600, prefix=70, width=1, branch_tokens=5, seed=56)
     else:
         wl = recipes.mcts_workload("gqa8_tree", dtype="bf16", q_heads=32, kv_heads=4, head_dim=128,
                                    root_tokens=300, branching=4, depth=5, leaves=128, node_tokens=16, seed=54)
