@@ -6,10 +6,11 @@
 // (rows = the group's queries x the query heads that share one KV head) and
 // lists each group's blocks once, with a mask of which queries see each block.
 //
-// One workgroup (4 waves) runs one work item (a run of a group's block list) for
-// one KV head.  Each wave takes every 4th block of the item and keeps, for all
-// of the group's rows, a flash-decoding state (running max m, sum l, output
-// accumulator) in registers:
+// One workgroup (W = 2, 4 or 8 waves) runs one work item (a run of a group's
+// block list) for one KV head.  Each wave takes every W-th super-block (two
+// blocks) of the item and keeps, for all of the group's rows, a
+// flash-decoding state (running max m, sum l, output accumulator) in
+// registers:
 //   * a block's K tile arrives with four contiguous 1 KiB wave loads already in
 //     MFMA operand order (layout.h) and S^T = K Q^T for 16 tokens x 16 rows is a
 //     handful of MFMAs: every key is fetched from HBM once per group, however
@@ -18,7 +19,7 @@
 //     P^T the P.V MFMA needs, so the softmax stays in registers;
 //   * the running max is rescaled lazily (only when it grows by more than 2^8,
 //     which bounds every weight by 2^8 and keeps fp32 sums exact enough).
-// At the end the 4 waves' states are merged through LDS; an item that covers its
+// At the end the W waves' states are merged through LDS; an item that covers its
 // whole group writes normalised outputs, otherwise it writes fp32 partials
 // (m, l, acc) and attn_merge combines them (log-sum-exp, exp2 domain).
 #include <hip/hip_runtime.h>

@@ -13,7 +13,9 @@
 //   * the loads are issued from inline asm so that the waits are ours: the
 //     compiler would otherwise wait for every outstanding LDS DMA at each
 //     barrier and serialise the ring; one s_waitcnt vmcnt(N) + one barrier per
-//     super-block keeps NS - 2 super-blocks in flight per wave;
+//     super-block keeps NS - 2 super-blocks in flight per wave besides the one
+//     being read (the launcher picks NS: about two 16 KiB super-blocks in
+//     flight per CU stream best);
 //   * each wave reads the staged K and V fragments from LDS (conflict-free 16-B
 //     lane-contiguous reads in the pool's MFMA operand order) and runs the same
 //     S^T = K Q^T, online softmax and O^T += V^T P^T steps as attn.hip for each of
