@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0
 # right.  Valid only for the kernel sources they were taken on (sha256 below);
 # after any change to them the bench line reports traffic as null.
 TRAFFIC_RECORD = {
-    "sources_sha256": "27f79b837aa05f1168c90b138fca83864893e2f2ce37d04b9949e7d490784a32",
+    "sources_sha256": "b65e13d3dd59497f783545cb5f72be68c05064715e63a1202cde6aaad82fb5fc",
     "fetch_kib_per_launch": 281757, "fetch_factor": 1.9999,   # 1 GiB read reads as 524309 KiB
     "write_kib_per_launch": 2048, "write_factor": 1.0,        # 1 GiB written reads as 1048576 KiB
     "hbm_bytes_per_launch": 577016056 + 2097152,
@@ -45,12 +45,18 @@ TRAFFIC_RECORD = {
 
 
 def _kernel_sources_sha():
+    """sha256 of the decode kernel's sources with // comments and blank lines
+    removed, so that an edit of the comments alone keeps the recorded traffic."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tree_structured_copy_amd", "csrc")
     for f in ("attn.hip", "attn_common.h", "layout.h", "tkv_types.h"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            for line in fh:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 
