@@ -421,7 +421,7 @@ def test_plan_cascade_shapes():
 
 def test_plan_classes_fill_one_round():
     """Each kernel class is cut to fill the GPU on its own, in one round of
-    workgroups: the shared groups of the search tree become 30 items (240
+    workgroups (two per CU for the 4- and 8-tile shapes): the shared groups of the search tree become 30 items (240
     workgroups for 256 CUs); groups that already give one workgroup per CU,
     or that cannot be cut below the chunk floor, are left whole (the 32-layer
     workload's 768-block lists fit one item each)."""

@@ -306,7 +306,10 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       const int cls = class_of(gi);
       const int64_t nb = gout[gi].blk_count;
       const int64_t floor = std::max<int32_t>(1, cls < 2 ? opt.min_chunk : opt.min_chunk / 4);
-      int64_t nc = nb * class_items / class_blocks[cls];
+      // the 4- and 8-tile LDS-staged shapes fit two workgroups per CU, and
+      // two per CU stream faster than one with a deeper ring: twice the items
+      const int64_t want = (cls == 2 || cls == 4) ? 2 * class_items : class_items;
+      int64_t nc = nb * want / class_blocks[cls];
       nc = std::min(nc, nb / floor);
       nc = std::max<int64_t>(nc, (nb + kRowsMaxItemBlocks - 1) / kRowsMaxItemBlocks);
       return static_cast<int32_t>(std::max<int64_t>(nc, 1));
