@@ -118,7 +118,8 @@ int tkv_append(tkv_cache* c, tkv_seq s, int32_t ntok, const void* k, const void*
 int tkv_truncate(tkv_cache* c, tkv_seq s, int64_t new_len);
 
 /* Device workspace needed by an attention call with these arguments (nq = NULL for
- * decode).  Builds (and caches) the call's plan.  *bytes may be 0. */
+ * decode).  Builds (and caches) the call's plan.  *bytes may be 0.  nseq >= 1 (an
+ * empty batch is TKV_E_INVAL here and in the attention calls). */
 int tkv_workspace_size(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
                        size_t* bytes);
 

@@ -450,3 +450,23 @@ def test_plan_small_lds_class_joins_the_largest():
                                requests=2, prefix=300, width=30, branch_tokens=5, seed=3)
     info = _host_plan(wl, [(tkv.TKV_OPT_TARGET_WGS, 256)])
     assert info["items_per_kernel"][4] > 0 and info["items_per_kernel"][5] == 0, info
+
+
+def test_empty_batch_and_query_counts_rejected():
+    """An attention call over no handles is TKV_E_INVAL; a verify query count of
+    0 or above the handle's length is TKV_E_RANGE (checked when the plan is
+    built, before anything could be launched)."""
+    c = host_cache(64, 1, 8, 2, 64)
+    try:
+        s = tkv.tkv_seq_new(c)
+        tkv.tkv_append(c, s, 20)
+        for bad, code in [(lambda: tkv.tkv_workspace_size(c, []), tkv.TKV_E_INVAL),
+                          (lambda: tkv.tkv_plan_info_get(c, [], None), tkv.TKV_E_INVAL),
+                          (lambda: tkv.tkv_workspace_size(c, [s], [0]), tkv.TKV_E_RANGE),
+                          (lambda: tkv.tkv_workspace_size(c, [s], [21]), tkv.TKV_E_RANGE)]:
+            with pytest.raises(tkv.TkvError) as e:
+                bad()
+            assert e.value.code == code
+        assert tkv.tkv_workspace_size(c, [s], [20]) >= 0  # all 20 positions as queries is fine
+    finally:
+        tkv.tkv_destroy(c)
