@@ -272,11 +272,11 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     a.max_blocks = P.bucket_max_blocks[cls];
     hipError_t e;
     const int64_t wgs = static_cast<int64_t>(n) * c->cfg.num_kv_heads;
-    if (cls == 0 && !c->waves && wgs > c->cus && P.bucket_blocks[cls] < 64LL * n) {
-      // One tile, more workgroups than CUs, short items (a search tree's
-      // private nodes): the LDS-staged kernel's 4-tile shape, whose shallow
-      // ring with two workgroups per CU streams these faster than the
-      // register kernel
+    if (cls == 0 && !c->waves && wgs > c->cus) {
+      // One tile, more workgroups than CUs (a search tree's private nodes, a
+      // large batch of sequences): the LDS-staged kernel's 4-tile shape,
+      // whose shallow ring with two workgroups per CU streams these faster
+      // than the register kernel
       e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, 1, P.causal, a, n, st, c->cus);
     } else if (cls < 2) {
       // One tile otherwise: two waves, i.e. few long streams of loads per CU,
