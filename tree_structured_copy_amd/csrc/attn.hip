@@ -47,8 +47,10 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
   const DevItem it = a.items[a.item0 + blockIdx.x / a.hkv];
   const int nb = it.blk_count;
   const int nsb = (nb + 1) >> 1;
-  // super-blocks of this wave: wave, wave + W, wave + 2W, ...
-  const int nmine = nsb > wave ? (nsb - wave + W - 1) / W : 0;
+  // super-blocks of this wave: a contiguous share of the item (two waves
+  // streaming far-apart halves measured about 1 % faster than alternating)
+  const int per_w = (nsb + W - 1) / W, start_w = wave * per_w;
+  const int nmine = nsb > start_w ? min(per_w, nsb - start_w) : 0;
   const DevBlock* bl = a.blocks + it.blk_begin;
   const size_t tile = 16 * D;
   const size_t bstride = static_cast<size_t>(a.hkv) * tile;
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
   const E* vbase = static_cast<const E*>(a.vpool) + static_cast<size_t>(kvh) * tile;
 
   // Block-list entries of this wave, one per lane, 32 super-blocks per batch:
-  // lane j holds block 2 * (wave + W * (32 * batch + j / 2)) + j % 2.  Reading
+  // lane j holds block 2 * (start_w + 32 * batch + j / 2) + j % 2.  Reading
   // them with readlane keeps scalar-load latency out of the streaming loop.
   int e_id = -1, e_valid = 0, e_pos = 0;
   uint32_t e_mlo = 0, e_mhi = 0;
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
   // pointer, which puts these registers on the stack)
   auto load_entries = [&](int batch) {
     const int sbk = 32 * batch + (lane >> 1);
-    const int b = 2 * (wave + W * sbk) + (lane & 1);
+    const int b = 2 * (start_w + sbk) + (lane & 1);
     DevBlock e{-1, 0, 0, 0, 0};
     if (sbk < nmine && b < nb) e = bl[b];
     e_id = e.id;
