@@ -197,24 +197,31 @@ def test_gather_returns_appended_kv_exactly():
             lib.close()
 
 
-def test_single_token_is_exact_v():
-    """One key: softmax weight 1, so the output is the value itself."""
+@pytest.mark.parametrize("requests,kv_heads,waves", [(5, 2, 0), (300, 8, 0), (300, 8, 2)])
+def test_single_token_is_exact_v(requests, kv_heads, waves):
+    """One key: softmax weight 1, so the output is the value itself -- in the
+    register kernel (5 sequences; 300 sequences with its wave count forced) and
+    in the LDS-staged kernel (300 sequences x 8 KV heads: more workgroups than
+    CUs).  9600 rows give scaled scores well above 1, where a weight formed as
+    exp2(s * c - m * c) would be off by the rounding of m * c."""
     torch = need_gpu()
     from tree_structured_copy_amd import tkv
     from tree_structured_copy_amd.replay import LibReplay
     from workloads import device as wdev
-    wl = recipes.fork_workload("one", dtype="bf16", layers=1, q_heads=8, kv_heads=2, head_dim=128,
-                               requests=5, prefix=1, width=1, branch_tokens=0, seed=2)
+    wl = recipes.fork_workload("one", dtype="bf16", layers=1, q_heads=4 * kv_heads, kv_heads=kv_heads,
+                               head_dim=128, requests=requests, prefix=1, width=1, branch_tokens=0, seed=2)
     lib = LibReplay(wl)
     try:
         lib.build()
+        if waves:
+            tkv.tkv_set_option(lib.c, tkv.TKV_OPT_WAVES, waves)
         op = wl.attend_ops()[0]
         out = lib.attend(op)
         for i, hname in enumerate(op[2]):
-            ko = torch.empty((1, 2, 128), dtype=torch.bfloat16, device="cuda")
+            ko = torch.empty((1, kv_heads, 128), dtype=torch.bfloat16, device="cuda")
             vo = torch.empty_like(ko)
             tkv.tkv_gather(lib.c, lib.h[hname], 0, ko, vo, torch.cuda.current_stream())
-            for h in range(8):
+            for h in range(4 * kv_heads):
                 assert torch.equal(out[i, h], vo[0, h // 4].float())
     finally:
         lib.close()

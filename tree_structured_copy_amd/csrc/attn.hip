@@ -193,10 +193,12 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
         for (int dt = 0; dt < NDT; ++dt) acc[t][dt] *= alpha;
         m[t] = mn;
       }
-      const float mc = (m[t] == kNegInf) ? 0.f : m[t] * sl2;
+      // m is kept in raw score units; the exponent is (s - m) * log2(e) / sqrt(D),
+      // the difference taken first so that the score equal to m weighs exactly 1
+      const float mm = (m[t] == kNegInf) ? 0.f : m[t];
       float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(sc[i], sl2, -mc));
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2((sc[i] - mm) * sl2);
       P::pv(v, p, acc[t], l[t]);
     }
   };

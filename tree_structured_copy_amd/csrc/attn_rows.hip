@@ -299,11 +299,12 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
         for (int dt = 0; dt < NDT; ++dt) acc[t][dt] *= alpha;
         m[t] = mn;
       }
-      // m is kept in raw score units; exponents are (s - m) * log2(e) / sqrt(D)
-      const float mc = (m[t] == kNegInf) ? 0.f : m[t] * sl2;
+      // m is kept in raw score units; the exponent is (s - m) * log2(e) / sqrt(D),
+      // the difference taken first so that the score equal to m weighs exactly 1
+      const float mm = (m[t] == kNegInf) ? 0.f : m[t];
       float p[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(x[i], sl2, -mc));
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2((x[i] - mm) * sl2);
       P::pv(vp, p, acc[t], l[t]);
       if constexpr (TPW > 1) __builtin_amdgcn_sched_barrier(0);  // one tile's weights live at a time
     }
@@ -327,10 +328,11 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
     if (it.part_base < 0) {
       const int qi = a.gq[it.q_begin + j];
       float* o = a.out + (static_cast<size_t>(qi) * a.hq + h) * D;
-      const float inv = 1.f / lt;
+      // divided, not multiplied by 1 / l: a single visible key then gives its
+      // value exactly, as the register kernel does
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        *reinterpret_cast<f32x4*>(o + 16 * dt + 4 * g) = acc[t][dt] * inv;
+        *reinterpret_cast<f32x4*>(o + 16 * dt + 4 * g) = acc[t][dt] / lt;
     } else {
       const size_t slot = static_cast<size_t>(it.part_base) + static_cast<size_t>(j) * a.hq + h;
       float* o = a.part_acc + slot * D;
