@@ -72,13 +72,13 @@ class _Copy:
     attend call of one step (one per layer for multi-layer workloads) with its
     query, output and workspace buffers."""
 
-    def __init__(self, wl):
+    def __init__(self, wl, extra_blocks=0):
         import torch
         from tree_structured_copy_amd import tkv
         from tree_structured_copy_amd.replay import LibReplay
         from workloads import device as wdev
         self.wl = wl
-        self.lib = LibReplay(wl, "cuda")
+        self.lib = LibReplay(wl, "cuda", extra_blocks=extra_blocks)
         i = self.lib.build()
         self.ops = []
         while i < len(wl.ops) and wl.ops[i][0] in ("decode", "verify"):
@@ -277,6 +277,52 @@ def _cpu_baseline(requests: int, reps: int):
             "branch_queries_per_s": 4 * requests / t}
 
 
+def _time_generation_loop(copies, windows, patch):
+    """A decode loop on the fork workload.  A step appends one token to each of
+    the 128 branches (one tkv_append_batch) and runs the decode call; copies
+    rotate step by step.  Windows of 16 steps per copy are timed (wall clock,
+    synchronised on both sides): in each, the first step opens a block in every
+    branch (its plan is rebuilt) and the other 15 fit in it (its plan is
+    updated in place, or with patch = 0 rebuilt).  Between windows, untimed,
+    the branches are truncated back to their 64 tokens.  Returns ms per step."""
+    import torch
+    from tree_structured_copy_amd import tkv
+    from workloads import device as wdev, gen, recipes
+    wl = recipes.llama_fork()
+    leaves = len(wl.attend_ops()[0][2])
+    items = [_Copy(wl, extra_blocks=leaves) for _ in range(copies)]
+    stream = torch.cuda.current_stream().cuda_stream
+    k = wdev.kv_tensor(wl, 1 << 20, leaves, gen.KIND_K)
+    v = wdev.kv_tensor(wl, 1 << 20, leaves, gen.KIND_V)
+    ones = tkv.i32_array([1] * leaves)
+    handles = [list(it.calls[0][1]) for it in items]
+    base_len = [[tkv.tkv_seq_len(it.lib.c, h) for h in hs] for it, hs in zip(items, handles)]
+    for it in items:
+        tkv.tkv_set_option(it.lib.c, tkv.TKV_OPT_PLAN_PATCH, patch)
+    torch.cuda.synchronize()
+    total = 0.0
+    counted = 0
+    for w in range(windows + 1):   # the first window warms up
+        t0 = time.perf_counter()
+        for i in range(16 * copies):
+            it = items[i % copies]
+            tkv.tkv_append_batch(it.lib.c, it.calls[0][1], ones, k, v, stream)
+            it.step(stream)
+        torch.cuda.synchronize()
+        if w > 0:
+            total += time.perf_counter() - t0
+            counted += 16 * copies
+        for it, hs, lens in zip(items, handles, base_len):
+            for h, L in zip(hs, lens):
+                tkv.tkv_truncate(it.lib.c, h, L)
+    counters = tkv.tkv_get_counters(items[0].lib.c)
+    for it in items:
+        it.close()
+    del items
+    torch.cuda.empty_cache()
+    return total / counted * 1e3, counters
+
+
 def measure(name, copies, steps, warmup, rebuild=False):
     """Wall time per step, kernel times and derived rates for one workload."""
     import torch
@@ -369,6 +415,15 @@ def main():
         return
 
     main_res = measure("llama_fork", args.copies, args.steps, args.warmup, rebuild=True)
+    loop_ms, loop_counters = _time_generation_loop(args.copies, 8, 1)
+    loop_rebuild_ms, _ = _time_generation_loop(args.copies, 8, 0)
+    generation_loop = {
+        "steps_timed": 8 * 16 * args.copies,
+        "ms_per_step": loop_ms,
+        "ms_per_step_plans_rebuilt": loop_rebuild_ms,
+        "branch_tokens_per_s": 128 / (loop_ms / 1e3),
+        "plans_built_patched_one_copy": [loop_counters["plans_built"], loop_counters["plans_patched"]],
+    }
     ms = main_res["ms_per_step"]
     ubytes = main_res["unique_kv_bytes"]
     value = main_res["unique_kv_GBps"]
@@ -408,6 +463,7 @@ def main():
         "hbm_peak_frac": value / HBM_PEAK_GBS,
         "branch_queries_per_s": main_res["queries_per_s"],
         "ms_per_step_plan_rebuild": main_res["ms_per_step_plan_rebuild"],
+        "generation_loop": generation_loop,
         "unique_kv_bytes": ubytes,
         "plan": main_res["plan"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -110,6 +110,19 @@ int tkv_release(tkv_cache* c, tkv_seq s);
  * nothing changes. */
 int tkv_append(tkv_cache* c, tkv_seq s, int32_t ntok, const void* k, const void* v, void* stream);
 
+/* Append ntok[i] >= 1 tokens to each of nseq >= 1 distinct handles seqs[i] in one
+ * call (one kernel launch per 128 blocks written): the same as tkv_append on each
+ * handle in batch order, with k, v device arrays [num_layers][sum ntok][Hkv][head_dim]
+ * holding the handles' tokens one after another in batch order.  k = v = NULL
+ * reserves the slots only.  All or nothing: a stale handle (TKV_E_BADSEQ), a count
+ * < 1 or a handle given twice (TKV_E_INVAL), a total over 2^31 - 1 tokens
+ * (TKV_E_RANGE) or too few free blocks for all of them (TKV_E_NOMEM) is found
+ * before anything changes.  A decode loop appends its step's token to every
+ * branch this way; appends that fit in the branches' last blocks leave the cached
+ * plan of the next attention call valid up to an in-place update. */
+int tkv_append_batch(tkv_cache* c, const tkv_seq* seqs, const int32_t* ntok, int32_t nseq,
+                     const void* k, const void* v, void* stream);
+
 /* Roll back s to new_len tokens (0 <= new_len <= length), e.g. to drop rejected
  * drafts after verification (DSpark blog, second layer: accept / roll back).  Only
  * tokens that s alone holds can be removed: if any position in [new_len, length) lies
@@ -174,7 +187,8 @@ typedef struct tkv_counters {
   int64_t nodes_freed;
   int64_t block_ids_copied;   /* block-table entries copied by any operation (fork: none) */
   int64_t plans_built;
-  int64_t plans_uploaded;
+  int64_t plans_uploaded;     /* whole plans copied to the device */
+  int64_t plans_patched;      /* cached plans updated in place after appends (TKV_OPT_PLAN_PATCH) */
 } tkv_counters;
 int tkv_get_counters(const tkv_cache* c, tkv_counters* out);
 
@@ -200,9 +214,14 @@ enum {
   TKV_OPT_WAVES = 5,        /* waves per one/two-tile workgroup: 2, 4 or 8 (0 = by launch size) */
   TKV_OPT_CASCADE = 6,      /* 1 = a group of 8+ row tiles hands blocks that only one row tile's
                                queries see to one-tile subgroups, merged after (default); 0 = off */
-  TKV_OPT_CONCURRENT = 7    /* how a call's kernel classes run: 0 = one after another on the call's
-                               stream; 1 = at once, on side streams of the library's own forked from
-                               and joined back to the call's stream (default) */
+  TKV_OPT_CONCURRENT = 7,   /* how a call's kernel classes run: 0 = one after another on the call's
+                               stream (default); 1 = at once, on side streams of the library's own
+                               forked from and joined back to the call's stream */
+  TKV_OPT_PLAN_PATCH = 8    /* 1 = a cached plan made before appends that each fitted in their tip
+                               node's last block (no new block, node, fork, release or truncation
+                               since) is updated in place: the changed block counts and query
+                               positions are written into its device copy by a small kernel
+                               (default); 0 = such a plan is rebuilt and uploaded whole */
 };
 int tkv_set_option(tkv_cache* c, int32_t key, int64_t value);
 int tkv_get_option(const tkv_cache* c, int32_t key, int64_t* value);

@@ -27,6 +27,15 @@ def _source_for(wl, call: int, ntok: int):
     return FunctionSource(ntok, fn)
 
 
+def _batch_source_for(wl, call: int, total: int, first: int, ntok: int):
+    """Rows [first, first + ntok) of a batched append's source arrays, which hold
+    ``total`` token rows (the handles' tokens one after another)."""
+    def fn(which, layer, kvh, t0, t1):
+        kind = gen.KIND_K if which == "k" else gen.KIND_V
+        return workloads.kv_slice(wl, call, total, kind, layer, kvh, first + t0, first + t1)
+    return FunctionSource(ntok, fn)
+
+
 class OracleReplay:
     def __init__(self, wl, with_alloc: bool = True):
         self.wl = wl
@@ -47,6 +56,15 @@ class OracleReplay:
             if self.alloc is not None:
                 self.alloc.append(self.h_alloc[h], ntok)
             self.mat.append(self.h_mat[h], _source_for(self.wl, call, ntok))
+        elif kind == "append_batch":
+            # by definition, the appends one after another in batch order
+            _, hs, ns, call = op
+            total, first = sum(ns), 0
+            for h, n in zip(hs, ns):
+                if self.alloc is not None:
+                    self.alloc.append(self.h_alloc[h], n)
+                self.mat.append(self.h_mat[h], _batch_source_for(self.wl, call, total, first, n))
+                first += n
         elif kind == "fork":
             _, h, n, kids = op
             if self.alloc is not None:

@@ -197,6 +197,50 @@ def test_gather_returns_appended_kv_exactly():
             lib.close()
 
 
+def test_append_batch_writes_what_the_appends_write():
+    """tkv_append_batch over a random session's live handles (1 to 40 tokens
+    each, three times, then one batch of more than 128 blocks, which takes two
+    launches) leaves in the pool exactly the K/V of the oracle's history, which
+    appends to each handle in batch order."""
+    import dataclasses
+    torch = need_gpu()
+    from oracle.replay import OracleReplay
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    for seed, dtype, hkv, d in [(31, "bf16", 2, 128), (32, "f32", 4, 64)]:
+        base = recipes.random_tree_workload("abatch", seed=seed, dtype=dtype, q_heads=hkv * 2, kv_heads=hkv,
+                                            head_dim=d, layers=2, verify=False)
+        live = [op for op in base.ops if op[0] == "decode"][0][2]
+        ops = [op for op in base.ops if op[0] != "decode"]
+        rng = np.random.default_rng(seed)
+        for r in range(3):
+            ops.append(("append_batch", list(live), [int(x) for x in rng.integers(1, 41, len(live))], 9000 + r))
+        big = -(-130 // len(live)) * 16 + 5
+        ops.append(("append_batch", list(live), [big] * len(live), 9003))
+        wl = dataclasses.replace(base, ops=ops, num_blocks=base.num_blocks + 400 + 3 * 4 * len(live))
+        say("append_batch seed %d %s: %d handles, last batch %d tokens each" % (seed, dtype, len(live), big))
+        lib, orc = LibReplay(wl), OracleReplay(wl)
+        try:
+            for op in wl.ops:
+                lib.apply(op)
+                orc.apply(op)
+            for name in live:
+                L = tkv.tkv_seq_len(lib.c, lib.h[name])
+                assert tkv.tkv_block_table(lib.c, lib.h[name]) == orc.alloc.table(orc.h_alloc[name])
+                for layer in range(wl.layers):
+                    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+                    ko = torch.empty((L, hkv, d), dtype=dt, device="cuda")
+                    vo = torch.empty_like(ko)
+                    tkv.tkv_gather(lib.c, lib.h[name], layer, ko, vo, torch.cuda.current_stream())
+                    torch.cuda.synchronize()
+                    for g in range(hkv):
+                        K, V = orc.mat.kv(orc.h_mat[name], layer, g)
+                        np.testing.assert_array_equal(ko[:, g].float().cpu().numpy(), K)
+                        np.testing.assert_array_equal(vo[:, g].float().cpu().numpy(), V)
+        finally:
+            lib.close()
+
+
 @pytest.mark.parametrize("requests,kv_heads,waves", [(5, 2, 0), (300, 8, 0), (300, 8, 2)])
 def test_single_token_is_exact_v(requests, kv_heads, waves):
     """One key: softmax weight 1, so the output is the value itself -- in the
@@ -321,3 +365,43 @@ def test_workspace_and_argument_errors():
         assert float(out.abs().max()) == 0.0
     finally:
         tkv.tkv_destroy(c)
+
+
+@pytest.mark.parametrize("kind,layers", [("decode", 1), ("verify", 1), ("decode", 2)])
+def test_generation_loop_plan_update(kind, layers):
+    """A generation loop: 20 rounds of one-token appends to most branches, each
+    followed by attention over every branch (and layer).  Every call matches
+    the oracle.  Most rounds' appends fit in the branches' last blocks, so the
+    cached plan is updated in place (block counts, query positions, their
+    minima) rather than rebuilt: the outputs must equal, bit for bit, those of
+    a library that rebuilds every such plan, and the counters must show both
+    paths taken."""
+    torch = need_gpu()
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    wl = recipes.decode_loop_workload("loop_%s_%d" % (kind, layers), layers=layers,
+                                      verify_nq=4 if kind == "verify" else 0, seed=71)
+    assert_close(run_both(wl), wl.dtype)
+    outs, counters = {}, {}
+    for patch in (1, 0):
+        lib = LibReplay(wl)
+        try:
+            tkv.tkv_set_option(lib.c, tkv.TKV_OPT_PLAN_PATCH, patch)
+            got = []
+            for op in wl.ops:
+                if op[0] in ("decode", "verify"):
+                    got.append(lib.attend(op).cpu())
+                lib.apply(op)
+            torch.cuda.synchronize()
+            outs[patch] = got
+            counters[patch] = tkv.tkv_get_counters(lib.c)
+        finally:
+            lib.close()
+    assert len(outs[1]) == 20 * layers
+    for a, b in zip(outs[1], outs[0]):
+        assert torch.equal(a, b)
+    say("counters with updates %s, without %s" % (counters[1], counters[0]))
+    assert counters[0]["plans_patched"] == 0
+    assert counters[1]["plans_patched"] >= 10
+    assert counters[1]["plans_built"] + counters[1]["plans_patched"] >= 20
+    assert counters[1]["plans_built"] < counters[0]["plans_built"]

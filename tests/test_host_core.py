@@ -283,6 +283,136 @@ def test_fork_bench_flat_over_prefix_and_depth():
         assert max(vals) < 3 * min(vals) + 50, (n, min(vals), max(vals))
 
 
+def test_plan_update_in_place_equals_rebuild(tmp_path):
+    """The planner's in-place update after appends that fit in tip blocks
+    (patch_plan): over 60 seeded random fork/append/truncate/release sessions,
+    12 rounds each of such appends, the updated plan equals a fresh build byte
+    for byte, and its list of changed words, written over the previous bytes
+    (what the device copy receives), gives the same bytes
+    (tests/plan_patch_check.cpp, compiled here against the library's host
+    sources)."""
+    import shutil
+    import subprocess
+    cxx = shutil.which("g++") or shutil.which("clang++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    csrc = os.path.join(ROOT, "tree_structured_copy_amd", "csrc")
+    exe = str(tmp_path / "plan_patch_check")
+    subprocess.run([cxx, "-O1", "-std=c++17", "-I" + csrc, "-I" + os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "plan_patch_check.cpp"), os.path.join(csrc, "tree.cpp"),
+                    os.path.join(csrc, "plan.cpp"), "-o", exe], check=True, timeout=300)
+    r = subprocess.run([exe, "60"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout[-2000:]
+    assert "all sessions ok: 720 rounds" in r.stdout
+    words = int(re.search(r"(\d+) changed words", r.stdout).group(1))
+    assert words > 1000
+
+
+def test_shape_epoch_only_moves_on_structural_change():
+    """Appends that fit in the tip node's last block leave the tree's shape
+    unchanged, so a cached plan is updated rather than rebuilt; a new block, a
+    fork, a truncation or a release changes it (observed through the plan
+    counters of a host-only cache: tkv_plan_info_get goes through the cache)."""
+    from tree_structured_copy_amd import tkv
+    c = host_cache(64)
+    try:
+        p = tkv.tkv_seq_new(c)
+        tkv.tkv_append(c, p, 20)
+        kids = tkv.tkv_fork(c, p, 2)
+        tkv.tkv_release(c, p)
+        for k in kids:
+            tkv.tkv_append(c, k, 3)
+
+        def info():
+            tkv.tkv_plan_info_get(c, kids)
+            return tkv.tkv_get_counters(c)
+
+        base = info()
+        tkv.tkv_append(c, kids[0], 5)      # 8 of 16: same block
+        tkv.tkv_append(c, kids[1], 13)     # 16 of 16: same block
+        a = info()
+        assert a["plans_built"] == base["plans_built"] and a["plans_patched"] == base["plans_patched"] + 1
+        assert tkv.tkv_plan_info_get(c, kids)["unique_tokens"] == 20 + 8 + 16
+        tkv.tkv_append(c, kids[1], 1)      # opens a block
+        b = info()
+        assert b["plans_built"] == a["plans_built"] + 1 and b["plans_patched"] == a["plans_patched"]
+        tkv.tkv_set_option(c, tkv.TKV_OPT_PLAN_PATCH, 0)
+        tkv.tkv_append(c, kids[0], 1)
+        d = info()
+        assert d["plans_built"] == b["plans_built"] + 1 and d["plans_patched"] == b["plans_patched"]
+        assert tkv.tkv_get_option(c, tkv.TKV_OPT_PLAN_PATCH) == 0
+        with pytest.raises(tkv.TkvError):
+            tkv.tkv_set_option(c, tkv.TKV_OPT_PLAN_PATCH, 2)
+    finally:
+        tkv.tkv_destroy(c)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_append_batch_is_the_appends_in_order(seed):
+    """tkv_append_batch over distinct handles gives the tables, lengths, sharer
+    counts and free set of the oracle allocator appending to each handle in
+    batch order (seeded random sessions; a batch over a random subset of live
+    handles with random counts, some opening blocks and nodes)."""
+    rng = random.Random(7000 + seed)
+    p = Pair(400)
+    try:
+        names = [0]
+        p.step(("new", 0))
+        nxt = 1
+        for _ in range(40):
+            h = rng.choice(names)
+            c = rng.random()
+            if c < 0.4:
+                p.step(("append", h, rng.randint(1, 40)))
+            elif c < 0.7 and len(names) < 16:
+                kids = list(range(nxt, nxt + rng.randint(1, 3)))
+                nxt += len(kids)
+                p.step(("fork", h, len(kids), kids))
+                names += kids
+            elif len(names) > 3:
+                p.step(("release", h))
+                names.remove(h)
+            for _ in range(2):
+                sub = rng.sample(names, rng.randint(1, len(names)))
+                ns = [rng.choice([1, 1, 2, 7, 16, 23]) for _ in sub]
+                tkv.tkv_append_batch(p.c, [p.lh[x] for x in sub], ns)
+                for x, n in zip(sub, ns):
+                    p.o.append(p.oh[x], n)
+                p.compare()
+    finally:
+        p.close()
+
+
+def test_append_batch_refusals_change_nothing():
+    """A repeated handle or a zero count (TKV_E_INVAL), a stale handle
+    (TKV_E_BADSEQ) and a batch the free blocks cannot hold (TKV_E_NOMEM) are
+    refused before any handle changes, even when the failing handle comes
+    last."""
+    c = host_cache(10)
+    try:
+        a = tkv.tkv_seq_new(c)
+        b = tkv.tkv_seq_new(c)
+        tkv.tkv_append(c, a, 5)
+        dead = tkv.tkv_seq_new(c)
+        tkv.tkv_release(c, dead)
+
+        def state():
+            return (tkv.tkv_block_table(c, a), tkv.tkv_block_table(c, b), tkv.tkv_num_free(c))
+
+        before = state()
+        for seqs, ns, err in [([a, b, a], [1, 1, 1], "inval"), ([a, b], [3, 0], "inval"),
+                              ([a, b, dead], [1, 1, 1], "badseq"), ([a, b], [11, 16 * 9 + 1], "nomem")]:
+            with pytest.raises(tkv.TkvError) as ei:
+                tkv.tkv_append_batch(c, seqs, ns)
+            assert ei.value.name == err
+            assert state() == before
+        tkv.tkv_append_batch(c, [b, a], [16 * 9, 11])   # exactly fits: b takes the 9 free blocks, a's tail holds 11
+        assert tkv.tkv_num_free(c) == 0
+        assert tkv.tkv_seq_len(c, a) == 16 and tkv.tkv_seq_len(c, b) == 144
+    finally:
+        tkv.tkv_destroy(c)
+
+
 def test_fork_latency_flat_in_prefix_and_depth():
     base = _median_fork_ns(16, 1)
     for prefix, depth in [(65536, 1), (16, 500), (65536, 500)]:

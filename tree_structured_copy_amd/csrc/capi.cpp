@@ -22,12 +22,15 @@ struct PlanSlot {
   std::vector<int32_t> nq;
   bool verify = false;
   uint64_t epoch = 0;
+  uint64_t shape_epoch = 0;
   uint64_t opt_epoch = 0;
   bool valid = false;
   Plan plan;
-  void* dev = nullptr;
+  void* dev = nullptr;  // the serialised plan, then room for a list of changed words
   size_t dev_cap = 0;
-  bool uploaded = false;
+  bool uploaded = false;  // dev holds the plan as of the last upload
+  // words changed by patch_plan since that upload (uploaded == true only)
+  std::vector<PlanWord> pending;
   uint64_t stamp = 0;
 };
 
@@ -57,10 +60,12 @@ struct tkv_cache {
   PlanOptions opt;
   uint64_t opt_epoch = 1;
   bool plan_cache = true;
+  bool plan_patch = true;  // TKV_OPT_PLAN_PATCH
   int32_t waves = 0;
   int32_t cus = 256;  // compute units of the device (set at create when pools are given)
   int32_t concurrent = 0;  // TKV_OPT_CONCURRENT
   PlanSlot slots[kPlanSlots];
+  PlanScratch scratch;
   uint64_t stamp = 0;
   // pinned staging for plan uploads
   void* pinned = nullptr;
@@ -109,13 +114,38 @@ namespace {
 
 int find_plan(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq, PlanSlot** out) {
   const bool verify = nq != nullptr;
-  const uint64_t ep = c->tree.epoch();
+  const uint64_t ep = c->tree.epoch(), shape = c->tree.shape_epoch();
   if (c->plan_cache) {
     for (auto& s : c->slots) {
-      if (!s.valid || s.epoch != ep || s.opt_epoch != c->opt_epoch || s.verify != verify) continue;
+      if (!s.valid || s.opt_epoch != c->opt_epoch || s.verify != verify) continue;
+      // a plan made before appends that all fitted in their tip nodes' last
+      // blocks is brought up to date in place instead of rebuilt
+      const bool patch = s.epoch != ep && c->plan_patch && s.shape_epoch == shape;
+      if (s.epoch != ep && !patch) continue;
       if (s.seqs.size() != static_cast<size_t>(nseq)) continue;
       if (std::memcmp(s.seqs.data(), seqs, nseq * sizeof(tkv_seq))) continue;
       if (verify && std::memcmp(s.nq.data(), nq, nseq * sizeof(int32_t))) continue;
+      if (patch) {
+        bool listed = false;
+        if (s.uploaded && s.pending.empty()) {
+          // the device copy is the plan as it stands: list the words that change
+          try {
+            patch_plan(c->tree, &s.plan, &s.pending);
+            listed = true;
+          } catch (const std::bad_alloc&) {
+            s.pending.clear();
+          }
+        }
+        if (!listed) {
+          // (patched again before an upload, or no memory for the list):
+          // upload the whole plan
+          patch_plan(c->tree, &s.plan, nullptr);
+          s.pending.clear();
+          s.uploaded = false;
+        }
+        s.epoch = ep;
+        ++c->tree.counters.plans_patched;
+      }
       s.stamp = ++c->stamp;
       *out = &s;
       return TKV_OK;
@@ -129,20 +159,23 @@ int find_plan(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq
     if (stale && !vstale) victim = &s;
     else if (stale == vstale && s.stamp < victim->stamp) victim = &s;
   }
-  Plan p;
+  // rebuilt in place: the slot's lists and the planner's scratch keep their
+  // memory, so a rebuild of a familiar size allocates nothing
+  victim->valid = false;
   const int32_t gsize = c->cfg.num_q_heads / c->cfg.num_kv_heads;
-  if (int rc = build_plan(c->tree, seqs, nq, nseq, gsize, c->cfg.num_kv_heads, c->opt, &p)) return rc;
+  if (int rc = build_plan(c->tree, seqs, nq, nseq, gsize, c->cfg.num_kv_heads, c->opt, &victim->plan, &c->scratch))
+    return rc;
   try {
     victim->seqs.assign(seqs, seqs + nseq);
     if (verify) victim->nq.assign(nq, nq + nseq);
     else victim->nq.clear();
   } catch (const std::bad_alloc&) {
-    victim->valid = false;
     return TKV_E_NOMEM;
   }
-  victim->plan = std::move(p);
   victim->verify = verify;
   victim->epoch = ep;
+  victim->shape_epoch = shape;
+  victim->pending.clear();
   victim->opt_epoch = c->opt_epoch;
   victim->valid = true;
   victim->uploaded = false;
@@ -152,24 +185,8 @@ int find_plan(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq
   return TKV_OK;
 }
 
-int upload_plan(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
-  if (s->uploaded) return TKV_OK;
-  const size_t bytes = std::max<size_t>(s->plan.bytes, 256);
-  if (s->dev_cap < bytes) {
-    if (s->dev) {
-      // the old buffer may still be read by queued kernels
-      if (hipStreamSynchronize(stream) != hipSuccess) return TKV_E_DEVICE;
-      (void)hipFree(s->dev);
-      s->dev = nullptr;
-      s->dev_cap = 0;
-    }
-    const size_t cap = align256(bytes + bytes / 4);
-    if (hipMalloc(&s->dev, cap) != hipSuccess) {
-      s->dev = nullptr;
-      return TKV_E_NOMEM;
-    }
-    s->dev_cap = cap;
-  }
+// Pinned staging of at least `bytes`, once the copy that last read it is done.
+int stage(tkv_cache* c, size_t bytes) {
   if (c->pinned_busy) {
     if (hipEventSynchronize(c->pinned_ev) != hipSuccess) return TKV_E_DEVICE;
     c->pinned_busy = false;
@@ -187,6 +204,69 @@ int upload_plan(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
   }
   if (!c->pinned_ev && hipEventCreateWithFlags(&c->pinned_ev, hipEventDisableTiming) != hipSuccess)
     return TKV_E_DEVICE;
+  return TKV_OK;
+}
+
+// The changed words of a patched plan: copied behind the plan in its device
+// buffer, then written into it by a small kernel, in stream order after the
+// kernels that read the plan before.
+int upload_patch(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
+  const size_t n = s->pending.size();
+  const size_t at = align256(s->plan.bytes);
+  const size_t bytes = n * sizeof(PlanWord);
+  const uint32_t limit = static_cast<uint32_t>(s->plan.bytes / 4);
+  for (const PlanWord& w : s->pending)
+    if (w.word >= limit) return TKV_E_INVAL;
+  char* dev = static_cast<char*>(s->dev);
+  if (n <= 4 * static_cast<size_t>(kPatchArgWords)) {
+    // a short list travels in the kernels' arguments: no copy to wait for
+    for (size_t i0 = 0; i0 < n; i0 += kPatchArgWords) {
+      PatchArgs a;
+      a.plan = reinterpret_cast<int32_t*>(dev);
+      a.n = static_cast<int32_t>(std::min<size_t>(kPatchArgWords, n - i0));
+      a.limit = limit;
+      std::memcpy(a.w, s->pending.data() + i0, a.n * sizeof(PlanWord));
+      if (launch_plan_patch_args(a, stream) != hipSuccess) return TKV_E_DEVICE;
+    }
+    s->pending.clear();
+    return TKV_OK;
+  }
+  if (int rc = stage(c, bytes)) return rc;
+  std::memcpy(c->pinned, s->pending.data(), bytes);
+  if (hipMemcpyAsync(dev + at, c->pinned, bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return TKV_E_DEVICE;
+  if (hipEventRecord(c->pinned_ev, stream) != hipSuccess) return TKV_E_DEVICE;
+  c->pinned_busy = true;
+  if (launch_plan_patch(reinterpret_cast<int32_t*>(dev), reinterpret_cast<const PlanWord*>(dev + at),
+                        static_cast<int32_t>(n), limit, stream) != hipSuccess)
+    return TKV_E_DEVICE;
+  s->pending.clear();
+  return TKV_OK;
+}
+
+int upload_plan(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
+  if (s->uploaded && s->pending.empty()) return TKV_OK;
+  // room behind the plan for the longest list of changed words a patch can make
+  const size_t words = s->plan.tail_entry.size() + s->plan.gq.size() + s->plan.items.size();
+  const size_t bytes = align256(std::max<size_t>(s->plan.bytes, 256)) + align256(words * sizeof(PlanWord));
+  if (s->uploaded && s->dev_cap >= bytes) return upload_patch(c, s, stream);
+  s->pending.clear();
+  s->uploaded = false;
+  if (s->dev_cap < bytes) {
+    if (s->dev) {
+      // the old buffer may still be read by queued kernels
+      if (hipStreamSynchronize(stream) != hipSuccess) return TKV_E_DEVICE;
+      (void)hipFree(s->dev);
+      s->dev = nullptr;
+      s->dev_cap = 0;
+    }
+    const size_t cap = align256(bytes + bytes / 4);
+    if (hipMalloc(&s->dev, cap) != hipSuccess) {
+      s->dev = nullptr;
+      return TKV_E_NOMEM;
+    }
+    s->dev_cap = cap;
+  }
+  if (int rc = stage(c, std::max<size_t>(s->plan.bytes, 256))) return rc;
   s->plan.serialise(c->pinned);
   if (hipMemcpyAsync(s->dev, c->pinned, s->plan.bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
     return TKV_E_DEVICE;
@@ -405,17 +485,67 @@ int tkv_truncate(tkv_cache* c, tkv_seq s, int64_t new_len) {
 }
 
 int tkv_append(tkv_cache* c, tkv_seq s, int32_t ntok, const void* k, const void* v, void* stream_) {
-  if (!c) return TKV_E_INVAL;
+  return tkv_append_batch(c, &s, &ntok, 1, k, v, stream_);
+}
+
+int tkv_append_batch(tkv_cache* c, const tkv_seq* seqs, const int32_t* ntok, int32_t nseq, const void* k,
+                     const void* v, void* stream_) {
+  if (!c || !seqs || !ntok || nseq < 1) return TKV_E_INVAL;
   if ((k == nullptr) != (v == nullptr)) return TKV_E_INVAL;
   if (k && !c->has_pools) return TKV_E_NODEVICE;
   if (k && ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)) return TKV_E_INVAL;
-  Placement pl;
-  if (int rc = c->tree.append(s, ntok, &pl)) return rc;
+  std::vector<Placement> pls;
+  std::vector<uint8_t> made;
+  std::vector<AppendEntry> ents;
+  try {
+    // everything that could refuse the batch is checked before any change:
+    // handles, counts, repeats (two appends to one handle would write one
+    // block from two workgroups), the source size and the free blocks
+    int64_t need = 0, total = 0;
+    for (int32_t i = 0; i < nseq; ++i) {
+      int64_t b = 0;
+      if (int rc = c->tree.append_need(seqs[i], ntok[i], &b)) return rc;
+      need += b;
+      total += ntok[i];
+    }
+    if (total > INT32_MAX) return TKV_E_RANGE;
+    if (nseq > 1) {
+      std::vector<tkv_seq> sorted(seqs, seqs + nseq);
+      std::sort(sorted.begin(), sorted.end());
+      if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return TKV_E_INVAL;
+    }
+    if (need > c->tree.num_free()) return TKV_E_NOMEM;
+    pls.resize(nseq);
+    made.resize(nseq);
+    ents.reserve(static_cast<size_t>(need + nseq));
+  } catch (const std::bad_alloc&) {
+    return TKV_E_NOMEM;
+  }
+  auto undo = [&](int32_t upto) {
+    for (int32_t i = upto - 1; i >= 0; --i) c->tree.undo_append(seqs[i], ntok[i], pls[i], made[i] != 0);
+  };
+  int32_t src = 0;
+  for (int32_t i = 0; i < nseq; ++i) {
+    if (int rc = c->tree.append(seqs[i], ntok[i], &pls[i])) {
+      undo(i);
+      return rc;
+    }
+    made[i] = c->tree.last_append_made_node() ? 1 : 0;
+    // the blocks it writes: the first from its first free slot, the rest whole
+    const Placement& pl = pls[i];
+    int32_t done = 0;
+    for (size_t j = 0; j < pl.blocks.size(); ++j) {
+      const int32_t slot = j == 0 ? pl.first_slot : 0;
+      const int32_t cnt = std::min(16 - slot, ntok[i] - done);
+      ents.push_back({pl.blocks[j], slot, src + done, cnt});
+      done += cnt;
+    }
+    src += ntok[i];
+  }
   if (!k) return TKV_OK;
-  const bool made = c->tree.last_append_made_node();
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   DeviceGuard dg(c->device);
-  const int32_t nent = static_cast<int32_t>(pl.blocks.size());
+  const int32_t nent = static_cast<int32_t>(ents.size());
   for (int32_t e0 = 0; e0 < nent; e0 += kAppendMaxBlocks) {
     AppendArgs a{};
     a.src_k = k;
@@ -423,14 +553,12 @@ int tkv_append(tkv_cache* c, tkv_seq s, int32_t ntok, const void* k, const void*
     a.kpool = c->cfg.k_pool;
     a.vpool = c->cfg.v_pool;
     a.layer_stride = static_cast<int64_t>(c->layer_elems());
-    a.ntok = ntok;
+    a.ntok = src;
     a.hkv = c->cfg.num_kv_heads;
     a.nent = std::min(kAppendMaxBlocks, nent - e0);
-    a.s0 = e0 == 0 ? pl.first_slot : 0;
-    a.tok0 = e0 == 0 ? 0 : (16 - pl.first_slot) + (e0 - 1) * 16;
-    for (int32_t i = 0; i < a.nent; ++i) a.blk[i] = pl.blocks[e0 + i];
+    for (int32_t i = 0; i < a.nent; ++i) a.ent[i] = ents[e0 + i];
     if (launch_append(c->cfg.dtype, c->cfg.head_dim, c->cfg.num_layers, a, stream) != hipSuccess) {
-      c->tree.undo_append(s, ntok, pl, made);
+      undo(nseq);
       return TKV_E_DEVICE;
     }
   }
@@ -560,6 +688,10 @@ int tkv_set_option(tkv_cache* c, int32_t key, int64_t value) {
       if (value != 0 && value != 1) return TKV_E_RANGE;
       c->concurrent = static_cast<int32_t>(value);
       break;
+    case TKV_OPT_PLAN_PATCH:
+      if (value != 0 && value != 1) return TKV_E_RANGE;
+      c->plan_patch = value != 0;
+      break;
     default:
       return TKV_E_INVAL;
   }
@@ -577,6 +709,7 @@ int tkv_get_option(const tkv_cache* c, int32_t key, int64_t* value) {
     case TKV_OPT_WAVES: *value = c->waves; break;
     case TKV_OPT_CASCADE: *value = c->opt.cascade; break;
     case TKV_OPT_CONCURRENT: *value = c->concurrent; break;
+    case TKV_OPT_PLAN_PATCH: *value = c->plan_patch ? 1 : 0; break;
     default: return TKV_E_INVAL;
   }
   return TKV_OK;

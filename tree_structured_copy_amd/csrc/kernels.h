@@ -26,6 +26,14 @@ hipError_t launch_attn_merge(int head_dim, const MergeArgs& args, hipStream_t st
 hipError_t launch_append(int dtype, int head_dim, int32_t layers, const AppendArgs& args,
                          hipStream_t stream);
 
+// Write words[i].value at 32-bit word words[i].word of plan, for i < n, skipping
+// words >= limit; grid = ceil(n / 256) workgroups of 256.
+hipError_t launch_plan_patch(int32_t* plan, const PlanWord* words, int32_t n, uint32_t limit, hipStream_t stream);
+
+// The same for args.n <= kPatchArgWords words held in the arguments; one
+// workgroup of 512.
+hipError_t launch_plan_patch_args(const PatchArgs& args, hipStream_t stream);
+
 // Copy a path's tiles back out in token order; grid = nent x Hkv.
 hipError_t launch_gather(int dtype, int head_dim, const GatherArgs& args, hipStream_t stream);
 

@@ -1,4 +1,4 @@
-// Append-scatter and gather kernels for the pool tiles.
+// Append-scatter and gather kernels for the pool tiles, and the in-place plan update.
 //
 // tkv_append writes each new token's K and V once into its block slot (DSpark
 // blog, third layer: each token's KV is computed once and reused).  One
@@ -38,11 +38,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
   const int e = blockIdx.x, kvh = blockIdx.y, layer = blockIdx.z;
   const int tid = threadIdx.x;
-  const int slot_lo = (e == 0) ? a.s0 : 0;
-  const int src0 = (e == 0) ? a.tok0 : a.tok0 + (16 - a.s0) + (e - 1) * 16;
-  const int cnt = min(16 - slot_lo, a.ntok - src0);
+  const AppendEntry ent = a.ent[e];
+  const int slot_lo = ent.slot, src0 = ent.src, cnt = ent.cnt;
   const bool fresh = slot_lo == 0;
-  if (cnt <= 0) return;
+  if (cnt <= 0 || slot_lo + cnt > 16) return;
 
   const E* srck = static_cast<const E*>(a.src_k);
   const E* srcv = static_cast<const E*>(a.src_v);
@@ -56,7 +55,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   __syncthreads();
 
   const size_t base = static_cast<size_t>(layer) * a.layer_stride +
-                      (static_cast<size_t>(a.blk[e]) * a.hkv + kvh) * (16 * D);
+                      (static_cast<size_t>(ent.blk) * a.hkv + kvh) * (16 * D);
   uint4* kt = reinterpret_cast<uint4*>(static_cast<E*>(a.kpool) + base);
   uint4* vt = reinterpret_cast<uint4*>(static_cast<E*>(a.vpool) + base);
   const int hi = slot_lo + cnt;
@@ -139,7 +138,39 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   }
 }
 
+// Writes a list of changed 32-bit words into a device plan (the in-place
+// update after appends that fitted in their tip blocks): one word per thread,
+// words at or past `limit` skipped.
+__global__ __launch_bounds__(256) void plan_patch_kernel(int32_t* __restrict__ plan,
+                                                         const PlanWord* __restrict__ words, int32_t n,
+                                                         uint32_t limit) {
+  const int32_t i = static_cast<int32_t>(blockIdx.x) * 256 + static_cast<int32_t>(threadIdx.x);
+  if (i >= n) return;
+  const PlanWord w = words[i];
+  if (w.word < limit) plan[w.word] = w.value;
+}
+
+// The same with the words in the kernel arguments.
+__global__ __launch_bounds__(512) void plan_patch_args_kernel(PatchArgs a) {
+  const int32_t i = static_cast<int32_t>(threadIdx.x);
+  if (i >= a.n) return;
+  const PlanWord w = a.w[i];
+  if (w.word < a.limit) a.plan[w.word] = w.value;
+}
+
 }  // namespace
+
+hipError_t launch_plan_patch_args(const PatchArgs& args, hipStream_t stream) {
+  if (args.n <= 0 || args.n > kPatchArgWords) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(plan_patch_args_kernel, dim3(1), dim3(512), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_patch(int32_t* plan, const PlanWord* words, int32_t n, uint32_t limit, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(plan_patch_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, plan, words, n, limit);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(int dtype, int head_dim, int32_t layers, const AppendArgs& args,
                          hipStream_t stream) {

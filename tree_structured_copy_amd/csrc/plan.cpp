@@ -1,28 +1,13 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <cstddef>
 #include <cstring>
 #include <new>
 
 namespace tkv {
 
 namespace {
-
-struct LNode {
-  int32_t node = -1;    // tree node id
-  int32_t parent = -1;  // local index
-  int32_t pre = 0;      // DFS preorder index
-  int32_t root = 0;     // index of its tree's root in the root list
-  int64_t qcount = 0;   // queries in the subtree
-  std::vector<int32_t> children;
-  std::vector<int32_t> handles;  // batch indices whose tip is this node
-};
-
-struct Query {
-  int32_t handle;  // batch index
-  int32_t global;  // global query index (row of q / out)
-  int32_t pos;     // absolute position
-};
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -49,130 +34,201 @@ void Plan::serialise(void* dst) const {
   std::memcpy(p + off_merge, merge.data(), merge.size() * sizeof(DevMerge));
 }
 
+void Plan::reset() {
+  items.clear();
+  groups.clear();
+  gq.clear();
+  gqpos.clear();
+  blocks.clear();
+  parts.clear();
+  merge.clear();
+  for (int c = 0; c <= kKernelClasses; ++c) bucket_begin[c] = 0;
+  for (int c = 0; c < kKernelClasses; ++c) {
+    bucket_max_blocks[c] = 0;
+    bucket_blocks[c] = 0;
+  }
+  nqueries = 0;
+  partial_slots = 0;
+  any_merge = false;
+  causal = false;
+  unique_blocks = 0;
+  unique_tokens = 0;
+  tail_entry.clear();
+  tail_node.clear();
+  gq_node.clear();
+  gq_back.clear();
+  open_nodes.clear();
+  closed_tokens = 0;
+  off_items = off_gq = off_gqpos = off_blocks = off_parts = off_merge = bytes = 0;
+}
+
+namespace {
+
+// Clears the tree-node -> local-node map on every way out of build_plan, so
+// the scratch map is all -1 again for the next call.
+struct LocReset {
+  PlanScratch& s;
+  ~LocReset() {
+    for (int32_t id : s.lnode) s.loc[id] = -1;
+    s.lnode.clear();
+  }
+};
+
+}  // namespace
+
 int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
-               int32_t q_per_kv, int32_t num_kv_heads, const PlanOptions& opt, Plan* out) {
+               int32_t q_per_kv, int32_t num_kv_heads, const PlanOptions& opt, Plan* out,
+               PlanScratch* scratch) {
   if (!seqs || nseq < 1 || !out || q_per_kv < 1 || q_per_kv > kMaxRows) return TKV_E_INVAL;
+  PlanScratch local;
+  PlanScratch& S = scratch ? *scratch : local;
   try {
     // 1. handles and queries
-    std::vector<int32_t> tip(nseq), qn(nseq), qbase(nseq);
-    std::vector<int64_t> len(nseq);
+    S.tip.resize(nseq);
+    S.qn.resize(nseq);
+    S.qbase.resize(nseq);
+    S.len.resize(nseq);
     int64_t total_q = 0;
     for (int32_t i = 0; i < nseq; ++i) {
-      if (int rc = tree.resolve(seqs[i], &tip[i])) return rc;
-      const Node& t = tree.node(tip[i]);
-      len[i] = t.base + t.ntok;
-      qn[i] = nq ? nq[i] : 1;
-      if (len[i] == 0) return TKV_E_EMPTY;
-      if (qn[i] < 1 || qn[i] > len[i] || len[i] > INT32_MAX) return TKV_E_RANGE;
-      qbase[i] = static_cast<int32_t>(total_q);
-      total_q += qn[i];
+      if (int rc = tree.resolve(seqs[i], &S.tip[i])) return rc;
+      const Node& t = tree.node(S.tip[i]);
+      S.len[i] = t.base + t.ntok;
+      S.qn[i] = nq ? nq[i] : 1;
+      if (S.len[i] == 0) return TKV_E_EMPTY;
+      if (S.qn[i] < 1 || S.qn[i] > S.len[i] || S.len[i] > INT32_MAX) return TKV_E_RANGE;
+      S.qbase[i] = static_cast<int32_t>(total_q);
+      total_q += S.qn[i];
       if (total_q > INT32_MAX / 4) return TKV_E_RANGE;
     }
 
-    // 2. local tree over the union of the paths
-    std::vector<int32_t> loc(tree.node_capacity(), -1);
-    std::vector<LNode> ln;
+    // 2. local tree over the union of the paths: nodes in order of discovery,
+    //    their handles and children as index ranges (children by node id)
+    if (static_cast<int32_t>(S.loc.size()) < tree.node_capacity()) S.loc.resize(tree.node_capacity(), -1);
+    S.lnode.clear();
+    S.lparent.clear();
+    LocReset reset_loc{S};
+    auto& loc = S.loc;
     for (int32_t i = 0; i < nseq; ++i) {
       int32_t prev = -1;
-      for (int32_t id = tip[i]; id >= 0; id = tree.node(id).parent) {
+      for (int32_t id = S.tip[i]; id >= 0; id = tree.node(id).parent) {
         if (loc[id] >= 0) {
-          if (prev >= 0) ln[prev].parent = loc[id];
+          if (prev >= 0) S.lparent[prev] = loc[id];
           break;
         }
-        loc[id] = static_cast<int32_t>(ln.size());
-        ln.emplace_back();
-        ln.back().node = id;
-        if (prev >= 0) ln[prev].parent = loc[id];
+        loc[id] = static_cast<int32_t>(S.lnode.size());
+        S.lnode.push_back(id);
+        S.lparent.push_back(-1);
+        if (prev >= 0) S.lparent[prev] = loc[id];
         prev = loc[id];
       }
-      ln[loc[tip[i]]].handles.push_back(i);
     }
-    const int32_t nl = static_cast<int32_t>(ln.size());
-    std::vector<int32_t> roots;
+    const int32_t nl = static_cast<int32_t>(S.lnode.size());
+    S.hbeg.assign(nl + 1, 0);
+    for (int32_t i = 0; i < nseq; ++i) ++S.hbeg[loc[S.tip[i]] + 1];
+    for (int32_t k = 0; k < nl; ++k) S.hbeg[k + 1] += S.hbeg[k];
+    S.cursor.assign(S.hbeg.begin(), S.hbeg.end() - 1);
+    S.hlist.resize(nseq);
+    for (int32_t i = 0; i < nseq; ++i) S.hlist[S.cursor[loc[S.tip[i]]]++] = i;
+    S.roots.clear();
+    S.cbeg.assign(nl + 1, 0);
     for (int32_t k = 0; k < nl; ++k) {
-      if (ln[k].parent >= 0) ln[ln[k].parent].children.push_back(k);
-      else roots.push_back(k);
+      if (S.lparent[k] >= 0) ++S.cbeg[S.lparent[k] + 1];
+      else S.roots.push_back(k);
     }
-    auto by_node = [&](int32_t a, int32_t b) { return ln[a].node < ln[b].node; };
-    std::sort(roots.begin(), roots.end(), by_node);
-    for (auto& n : ln) std::sort(n.children.begin(), n.children.end(), by_node);
+    for (int32_t k = 0; k < nl; ++k) S.cbeg[k + 1] += S.cbeg[k];
+    S.cursor.assign(S.cbeg.begin(), S.cbeg.end() - 1);
+    S.child.resize(S.cbeg[nl]);
+    for (int32_t k = 0; k < nl; ++k)
+      if (S.lparent[k] >= 0) S.child[S.cursor[S.lparent[k]]++] = k;
+    auto by_node = [&](int32_t a, int32_t b) { return S.lnode[a] < S.lnode[b]; };
+    std::sort(S.roots.begin(), S.roots.end(), by_node);
+    for (int32_t k = 0; k < nl; ++k)
+      if (S.cbeg[k + 1] - S.cbeg[k] > 1) std::sort(S.child.begin() + S.cbeg[k], S.child.begin() + S.cbeg[k + 1], by_node);
 
-    // subtree query counts, bottom-up by depth
-    {
-      std::vector<int32_t> order(nl);
-      for (int32_t k = 0; k < nl; ++k) order[k] = k;
-      std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-        return tree.node(ln[a].node).depth > tree.node(ln[b].node).depth;
-      });
-      for (int32_t k : order) {
-        for (int32_t h : ln[k].handles) ln[k].qcount += qn[h];
-        if (ln[k].parent >= 0) ln[ln[k].parent].qcount += ln[k].qcount;
-      }
-    }
-    // DFS preorder
+    // DFS preorder (children in node order), then subtree query counts in
+    // reverse preorder, where every node comes after its descendants
+    S.pre.resize(nl);
+    S.by_pre.resize(nl);
     {
       int32_t pre = 0;
-      std::vector<int32_t> st;
-      for (size_t r = 0; r < roots.size(); ++r) {
-        st.push_back(roots[r]);
+      auto& st = S.st;
+      st.clear();
+      for (int32_t r : S.roots) {
+        st.push_back(r);
         while (!st.empty()) {
           const int32_t k = st.back();
           st.pop_back();
-          ln[k].pre = pre++;
-          ln[k].root = static_cast<int32_t>(r);
-          for (auto it = ln[k].children.rbegin(); it != ln[k].children.rend(); ++it) st.push_back(*it);
+          S.pre[k] = pre;
+          S.by_pre[pre++] = k;
+          for (int32_t c = S.cbeg[k + 1] - 1; c >= S.cbeg[k]; --c) st.push_back(S.child[c]);
         }
       }
+    }
+    S.qcount.assign(nl, 0);
+    for (int32_t p = nl - 1; p >= 0; --p) {
+      const int32_t k = S.by_pre[p];
+      for (int32_t x = S.hbeg[k]; x < S.hbeg[k + 1]; ++x) S.qcount[k] += S.qn[S.hlist[x]];
+      if (S.lparent[k] >= 0) S.qcount[S.lparent[k]] += S.qcount[k];
     }
 
     // 3. groups: subtrees with <= qg queries become units; units of one tree are
-    //    packed in DFS order up to qg queries
+    //    packed in DFS order up to qg queries.  Units are consecutive runs of
+    //    one query array, so a group is a run of it too.
     const int32_t rows = std::max(16, std::min<int32_t>(opt.max_rows, kMaxRows));
     const int32_t qg = std::max(1, std::min(kMaxGroupQueries, rows / q_per_kv));
-    auto queries_of_handle = [&](int32_t h, std::vector<Query>& dst) {
-      for (int32_t k = 0; k < qn[h]; ++k)
-        dst.push_back({h, qbase[h] + k, static_cast<int32_t>(len[h] - qn[h] + k)});
+    auto& uq = S.uq;
+    uq.clear();
+    auto queries_of_handle = [&](int32_t h) {
+      for (int32_t k = 0; k < S.qn[h]; ++k)
+        uq.push_back({h, S.qbase[h] + k, static_cast<int32_t>(S.len[h] - S.qn[h] + k)});
     };
-    std::vector<std::vector<Query>> group_q;
-    std::vector<int32_t> group_root;
+    S.gbeg.clear();
+    S.gsize.clear();
+    S.groot.clear();
     {
-      std::vector<int32_t> st, sub;
-      for (size_t r = 0; r < roots.size(); ++r) {
-        std::vector<std::vector<Query>> units;
-        st.push_back(roots[r]);
+      auto& st = S.st;
+      auto& sub = S.sub;
+      auto& ub = S.ub;
+      for (size_t r = 0; r < S.roots.size(); ++r) {
+        ub.clear();
+        st.push_back(S.roots[r]);
         while (!st.empty()) {
           const int32_t k = st.back();
           st.pop_back();
-          if (ln[k].qcount <= qg) {
-            std::vector<Query> u;
+          if (S.qcount[k] <= qg) {
+            const size_t u0 = uq.size();
             sub.push_back(k);
             while (!sub.empty()) {
               const int32_t s = sub.back();
               sub.pop_back();
-              for (int32_t h : ln[s].handles) queries_of_handle(h, u);
-              for (auto it = ln[s].children.rbegin(); it != ln[s].children.rend(); ++it) sub.push_back(*it);
+              for (int32_t x = S.hbeg[s]; x < S.hbeg[s + 1]; ++x) queries_of_handle(S.hlist[x]);
+              for (int32_t c = S.cbeg[s + 1] - 1; c >= S.cbeg[s]; --c) sub.push_back(S.child[c]);
             }
-            if (!u.empty()) units.push_back(std::move(u));
+            if (uq.size() > u0) ub.push_back(static_cast<int32_t>(u0));
           } else {
-            std::vector<Query> own;
-            for (int32_t h : ln[k].handles) queries_of_handle(h, own);
-            for (size_t a = 0; a < own.size(); a += qg)
-              units.emplace_back(own.begin() + a, own.begin() + std::min(own.size(), a + qg));
-            for (auto it = ln[k].children.rbegin(); it != ln[k].children.rend(); ++it) st.push_back(*it);
+            const size_t o0 = uq.size();
+            for (int32_t x = S.hbeg[k]; x < S.hbeg[k + 1]; ++x) queries_of_handle(S.hlist[x]);
+            for (size_t a = o0; a < uq.size(); a += qg) ub.push_back(static_cast<int32_t>(a));
+            for (int32_t c = S.cbeg[k + 1] - 1; c >= S.cbeg[k]; --c) st.push_back(S.child[c]);
           }
         }
-        std::vector<Query> cur;
-        for (auto& u : units) {
-          if (!cur.empty() && cur.size() + u.size() > (size_t)qg) {
-            group_q.push_back(std::move(cur));
-            group_root.push_back(static_cast<int32_t>(r));
-            cur.clear();
+        // unit u of this tree = uq[ub[u] .. ub[u + 1]), the last one ending at uq.size()
+        int32_t cur_begin = 0, cur_size = 0;
+        for (size_t u = 0; u < ub.size(); ++u) {
+          const int32_t usz = (u + 1 < ub.size() ? ub[u + 1] : static_cast<int32_t>(uq.size())) - ub[u];
+          if (cur_size > 0 && cur_size + usz > qg) {
+            S.gbeg.push_back(cur_begin);
+            S.gsize.push_back(cur_size);
+            S.groot.push_back(static_cast<int32_t>(r));
+            cur_size = 0;
           }
-          cur.insert(cur.end(), u.begin(), u.end());
+          if (cur_size == 0) cur_begin = ub[u];
+          cur_size += usz;
         }
-        if (!cur.empty()) {
-          group_q.push_back(std::move(cur));
-          group_root.push_back(static_cast<int32_t>(r));
+        if (cur_size > 0) {
+          S.gbeg.push_back(cur_begin);
+          S.gsize.push_back(cur_size);
+          S.groot.push_back(static_cast<int32_t>(r));
         }
       }
     }
@@ -185,19 +241,25 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     //    a one-tile group about its memory time.  A query then has partial
     //    records in both groups, merged afterwards.
     Plan& P = *out;
-    P = Plan();
+    P.reset();
     P.nqueries = static_cast<int32_t>(total_q);
     P.causal = nq != nullptr;
-    struct GroupOut {
-      int32_t blk_begin, blk_count, root;
-      bool partials;  // its queries have records in another group too
-    };
-    std::vector<GroupOut> gout;
-    std::vector<std::vector<std::pair<int32_t, int32_t>>> qmem(total_q);  // (group, j)
-    std::vector<uint64_t> mask(nl, 0);
-    std::vector<int32_t> touched;
+    // groups made, in order: block range, tree, whether its queries have records elsewhere too
+    S.go_begin.clear();
+    S.go_count.clear();
+    S.go_root.clear();
+    S.go_partials.clear();
+    // the (group, index in group) of each query's at most two groups: its own
+    // and possibly one cascade subgroup of it
+    S.qm_n.assign(total_q, 0);
+    S.qm_g.resize(2 * total_q);
+    S.qm_j.resize(2 * total_q);
+    S.mask.assign(nl, 0);
+    S.emitted.assign(nl, 0);
+    auto& mask = S.mask;
+    auto& touched = S.touched;
     const int32_t sub = std::max(1, 16 / q_per_kv);  // queries of a one-tile subgroup
-    auto emit_group = [&](const Query* qs, int32_t n, int32_t root, bool partials) {
+    auto emit_group = [&](const PlanQuery* qs, int32_t n, int32_t root, bool partials) {
       const int32_t gi = static_cast<int32_t>(P.groups.size());
       DevGroup g;
       g.q_begin = static_cast<int32_t>(P.gq.size());
@@ -205,17 +267,25 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       g.min_pos = INT32_MAX;
       g.pad1 = 0;
       for (int32_t j = 0; j < n; ++j) {
-        P.gq.push_back(qs[j].global);
+        const int32_t q = qs[j].global;
+        P.gq.push_back(q);
         P.gqpos.push_back(qs[j].pos);
+        P.gq_node.push_back(S.tip[qs[j].handle]);
+        P.gq_back.push_back(static_cast<int32_t>(S.len[qs[j].handle] - qs[j].pos));
         g.min_pos = std::min(g.min_pos, qs[j].pos);
-        qmem[qs[j].global].push_back({gi, j});
+        const int32_t at = 2 * q + S.qm_n[q]++;
+        S.qm_g[at] = gi;
+        S.qm_j[at] = j;
       }
       P.groups.push_back(g);
-      gout.push_back({static_cast<int32_t>(P.blocks.size()), 0, root, partials});
-      return gi;
+      S.go_begin.push_back(static_cast<int32_t>(P.blocks.size()));
+      S.go_count.push_back(0);
+      S.go_root.push_back(root);
+      S.go_partials.push_back(partials ? 1 : 0);
     };
+    // a node's blocks, once per group that reads it; the statistics count each node once
     auto emit_node = [&](int32_t k, uint64_t m) {
-      const Node& nd = tree.node(ln[k].node);
+      const Node& nd = tree.node(S.lnode[k]);
       const int32_t nb = static_cast<int32_t>(nd.blocks.size());
       for (int32_t b = 0; b < nb; ++b) {
         DevBlock e;
@@ -226,34 +296,45 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
         e.mask = m;
         P.blocks.push_back(e);
       }
+      if (!nd.frozen && nb > 0) {
+        P.tail_entry.push_back(static_cast<int32_t>(P.blocks.size()) - 1);
+        P.tail_node.push_back(S.lnode[k]);
+      }
+      if (!S.emitted[k]) {
+        S.emitted[k] = 1;
+        P.unique_blocks += nb;
+        P.unique_tokens += nd.ntok;
+        if (nd.frozen) P.closed_tokens += nd.ntok;
+        else P.open_nodes.push_back(S.lnode[k]);
+      }
     };
-    auto close_group = [&]() { gout.back().blk_count = static_cast<int32_t>(P.blocks.size()) - gout.back().blk_begin; };
+    auto close_group = [&]() { S.go_count.back() = static_cast<int32_t>(P.blocks.size()) - S.go_begin.back(); };
     // the subgroup a node's queries fit in, or -1
     auto narrow = [&](uint64_t m) {
       const int32_t lo = __builtin_ctzll(m), hi = 63 - __builtin_clzll(m);
       return lo / sub == hi / sub ? lo / sub : -1;
     };
-    for (size_t g0 = 0; g0 < group_q.size(); ++g0) {
-      const auto& qs = group_q[g0];
-      const int32_t n = static_cast<int32_t>(qs.size());
+    for (size_t g0 = 0; g0 < S.gbeg.size(); ++g0) {
+      const PlanQuery* qs = uq.data() + S.gbeg[g0];
+      const int32_t n = S.gsize[g0];
       touched.clear();
       for (int32_t j = 0; j < n; ++j)
-        for (int32_t k = loc[tip[qs[j].handle]]; k >= 0; k = ln[k].parent) {
+        for (int32_t k = loc[S.tip[qs[j].handle]]; k >= 0; k = S.lparent[k]) {
           if (!mask[k]) touched.push_back(k);
           mask[k] |= 1ull << j;
         }
-      std::sort(touched.begin(), touched.end(), [&](int32_t a, int32_t b) { return ln[a].pre < ln[b].pre; });
+      std::sort(touched.begin(), touched.end(), [&](int32_t a, int32_t b) { return S.pre[a] < S.pre[b]; });
       bool cascade = false;
       if (opt.cascade && (n * q_per_kv + 15) / 16 >= 8 && n > sub) {
         int64_t all = 0, thin = 0;
         for (int32_t k : touched) {
-          const int64_t nb = static_cast<int64_t>(tree.node(ln[k].node).blocks.size());
+          const int64_t nb = static_cast<int64_t>(tree.node(S.lnode[k]).blocks.size());
           all += nb;
           if (narrow(mask[k]) >= 0) thin += nb;
         }
         cascade = thin * 8 >= all && thin > 0;
       }
-      emit_group(qs.data(), n, group_root[g0], cascade);
+      emit_group(qs, n, S.groot[g0], cascade);
       for (int32_t k : touched)
         if (!cascade || narrow(mask[k]) < 0) emit_node(k, mask[k]);
       close_group();
@@ -262,7 +343,7 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
           bool any = false;
           for (int32_t k : touched) any |= narrow(mask[k]) == t;
           if (!any) continue;
-          emit_group(qs.data() + t * sub, std::min(sub, n - t * sub), group_root[g0], true);
+          emit_group(qs + t * sub, std::min(sub, n - t * sub), S.groot[g0], true);
           for (int32_t k : touched)
             if (narrow(mask[k]) == t) emit_node(k, mask[k] >> (t * sub));
           close_group();
@@ -285,12 +366,13 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     //    An LDS-staged class whose work (blocks x row tiles) is smaller than
     //    that of the largest LDS-staged class present runs in that class's
     //    kernel instead (its extra waves idle): one launch and one ramp fewer.
-    std::vector<int8_t> gclass(ngroups);
+    auto& gclass = S.gclass;
+    gclass.resize(ngroups);
     int64_t class_work[kKernelClasses] = {0, 0, 0, 0, 0, 0};
     for (int32_t gi = 0; gi < ngroups; ++gi) {
       const int32_t tiles = (P.groups[gi].nq * q_per_kv + 15) / 16;
       gclass[gi] = static_cast<int8_t>(kernel_class(tiles));
-      class_work[gclass[gi]] += static_cast<int64_t>(gout[gi].blk_count) * tiles;
+      class_work[gclass[gi]] += static_cast<int64_t>(S.go_count[gi]) * tiles;
     }
     int top = -1;
     for (int c = 2; c < kKernelClasses; ++c)
@@ -300,11 +382,11 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
         if (gclass[gi] >= 2 && gclass[gi] < top && class_work[gclass[gi]] < class_work[top]) gclass[gi] = top;
     int64_t class_blocks[kKernelClasses] = {0, 0, 0, 0, 0, 0};
     auto class_of = [&](int32_t gi) { return static_cast<int>(gclass[gi]); };
-    for (int32_t gi = 0; gi < ngroups; ++gi) class_blocks[class_of(gi)] += gout[gi].blk_count;
+    for (int32_t gi = 0; gi < ngroups; ++gi) class_blocks[class_of(gi)] += S.go_count[gi];
     const int64_t class_items = std::max<int64_t>(1, std::max<int32_t>(1, opt.target_wgs) / num_kv_heads);
     auto chunks_of = [&](int32_t gi) -> int32_t {
       const int cls = class_of(gi);
-      const int64_t nb = gout[gi].blk_count;
+      const int64_t nb = S.go_count[gi];
       const int64_t floor = std::max<int32_t>(1, cls < 2 ? opt.min_chunk : opt.min_chunk / 4);
       // the 4- and 8-tile LDS-staged shapes fit two workgroups per CU, and
       // two per CU stream faster than one with a deeper ring: twice the items
@@ -314,29 +396,26 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       nc = std::max<int64_t>(nc, (nb + kRowsMaxItemBlocks - 1) / kRowsMaxItemBlocks);
       return static_cast<int32_t>(std::max<int64_t>(nc, 1));
     };
-    struct Tmp {
-      DevItem it;
-      int32_t tiles, root, chunk;
-    };
-    std::vector<Tmp> tmp;
+    auto& tmp = S.tmp;
+    tmp.clear();
     int64_t slots = 0;
     for (int32_t gi = 0; gi < ngroups; ++gi) {
-      const int32_t nb = gout[gi].blk_count;
+      const int32_t nb = S.go_count[gi];
       if (nb == 0) continue;
       const int32_t nc = chunks_of(gi);
       const int32_t tiles = class_of(gi);
       int32_t at = 0;
       for (int32_t c = 0; c < nc; ++c) {
         const int32_t cnt = nb / nc + (c < nb % nc ? 1 : 0);
-        Tmp t;
+        PlanItemTmp t;
         t.it.group = gi;
-        t.it.blk_begin = gout[gi].blk_begin + at;
+        t.it.blk_begin = S.go_begin[gi] + at;
         t.it.blk_count = cnt;
         t.it.q_begin = P.groups[gi].q_begin;
         t.it.nq = P.groups[gi].nq;
         t.it.min_pos = P.groups[gi].min_pos;
         t.it.pad = 0;
-        if (nc == 1 && !gout[gi].partials) {
+        if (nc == 1 && !S.go_partials[gi]) {
           t.it.part_base = -1;
         } else {
           t.it.part_base = static_cast<int32_t>(slots);
@@ -344,7 +423,7 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
           if (slots > INT32_MAX) return TKV_E_RANGE;
         }
         t.tiles = tiles;
-        t.root = gout[gi].root;
+        t.root = S.go_root[gi];
         t.chunk = c;
         tmp.push_back(t);
         at += cnt;
@@ -355,27 +434,30 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     // more workgroups than the GPU holds at once the ones that start late are
     // short; then items that read the same blocks next to each other (same
     // tree, same chunk index), so the KV heads' workgroups of neighbouring
-    // items share L2
-    std::stable_sort(tmp.begin(), tmp.end(), [](const Tmp& a, const Tmp& b) {
+    // items share L2.  (group, chunk) is unique, so the order is total.
+    std::sort(tmp.begin(), tmp.end(), [](const PlanItemTmp& a, const PlanItemTmp& b) {
       if (a.tiles != b.tiles) return a.tiles < b.tiles;
       if (a.it.blk_count != b.it.blk_count) return a.it.blk_count > b.it.blk_count;
       if (a.root != b.root) return a.root < b.root;
       if (a.chunk != b.chunk) return a.chunk < b.chunk;
       return a.it.group < b.it.group;
     });
-    P.items.resize(tmp.size());
-    for (int t = 0; t <= kKernelClasses; ++t) P.bucket_begin[t] = 0;
-    std::vector<std::vector<int32_t>> gitems(ngroups);
-    for (size_t k = 0; k < tmp.size(); ++k) {
+    const int32_t nitems = static_cast<int32_t>(tmp.size());
+    P.items.resize(nitems);
+    // the items of each group, in item order
+    S.ibeg.assign(ngroups + 1, 0);
+    for (int32_t k = 0; k < nitems; ++k) {
       P.items[k] = tmp[k].it;
-      gitems[tmp[k].it.group].push_back(static_cast<int32_t>(k));
+      ++S.ibeg[tmp[k].it.group + 1];
     }
+    for (int32_t g = 0; g < ngroups; ++g) S.ibeg[g + 1] += S.ibeg[g];
+    S.cursor.assign(S.ibeg.begin(), S.ibeg.end() - 1);
+    S.ilist.resize(nitems);
+    for (int32_t k = 0; k < nitems; ++k) S.ilist[S.cursor[tmp[k].it.group]++] = k;
     for (int c = 0; c < kKernelClasses; ++c) {
       int32_t cnt = 0;
       for (const auto& x : tmp) cnt += (x.tiles <= c);
       P.bucket_begin[c + 1] = cnt;
-      P.bucket_max_blocks[c] = 0;
-      P.bucket_blocks[c] = 0;
     }
     for (const auto& x : tmp) {
       P.bucket_max_blocks[x.tiles] = std::max(P.bucket_max_blocks[x.tiles], x.it.blk_count);
@@ -387,37 +469,64 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       DevMerge m;
       m.p_begin = static_cast<int32_t>(P.parts.size());
       int32_t direct = 0;
-      for (const auto& gj : qmem[q])
-        for (int32_t item : gitems[gj.first]) {
+      for (int32_t x = 0; x < S.qm_n[q]; ++x) {
+        const int32_t g = S.qm_g[2 * q + x], j = S.qm_j[2 * q + x];
+        for (int32_t y = S.ibeg[g]; y < S.ibeg[g + 1]; ++y) {
+          const int32_t item = S.ilist[y];
           if (P.items[item].part_base < 0) {
             ++direct;
             continue;
           }
-          P.parts.push_back({P.items[item].part_base + gj.second * q_per_kv * num_kv_heads, item});
+          P.parts.push_back({P.items[item].part_base + j * q_per_kv * num_kv_heads, item});
         }
+      }
       m.p_count = static_cast<int32_t>(P.parts.size()) - m.p_begin;
       if (direct + m.p_count == 0 || (direct > 0 && (direct > 1 || m.p_count > 0))) return TKV_E_INVAL;
       P.merge[q] = m;
       if (m.p_count) P.any_merge = true;
-    }
-
-    // statistics: distinct blocks read and their valid slots
-    {
-      std::vector<std::pair<int32_t, int32_t>> ids;
-      ids.reserve(P.blocks.size());
-      for (const auto& b : P.blocks) ids.push_back({b.id, b.valid});
-      std::sort(ids.begin(), ids.end());
-      ids.erase(std::unique(ids.begin(), ids.end(),
-                            [](const auto& a, const auto& b) { return a.first == b.first; }),
-                ids.end());
-      P.unique_blocks = static_cast<int32_t>(ids.size());
-      for (const auto& x : ids) P.unique_tokens += x.second;
     }
     P.layout();
   } catch (const std::bad_alloc&) {
     return TKV_E_NOMEM;
   }
   return TKV_OK;
+}
+
+void patch_plan(const Tree& tree, Plan* plan, std::vector<PlanWord>* changed) {
+  Plan& P = *plan;
+  auto put = [&](size_t byte_offset, int32_t value) {
+    if (changed) changed->push_back({static_cast<uint32_t>(byte_offset / 4), value});
+  };
+  for (size_t t = 0; t < P.tail_entry.size(); ++t) {
+    const int32_t e = P.tail_entry[t];
+    const int32_t v = tree.node(P.tail_node[t]).tail_valid();
+    if (P.blocks[e].valid != v) {
+      P.blocks[e].valid = v;
+      put(P.off_blocks + e * sizeof(DevBlock) + offsetof(DevBlock, valid), v);
+    }
+  }
+  for (size_t j = 0; j < P.gq.size(); ++j) {
+    const Node& nd = tree.node(P.gq_node[j]);
+    const int32_t pos = static_cast<int32_t>(nd.base + nd.ntok - P.gq_back[j]);
+    if (P.gqpos[j] != pos) {
+      P.gqpos[j] = pos;
+      put(P.off_gqpos + j * sizeof(int32_t), pos);
+    }
+  }
+  for (auto& g : P.groups) {
+    g.min_pos = INT32_MAX;
+    for (int32_t j = g.q_begin; j < g.q_begin + g.nq; ++j) g.min_pos = std::min(g.min_pos, P.gqpos[j]);
+  }
+  for (size_t i = 0; i < P.items.size(); ++i) {
+    DevItem& it = P.items[i];
+    const int32_t m = P.groups[it.group].min_pos;
+    if (it.min_pos != m) {
+      it.min_pos = m;
+      put(P.off_items + i * sizeof(DevItem) + offsetof(DevItem, min_pos), m);
+    }
+  }
+  P.unique_tokens = P.closed_tokens;
+  for (int32_t id : P.open_nodes) P.unique_tokens += tree.node(id).ntok;
 }
 
 }  // namespace tkv

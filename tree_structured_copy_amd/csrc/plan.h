@@ -51,12 +51,58 @@ struct Plan {
   // statistics
   int32_t unique_blocks = 0;
   int64_t unique_tokens = 0;
+  // What an append inside a tip node's last block can change, for patch_plan:
+  // the last block entry of every listing of an unfrozen node; each query's
+  // tip node and distance from the end (its position = length - back); the
+  // distinct unfrozen nodes read, and the tokens of all other nodes read.
+  std::vector<int32_t> tail_entry, tail_node;
+  std::vector<int32_t> gq_node, gq_back;
+  std::vector<int32_t> open_nodes;
+  int64_t closed_tokens = 0;
 
   // serialised layout (byte offsets into one device buffer)
   size_t off_items = 0, off_gq = 0, off_gqpos = 0, off_blocks = 0,
          off_parts = 0, off_merge = 0, bytes = 0;
   void layout();
   void serialise(void* dst) const;
+  // Empty every list (keeping its memory) and zero every count.
+  void reset();
+};
+
+struct PlanQuery {
+  int32_t handle;  // batch index
+  int32_t global;  // global query index (row of q / out)
+  int32_t pos;     // absolute position
+};
+
+struct PlanItemTmp {
+  DevItem it;
+  int32_t tiles, root, chunk;
+};
+
+// Working memory of build_plan, kept between calls so that rebuilding a plan
+// of a size seen before allocates nothing.  `loc` is all -1 between calls.
+struct PlanScratch {
+  std::vector<int32_t> loc;  // tree node -> local node
+  std::vector<int32_t> tip, qn, qbase;
+  std::vector<int64_t> len;
+  // local nodes: tree node, parent, handles (hlist[hbeg[k] .. hbeg[k + 1])),
+  // children (child[cbeg[k] .. cbeg[k + 1]), by tree node), DFS preorder
+  std::vector<int32_t> lnode, lparent, hbeg, hlist, cbeg, child, cursor, roots, pre, by_pre, st, sub;
+  std::vector<int64_t> qcount;
+  // query runs: units of one tree (ub), groups (gbeg, gsize, groot)
+  std::vector<PlanQuery> uq;
+  std::vector<int32_t> ub, gbeg, gsize, groot;
+  std::vector<uint64_t> mask;
+  std::vector<int32_t> touched;
+  std::vector<uint8_t> emitted;
+  std::vector<int32_t> go_begin, go_count, go_root;
+  std::vector<uint8_t> go_partials;
+  std::vector<uint8_t> qm_n;
+  std::vector<int32_t> qm_g, qm_j;
+  std::vector<int8_t> gclass;
+  std::vector<PlanItemTmp> tmp;
+  std::vector<int32_t> ibeg, ilist;
 };
 
 // Which kernel runs a group of `tiles` row tiles of 16: 0, 1 = attn.hip with 1
@@ -69,7 +115,16 @@ inline int kernel_class(int tiles) {
 
 // Build the plan for a decode (nq == nullptr) or verify call.  Validates the
 // handles (TKV_E_BADSEQ), query counts (TKV_E_RANGE) and emptiness (TKV_E_EMPTY).
+// Bring a plan built from `tree` up to date after appends that each fitted in
+// their tip node's last block (the tree's shape_epoch unchanged since the
+// build): valid counts of those blocks, query positions and their minima, and
+// the statistics.  The result equals a fresh build_plan.  Every 32-bit word of
+// the serialised plan that changed is appended to `changed` (if given).
+void patch_plan(const Tree& tree, Plan* plan, std::vector<PlanWord>* changed);
+
+// `scratch` (optional) is working memory reused across calls.
 int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
-               int32_t q_per_kv, int32_t num_kv_heads, const PlanOptions& opt, Plan* out);
+               int32_t q_per_kv, int32_t num_kv_heads, const PlanOptions& opt, Plan* out,
+               PlanScratch* scratch = nullptr);
 
 }  // namespace tkv

@@ -65,6 +65,24 @@ struct DevMerge {
   int32_t p_count;
 };
 
+// One 32-bit word of a serialised plan to overwrite in place (the device copy
+// of a plan brought up to date after appends inside tip blocks).
+struct PlanWord {
+  uint32_t word;  // byte offset / 4
+  int32_t value;
+};
+
+// Changed words passed to the patch kernel as its arguments (no copy of the
+// list beforehand): up to kPatchArgWords per launch, within the 4 KiB
+// kernel-argument limit.
+constexpr int kPatchArgWords = 480;
+struct PatchArgs {
+  int32_t* plan;
+  int32_t n;
+  uint32_t limit;
+  PlanWord w[kPatchArgWords];
+};
+
 struct AttnArgs {
   const void* kpool;  // layer base
   const void* vpool;
@@ -96,19 +114,27 @@ struct MergeArgs {
   int32_t pad;
 };
 
+// One block an append writes: slots [slot, slot + cnt) of block blk take
+// source token rows [src, src + cnt); slot == 0 means the block is fresh (its
+// other slots are zeroed).
+struct AppendEntry {
+  int32_t blk;
+  int32_t slot;
+  int32_t src;
+  int32_t cnt;
+};
+
 struct AppendArgs {
   const void* src_k;   // [L][ntok][Hkv][D]
   const void* src_v;
   void* kpool;         // pool base (layer 0)
   void* vpool;
   int64_t layer_stride;  // elements per layer of a pool
-  int32_t ntok;        // tokens in the source arrays
+  int32_t ntok;        // token rows in the source arrays
   int32_t hkv;
   int32_t nent;        // blocks in this launch
-  int32_t s0;          // first slot written in entry 0 (0 = entry 0 is a fresh block)
-  int32_t tok0;        // source token written into entry 0's slot s0
-  int32_t pad;
-  int32_t blk[kAppendMaxBlocks];
+  int32_t pad[3];
+  AppendEntry ent[kAppendMaxBlocks];
 };
 
 struct GatherArgs {

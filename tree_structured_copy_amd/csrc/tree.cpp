@@ -113,6 +113,7 @@ int Tree::seq_new(tkv_seq* out) {
     return TKV_E_NOMEM;
   }
   ++epoch_;
+  ++shape_epoch_;
   return TKV_OK;
 }
 
@@ -133,6 +134,7 @@ int Tree::fork(tkv_seq parent, int32_t n, tkv_seq* out) {
   t.nhandles += n;
   for (int32_t i = 0; i < n; ++i) new_handle(tip, &out[i]);
   ++epoch_;
+  ++shape_epoch_;
   return TKV_OK;
 }
 
@@ -154,6 +156,7 @@ int Tree::release(tkv_seq s) {
     id = p;
   }
   ++epoch_;
+  ++shape_epoch_;
   return TKV_OK;
 }
 
@@ -176,6 +179,17 @@ int Tree::truncate(tkv_seq s, int64_t new_len) {
   t.blocks.resize(keep_blk);
   t.ntok = keep_tok;
   ++epoch_;
+  ++shape_epoch_;
+  return TKV_OK;
+}
+
+int Tree::append_need(tkv_seq s, int32_t ntok, int64_t* blocks) const {
+  if (ntok < 1 || !blocks) return TKV_E_INVAL;
+  int32_t tip;
+  if (int rc = resolve(s, &tip)) return rc;
+  const Node& t = nodes_[tip];
+  const int32_t room = t.frozen ? 0 : (t.blocks.empty() ? 0 : 16 - t.tail_valid());
+  *blocks = (std::max<int64_t>(0, (int64_t)ntok - room) + 15) / 16;
   return TKV_OK;
 }
 
@@ -235,6 +249,7 @@ int Tree::append(tkv_seq s, int32_t ntok, Placement* pl) {
   }
   n.ntok += ntok;
   ++epoch_;
+  if (need_node || need > 0) ++shape_epoch_;
   return TKV_OK;
 }
 
@@ -261,6 +276,7 @@ void Tree::undo_append(tkv_seq s, int32_t ntok, const Placement& pl, bool made_n
     --counters.nodes_created;
   }
   ++epoch_;
+  ++shape_epoch_;
 }
 
 int Tree::seq_len(tkv_seq s, int64_t* len) const {

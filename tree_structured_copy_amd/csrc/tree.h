@@ -77,6 +77,8 @@ class Tree {
   int release(tkv_seq s);
   int truncate(tkv_seq s, int64_t new_len);
   int append(tkv_seq s, int32_t ntok, Placement* pl);
+  // Fresh blocks append(s, ntok) would take (validates s and ntok like it).
+  int append_need(tkv_seq s, int32_t ntok, int64_t* blocks) const;
   // Undo the metadata of the latest successful append (used when its device
   // part could not be launched).  Only valid immediately after that append.
   void undo_append(tkv_seq s, int32_t ntok, const Placement& pl, bool made_node);
@@ -92,7 +94,11 @@ class Tree {
   int resolve(tkv_seq s, int32_t* tip) const;
   const Node& node(int32_t id) const { return nodes_[id]; }
   int32_t node_capacity() const { return static_cast<int32_t>(nodes_.size()); }
+  // epoch: bumped by every change.  shape_epoch: bumped by every change except
+  // an append that fits in its tip node's last block (it then changes only
+  // that block's valid count and the handle's length).
   uint64_t epoch() const { return epoch_; }
+  uint64_t shape_epoch() const { return shape_epoch_; }
   bool last_append_made_node() const { return last_made_node_; }
 
   tkv_counters counters{};
@@ -109,6 +115,7 @@ class Tree {
   std::vector<int32_t> block_owner_;  // node owning each used block
   BlockPool pool_;
   uint64_t epoch_ = 1;
+  uint64_t shape_epoch_ = 1;
   bool last_made_node_ = false;
 };
 

@@ -59,6 +59,18 @@ class LibReplay:
                 k = wdev.kv_tensor(self.wl, call, ntok, gen.KIND_K, self.device)
                 v = wdev.kv_tensor(self.wl, call, ntok, gen.KIND_V, self.device)
                 tkv.tkv_append(self.c, self.h[h], ntok, k, v, torch.cuda.current_stream())
+        elif kind == "append_batch":
+            _, hs, ns, call = op
+            seqs = [self.h[h] for h in hs]
+            if self.device is None:
+                tkv.tkv_append_batch(self.c, seqs, ns)
+            else:
+                import torch
+                from workloads import device as wdev, gen
+                total = sum(ns)
+                k = wdev.kv_tensor(self.wl, call, total, gen.KIND_K, self.device)
+                v = wdev.kv_tensor(self.wl, call, total, gen.KIND_V, self.device)
+                tkv.tkv_append_batch(self.c, seqs, ns, k, v, torch.cuda.current_stream())
         elif kind == "fork":
             _, h, n, kids = op
             for name, s in zip(kids, tkv.tkv_fork(self.c, self.h[h], n)):

@@ -38,6 +38,7 @@ TKV_OPT_PLAN_CACHE = 4
 TKV_OPT_WAVES = 5
 TKV_OPT_CASCADE = 6
 TKV_OPT_CONCURRENT = 7
+TKV_OPT_PLAN_PATCH = 8
 
 STATUS_NAMES = {
     TKV_E_INVAL: "inval", TKV_E_NOMEM: "nomem", TKV_E_BADSEQ: "badseq", TKV_E_SHARED: "shared",
@@ -64,7 +65,7 @@ class tkv_config(ctypes.Structure):
 class tkv_counters(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("blocks_taken", "blocks_freed", "nodes_created",
                                               "nodes_freed", "block_ids_copied", "plans_built",
-                                              "plans_uploaded")]
+                                              "plans_uploaded", "plans_patched")]
 
 
 class tkv_plan_info(ctypes.Structure):
@@ -107,6 +108,7 @@ _SIGS = {
     "tkv_fork": [_P, _U64, _I32, _pU64],
     "tkv_release": [_P, _U64],
     "tkv_append": [_P, _U64, _I32, _P, _P, _P],
+    "tkv_append_batch": [_P, _pU64, _pI32, _I32, _P, _P, _P],
     "tkv_truncate": [_P, _U64, _I64],
     "tkv_workspace_size": [_P, _pU64, _pI32, _I32, ctypes.POINTER(_SZ)],
     "tkv_attend_decode": [_P, _I32, _pU64, _I32, _P, _P, _P, _SZ, _P],
@@ -208,6 +210,14 @@ def tkv_release(c, s: int) -> None:
 
 def tkv_append(c, s: int, ntok: int, k=None, v=None, stream=None) -> None:
     _check(_lib.tkv_append(c, s, ntok, _ptr(k), _ptr(v), _stream(stream)), "tkv_append")
+
+
+def tkv_append_batch(c, seqs, ntok, k=None, v=None, stream=None) -> None:
+    sa = seq_array(seqs)
+    na = i32_array(ntok)
+    if len(na) != len(sa):
+        raise ValueError("one token count per handle")
+    _check(_lib.tkv_append_batch(c, sa, na, len(sa), _ptr(k), _ptr(v), _stream(stream)), "tkv_append_batch")
 
 
 def tkv_truncate(c, s: int, new_len: int) -> None:

@@ -11,6 +11,10 @@ Operations:
 * ``("append", h, ntok, call)``           -- append ``ntok`` tokens; K values come from
   stream ``(KIND_K, call)`` and V values from ``(KIND_V, call)``, each laid out
   ``[layers][ntok][kv_heads][head_dim]``
+* ``("append_batch", [h...], [ntok...], call)`` -- append ``ntok[i]`` tokens to each
+  (distinct) ``h[i]`` in one call; the source arrays from stream ``(KIND_K, call)``
+  / ``(KIND_V, call)`` are laid out ``[layers][sum ntok][kv_heads][head_dim]``, the
+  handles' tokens one after another in list order
 * ``("fork", h, n, [c0, ..., c(n-1)])``   -- n children of ``h``; ``h`` stays live
 * ``("release", h)``
 * ``("truncate", h, new_len)``
@@ -198,6 +202,53 @@ def verify_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_hea
     need = requests * (_blocks_for(prefix, bs) + paths * _blocks_for(drafts, bs))
     return Workload(name, dtype, 1, q_heads, kv_heads, head_dim, need + extra_blocks, ops,
                     seed=seed, description=description)
+
+
+def decode_loop_workload(name: str, *, dtype: str = "bf16", layers: int = 1, q_heads: int = 8,
+                         kv_heads: int = 2, head_dim: int = 128, requests: int = 3, prefix: int = 40,
+                         width: int = 3, branch_tokens: int = 5, rounds: int = 20, verify_nq: int = 0,
+                         batched: bool = True, seed: int = 0, description: str = "") -> Workload:
+    """A generation loop over the fork workload's tree: per request, P = new;
+    append(P, prefix); C = fork(P, width); release(P); append(C[b],
+    branch_tokens).  Then ``rounds`` rounds of: append one token to each branch
+    except those with (round + branch index) % 3 == 2, then one attention call
+    over all branches and every layer -- a decode, or with ``verify_nq`` > 0 a
+    verify of each branch's last ``verify_nq`` tokens.  Most rounds' tokens fit
+    in the branches' last blocks; now and then one opens a block.  A round's
+    appends are one ``append_batch`` (``batched``) or one ``append`` each."""
+    nm = _Names()
+    ops: List[tuple] = []
+    call = 0
+    leaves = []
+    for _ in range(requests):
+        p = nm()
+        ops.append(("new", p))
+        ops.append(("append", p, prefix, call)); call += 1
+        kids = [nm() for _ in range(width)]
+        ops.append(("fork", p, width, kids))
+        ops.append(("release", p))
+        for c in kids:
+            ops.append(("append", c, branch_tokens, call)); call += 1
+        leaves.extend(kids)
+    qcall = 0
+    for r in range(rounds):
+        grow = [c for b, c in enumerate(leaves) if (r + b) % 3 != 2]
+        if batched:
+            ops.append(("append_batch", grow, [1] * len(grow), call)); call += 1
+        else:
+            for c in grow:
+                ops.append(("append", c, 1, call)); call += 1
+        for layer in range(layers):
+            if verify_nq > 0:
+                ops.append(("verify", layer, list(leaves), [verify_nq] * len(leaves), qcall))
+            else:
+                ops.append(("decode", layer, list(leaves), qcall))
+            qcall += 1
+    bs = 16
+    need = requests * (_blocks_for(prefix, bs) + width * _blocks_for(branch_tokens + rounds, bs))
+    return Workload(name, dtype, layers, q_heads, kv_heads, head_dim, need, ops, seed=seed,
+                    description=description or "fork tree, then %d rounds of one-token appends and "
+                                               "attention over every branch" % rounds)
 
 
 # ---------------------------------------------------------------------------
