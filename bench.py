@@ -37,10 +37,10 @@ HBM_PEAK_GBS = 8000.0
 # right.  Valid only for the kernel sources they were taken on (sha256 below);
 # after any change to them the bench line reports traffic as null.
 TRAFFIC_RECORD = {
-    "sources_sha256": "3d1c393894e12f06fd34de86fc9b4ed6528c9523514cf3248566a300c9909a04",
-    "fetch_kib_per_launch": 281838, "fetch_factor": 1.9999,   # 1 GiB read reads as 524309 KiB
+    "sources_sha256": "57540aa8425b3c462e0098f2b150921cd0d8ae657dd0602cf110159de0609c59",
+    "fetch_kib_per_launch": 281848, "fetch_factor": 1.9999,   # 1 GiB read reads as 524309 KiB
     "write_kib_per_launch": 2048, "write_factor": 1.0,        # 1 GiB written reads as 1048576 KiB
-    "hbm_bytes_per_launch": 577181169 + 2097152,
+    "hbm_bytes_per_launch": 577200561 + 2097152,
 }
 
 
@@ -277,6 +277,46 @@ def _cpu_baseline(requests: int, reps: int):
             "branch_queries_per_s": 4 * requests / t}
 
 
+def _native_loops():
+    """The speculative loop and the tree-search loop at full size, timed by the
+    native replayer (tree_structured_copy_amd/replay_bench) from their recipes:
+    * spec_loop: the verify workload's 64 requests (2048-token prefixes, 3 draft
+      paths of 8 tokens) through 8 rounds of fork, draft, verify, accept or
+      roll back and a bonus token;
+    * search_loop: 500 tree-search simulations, branching 4, depth 12, a
+      2048-token root and 16 tokens per node (GQA 32/8, d = 128, bf16)."""
+    import subprocess
+    import tempfile
+    from workloads import recipes
+    exe = os.path.join(ROOT, "tree_structured_copy_amd", "replay_bench")
+    res = {}
+    for key, wl in (("spec_loop", recipes.spec_loop_workload("spec_loop", rounds=8)),
+                    ("search_loop", recipes.mcts_loop_workload("search_loop"))):
+        with tempfile.NamedTemporaryFile("w", suffix=".ops", delete=False) as f:
+            f.write(recipes.ops_text(wl))
+            path = f.name
+        try:
+            r = subprocess.run([exe, path], capture_output=True, text=True, timeout=300)
+        finally:
+            os.unlink(path)
+        if r.returncode != 0:
+            raise RuntimeError("replay_bench failed on %s: %s" % (key, r.stderr[-2000:]))
+        d = json.loads(r.stdout)
+        sec = d["wall_ms"] / 1e3
+        if key == "spec_loop":
+            d["rounds"] = 8
+            d["verify_tokens_per_s"] = d["verify_tokens"] / sec
+            d["ms_per_round"] = d["wall_ms"] / 8
+        else:
+            d["simulations"] = 500
+            d["ms_per_simulation"] = d["wall_ms"] / 500
+            d["branch_queries_per_s"] = d["decode_queries"] / sec
+            d["full_copy_over_cow"] = d["full_copy_bytes"] / max(1, d["cow_peak_bytes"])
+        d["attend_share_of_wall"] = d["attend_kernel_ms"] / max(1e-9, d["wall_ms"])
+        res[key] = d
+    return res
+
+
 def _time_generation_loop(copies, windows, patch):
     """A decode loop on the fork workload.  A step appends one token to each of
     the 128 branches (one tkv_append_batch) and runs the decode call; copies
@@ -464,6 +504,7 @@ def main():
         "branch_queries_per_s": main_res["queries_per_s"],
         "ms_per_step_plan_rebuild": main_res["ms_per_step_plan_rebuild"],
         "generation_loop": generation_loop,
+        "native_loops": _native_loops(),
         "unique_kv_bytes": ubytes,
         "plan": main_res["plan"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

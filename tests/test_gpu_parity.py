@@ -405,3 +405,21 @@ def test_generation_loop_plan_update(kind, layers):
     assert counters[1]["plans_patched"] >= 10
     assert counters[1]["plans_built"] + counters[1]["plans_patched"] >= 20
     assert counters[1]["plans_built"] < counters[0]["plans_built"]
+
+
+@pytest.mark.parametrize("kind", ["spec_loop", "mcts_loop"])
+def test_loop_recipes_match_oracle(kind):
+    """The multi-round speculative loop (6 rounds of forking at unaligned
+    lengths, drafts in fresh blocks, verify, rollback by truncation, a bonus
+    token) and the tree-search loop (60 simulations with terminal
+    re-evaluations), replayed through the library: every attention call
+    matches the oracle; tables and free blocks are bit-exact."""
+    if kind == "spec_loop":
+        wl = recipes.spec_loop_workload("spec_loop_small", q_heads=8, kv_heads=2, requests=5, prefix=40, paths=3,
+                                        drafts=5, rounds=6, seed=3)
+    else:
+        wl = recipes.mcts_loop_workload("mcts_loop_small", q_heads=8, kv_heads=2, root_tokens=40, branching=3,
+                                        depth=4, iterations=60, node_tokens=5, seed=4)
+    res = run_both(wl)
+    assert len(res) == len(wl.attend_ops())
+    assert_close(res, wl.dtype)

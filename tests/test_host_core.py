@@ -413,6 +413,102 @@ def test_append_batch_refusals_change_nothing():
         tkv.tkv_destroy(c)
 
 
+@pytest.mark.parametrize("kind", ["spec_loop", "mcts_loop"])
+def test_replay_bench_host_mode_matches_the_oracle(kind, tmp_path):
+    """The native replayer (replay_bench), run host-only on the loop recipes:
+    its block high-water mark after time_begin equals the oracle allocator's
+    over the same operations, its call, query, token and fork counts equal the
+    recipe's, and its full-copy figure is the sum over forks of n x the
+    parent's length (oracle lengths) x bytes per token."""
+    import subprocess
+    exe = os.path.join(ROOT, "tree_structured_copy_amd", "replay_bench")
+    if not os.path.exists(exe):
+        pytest.skip("replay_bench not built")
+    if kind == "spec_loop":
+        wl = recipes.spec_loop_workload("s", requests=5, prefix=40, paths=3, drafts=5, rounds=6, seed=3)
+    else:
+        wl = recipes.mcts_loop_workload("m", root_tokens=40, branching=3, depth=4, iterations=60,
+                                        node_tokens=5, seed=4)
+    path = tmp_path / "ops.txt"
+    path.write_text(recipes.ops_text(wl))
+    r = subprocess.run([exe, str(path), "--host"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    got = json.loads(r.stdout)
+    o = A.FlatAllocator(wl.num_blocks, 16)
+    names = {}
+    timed = False
+    peak = 0
+    full_copy = forks = queries = vtokens = calls = appended = 0
+    for op in wl.ops:
+        k = op[0]
+        if k == "time_begin":
+            timed = True
+            peak = wl.num_blocks - o.num_free()
+            continue
+        if k == "new":
+            names[op[1]] = o.seq_new()
+        elif k == "append":
+            o.append(names[op[1]], op[2])
+            appended += op[2] if timed else 0
+        elif k == "append_batch":
+            for h, n in zip(op[1], op[2]):
+                o.append(names[h], n)
+            appended += sum(op[2]) if timed else 0
+        elif k == "fork":
+            if timed:
+                full_copy += op[2] * o.length(names[op[1]])
+                forks += 1
+            for c, s in zip(op[3], o.fork(names[op[1]], op[2])):
+                names[c] = s
+        elif k == "release":
+            o.release(names.pop(op[1]))
+        elif k == "truncate":
+            o.truncate(names[op[1]], op[2])
+        elif k == "decode":
+            calls += 1
+            queries += len(op[2])
+        elif k == "verify":
+            calls += 1
+            vtokens += sum(op[3])
+        if timed:
+            peak = max(peak, wl.num_blocks - o.num_free())
+    token_bytes = wl.layers * wl.kv_heads * wl.head_dim * wl.elem_bytes * 2
+    assert got["peak_blocks"] == peak
+    assert got["attend_calls"] == calls and got["decode_queries"] == queries and got["verify_tokens"] == vtokens
+    assert got["forks"] == forks and got["appended_tokens"] == appended
+    assert got["full_copy_bytes"] == full_copy * token_bytes
+    assert got["plans_built"] == 0  # host mode runs no attention call
+
+
+def test_fork_and_node_creation_do_not_scale_with_tree_size():
+    """fork and a node-creating append cost about the same beside 20 000 live
+    handles and nodes as beside a handful (each handle or node added must not
+    move every existing one: growth is geometric)."""
+    def per_step_us(live):
+        c = host_cache(live + 2600)
+        try:
+            root = tkv.tkv_seq_new(c)
+            tkv.tkv_append(c, root, 16)
+            if live > 1:
+                many = tkv.tkv_fork(c, root, live)
+                tkv.tkv_append_batch(c, many, [1] * live)   # one node each
+            h = tkv.tkv_fork(c, root, 1)[0]
+            ones = tkv.i32_array([1] * 4)
+            # the children are kept, so the handle and node tables grow as in a search
+            best = float("inf")
+            for _ in range(3):
+                t0 = time.perf_counter()
+                for _ in range(200):
+                    kids = tkv.tkv_fork(c, h, 4)
+                    tkv.tkv_append_batch(c, kids, ones)
+                best = min(best, (time.perf_counter() - t0) / 200 * 1e6)
+            return best
+        finally:
+            tkv.tkv_destroy(c)
+    small, large = per_step_us(4), per_step_us(20000)
+    assert large < 3 * small + 5, (small, large)
+
+
 def test_fork_latency_flat_in_prefix_and_depth():
     base = _median_fork_ns(16, 1)
     for prefix, depth in [(65536, 1), (16, 500), (65536, 500)]:

@@ -89,7 +89,13 @@ def build(verbose: bool = False, jobs: int = 8) -> dict:
     _run([CXX, "-O2", "-std=c++17", "-I" + INCLUDE, os.path.join(HERE, "fork_bench.cpp"), "-L" + HERE, "-ltkv",
           "-Wl,-rpath,$ORIGIN", "-o", fb + ".tmp"], verbose)
     os.replace(fb + ".tmp", fb)
-    return {"libtkv": lib, "libtkvgen": genlib, "fork_bench": fb}
+    # native recipe replayer (loop timings), linked against the library and the HIP runtime
+    rb = os.path.join(HERE, "replay_bench")
+    _run([CXX] + HOST_FLAGS + ["-I" + INCLUDE, os.path.join(HERE, "replay_bench.cpp"), "-L" + HERE, "-ltkv",
+                               "-L" + os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath,$ORIGIN",
+                               "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-o", rb + ".tmp"], verbose)
+    os.replace(rb + ".tmp", rb)
+    return {"libtkv": lib, "libtkvgen": genlib, "fork_bench": fb, "replay_bench": rb}
 
 
 if __name__ == "__main__":

@@ -5,6 +5,19 @@
 
 namespace tkv {
 
+namespace {
+
+// Room for `more` further elements, growing geometrically: an exact reserve
+// reallocates (and moves every element) on each call, which would make fork
+// O(handles) and node creation O(nodes).
+template <class V>
+void make_room(V& v, size_t more) {
+  const size_t need = v.size() + more;
+  if (v.capacity() < need) v.reserve(std::max(need, 2 * v.capacity()));
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------- BlockPool
 
 void BlockPool::init(int32_t n) {
@@ -103,8 +116,8 @@ int Tree::resolve(tkv_seq s, int32_t* tip) const {
 int Tree::seq_new(tkv_seq* out) {
   if (!out) return TKV_E_INVAL;
   try {
-    handles_.reserve(handles_.size() + 1);
-    nodes_.reserve(nodes_.size() + 1);
+    make_room(handles_, 1);
+    make_room(nodes_, 1);
     const int32_t n = new_node();
     nodes_[n].refs = 1;
     nodes_[n].nhandles = 1;
@@ -124,7 +137,7 @@ int Tree::fork(tkv_seq parent, int32_t n, tkv_seq* out) {
   try {
     // Make room first so that nothing below can fail half-way.
     const size_t need = n > (int32_t)free_handles_.size() ? n - free_handles_.size() : 0;
-    handles_.reserve(handles_.size() + need);
+    make_room(handles_, need);
   } catch (const std::bad_alloc&) {
     return TKV_E_NOMEM;
   }
@@ -205,8 +218,8 @@ int Tree::append(tkv_seq s, int32_t ntok, Placement* pl) {
   try {
     pl->blocks.clear();
     pl->blocks.reserve(need + 1);
-    nodes_.reserve(nodes_.size() + 1);
-    nodes_[tip].blocks.reserve(nodes_[tip].blocks.size() + need);
+    make_room(nodes_, 1);
+    make_room(nodes_[tip].blocks, static_cast<size_t>(need));
   } catch (const std::bad_alloc&) {
     return TKV_E_NOMEM;
   }

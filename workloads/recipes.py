@@ -18,6 +18,8 @@ Operations:
 * ``("fork", h, n, [c0, ..., c(n-1)])``   -- n children of ``h``; ``h`` stays live
 * ``("release", h)``
 * ``("truncate", h, new_len)``
+* ``("time_begin",)``                     -- no effect on the cache: where a timed
+  replay of a loop starts (after its set-up)
 * ``("decode", layer, [h...], qcall)``    -- one query per handle; Q from stream
   ``(KIND_Q, qcall)``, laid out ``[n][q_heads][head_dim]``
 * ``("verify", layer, [h...], [nq...], qcall)`` -- the last ``nq[i]`` positions of each
@@ -249,6 +251,147 @@ def decode_loop_workload(name: str, *, dtype: str = "bf16", layers: int = 1, q_h
     return Workload(name, dtype, layers, q_heads, kv_heads, head_dim, need, ops, seed=seed,
                     description=description or "fork tree, then %d rounds of one-token appends and "
                                                "attention over every branch" % rounds)
+
+
+def spec_loop_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_heads: int = 8,
+                       head_dim: int = 128, requests: int = 64, prefix: int = 2048, paths: int = 3,
+                       drafts: int = 8, rounds: int = 8, seed: int = 0, description: str = "") -> Workload:
+    """The multi-round speculative loop: per request, P = new; append(P, prefix).
+    Each round: every request forks P into ``paths`` draft paths and releases P;
+    one append_batch gives every path ``drafts`` tokens; one verify covers every
+    path's last ``drafts`` tokens; then per request a path a ~ U{0..paths-1}
+    and an accepted count k ~ U{0..drafts} are drawn (stream (KIND_ACCEPT,
+    100000 * (round + 1) + request)), path a is truncated to len(P) + k, the
+    other paths are released, and one append_batch gives every request the
+    token the target model emits after its accepted drafts.  Path a is the next
+    round's P.  From the second round on the forks fall at unaligned lengths,
+    so a fork point's partial block is shared, frozen, and each path's drafts
+    start a fresh block."""
+    nm = _Names()
+    ops: List[tuple] = []
+    call = 0
+    cur = []
+    for _ in range(requests):
+        p = nm()
+        ops.append(("new", p))
+        ops.append(("append", p, prefix, call)); call += 1
+        cur.append(p)
+    lens = [prefix] * requests
+    ops.append(("time_begin",))
+    qcall = 0
+    for rnd in range(rounds):
+        kids = []
+        for p in cur:
+            ks = [nm() for _ in range(paths)]
+            ops.append(("fork", p, paths, ks))
+            ops.append(("release", p))
+            kids.append(ks)
+        allk = [h for ks in kids for h in ks]
+        ops.append(("append_batch", allk, [drafts] * len(allk), call)); call += 1
+        ops.append(("verify", 0, allk, [drafts] * len(allk), qcall)); qcall += 1
+        nxt = []
+        for r, ks in enumerate(kids):
+            st = gen.stream_id(gen.KIND_ACCEPT, 100000 * (rnd + 1) + r)
+            a = gen.uniform_int(seed, st, 0, paths)
+            k = gen.uniform_int(seed, st, 1, drafts + 1)
+            ops.append(("truncate", ks[a], lens[r] + k))
+            lens[r] += k + 1
+            for b, c in enumerate(ks):
+                if b != a:
+                    ops.append(("release", c))
+            nxt.append(ks[a])
+        ops.append(("append_batch", list(nxt), [1] * len(nxt), call)); call += 1
+        cur = nxt
+    bs = 16
+    per_req = _blocks_for(prefix, bs) + 1 + rounds * (paths * (_blocks_for(drafts + 1, bs) + 1) + 1)
+    return Workload(name, dtype, 1, q_heads, kv_heads, head_dim, requests * per_req, ops, seed=seed,
+                    description=description or "%d rounds of fork, draft, verify, accept or roll back" % rounds)
+
+
+def mcts_loop_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_heads: int = 8,
+                       head_dim: int = 128, root_tokens: int = 2048, branching: int = 4, depth: int = 12,
+                       iterations: int = 500, node_tokens: int = 16, seed: int = 0,
+                       description: str = "") -> Workload:
+    """A tree search run as ``iterations`` simulations (the Dendrite demo tape's
+    MCTS run: 500 simulations, branching 4, depth 12, head_dim 128): root = new;
+    append(root, root_tokens).  A simulation descends from the root, taking at
+    every expanded node a child drawn uniformly (stream (KIND_SHAPE, 2)), to
+    the first node not yet expanded.  A node at depth ``depth`` is terminal: its
+    handle decodes one query.  Any other is expanded: forked into ``branching``
+    children and released (the children keep its path), one append_batch gives
+    every child ``node_tokens`` tokens, and one decode evaluates the new
+    children."""
+    nm = _Names()
+    ops: List[tuple] = []
+    call = 0
+    qcall = 0
+    root = nm()
+    ops.append(("new", root))
+    ops.append(("append", root, root_tokens, call)); call += 1
+    ops.append(("time_begin",))
+    children = {}          # expanded node -> its children
+    level = {root: 0}      # node -> depth
+    stream = gen.stream_id(gen.KIND_SHAPE, 2)
+    counter = 0
+    expansions = 0
+    for _ in range(iterations):
+        h = root
+        while h in children:
+            h = children[h][gen.uniform_int(seed, stream, counter, branching)]
+            counter += 1
+        if level[h] >= depth:
+            ops.append(("decode", 0, [h], qcall)); qcall += 1
+            continue
+        kids = [nm() for _ in range(branching)]
+        ops.append(("fork", h, branching, kids))
+        ops.append(("release", h))
+        ops.append(("append_batch", list(kids), [node_tokens] * branching, call)); call += 1
+        ops.append(("decode", 0, list(kids), qcall)); qcall += 1
+        children[h] = kids
+        for c in kids:
+            level[c] = level[h] + 1
+        expansions += 1
+    bs = 16
+    need = _blocks_for(root_tokens, bs) + expansions * branching * _blocks_for(node_tokens, bs)
+    return Workload(name, dtype, 1, q_heads, kv_heads, head_dim, need, ops, seed=seed,
+                    description=description or "%d tree-search simulations, branching %d, depth %d"
+                    % (iterations, branching, depth))
+
+
+def ops_text(wl: Workload) -> str:
+    """The recipe as the text the native replayer (replay_bench) reads: a config
+    line, then one operation per line, handle names as integers:
+    ``config layers q_heads kv_heads head_dim num_blocks dtype(0 f32, 1 bf16)``,
+    ``new h``, ``append h ntok``, ``append_batch n h1 n1 ... hn nn``,
+    ``fork h n c1 ... cn``, ``release h``, ``truncate h len``, ``time_begin``,
+    ``decode layer n h1 ... hn``, ``verify layer n h1 q1 ... hn qn``.  K/V/Q
+    values are not carried: the replayer measures time and memory, while the
+    parity tests replay the same recipe against the oracle."""
+    out = ["config %d %d %d %d %d %d" % (wl.layers, wl.q_heads, wl.kv_heads, wl.head_dim, wl.num_blocks,
+                                         1 if wl.dtype == "bf16" else 0)]
+    for op in wl.ops:
+        k = op[0]
+        if k == "new":
+            out.append("new %d" % op[1])
+        elif k == "append":
+            out.append("append %d %d" % (op[1], op[2]))
+        elif k == "append_batch":
+            out.append("append_batch %d %s" % (len(op[1]), " ".join("%d %d" % x for x in zip(op[1], op[2]))))
+        elif k == "fork":
+            out.append("fork %d %d %s" % (op[1], op[2], " ".join(str(c) for c in op[3])))
+        elif k == "release":
+            out.append("release %d" % op[1])
+        elif k == "truncate":
+            out.append("truncate %d %d" % (op[1], op[2]))
+        elif k == "time_begin":
+            out.append("time_begin")
+        elif k == "decode":
+            out.append("decode %d %d %s" % (op[1], len(op[2]), " ".join(str(h) for h in op[2])))
+        elif k == "verify":
+            out.append("verify %d %d %s" % (op[1], len(op[2]), " ".join("%d %d" % x for x in zip(op[2], op[3]))))
+        else:
+            raise ValueError(k)
+    return "\n".join(out) + "\n"
 
 
 # ---------------------------------------------------------------------------
