@@ -66,6 +66,13 @@ struct tkv_cache {
   int32_t concurrent = 0;  // TKV_OPT_CONCURRENT
   PlanSlot slots[kPlanSlots];
   PlanScratch scratch;
+  // tkv_append_batch's working lists, kept so a call of a familiar size
+  // allocates nothing; seen[slot] == seen_stamp marks a handle of the batch
+  std::vector<Placement> app_pl;
+  std::vector<uint8_t> app_made;
+  std::vector<AppendEntry> app_ents;
+  std::vector<uint64_t> seen;
+  uint64_t seen_stamp = 0;
   uint64_t stamp = 0;
   // pinned staging for plan uploads
   void* pinned = nullptr;
@@ -494,29 +501,30 @@ int tkv_append_batch(tkv_cache* c, const tkv_seq* seqs, const int32_t* ntok, int
   if ((k == nullptr) != (v == nullptr)) return TKV_E_INVAL;
   if (k && !c->has_pools) return TKV_E_NODEVICE;
   if (k && ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)) return TKV_E_INVAL;
-  std::vector<Placement> pls;
-  std::vector<uint8_t> made;
-  std::vector<AppendEntry> ents;
+  std::vector<Placement>& pls = c->app_pl;
+  std::vector<uint8_t>& made = c->app_made;
+  std::vector<AppendEntry>& ents = c->app_ents;
   try {
     // everything that could refuse the batch is checked before any change:
     // handles, counts, repeats (two appends to one handle would write one
     // block from two workgroups), the source size and the free blocks
+    if (c->seen.size() < c->tree.handle_slots()) c->seen.resize(c->tree.handle_slots() * 2, 0);
+    const uint64_t stamp = ++c->seen_stamp;
     int64_t need = 0, total = 0;
     for (int32_t i = 0; i < nseq; ++i) {
       int64_t b = 0;
       if (int rc = c->tree.append_need(seqs[i], ntok[i], &b)) return rc;
+      uint64_t& mark = c->seen[Tree::slot_of(seqs[i])];
+      if (mark == stamp) return TKV_E_INVAL;
+      mark = stamp;
       need += b;
       total += ntok[i];
     }
     if (total > INT32_MAX) return TKV_E_RANGE;
-    if (nseq > 1) {
-      std::vector<tkv_seq> sorted(seqs, seqs + nseq);
-      std::sort(sorted.begin(), sorted.end());
-      if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return TKV_E_INVAL;
-    }
     if (need > c->tree.num_free()) return TKV_E_NOMEM;
-    pls.resize(nseq);
+    if (pls.size() < static_cast<size_t>(nseq)) pls.resize(nseq);
     made.resize(nseq);
+    ents.clear();
     ents.reserve(static_cast<size_t>(need + nseq));
   } catch (const std::bad_alloc&) {
     return TKV_E_NOMEM;

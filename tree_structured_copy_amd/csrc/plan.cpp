@@ -387,10 +387,14 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     auto chunks_of = [&](int32_t gi) -> int32_t {
       const int cls = class_of(gi);
       const int64_t nb = S.go_count[gi];
-      const int64_t floor = std::max<int32_t>(1, cls < 2 ? opt.min_chunk : opt.min_chunk / 4);
       // the 4- and 8-tile LDS-staged shapes fit two workgroups per CU, and
       // two per CU stream faster than one with a deeper ring: twice the items
       const int64_t want = (cls == 2 || cls == 4) ? 2 * class_items : class_items;
+      // a class too small to give every item its floor of blocks (a few
+      // queries over a few thousand tokens) is latency-bound, not
+      // bandwidth-bound: its floor drops to what fills the GPU, at least 4
+      const int64_t base = std::max<int32_t>(1, cls < 2 ? opt.min_chunk : opt.min_chunk / 4);
+      const int64_t floor = std::max<int64_t>(1, std::min(base, std::max<int64_t>(4, class_blocks[cls] / want)));
       int64_t nc = nb * want / class_blocks[cls];
       nc = std::min(nc, nb / floor);
       nc = std::max<int64_t>(nc, (nb + kRowsMaxItemBlocks - 1) / kRowsMaxItemBlocks);

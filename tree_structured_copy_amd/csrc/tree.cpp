@@ -62,7 +62,7 @@ int32_t Tree::new_node() {
   if (!free_nodes_.empty()) {
     id = free_nodes_.back();
     free_nodes_.pop_back();
-    nodes_[id] = Node();
+    nodes_[id].reset();
   } else {
     id = static_cast<int32_t>(nodes_.size());
     nodes_.emplace_back();
@@ -79,7 +79,7 @@ void Tree::free_node(int32_t id) {
     block_owner_[b] = -1;
     ++counters.blocks_freed;
   }
-  n = Node();
+  n.reset();
   free_nodes_.push_back(id);
   ++counters.nodes_freed;
 }
@@ -284,7 +284,7 @@ void Tree::undo_append(tkv_seq s, int32_t ntok, const Placement& pl, bool made_n
     const uint32_t slot = static_cast<uint32_t>(s & 0xffffffffu);
     handles_[slot].tip = p;
     nodes_[p].nhandles += 1;
-    n = Node();
+    n.reset();
     free_nodes_.push_back(tip);
     --counters.nodes_created;
   }

@@ -53,6 +53,15 @@ struct Node {
   int32_t tail_valid() const {
     return blocks.empty() ? 0 : static_cast<int32_t>(ntok - 16 * (int64_t)(blocks.size() - 1));
   }
+  // Back to a fresh node, keeping the block list's memory for the next user
+  // of this slot.
+  void reset() {
+    parent = -1;
+    refs = nhandles = depth = 0;
+    base = ntok = 0;
+    frozen = live = false;
+    blocks.clear();
+  }
 };
 
 struct Handle {
@@ -89,6 +98,10 @@ class Tree {
   int block_refcount(int32_t b, int32_t* rc) const;
   int num_free() const { return pool_.num_free(); }
   int32_t num_blocks() const { return pool_.size(); }
+  // Slot of a handle (valid after resolve() succeeded on it), and the number
+  // of slots, for per-handle marks kept outside the tree.
+  static uint32_t slot_of(tkv_seq s) { return static_cast<uint32_t>(s & 0xffffffffu); }
+  size_t handle_slots() const { return handles_.size(); }
 
   // For the planner.
   int resolve(tkv_seq s, int32_t* tip) const;
