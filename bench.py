@@ -317,14 +317,17 @@ def _native_loops():
     return res
 
 
-def _time_generation_loop(copies, windows, patch):
+def _time_generation_loop(copies, windows, patch, fused=False):
     """A decode loop on the fork workload.  A step appends one token to each of
     the 128 branches (one tkv_append_batch) and runs the decode call; copies
     rotate step by step.  Windows of 16 steps per copy are timed (wall clock,
     synchronised on both sides): in each, the first step opens a block in every
     branch (its plan is rebuilt) and the other 15 fit in it (its plan is
     updated in place, or with patch = 0 rebuilt).  Between windows, untimed,
-    the branches are truncated back to their 64 tokens.  Returns ms per step."""
+    the branches are truncated back to their 64 tokens.  With fused, a step
+    reserves the token (tkv_append_batch without K/V) and writes it in the
+    decode call (tkv_attend_decode_new_token): one launch fewer.  Returns ms
+    per step."""
     import torch
     from tree_structured_copy_amd import tkv
     from workloads import device as wdev, gen, recipes
@@ -346,8 +349,13 @@ def _time_generation_loop(copies, windows, patch):
         t0 = time.perf_counter()
         for i in range(16 * copies):
             it = items[i % copies]
-            tkv.tkv_append_batch(it.lib.c, it.calls[0][1], ones, k, v, stream)
-            it.step(stream)
+            if fused:
+                layer, seqs, _, q, out = it.calls[0]
+                tkv.tkv_append_batch(it.lib.c, seqs, ones)
+                tkv.tkv_attend_decode_new_token(it.lib.c, layer, seqs, k, v, q, out, it.ws, it.need, stream)
+            else:
+                tkv.tkv_append_batch(it.lib.c, it.calls[0][1], ones, k, v, stream)
+                it.step(stream)
         torch.cuda.synchronize()
         if w > 0:
             total += time.perf_counter() - t0
@@ -432,7 +440,8 @@ def main():
     ap.add_argument("--counters-workload", default="llama_fork",
                     help="workload of the --counters run (llama_fork, spec_verify, mcts_tree, ...)")
     ap.add_argument("--only", default=None,
-                    help="measure just this workload (mcts_tree, spec_verify, full_depth, llama_fork) and print "
+                    help="measure just this workload (mcts_tree, spec_verify, full_depth, llama_fork, or "
+                         "generation_loop: the decode loop with batched appends) and print "
                          "its figures as one JSON line: a short run for a kernel trace of that workload alone")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -447,6 +456,13 @@ def main():
     if args.counters:
         _counters_run(args.copies, args.counters_workload)
         return
+    if args.only == "generation_loop":
+        ms, counters = _time_generation_loop(args.copies, 8, 1)
+        fused_ms, _ = _time_generation_loop(args.copies, 8, 1, fused=True)
+        print(json.dumps({"only": "generation_loop", "ms_per_step": ms, "ms_per_step_fused": fused_ms,
+                          "plans_built_patched_one_copy": [counters["plans_built"], counters["plans_patched"]]}),
+              flush=True)
+        return
     if args.only:
         copies = 1 if args.only == "full_depth" else args.copies
         steps, warmup = (max(3, args.steps // 10), 1) if args.only == "full_depth" else (args.steps, args.warmup)
@@ -457,10 +473,12 @@ def main():
     main_res = measure("llama_fork", args.copies, args.steps, args.warmup, rebuild=True)
     loop_ms, loop_counters = _time_generation_loop(args.copies, 8, 1)
     loop_rebuild_ms, _ = _time_generation_loop(args.copies, 8, 0)
+    loop_fused_ms, _ = _time_generation_loop(args.copies, 8, 1, fused=True)
     generation_loop = {
         "steps_timed": 8 * 16 * args.copies,
         "ms_per_step": loop_ms,
         "ms_per_step_plans_rebuilt": loop_rebuild_ms,
+        "ms_per_step_token_written_in_decode_call": loop_fused_ms,
         "branch_tokens_per_s": 128 / (loop_ms / 1e3),
         "plans_built_patched_one_copy": [loop_counters["plans_built"], loop_counters["plans_patched"]],
     }

@@ -152,6 +152,22 @@ int tkv_workspace_size(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int
 int tkv_attend_decode(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t nseq,
                       const void* q, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* One layer of a decode step whose new token is written by the call (fused append
+ * + decode, in the generation loop of the article's fork-based decoding): for each
+ * handle i (each at most once), its last token -- which must lie in the handle's
+ * own tip node, e.g. reserved for all layers by tkv_append_batch with k = v = NULL
+ * -- gets K = k_new[i], V = v_new[i] for `layer` (device [nseq][Hkv][head_dim], cache
+ * dtype), then the call is tkv_attend_decode over the paths that include it.  The
+ * tokens are written in the same launch as the plan's in-place update (one launch
+ * per 128 tokens) before the attention kernels, on `stream`.  A token that opened
+ * its block is written with zeros in the block's other slots.  Errors as
+ * tkv_attend_decode, plus TKV_E_INVAL for a handle given twice or a null k_new /
+ * v_new, and TKV_E_SHARED when a handle's last token is shared with other branches
+ * (its tip node was forked, or it has no tokens of its own). */
+int tkv_attend_decode_new_token(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t nseq,
+                                const void* k_new, const void* v_new, const void* q, float* out,
+                                void* ws, size_t ws_bytes, void* stream);
+
 /* Verification attention (DSpark blog, second layer: a block of drafts checked in one
  * parallel pass).  The last nq[i] tokens of handle i (1 <= nq[i] <= L_i) are queries;
  * the query at absolute position p attends over positions 0..p of its own path.

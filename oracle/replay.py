@@ -65,6 +65,11 @@ class OracleReplay:
                     self.alloc.append(self.h_alloc[h], n)
                 self.mat.append(self.h_mat[h], _batch_source_for(self.wl, call, total, first, n))
                 first += n
+        elif kind == "reserve_batch":
+            # one token per handle whose K/V (every layer) are those of batched
+            # append `call`, written later by the decode_new ops
+            _, hs, call = op
+            self.apply(("append_batch", hs, [1] * len(hs), call))
         elif kind == "fork":
             _, h, n, kids = op
             if self.alloc is not None:
@@ -81,7 +86,7 @@ class OracleReplay:
             if self.alloc is not None:
                 self.alloc.truncate(self.h_alloc[h], L)
             self.mat.truncate(self.h_mat[h], L)
-        elif kind in ("decode", "verify", "time_begin"):
+        elif kind in ("decode", "decode_new", "verify", "time_begin"):
             pass
         else:
             raise ValueError(kind)
@@ -90,7 +95,7 @@ class OracleReplay:
     def query_rows(self, op):
         """(handle name, absolute position) of every query row of a decode/verify op."""
         rows = []
-        if op[0] == "decode":
+        if op[0] in ("decode", "decode_new"):
             for h in op[2]:
                 rows.append((h, self.mat.length(self.h_mat[h]) - 1))
         else:

@@ -423,3 +423,91 @@ def test_loop_recipes_match_oracle(kind):
     res = run_both(wl)
     assert len(res) == len(wl.attend_ops())
     assert_close(res, wl.dtype)
+
+
+@pytest.mark.parametrize("dtype,layers", [("bf16", 1), ("bf16", 2), ("f32", 1)])
+def test_decode_with_new_token_written_in_the_call(dtype, layers):
+    """The fused decode step: each round reserves one token per branch
+    (tkv_append_batch without K/V), then per layer tkv_attend_decode_new_token
+    writes that layer's K/V of the token and decodes.  Every call matches the
+    oracle; outputs and pool contents equal, bit for bit, those of the same
+    loop run as a batched append with K/V followed by tkv_attend_decode."""
+    torch = need_gpu()
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    import dataclasses
+    wl = recipes.decode_loop_workload("fused_%s_%d" % (dtype, layers), dtype=dtype, layers=layers,
+                                      head_dim=128 if dtype == "bf16" else 64, rounds=14, fused=True, seed=81)
+    assert_close(run_both(wl), wl.dtype)
+    plain_ops = []
+    for op in wl.ops:
+        if op[0] == "reserve_batch":
+            plain_ops.append(("append_batch", op[1], [1] * len(op[1]), op[2]))
+        elif op[0] == "decode_new":
+            plain_ops.append(("decode", op[1], op[2], op[4]))
+        else:
+            plain_ops.append(op)
+    plain = dataclasses.replace(wl, ops=plain_ops)
+    outs, pools = {}, {}
+    for key, w in (("fused", wl), ("plain", plain)):
+        lib = LibReplay(w)
+        try:
+            got = []
+            for op in w.ops:
+                if op[0] in ("decode", "decode_new"):
+                    got.append(lib.attend(op).cpu())
+                lib.apply(op)
+            torch.cuda.synchronize()
+            outs[key] = got
+            views = {}
+            for name in sorted(lib.h):
+                L = tkv.tkv_seq_len(lib.c, lib.h[name])
+                for layer in range(w.layers):
+                    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+                    ko = torch.empty((L, w.kv_heads, w.head_dim), dtype=dt, device="cuda")
+                    vo = torch.empty_like(ko)
+                    tkv.tkv_gather(lib.c, lib.h[name], layer, ko, vo, torch.cuda.current_stream())
+                    views[(name, layer)] = (ko.cpu(), vo.cpu())
+            torch.cuda.synchronize()
+            pools[key] = views
+        finally:
+            lib.close()
+    assert len(outs["fused"]) == 14 * layers
+    for a, b in zip(outs["fused"], outs["plain"]):
+        assert torch.equal(a, b)
+    assert pools["fused"].keys() == pools["plain"].keys()
+    for k in pools["fused"]:
+        assert torch.equal(pools["fused"][k][0], pools["plain"][k][0])
+        assert torch.equal(pools["fused"][k][1], pools["plain"][k][1])
+
+
+def test_decode_with_new_token_refusals():
+    """tkv_attend_decode_new_token refuses, before any launch: a handle given
+    twice or a null K/V (TKV_E_INVAL), a handle whose last token is shared
+    with other branches (TKV_E_SHARED: its tip was forked, or a fresh child
+    has no token of its own) and an empty handle (TKV_E_EMPTY)."""
+    torch = need_gpu()
+    from tree_structured_copy_amd import tkv
+    n = 1 * 64 * 2 * 16 * 128
+    kp = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    c = tkv.tkv_create(1, 8, 2, 128, 64, tkv.TKV_BF16, kp, vp)
+    try:
+        p = tkv.tkv_seq_new(c)
+        tkv.tkv_append(c, p, 20)
+        kids = tkv.tkv_fork(c, p, 2)
+        tkv.tkv_append_batch(c, [kids[0]], [1])
+        empty = tkv.tkv_seq_new(c)
+        q = torch.zeros((2, 8, 128), dtype=torch.bfloat16, device="cuda")
+        kn = torch.zeros((2, 2, 128), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((2, 8, 128), dtype=torch.float32, device="cuda")
+        st = torch.cuda.current_stream()
+        for seqs, k, err in [([kids[0], kids[0]], kn, "TKV_E_INVAL"), ([kids[1]], kn, "TKV_E_SHARED"),
+                             ([p], kn, "TKV_E_SHARED"), ([empty], kn, "TKV_E_EMPTY"), ([kids[0]], None, "TKV_E_INVAL")]:
+            with pytest.raises(tkv.TkvError) as ei:
+                tkv.tkv_attend_decode_new_token(c, 0, seqs, k, kn, q, out, None, 0, st)
+            assert ei.value.code == getattr(tkv, err), (seqs, err)
+        tkv.tkv_attend_decode_new_token(c, 0, [kids[0]], kn, kn, q, out, None, 0, st)
+        torch.cuda.synchronize()
+    finally:
+        tkv.tkv_destroy(c)

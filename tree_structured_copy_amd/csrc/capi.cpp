@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <array>
 #include <cmath>
+#include <cstddef>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -119,6 +120,18 @@ struct tkv_cache {
 
 namespace {
 
+// Query positions (and their minima in the items) are read by the causal
+// kernels only: a decode plan's device copy does not need them updated.
+void drop_position_words(const Plan& p, std::vector<PlanWord>* words) {
+  const size_t q0 = p.off_gqpos / 4, q1 = q0 + p.gqpos.size();
+  const size_t i0 = p.off_items / 4, i1 = i0 + p.items.size() * (sizeof(DevItem) / 4);
+  const size_t mp = offsetof(DevItem, min_pos) / 4;
+  auto position = [&](const PlanWord& w) {
+    return (w.word >= q0 && w.word < q1) || (w.word >= i0 && w.word < i1 && (w.word - i0) % (sizeof(DevItem) / 4) == mp);
+  };
+  words->erase(std::remove_if(words->begin(), words->end(), position), words->end());
+}
+
 int find_plan(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq, PlanSlot** out) {
   const bool verify = nq != nullptr;
   const uint64_t ep = c->tree.epoch(), shape = c->tree.shape_epoch();
@@ -138,6 +151,7 @@ int find_plan(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq
           // the device copy is the plan as it stands: list the words that change
           try {
             patch_plan(c->tree, &s.plan, &s.pending);
+            if (!s.plan.causal) drop_position_words(s.plan, &s.pending);
             listed = true;
           } catch (const std::bad_alloc&) {
             s.pending.clear();
@@ -290,14 +304,76 @@ size_t partial_bytes(const tkv_cache* c, const Plan& p) {
   return acc + align256(static_cast<size_t>(p.partial_slots) * 2 * sizeof(float));
 }
 
+// Before a decode call that writes its new tokens: the plan's device copy
+// (a whole upload; or its changed words, carried by the preparation launch
+// when they fit) and the tokens' K/V of this layer, in one launch per 128
+// tokens.
+int prepare_new_tokens(tkv_cache* c, PlanSlot* s, int32_t layer, int32_t nseq, const void* k_new,
+                       const void* v_new, hipStream_t stream) {
+  bool carry = false;
+  if (!s->uploaded || s->pending.size() > static_cast<size_t>(kPrepPatchWords)) {
+    if (int rc = upload_plan(c, s, stream)) return rc;
+  } else {
+    carry = !s->pending.empty();
+  }
+  const uint32_t limit = static_cast<uint32_t>(s->plan.bytes / 4);
+  DecodePrepArgs a{};
+  a.app.src_k = k_new;
+  a.app.src_v = v_new;
+  a.app.kpool = const_cast<char*>(c->kpool_layer(layer));
+  a.app.vpool = const_cast<char*>(c->vpool_layer(layer));
+  a.app.layer_stride = 0;
+  a.app.ntok = nseq;
+  a.app.hkv = c->cfg.num_kv_heads;
+  a.plan = static_cast<int32_t*>(s->dev);
+  a.limit = limit;
+  const std::vector<AppendEntry>& ents = c->app_ents;
+  for (int32_t e0 = 0; e0 < nseq; e0 += kAppendMaxBlocks) {
+    a.app.nent = std::min(kAppendMaxBlocks, nseq - e0);
+    for (int32_t i = 0; i < a.app.nent; ++i) a.app.ent[i] = ents[e0 + i];
+    a.npatch = 0;
+    if (e0 == 0 && carry) {
+      for (const PlanWord& w : s->pending)
+        if (w.word >= limit) return TKV_E_INVAL;
+      a.npatch = static_cast<int32_t>(s->pending.size());
+      std::memcpy(a.patch, s->pending.data(), s->pending.size() * sizeof(PlanWord));
+    }
+    if (launch_decode_prep(c->cfg.dtype, c->cfg.head_dim, a, stream) != hipSuccess) return TKV_E_DEVICE;
+  }
+  if (carry) s->pending.clear();
+  return TKV_OK;
+}
+
 int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
-           const void* q, float* out, void* ws, size_t ws_bytes, void* stream_) {
+           const void* q, float* out, void* ws, size_t ws_bytes, void* stream_,
+           const void* k_new = nullptr, const void* v_new = nullptr) {
   if (!c) return TKV_E_INVAL;
   if (!c->has_pools) return TKV_E_NODEVICE;
   if (layer < 0 || layer >= c->cfg.num_layers) return TKV_E_RANGE;
   if (!seqs || nseq < 1 || !q || !out) return TKV_E_INVAL;
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(ws)) & 15)
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(ws) |
+       reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
     return TKV_E_INVAL;
+  if ((k_new == nullptr) != (v_new == nullptr)) return TKV_E_INVAL;
+  if (k_new) {
+    // every handle once (two writes to one slot would race), and where its
+    // last token lives
+    try {
+      if (c->seen.size() < c->tree.handle_slots()) c->seen.resize(c->tree.handle_slots() * 2, 0);
+      c->app_ents.resize(nseq);
+    } catch (const std::bad_alloc&) {
+      return TKV_E_NOMEM;
+    }
+    const uint64_t stamp = ++c->seen_stamp;
+    for (int32_t i = 0; i < nseq; ++i) {
+      int32_t blk, slot;
+      if (int rc = c->tree.own_last_token(seqs[i], &blk, &slot)) return rc;
+      uint64_t& mark = c->seen[Tree::slot_of(seqs[i])];
+      if (mark == stamp) return TKV_E_INVAL;
+      mark = stamp;
+      c->app_ents[i] = {blk, slot, i, 1};
+    }
+  }
   PlanSlot* s = nullptr;
   if (int rc = find_plan(c, seqs, nq, nseq, &s)) return rc;
   const Plan& P = s->plan;
@@ -305,7 +381,11 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   if (need > 0 && (!ws || ws_bytes < need)) return TKV_E_WORKSPACE;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   DeviceGuard dg(c->device);
-  if (int rc = upload_plan(c, s, stream)) return rc;
+  if (k_new) {
+    if (int rc = prepare_new_tokens(c, s, layer, nseq, k_new, v_new, stream)) return rc;
+  } else if (int rc = upload_plan(c, s, stream)) {
+    return rc;
+  }
 
   const char* dev = static_cast<const char*>(s->dev);
   AttnArgs a{};
@@ -584,6 +664,13 @@ int tkv_workspace_size(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int
 int tkv_attend_decode(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t nseq, const void* q,
                       float* out, void* ws, size_t ws_bytes, void* stream) {
   return attend(c, layer, seqs, nullptr, nseq, q, out, ws, ws_bytes, stream);
+}
+
+int tkv_attend_decode_new_token(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t nseq, const void* k_new,
+                                const void* v_new, const void* q, float* out, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (!k_new || !v_new) return TKV_E_INVAL;
+  return attend(c, layer, seqs, nullptr, nseq, q, out, ws, ws_bytes, stream, k_new, v_new);
 }
 
 int tkv_attend_verify(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,

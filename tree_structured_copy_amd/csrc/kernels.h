@@ -34,6 +34,10 @@ hipError_t launch_plan_patch(int32_t* plan, const PlanWord* words, int32_t n, ui
 // workgroup of 512.
 hipError_t launch_plan_patch_args(const PatchArgs& args, hipStream_t stream);
 
+// A decode step's new tokens of one layer plus its plan's changed words, one
+// launch; grid = (nent + (npatch > 0)) x Hkv.
+hipError_t launch_decode_prep(int dtype, int head_dim, const DecodePrepArgs& args, hipStream_t stream);
+
 // Copy a path's tiles back out in token order; grid = nent x Hkv.
 hipError_t launch_gather(int dtype, int head_dim, const GatherArgs& args, hipStream_t stream);
 

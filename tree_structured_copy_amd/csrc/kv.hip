@@ -26,8 +26,12 @@ struct Elem<4> {
   using T = uint32_t;
 };
 
+// One entry's tokens in one (layer, KV head) tile: source rows [ent.src,
+// ent.src + ent.cnt) of the [L][ntok][Hkv][D] arrays go to slots [ent.slot,
+// ...) of block ent.blk; a fresh block (slot 0) is written whole.  Called by
+// every thread of a 256-thread workgroup.
 template <int EB, int D>
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+__device__ void write_tile(const AppendArgs& a, const AppendEntry ent, int kvh, int layer) {
   using L = Layout<EB>;
   using E = typename Elem<EB>::T;
   constexpr int PC = L::kPerChunk;
@@ -36,9 +40,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   __shared__ __align__(16) E sk[16 * D];
   __shared__ __align__(16) E sv[16 * D];
 
-  const int e = blockIdx.x, kvh = blockIdx.y, layer = blockIdx.z;
   const int tid = threadIdx.x;
-  const AppendEntry ent = a.ent[e];
   const int slot_lo = ent.slot, src0 = ent.src, cnt = ent.cnt;
   const bool fresh = slot_lo == 0;
   if (cnt <= 0 || slot_lo + cnt > 16) return;
@@ -97,6 +99,28 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         vt[ch] = *reinterpret_cast<uint4*>(vals);
       }
     }
+  }
+}
+
+template <int EB, int D>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  write_tile<EB, D>(a, a.ent[blockIdx.x], blockIdx.y, blockIdx.z);
+}
+
+// The new tokens of a decode step in one layer (workgroups x < nent, one per
+// entry and KV head), and the changed words of the call's plan (the
+// workgroup after them, with y = 0): everything the step's attention launch
+// needs written before it, in one launch.
+template <int EB, int D>
+__global__ __launch_bounds__(256) void decode_prep_kernel(DecodePrepArgs a) {
+  if (static_cast<int32_t>(blockIdx.x) < a.app.nent) {
+    write_tile<EB, D>(a.app, a.app.ent[blockIdx.x], blockIdx.y, 0);  // app's pools are the layer's
+    return;
+  }
+  if (blockIdx.y != 0) return;
+  for (int32_t i = static_cast<int32_t>(threadIdx.x); i < a.npatch; i += 256) {
+    const PlanWord w = a.patch[i];
+    if (w.word < a.limit) a.plan[w.word] = w.value;
   }
 }
 
@@ -179,6 +203,20 @@ hipError_t launch_append(int dtype, int head_dim, int32_t layers, const AppendAr
   else if (dtype == 1 && head_dim == 64) hipLaunchKernelGGL((append_kernel<2, 64>), grid, dim3(256), 0, stream, args);
   else if (dtype == 0 && head_dim == 128) hipLaunchKernelGGL((append_kernel<4, 128>), grid, dim3(256), 0, stream, args);
   else if (dtype == 0 && head_dim == 64) hipLaunchKernelGGL((append_kernel<4, 64>), grid, dim3(256), 0, stream, args);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_prep(int dtype, int head_dim, const DecodePrepArgs& args, hipStream_t stream) {
+  if (args.app.nent < 0 || args.app.nent > kAppendMaxBlocks || args.npatch < 0 || args.npatch > kPrepPatchWords)
+    return hipErrorInvalidValue;
+  const int extra = args.npatch > 0 ? 1 : 0;
+  if (args.app.nent + extra == 0) return hipSuccess;
+  const dim3 grid(args.app.nent + extra, args.app.hkv, 1);
+  if (dtype == 1 && head_dim == 128) hipLaunchKernelGGL((decode_prep_kernel<2, 128>), grid, dim3(256), 0, stream, args);
+  else if (dtype == 1 && head_dim == 64) hipLaunchKernelGGL((decode_prep_kernel<2, 64>), grid, dim3(256), 0, stream, args);
+  else if (dtype == 0 && head_dim == 128) hipLaunchKernelGGL((decode_prep_kernel<4, 128>), grid, dim3(256), 0, stream, args);
+  else if (dtype == 0 && head_dim == 64) hipLaunchKernelGGL((decode_prep_kernel<4, 64>), grid, dim3(256), 0, stream, args);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

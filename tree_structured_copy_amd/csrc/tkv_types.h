@@ -137,6 +137,21 @@ struct AppendArgs {
   AppendEntry ent[kAppendMaxBlocks];
 };
 
+// The preparation launch of a decode step that writes its new tokens
+// (tkv_attend_decode_new_token): the tokens of one layer (app: a one-layer
+// source, pools at that layer's base) and up to kPrepPatchWords changed words
+// of the call's plan, all in the kernel's arguments (within the 4 KiB limit).
+constexpr int kPrepPatchWords = 240;
+struct DecodePrepArgs {
+  AppendArgs app;
+  int32_t* plan;
+  int32_t pad0;
+  int32_t npatch;
+  uint32_t limit;
+  int32_t pad;
+  PlanWord patch[kPrepPatchWords];
+};
+
 struct GatherArgs {
   const void* kpool;   // layer base
   const void* vpool;

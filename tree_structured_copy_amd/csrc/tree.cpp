@@ -300,6 +300,17 @@ int Tree::seq_len(tkv_seq s, int64_t* len) const {
   return TKV_OK;
 }
 
+int Tree::own_last_token(tkv_seq s, int32_t* block, int32_t* slot) const {
+  if (!block || !slot) return TKV_E_INVAL;
+  int32_t id;
+  if (int rc = resolve(s, &id)) return rc;
+  const Node& t = nodes_[id];
+  if (t.ntok == 0 || t.frozen) return t.base + t.ntok == 0 ? TKV_E_EMPTY : TKV_E_SHARED;
+  *block = t.blocks.back();
+  *slot = t.tail_valid() - 1;
+  return TKV_OK;
+}
+
 int Tree::block_table(tkv_seq s, int32_t* ids, int32_t* valid, int32_t cap, int32_t* n) const {
   if (!n) return TKV_E_INVAL;
   int32_t tip;

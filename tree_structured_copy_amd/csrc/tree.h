@@ -93,6 +93,10 @@ class Tree {
   void undo_append(tkv_seq s, int32_t ntok, const Placement& pl, bool made_node);
 
   int seq_len(tkv_seq s, int64_t* len) const;
+  // Block and slot of s's last token when it lies in s's own tip node (never
+  // forked, so no other handle shares it); TKV_E_EMPTY if s has no token,
+  // TKV_E_SHARED if its last token is shared with other branches.
+  int own_last_token(tkv_seq s, int32_t* block, int32_t* slot) const;
   int block_table(tkv_seq s, int32_t* ids, int32_t* valid, int32_t cap, int32_t* n) const;
   int block_refcounts(int32_t* rc) const;
   int block_refcount(int32_t b, int32_t* rc) const;

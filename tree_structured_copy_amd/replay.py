@@ -71,6 +71,9 @@ class LibReplay:
                 k = wdev.kv_tensor(self.wl, call, total, gen.KIND_K, self.device)
                 v = wdev.kv_tensor(self.wl, call, total, gen.KIND_V, self.device)
                 tkv.tkv_append_batch(self.c, seqs, ns, k, v, torch.cuda.current_stream())
+        elif kind == "reserve_batch":
+            _, hs, call = op
+            tkv.tkv_append_batch(self.c, [self.h[h] for h in hs], [1] * len(hs))
         elif kind == "fork":
             _, h, n, kids = op
             for name, s in zip(kids, tkv.tkv_fork(self.c, self.h[h], n)):
@@ -80,7 +83,7 @@ class LibReplay:
         elif kind == "truncate":
             _, h, L = op
             tkv.tkv_truncate(self.c, self.h[h], L)
-        elif kind in ("decode", "verify", "time_begin"):
+        elif kind in ("decode", "decode_new", "verify", "time_begin"):
             pass
         else:
             raise ValueError(kind)
@@ -88,7 +91,7 @@ class LibReplay:
     def build(self, stop_at_attend: bool = True):
         """Apply ops up to (not including) the first decode/verify; returns its index."""
         for i, op in enumerate(self.wl.ops):
-            if stop_at_attend and op[0] in ("decode", "verify"):
+            if stop_at_attend and op[0] in ("decode", "decode_new", "verify"):
                 return i
             self.apply(op)
         return len(self.wl.ops)
@@ -98,7 +101,7 @@ class LibReplay:
         return [self.h[x] for x in op[2]]
 
     def nrows(self, op) -> int:
-        return len(op[2]) if op[0] == "decode" else sum(op[3])
+        return sum(op[3]) if op[0] == "verify" else len(op[2])
 
     def workspace(self, op):
         import torch
@@ -123,6 +126,12 @@ class LibReplay:
         stream = torch.cuda.current_stream()
         if op[0] == "decode":
             tkv.tkv_attend_decode(self.c, op[1], self.handles(op), q, out, ws, need, stream)
+        elif op[0] == "decode_new":
+            # the reserved tokens' K/V of this layer: rows of batched append call op[3]
+            from workloads import gen
+            k = wdev.kv_tensor(wl, op[3], rows, gen.KIND_K, self.device)[op[1]].contiguous()
+            v = wdev.kv_tensor(wl, op[3], rows, gen.KIND_V, self.device)[op[1]].contiguous()
+            tkv.tkv_attend_decode_new_token(self.c, op[1], self.handles(op), k, v, q, out, ws, need, stream)
         else:
             tkv.tkv_attend_verify(self.c, op[1], self.handles(op), op[3], q, out, ws, need, stream)
         return out

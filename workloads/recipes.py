@@ -18,6 +18,11 @@ Operations:
 * ``("fork", h, n, [c0, ..., c(n-1)])``   -- n children of ``h``; ``h`` stays live
 * ``("release", h)``
 * ``("truncate", h, new_len)``
+* ``("reserve_batch", [h...], call)``     -- one token per (distinct) handle, slots only;
+  its K/V are those of a batched append ``call`` of one token per handle, written
+  layer by layer by the ``decode_new`` ops that follow
+* ``("decode_new", layer, [h...], call, qcall)`` -- write layer ``layer`` of those
+  tokens' K/V and decode, in one call (``tkv_attend_decode_new_token``)
 * ``("time_begin",)``                     -- no effect on the cache: where a timed
   replay of a loop starts (after its set-up)
 * ``("decode", layer, [h...], qcall)``    -- one query per handle; Q from stream
@@ -63,7 +68,7 @@ class Workload:
         return 4 if self.dtype == "f32" else 2
 
     def attend_ops(self):
-        return [op for op in self.ops if op[0] in ("decode", "verify")]
+        return [op for op in self.ops if op[0] in ("decode", "decode_new", "verify")]
 
 
 class _Names:
@@ -209,7 +214,8 @@ def verify_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_hea
 def decode_loop_workload(name: str, *, dtype: str = "bf16", layers: int = 1, q_heads: int = 8,
                          kv_heads: int = 2, head_dim: int = 128, requests: int = 3, prefix: int = 40,
                          width: int = 3, branch_tokens: int = 5, rounds: int = 20, verify_nq: int = 0,
-                         batched: bool = True, seed: int = 0, description: str = "") -> Workload:
+                         batched: bool = True, fused: bool = False, seed: int = 0,
+                         description: str = "") -> Workload:
     """A generation loop over the fork workload's tree: per request, P = new;
     append(P, prefix); C = fork(P, width); release(P); append(C[b],
     branch_tokens).  Then ``rounds`` rounds of: append one token to each branch
@@ -217,7 +223,9 @@ def decode_loop_workload(name: str, *, dtype: str = "bf16", layers: int = 1, q_h
     over all branches and every layer -- a decode, or with ``verify_nq`` > 0 a
     verify of each branch's last ``verify_nq`` tokens.  Most rounds' tokens fit
     in the branches' last blocks; now and then one opens a block.  A round's
-    appends are one ``append_batch`` (``batched``) or one ``append`` each."""
+    appends are one ``append_batch`` (``batched``) or one ``append`` each.
+    With ``fused`` (decode only) every branch gets a token each round, reserved
+    by one ``reserve_batch`` and written layer by layer by ``decode_new``."""
     nm = _Names()
     ops: List[tuple] = []
     call = 0
@@ -234,6 +242,13 @@ def decode_loop_workload(name: str, *, dtype: str = "bf16", layers: int = 1, q_h
         leaves.extend(kids)
     qcall = 0
     for r in range(rounds):
+        if fused:
+            ops.append(("reserve_batch", list(leaves), call))
+            for layer in range(layers):
+                ops.append(("decode_new", layer, list(leaves), call, qcall))
+                qcall += 1
+            call += 1
+            continue
         grow = [c for b, c in enumerate(leaves) if (r + b) % 3 != 2]
         if batched:
             ops.append(("append_batch", grow, [1] * len(grow), call)); call += 1
