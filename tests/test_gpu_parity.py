@@ -511,3 +511,13 @@ def test_decode_with_new_token_refusals():
         torch.cuda.synchronize()
     finally:
         tkv.tkv_destroy(c)
+
+
+def test_decode_with_new_token_more_than_128_handles():
+    """135 branches in one fused decode call: its tokens are written by two
+    preparation launches (128 + 7), the first also carrying the plan's changed
+    words.  Every call matches the oracle."""
+    wl = recipes.decode_loop_workload("fused_wide", requests=45, width=3, branch_tokens=14, rounds=4, fused=True,
+                                      seed=83)
+    assert len(wl.attend_ops()[0][2]) == 135
+    assert_close(run_both(wl), wl.dtype)
