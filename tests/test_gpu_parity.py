@@ -425,8 +425,9 @@ def test_loop_recipes_match_oracle(kind):
     assert_close(res, wl.dtype)
 
 
-@pytest.mark.parametrize("dtype,layers", [("bf16", 1), ("bf16", 2), ("f32", 1)])
-def test_decode_with_new_token_written_in_the_call(dtype, layers):
+@pytest.mark.parametrize("dtype,layers,head_dim", [("bf16", 1, 128), ("bf16", 2, 128), ("f32", 1, 64),
+                                                   ("bf16", 1, 64), ("f32", 2, 128)])
+def test_decode_with_new_token_written_in_the_call(dtype, layers, head_dim):
     """The fused decode step: each round reserves one token per branch
     (tkv_append_batch without K/V), then per layer tkv_attend_decode_new_token
     writes that layer's K/V of the token and decodes.  Every call matches the
@@ -436,8 +437,8 @@ def test_decode_with_new_token_written_in_the_call(dtype, layers):
     from tree_structured_copy_amd import tkv
     from tree_structured_copy_amd.replay import LibReplay
     import dataclasses
-    wl = recipes.decode_loop_workload("fused_%s_%d" % (dtype, layers), dtype=dtype, layers=layers,
-                                      head_dim=128 if dtype == "bf16" else 64, rounds=14, fused=True, seed=81)
+    wl = recipes.decode_loop_workload("fused_%s_%d_%d" % (dtype, layers, head_dim), dtype=dtype, layers=layers,
+                                      head_dim=head_dim, rounds=14, fused=True, seed=81)
     assert_close(run_both(wl), wl.dtype)
     plain_ops = []
     for op in wl.ops:
