@@ -266,12 +266,18 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       g.nq = n;
       g.min_pos = INT32_MAX;
       g.pad1 = 0;
+      // sized once, then written: element-wise push_back costs several times more
+      const size_t at0 = P.gq.size();
+      P.gq.resize(at0 + n);
+      P.gqpos.resize(at0 + n);
+      P.gq_node.resize(at0 + n);
+      P.gq_back.resize(at0 + n);
       for (int32_t j = 0; j < n; ++j) {
         const int32_t q = qs[j].global;
-        P.gq.push_back(q);
-        P.gqpos.push_back(qs[j].pos);
-        P.gq_node.push_back(S.tip[qs[j].handle]);
-        P.gq_back.push_back(static_cast<int32_t>(S.len[qs[j].handle] - qs[j].pos));
+        P.gq[at0 + j] = q;
+        P.gqpos[at0 + j] = qs[j].pos;
+        P.gq_node[at0 + j] = S.tip[qs[j].handle];
+        P.gq_back[at0 + j] = static_cast<int32_t>(S.len[qs[j].handle] - qs[j].pos);
         g.min_pos = std::min(g.min_pos, qs[j].pos);
         const int32_t at = 2 * q + S.qm_n[q]++;
         S.qm_g[at] = gi;
@@ -287,15 +293,19 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     auto emit_node = [&](int32_t k, uint64_t m) {
       const Node& nd = tree.node(S.lnode[k]);
       const int32_t nb = static_cast<int32_t>(nd.blocks.size());
+      const size_t at = P.blocks.size();
+      P.blocks.resize(at + nb);
+      DevBlock* out = P.blocks.data() + at;
+      const int32_t* ids = nd.blocks.data();
+      const int32_t pos0 = static_cast<int32_t>(nd.base);
       for (int32_t b = 0; b < nb; ++b) {
-        DevBlock e;
-        e.id = nd.blocks[b];
-        e.pos = static_cast<int32_t>(nd.base + 16 * (int64_t)b);
-        e.valid = (b == nb - 1) ? nd.tail_valid() : 16;
-        e.pad = 0;
-        e.mask = m;
-        P.blocks.push_back(e);
+        out[b].id = ids[b];
+        out[b].pos = pos0 + 16 * b;
+        out[b].valid = 16;
+        out[b].pad = 0;
+        out[b].mask = m;
       }
+      if (nb > 0) out[nb - 1].valid = nd.tail_valid();
       if (!nd.frozen && nb > 0) {
         P.tail_entry.push_back(static_cast<int32_t>(P.blocks.size()) - 1);
         P.tail_node.push_back(S.lnode[k]);
@@ -325,27 +335,45 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
         }
       std::sort(touched.begin(), touched.end(), [&](int32_t a, int32_t b) { return S.pre[a] < S.pre[b]; });
       bool cascade = false;
+      const int32_t ntouch = static_cast<int32_t>(touched.size());
       if (opt.cascade && (n * q_per_kv + 15) / 16 >= 8 && n > sub) {
+        // each node's subgroup (or -1) once, and the narrow nodes bucketed by
+        // subgroup in touched order
+        const int32_t nsub = (n + sub - 1) / sub;
+        S.nar.resize(ntouch);
+        S.sbeg.assign(nsub + 1, 0);
         int64_t all = 0, thin = 0;
-        for (int32_t k : touched) {
+        for (int32_t i = 0; i < ntouch; ++i) {
+          const int32_t k = touched[i];
           const int64_t nb = static_cast<int64_t>(tree.node(S.lnode[k]).blocks.size());
+          S.nar[i] = narrow(mask[k]);
           all += nb;
-          if (narrow(mask[k]) >= 0) thin += nb;
+          if (S.nar[i] >= 0) {
+            thin += nb;
+            ++S.sbeg[S.nar[i] + 1];
+          }
         }
         cascade = thin * 8 >= all && thin > 0;
+        if (cascade) {
+          for (int32_t t = 0; t < nsub; ++t) S.sbeg[t + 1] += S.sbeg[t];
+          S.cursor.assign(S.sbeg.begin(), S.sbeg.end() - 1);
+          S.sorder.resize(S.sbeg[nsub]);
+          for (int32_t i = 0; i < ntouch; ++i)
+            if (S.nar[i] >= 0) S.sorder[S.cursor[S.nar[i]]++] = i;
+        }
       }
       emit_group(qs, n, S.groot[g0], cascade);
-      for (int32_t k : touched)
-        if (!cascade || narrow(mask[k]) < 0) emit_node(k, mask[k]);
+      for (int32_t i = 0; i < ntouch; ++i)
+        if (!cascade || S.nar[i] < 0) emit_node(touched[i], mask[touched[i]]);
       close_group();
       if (cascade) {
         for (int32_t t = 0; t * sub < n; ++t) {
-          bool any = false;
-          for (int32_t k : touched) any |= narrow(mask[k]) == t;
-          if (!any) continue;
+          if (S.sbeg[t + 1] == S.sbeg[t]) continue;
           emit_group(qs + t * sub, std::min(sub, n - t * sub), S.groot[g0], true);
-          for (int32_t k : touched)
-            if (narrow(mask[k]) == t) emit_node(k, mask[k] >> (t * sub));
+          for (int32_t x = S.sbeg[t]; x < S.sbeg[t + 1]; ++x) {
+            const int32_t k = touched[S.sorder[x]];
+            emit_node(k, mask[k] >> (t * sub));
+          }
           close_group();
         }
       }

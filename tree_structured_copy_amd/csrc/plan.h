@@ -95,6 +95,9 @@ struct PlanScratch {
   std::vector<int32_t> ub, gbeg, gsize, groot;
   std::vector<uint64_t> mask;
   std::vector<int32_t> touched;
+  // cascade: each touched node's one-tile subgroup (or -1); the narrow nodes
+  // by subgroup (sorder[sbeg[t] .. sbeg[t + 1]), indices into touched)
+  std::vector<int32_t> nar, sbeg, sorder;
   std::vector<uint8_t> emitted;
   std::vector<int32_t> go_begin, go_count, go_root;
   std::vector<uint8_t> go_partials;
