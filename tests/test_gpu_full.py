@@ -86,3 +86,19 @@ def test_longest_lds_staged_item(kind):
     s = _sampler(64, seed=5)
     s.heads = wl.q_heads
     assert_close(run_both(wl, sample=s, options={tkv.TKV_OPT_TARGET_WGS: 2}), wl.dtype)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_fork_workload_decode_loop_sampled(fused):
+    """The decode loop bench.py times, at the fork workload's full size (32
+    requests x 4096-token prefix forked 4 ways, 64 tokens per branch; GQA 32/8,
+    d = 128, bf16), for 3 rounds of one token per branch -- appended in a batch
+    then decoded, or reserved and written inside the decode call -- with plans
+    updated in place between rounds.  Sampled against the oracle."""
+    wl = recipes.decode_loop_workload("llama_loop", layers=1, q_heads=32, kv_heads=8, head_dim=128, requests=32,
+                                      prefix=4096, width=4, branch_tokens=64, rounds=3, fused=fused, seed=91)
+    s = _sampler(24, seed=7)
+    s.heads = wl.q_heads
+    res = run_both(wl, sample=s)
+    assert len(res) == 3
+    assert_close(res, wl.dtype)
