@@ -111,7 +111,7 @@ int tkv_release(tkv_cache* c, tkv_seq s);
 int tkv_append(tkv_cache* c, tkv_seq s, int32_t ntok, const void* k, const void* v, void* stream);
 
 /* Append ntok[i] >= 1 tokens to each of nseq >= 1 distinct handles seqs[i] in one
- * call (one kernel launch per 128 blocks written): the same as tkv_append on each
+ * call (one kernel launch per 240 blocks written): the same as tkv_append on each
  * handle in batch order, with k, v device arrays [num_layers][sum ntok][Hkv][head_dim]
  * holding the handles' tokens one after another in batch order.  k = v = NULL
  * reserves the slots only.  All or nothing: a stale handle (TKV_E_BADSEQ), a count

@@ -199,7 +199,7 @@ def test_gather_returns_appended_kv_exactly():
 
 def test_append_batch_writes_what_the_appends_write():
     """tkv_append_batch over a random session's live handles (1 to 40 tokens
-    each, three times, then one batch of more than 128 blocks, which takes two
+    each, three times, then one batch of more than 240 blocks, which takes two
     launches) leaves in the pool exactly the K/V of the oracle's history, which
     appends to each handle in batch order."""
     import dataclasses
@@ -215,9 +215,9 @@ def test_append_batch_writes_what_the_appends_write():
         rng = np.random.default_rng(seed)
         for r in range(3):
             ops.append(("append_batch", list(live), [int(x) for x in rng.integers(1, 41, len(live))], 9000 + r))
-        big = -(-130 // len(live)) * 16 + 5
+        big = -(-250 // len(live)) * 16 + 5
         ops.append(("append_batch", list(live), [big] * len(live), 9003))
-        wl = dataclasses.replace(base, ops=ops, num_blocks=base.num_blocks + 400 + 3 * 4 * len(live))
+        wl = dataclasses.replace(base, ops=ops, num_blocks=base.num_blocks + 700 + 3 * 4 * len(live))
         say("append_batch seed %d %s: %d handles, last batch %d tokens each" % (seed, dtype, len(live), big))
         lib, orc = LibReplay(wl), OracleReplay(wl)
         try:

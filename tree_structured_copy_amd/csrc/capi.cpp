@@ -634,7 +634,7 @@ int tkv_append_batch(tkv_cache* c, const tkv_seq* seqs, const int32_t* ntok, int
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   DeviceGuard dg(c->device);
   const int32_t nent = static_cast<int32_t>(ents.size());
-  for (int32_t e0 = 0; e0 < nent; e0 += kAppendMaxBlocks) {
+  for (int32_t e0 = 0; e0 < nent; e0 += kAppendWideBlocks) {
     AppendArgs a{};
     a.src_k = k;
     a.src_v = v;
@@ -643,7 +643,7 @@ int tkv_append_batch(tkv_cache* c, const tkv_seq* seqs, const int32_t* ntok, int
     a.layer_stride = static_cast<int64_t>(c->layer_elems());
     a.ntok = src;
     a.hkv = c->cfg.num_kv_heads;
-    a.nent = std::min(kAppendMaxBlocks, nent - e0);
+    a.nent = std::min(kAppendWideBlocks, nent - e0);
     for (int32_t i = 0; i < a.nent; ++i) a.ent[i] = ents[e0 + i];
     if (launch_append(c->cfg.dtype, c->cfg.head_dim, c->cfg.num_layers, a, stream) != hipSuccess) {
       undo(nseq);

@@ -30,8 +30,8 @@ struct Elem<4> {
 // ent.src + ent.cnt) of the [L][ntok][Hkv][D] arrays go to slots [ent.slot,
 // ...) of block ent.blk; a fresh block (slot 0) is written whole.  Called by
 // every thread of a 256-thread workgroup.
-template <int EB, int D>
-__device__ void write_tile(const AppendArgs& a, const AppendEntry ent, int kvh, int layer) {
+template <int EB, int D, class Args>
+__device__ void write_tile(const Args& a, const AppendEntry ent, int kvh, int layer) {
   using L = Layout<EB>;
   using E = typename Elem<EB>::T;
   constexpr int PC = L::kPerChunk;

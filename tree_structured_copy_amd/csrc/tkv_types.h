@@ -10,7 +10,8 @@ constexpr int kMaxGroupQueries = 64; // one bit per query in a block's visibilit
 constexpr int kKernelClasses = 6;   // A1, A2 (attn.hip), B4, B6, B8, B16 (attn_rows.hip)
 constexpr int kRowsMaxItemBlocks = 1024;  // longest block list of one attn_rows.hip work item (16 KiB of LDS)
 constexpr int kMaxPoolBlocks = 1 << 27;   // block ids fit 27 bits (attn_rows.hip packs the valid count beside them)
-constexpr int kAppendMaxBlocks = 128;
+constexpr int kAppendMaxBlocks = 128;   // blocks per decode-step preparation launch
+constexpr int kAppendWideBlocks = 240;  // blocks per plain append launch
 constexpr int kGatherMaxBlocks = 64;
 
 // A query group: up to kMaxRows rows that share one pass over the union of
@@ -124,7 +125,10 @@ struct AppendEntry {
   int32_t cnt;
 };
 
-struct AppendArgs {
+// An append launch: the source arrays, the pools and up to N blocks to write
+// (in the kernel's arguments).
+template <int N>
+struct AppendArgsN {
   const void* src_k;   // [L][ntok][Hkv][D]
   const void* src_v;
   void* kpool;         // pool base (layer 0)
@@ -134,8 +138,13 @@ struct AppendArgs {
   int32_t hkv;
   int32_t nent;        // blocks in this launch
   int32_t pad[3];
-  AppendEntry ent[kAppendMaxBlocks];
+  AppendEntry ent[N];
 };
+// a plain append launch: as many blocks as the 4 KiB argument limit allows
+using AppendArgs = AppendArgsN<kAppendWideBlocks>;
+// the blocks part of a decode step's preparation launch, which also carries
+// the plan's changed words
+using PrepAppendArgs = AppendArgsN<kAppendMaxBlocks>;
 
 // The preparation launch of a decode step that writes its new tokens
 // (tkv_attend_decode_new_token): the tokens of one layer (app: a one-layer
@@ -143,7 +152,7 @@ struct AppendArgs {
 // of the call's plan, all in the kernel's arguments (within the 4 KiB limit).
 constexpr int kPrepPatchWords = 240;
 struct DecodePrepArgs {
-  AppendArgs app;
+  PrepAppendArgs app;
   int32_t* plan;
   int32_t pad0;
   int32_t npatch;
