@@ -225,11 +225,11 @@ int tkv_plan_info_get(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int3
 enum {
   TKV_OPT_TARGET_WGS = 1,   /* workgroups an attention call aims for (default: the device's CU count) */
   TKV_OPT_MIN_CHUNK = 2,    /* fewest blocks per work item (default 32) */
-  TKV_OPT_MAX_ROWS = 3,     /* max rows (queries x Hq/Hkv) per group: 16..256 (default 256) */
+  TKV_OPT_MAX_ROWS = 3,     /* max rows (queries x Hq/Hkv) per group: 16..256 (default 128) */
   TKV_OPT_PLAN_CACHE = 4,   /* 1 = reuse uploaded plans while the tree is unchanged (default) */
   TKV_OPT_WAVES = 5,        /* waves per one/two-tile workgroup: 2, 4 or 8 (0 = by launch size) */
   TKV_OPT_CASCADE = 6,      /* 1 = a group of 8+ row tiles hands blocks that only one row tile's
-                               queries see to one-tile subgroups, merged after (default); 0 = off */
+                               queries see to one-tile subgroups, merged after; 0 = off (default) */
   TKV_OPT_CONCURRENT = 7,   /* how a call's kernel classes run: 0 = one after another on the call's
                                stream (default); 1 = at once, on side streams of the library's own
                                forked from and joined back to the call's stream */

@@ -68,7 +68,9 @@ def test_extreme_shapes_sampled(case):
                                    root_tokens=300, branching=4, depth=5, leaves=128, node_tokens=16, seed=54)
     s = _sampler(64, seed=3)
     s.heads = wl.q_heads
-    assert_close(run_both(wl, sample=s), wl.dtype)
+    # the search tree at GQA 8 runs with 16-tile groups and the cascade on (subgroups of 2 queries)
+    opts = {3: 256, 6: 1} if case == "gqa8_tree" else None
+    assert_close(run_both(wl, sample=s, options=opts), wl.dtype)
 
 
 @pytest.mark.parametrize("kind", ["decode", "verify"])

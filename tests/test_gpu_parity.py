@@ -56,6 +56,7 @@ def test_mcts_cascade(cascade, dtype, hq, hkv, d):
     need_gpu()
     lib = LibReplay(wl)
     try:
+        tkv.tkv_set_option(lib.c, tkv.TKV_OPT_MAX_ROWS, 256)
         tkv.tkv_set_option(lib.c, tkv.TKV_OPT_CASCADE, cascade)
         i = lib.build()
         op = wl.ops[i]
@@ -68,7 +69,7 @@ def test_mcts_cascade(cascade, dtype, hq, hkv, d):
             assert ipk[0] == 0, info
     finally:
         lib.close()
-    assert_close(run_both(wl, options={6: cascade}), dtype)
+    assert_close(run_both(wl, options={3: 256, 6: cascade}), dtype)
 
 
 @pytest.mark.parametrize("mode", [0, 1])

@@ -631,16 +631,17 @@ def test_plan_cascade_shapes():
     twice more than before), one-tile items; the fork and verify workloads,
     whose groups are small or whose blocks are all wide, are unchanged."""
     wl = recipes.mcts_tree()
-    on = _host_plan(wl, [(tkv.TKV_OPT_TARGET_WGS, 256)])
-    off = _host_plan(wl, [(tkv.TKV_OPT_TARGET_WGS, 256), (tkv.TKV_OPT_CASCADE, 0)])
+    big = [(tkv.TKV_OPT_TARGET_WGS, 256), (tkv.TKV_OPT_MAX_ROWS, 256)]
+    on = _host_plan(wl, big + [(tkv.TKV_OPT_CASCADE, 1)])
+    off = _host_plan(wl, big + [(tkv.TKV_OPT_CASCADE, 0)])
     assert on["block_entries"] == off["block_entries"]
     assert on["unique_blocks"] == off["unique_blocks"]
     assert on["groups"] > off["groups"]
     assert on["items_per_kernel"][0] > 0 and off["items_per_kernel"][0] == 0
     for name in ("llama_fork", "spec_verify"):
         w = recipes.STANDARD[name]()
-        a = _host_plan(w, [(tkv.TKV_OPT_TARGET_WGS, 256)])
-        b = _host_plan(w, [(tkv.TKV_OPT_TARGET_WGS, 256), (tkv.TKV_OPT_CASCADE, 0)])
+        a = _host_plan(w, big + [(tkv.TKV_OPT_CASCADE, 1)])
+        b = _host_plan(w, big + [(tkv.TKV_OPT_CASCADE, 0)])
         assert a == b, name
         assert a["partial_slots"] == 0
 
@@ -656,13 +657,22 @@ def test_plan_classes_fill_one_round():
     for name, ipk in expect.items():
         info = _host_plan(recipes.STANDARD[name](), [(tkv.TKV_OPT_TARGET_WGS, 256)])
         assert info["items_per_kernel"] == ipk, (name, info)
+    # the search tree with the defaults: groups of 32 leaves (8 row tiles), one
+    # launch of the 8-tile shape, cut to two workgroups per CU
     info = _host_plan(recipes.mcts_tree(), [(tkv.TKV_OPT_TARGET_WGS, 256)])
+    ipk = info["items_per_kernel"]
+    assert ipk == [0, 0, 0, 0, 60, 0], info
+    assert ipk[4] * 8 <= 2 * 256
+    # with 16-tile groups and the cascade: 30 shared items (240 workgroups) plus
+    # the one-tile subgroups
+    big = [(tkv.TKV_OPT_MAX_ROWS, 256), (tkv.TKV_OPT_CASCADE, 1)]
+    info = _host_plan(recipes.mcts_tree(), [(tkv.TKV_OPT_TARGET_WGS, 256)] + big)
     ipk = info["items_per_kernel"]
     assert ipk[0] == 65 and ipk[5] == 30 and sum(ipk[1:5]) == 0, info
     assert ipk[5] * 8 <= 256
     # twice the workgroups asked for: the shared groups are cut about twice as
     # fine, still within one round
-    info2 = _host_plan(recipes.mcts_tree(), [(tkv.TKV_OPT_TARGET_WGS, 512)])
+    info2 = _host_plan(recipes.mcts_tree(), [(tkv.TKV_OPT_TARGET_WGS, 512)] + big)
     assert 2 * ipk[5] <= info2["items_per_kernel"][5] and info2["items_per_kernel"][5] * 8 <= 512, info2
 
 
@@ -670,7 +680,8 @@ def test_plan_small_lds_class_joins_the_largest():
     """An LDS-staged class with less work than the largest one present runs in
     the largest one's kernel: the search tree's one 8-tile group (30 queries)
     joins its 16-tile groups; a workload with only 8-tile groups keeps them."""
-    on = _host_plan(recipes.mcts_tree(), [(tkv.TKV_OPT_TARGET_WGS, 256)])
+    on = _host_plan(recipes.mcts_tree(), [(tkv.TKV_OPT_TARGET_WGS, 256), (tkv.TKV_OPT_MAX_ROWS, 256),
+                                          (tkv.TKV_OPT_CASCADE, 1)])
     assert on["items_per_kernel"][4] == 0 and on["items_per_kernel"][5] > 0
     wl = recipes.fork_workload("eight", dtype="bf16", layers=1, q_heads=32, kv_heads=8, head_dim=128,
                                requests=2, prefix=300, width=30, branch_tokens=5, seed=3)

@@ -26,8 +26,14 @@ namespace tkv {
 struct PlanOptions {
   int32_t target_wgs = 256;
   int32_t min_chunk = 32;
-  int32_t max_rows = kMaxRows;
-  int32_t cascade = 1;  // split narrow blocks of large groups into one-tile subgroups
+  // Groups of at most 128 rows (8 row tiles) by default: a search tree's
+  // leaves then run in one launch of the 8-tile shape, two workgroups per CU,
+  // each group reading its private nodes with the shared ones; this measured
+  // faster than 16-tile groups with their narrow nodes moved to one-tile
+  // subgroups (the cascade, kept as an option) on every search-tree shape
+  // tried, and the same on the fork and verify workloads.
+  int32_t max_rows = 128;
+  int32_t cascade = 0;  // split narrow blocks of large groups into one-tile subgroups
 };
 
 struct Plan {
