@@ -523,3 +523,28 @@ def test_decode_with_new_token_more_than_128_handles():
                                       seed=83)
     assert len(wl.attend_ops()[0][2]) == 135
     assert_close(run_both(wl), wl.dtype)
+
+
+@pytest.mark.parametrize("concurrent", [0, 1])
+def test_search_tree_decode_loop_with_cascade(concurrent):
+    """A search tree (64 leaves, 256-row groups with the cascade: a one-tile
+    class and a 16-tile class, run one after another or on side streams),
+    then 6 rounds of one token appended to every leaf and a decode of all
+    leaves: the plan is updated in place across both classes.  Every call
+    matches the oracle."""
+    import dataclasses
+    from tree_structured_copy_amd import tkv
+    base = recipes.mcts_workload("mcts_loop_cascade", q_heads=8, kv_heads=2, root_tokens=70, branching=4, depth=5,
+                                 leaves=64, node_tokens=9, seed=47)
+    dec = base.ops[-1]
+    assert dec[0] == "decode"
+    leaves = dec[2]
+    ops = list(base.ops)
+    for r in range(6):
+        ops.append(("append_batch", list(leaves), [1] * len(leaves), 5000 + r))
+        ops.append(("decode", 0, list(leaves), 100 + r))
+    wl = dataclasses.replace(base, ops=ops, num_blocks=base.num_blocks + len(leaves))
+    res = run_both(wl, options={tkv.TKV_OPT_MAX_ROWS: 256, tkv.TKV_OPT_CASCADE: 1,
+                                tkv.TKV_OPT_CONCURRENT: concurrent})
+    assert len(res) == 7
+    assert_close(res, wl.dtype)
