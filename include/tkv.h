@@ -224,7 +224,9 @@ int tkv_plan_info_get(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int3
 /* ---- tuning knobs (keys) ---- */
 enum {
   TKV_OPT_TARGET_WGS = 1,   /* workgroups an attention call aims for (default: the device's CU count) */
-  TKV_OPT_MIN_CHUNK = 2,    /* fewest blocks per work item (default 32) */
+  TKV_OPT_MIN_CHUNK = 2,    /* fewest blocks per split-K work item (default 32; a quarter of it for
+                               groups of 3+ row tiles); a call too small to fill the GPU at that
+                               size is cut into items of at least 4 blocks instead */
   TKV_OPT_MAX_ROWS = 3,     /* max rows (queries x Hq/Hkv) per group: 16..256 (default 128) */
   TKV_OPT_PLAN_CACHE = 4,   /* 1 = reuse uploaded plans while the tree is unchanged (default) */
   TKV_OPT_WAVES = 5,        /* waves per one/two-tile workgroup: 2, 4 or 8 (0 = by launch size) */
