@@ -433,7 +433,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--all", action="store_true", help="also measure the 32-layer workload")
     ap.add_argument("--cpu-requests", type=int, default=32)
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=7)
     ap.add_argument("--counters", action="store_true",
                     help="a short run for rocprofv3 --pmc passes: a plain 1 GiB streaming kernel (the "
                          "counters' calibration), then 8 steps of --counters-workload")
