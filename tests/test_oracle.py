@@ -201,6 +201,34 @@ def test_fork_does_not_change_prefix_output():
     np.testing.assert_array_equal(before, after)
 
 
+def test_branch_kv_is_its_path_and_identical_siblings_agree():
+    """A branch's materialised K/V is its ancestors' tokens followed by its own, in order
+    (written out by hand over a two-level fork); siblings given identical tokens give
+    identical outputs, and a sibling given other tokens does not."""
+    r = _rng(9)
+    mc = MaterializedCache()
+    root = mc.seq_new()
+    pk, pv = r.standard_normal((1, 19, 2, 8)), r.standard_normal((1, 19, 2, 8))
+    mc.append(root, ArraySource(pk, pv))
+    a, b, c = mc.fork(root, 3)
+    sk, sv = r.standard_normal((1, 6, 2, 8)), r.standard_normal((1, 6, 2, 8))
+    for h in (a, b):
+        mc.append(h, ArraySource(sk.copy(), sv.copy()))
+    mc.append(c, ArraySource(r.standard_normal((1, 6, 2, 8)), r.standard_normal((1, 6, 2, 8))))
+    (g,) = mc.fork(a, 1)
+    gk, gv = r.standard_normal((1, 3, 2, 8)), r.standard_normal((1, 3, 2, 8))
+    mc.append(g, ArraySource(gk, gv))
+    for head in range(2):
+        K, V = mc.kv(g, 0, head)
+        np.testing.assert_array_equal(K, np.concatenate([pk[0, :, head], sk[0, :, head], gk[0, :, head]]))
+        np.testing.assert_array_equal(V, np.concatenate([pv[0, :, head], sv[0, :, head], gv[0, :, head]]))
+    q = r.standard_normal((4, 8))
+    out = {h: attention.decode(*(np.stack([mc.kv(h, 0, k)[i] for k in range(2)], axis=1) for i in (0, 1)), q, 2)
+           for h in (a, b, c)}
+    np.testing.assert_array_equal(out[a], out[b])
+    assert np.abs(out[a] - out[c]).max() > 1e-3
+
+
 # ---------------------------------------------------------------------------
 # planted mistakes: each must be caught by at least one pin
 
