@@ -707,3 +707,15 @@ def test_empty_batch_and_query_counts_rejected():
         assert tkv.tkv_workspace_size(c, [s], [20]) >= 0  # all 20 positions as queries is fine
     finally:
         tkv.tkv_destroy(c)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits non-zero with a message, before
+    touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+    assert r.stdout.strip() == "" or not r.stdout.strip().startswith("{")
