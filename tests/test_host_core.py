@@ -719,3 +719,21 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
     assert r.stdout.strip() == "" or not r.stdout.strip().startswith("{")
+
+
+def test_binding_fails_loudly_without_the_library():
+    """With libtkv.so absent, importing the binding raises ImportError naming the
+    library: there is no fallback path."""
+    import subprocess
+    import sys
+    code = ("import os, sys\n"
+            "real = os.path.exists\n"
+            "os.path.exists = lambda p: False if str(p).endswith('libtkv.so') else real(p)\n"
+            "try:\n"
+            "    import tree_structured_copy_amd.tkv\n"
+            "except ImportError as e:\n"
+            "    print('refused:', e); sys.exit(0)\n"
+            "sys.exit(3)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "libtkv.so is not built" in r.stdout
