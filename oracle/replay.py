@@ -8,6 +8,8 @@ sample of (query row, head) pairs.
 
 from __future__ import annotations
 
+import threading
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, Iterable, Optional
 
 import numpy as np
@@ -20,29 +22,76 @@ from .allocator import FlatAllocator
 from .cache import FunctionSource, MaterializedCache
 
 
-def _source_for(wl, call: int, ntok: int):
-    def fn(which, layer, kvh, t0, t1):
-        kind = gen.KIND_K if which == "k" else gen.KIND_V
-        return workloads.kv_slice(wl, call, ntok, kind, layer, kvh, t0, t1)
-    return FunctionSource(ntok, fn)
+class _LayerArrays:
+    """The values of append calls, one layer at a time: each (call, K | V, layer)
+    is generated once, as the contiguous range of the call's stream that holds
+    that layer ([layers][ntok][kv_heads][d] order), and kept until a different
+    layer is asked for.  The same numbers as ``workloads.kv_slice``, generated
+    in bulk (and by several threads) for checks that read whole layers."""
+
+    def __init__(self, wl, threads: int):
+        self.wl = wl
+        self.threads = max(1, threads)
+        self.layer = None
+        self.arrays: Dict[tuple, np.ndarray] = {}
+        self.lock = threading.Lock()
+
+    def _generate(self, stream: int, start: int, count: int) -> np.ndarray:
+        wl = self.wl
+        if self.threads == 1 or count < (1 << 20):
+            return gen.values_range(wl.seed, stream, start, count, wl.dtype)
+        n = self.threads
+        bounds = [start + count * i // n for i in range(n + 1)]
+        with ThreadPoolExecutor(n) as ex:
+            parts = list(ex.map(lambda i: gen.values_range(wl.seed, stream, bounds[i], bounds[i + 1] - bounds[i],
+                                                           wl.dtype), range(n)))
+        return np.concatenate(parts)
+
+    def get(self, call: int, ntok: int, kind: int, layer: int) -> np.ndarray:
+        """[ntok][kv_heads][d] float32 values of one layer of an append call."""
+        wl = self.wl
+        key = (call, kind, layer)
+        with self.lock:
+            if self.layer != layer:
+                self.arrays.clear()
+                self.layer = layer
+            a = self.arrays.get(key)
+            if a is None:
+                per_layer = ntok * wl.kv_heads * wl.head_dim
+                a = self._generate(gen.stream_id(kind, call), layer * per_layer, per_layer).reshape(
+                    ntok, wl.kv_heads, wl.head_dim)
+                self.arrays[key] = a
+            return a
 
 
-def _batch_source_for(wl, call: int, total: int, first: int, ntok: int):
+def _source_for(wl, call: int, ntok: int, arrays: Optional[_LayerArrays] = None):
+    return _batch_source_for(wl, call, ntok, 0, ntok, arrays)
+
+
+def _batch_source_for(wl, call: int, total: int, first: int, ntok: int, arrays: Optional[_LayerArrays] = None):
     """Rows [first, first + ntok) of a batched append's source arrays, which hold
     ``total`` token rows (the handles' tokens one after another)."""
     def fn(which, layer, kvh, t0, t1):
         kind = gen.KIND_K if which == "k" else gen.KIND_V
+        if arrays is not None:
+            return arrays.get(call, total, kind, layer)[first + t0:first + t1, kvh, :]
         return workloads.kv_slice(wl, call, total, kind, layer, kvh, first + t0, first + t1)
     return FunctionSource(ntok, fn)
 
 
 class OracleReplay:
-    def __init__(self, wl, with_alloc: bool = True):
+    """``threads`` > 1: append values are generated a whole layer of a call at a
+    time (the same numbers) and ``attend`` works on several handles at once;
+    the arithmetic of each output is unchanged."""
+
+    def __init__(self, wl, with_alloc: bool = True, threads: int = 1):
         self.wl = wl
         self.alloc = FlatAllocator(wl.num_blocks, wl.block_size) if with_alloc else None
         self.mat = MaterializedCache()
         self.h_alloc: Dict[int, int] = {}
         self.h_mat: Dict[int, int] = {}
+        self.threads = max(1, threads)
+        self.arrays = _LayerArrays(wl, self.threads) if self.threads > 1 else None
 
     # -- structural ops --------------------------------------------------------
     def apply(self, op) -> None:
@@ -55,7 +104,7 @@ class OracleReplay:
             _, h, ntok, call = op
             if self.alloc is not None:
                 self.alloc.append(self.h_alloc[h], ntok)
-            self.mat.append(self.h_mat[h], _source_for(self.wl, call, ntok))
+            self.mat.append(self.h_mat[h], _source_for(self.wl, call, ntok, self.arrays))
         elif kind == "append_batch":
             # by definition, the appends one after another in batch order
             _, hs, ns, call = op
@@ -63,7 +112,7 @@ class OracleReplay:
             for h, n in zip(hs, ns):
                 if self.alloc is not None:
                     self.alloc.append(self.h_alloc[h], n)
-                self.mat.append(self.h_mat[h], _batch_source_for(self.wl, call, total, first, n))
+                self.mat.append(self.h_mat[h], _batch_source_for(self.wl, call, total, first, n, self.arrays))
                 first += n
         elif kind == "reserve_batch":
             # one token per handle whose K/V (every layer) are those of batched
@@ -126,7 +175,8 @@ class OracleReplay:
         by_handle: Dict[int, list] = {}
         for r, heads in want.items():
             by_handle.setdefault(rows[r][0], []).append((r, heads))
-        for h, items in by_handle.items():
+        def one_handle(h):
+            items = by_handle[h]
             mh = self.h_mat[h]
             heads_needed = sorted({hq for _, hs in items for hq in hs})
             kv = {}
@@ -140,4 +190,11 @@ class OracleReplay:
                     g = attention.kv_head_of(hq, wl.q_heads, wl.kv_heads)
                     K, V = kv[g]
                     out[r, hq] = attention.attend_one(K[: pos + 1], V[: pos + 1], Q[r, hq])
+
+        if self.threads > 1 and len(by_handle) > 1:
+            with ThreadPoolExecutor(self.threads) as ex:
+                list(ex.map(one_handle, list(by_handle)))
+        else:
+            for h in by_handle:
+                one_handle(h)
         return out

@@ -24,10 +24,18 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def run_both(wl, sample=None, options=None, extra_blocks=0, check_tables=True):
+def oracle_threads():
+    """Threads for the oracle's bulk checks: the host's cores, at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def run_both(wl, sample=None, options=None, extra_blocks=0, check_tables=True, threads=1):
     """Replay wl on the library (GPU) and the oracle; compare every attend op.
 
-    sample: None = every row and head, or a function (op, nrows) -> [(row, head)].
+    sample: None = every row and head, or a function (op, nrows) -> [(row, head)]
+    (or None for every row and head of that op, or [] for none of it).  threads: the oracle's
+    (OracleReplay) for large checks.
     Returns a list of (op, max_abs_err, n_compared).
     """
     torch = need_gpu()
@@ -38,7 +46,7 @@ def run_both(wl, sample=None, options=None, extra_blocks=0, check_tables=True):
     say("run_both: %s dtype=%s Hq=%d Hkv=%d D=%d blocks=%d" % (wl.name, wl.dtype, wl.q_heads, wl.kv_heads,
                                                               wl.head_dim, wl.num_blocks))
     lib = LibReplay(wl, "cuda", extra_blocks=extra_blocks)
-    orc = OracleReplay(wl)
+    orc = OracleReplay(wl, threads=threads)
     for k, v in (options or {}).items():
         tkv.tkv_set_option(lib.c, k, v)
     results = []
@@ -49,6 +57,11 @@ def run_both(wl, sample=None, options=None, extra_blocks=0, check_tables=True):
                 torch.cuda.synchronize()
                 rows = lib.nrows(op)
                 smp = None if sample is None else sample(op, rows)
+                if smp is not None and len(smp) == 0:
+                    # nothing of this call is compared (a later one is)
+                    lib.apply(op)
+                    orc.apply(op)
+                    continue
                 ref = orc.attend(op, smp)
                 got = out.double().cpu().numpy()
                 if smp is None:

@@ -1,8 +1,11 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py times.
 
-The float64 oracle cannot evaluate every output of these workloads in seconds,
-so it checks a seeded sample of (query row, head) outputs one by one; block
-tables are still compared in full.  The sample always includes the first and
+The fork, search-tree and verify workloads are compared in full: every query
+row and head of the call against the float64 oracle (run on several host
+threads, its arithmetic unchanged).  The 32-layer workload is compared in full
+on its first layer call and sampled on the other 31 (rows of a few requests
+per layer, every head drawn); block tables are compared in full everywhere.
+Loops and extreme shapes are sampled; the sample always includes the first and
 last rows.
 """
 
@@ -11,7 +14,7 @@ import pytest
 
 from workloads import recipes
 
-from _gpu_common import assert_close, run_both
+from _gpu_common import assert_close, oracle_threads, run_both
 
 pytestmark = pytest.mark.gpu
 
@@ -28,13 +31,42 @@ def _sampler(per_op, seed=0):
     return sample
 
 
-@pytest.mark.parametrize("name,per_op", [("llama_fork", 48), ("mcts_tree", 48), ("spec_verify", 64),
-                                         ("full_depth", 6)])
-def test_standard_workload_sampled(name, per_op):
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["llama_fork", "mcts_tree", "spec_verify"])
+def test_standard_workload_every_output(name):
+    """Every (query row, head) output of the call at full size against the oracle."""
     wl = recipes.STANDARD[name]()
-    s = _sampler(per_op)
-    s.heads = wl.q_heads
-    assert_close(run_both(wl, sample=s), wl.dtype)
+    res = run_both(wl, threads=oracle_threads())
+    op = wl.attend_ops()[0]
+    rows = sum(op[3]) if op[0] == "verify" else len(op[2])
+    assert [n for _, _, n in res] == [rows * wl.q_heads * wl.head_dim]
+    assert_close(res, wl.dtype)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("part", ["first_layer_whole", "every_layer_sampled"])
+def test_full_depth(part):
+    """The 32-layer workload (64 requests, 8192-token prefixes forked 16 ways, 256
+    tokens per branch; 103 GB of K/V), one decode step of 32 layer calls.
+    first_layer_whole: layer 0's call on every one of its 1024 rows x 32 heads.
+    every_layer_sampled: each layer's call on 128 (row, head) pairs drawn from
+    the rows of 4 requests chosen per layer, every head drawn."""
+    wl = recipes.STANDARD["full_depth"]()
+
+    def sample(op, nrows):
+        if part == "first_layer_whole":
+            return None if op[1] == 0 else []
+        rng = np.random.default_rng(100 + op[1])
+        reqs = rng.choice(nrows // 16, 4, replace=False)
+        rows = (reqs[:, None] * 16 + np.arange(16)[None, :]).reshape(-1)
+        pts = [(int(r), int(h)) for r in rows for h in rng.choice(wl.q_heads, 2, replace=False)]
+        return sorted(set(pts + [(0, 0), (nrows - 1, wl.q_heads - 1)]))
+    res = run_both(wl, sample=sample, threads=oracle_threads())
+    if part == "first_layer_whole":
+        assert [n for _, _, n in res] == [1024 * 32 * 128]
+    else:
+        assert len(res) == 32
+    assert_close(res, wl.dtype)
 
 
 @pytest.mark.parametrize("case", ["long_decode", "long_verify", "wide_batch", "gqa8_tree", "wide_batch_f32",

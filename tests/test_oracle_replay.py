@@ -257,7 +257,8 @@ def test_pins_catch_decode_position_off_by_one(monkeypatch):
 
 def test_pins_catch_wrong_batch_offset(monkeypatch):
     orig = orp._batch_source_for
-    monkeypatch.setattr(orp, "_batch_source_for", lambda wl, call, total, first, ntok: orig(wl, call, total, 0, ntok))
+    monkeypatch.setattr(orp, "_batch_source_for",
+                        lambda wl, call, total, first, ntok, arrays=None: orig(wl, call, total, 0, ntok, arrays))
     assert _caught() > 0
 
 
@@ -289,3 +290,15 @@ def test_pins_catch_dropped_last_key(monkeypatch):
         return orig(K[:-1], V[:-1], q) if len(K) > 1 else orig(K, V, q)
     monkeypatch.setattr(attention, "attend_one", drop_last)
     assert _caught() > 0
+
+
+def test_bulk_generated_replay_is_the_same_replay():
+    """OracleReplay with threads (append values generated a whole layer of a call
+    at a time, handles attended in parallel) gives bit-identical outputs."""
+    wl = _wl()
+    a, b = OracleReplay(wl), OracleReplay(wl, threads=4)
+    for op in wl.ops:
+        if op[0] in ("decode", "decode_new", "verify"):
+            np.testing.assert_array_equal(a.attend(op), b.attend(op))
+        a.apply(op)
+        b.apply(op)
