@@ -97,8 +97,12 @@ int tkv_seq_new(tkv_cache* c, tkv_seq* out);
  * out_children: host array of n handles, written only on success. */
 int tkv_fork(tkv_cache* c, tkv_seq parent, int32_t n, tkv_seq* out_children);
 
-/* Release a handle.  Blocks no live handle can reach any more return to the free
- * set.  The handle becomes stale (TKV_E_BADSEQ afterwards). */
+/* Release a handle: a branch that lost is dropped (the article's case studies, AI
+ * agent frameworks: several plans explored as branches, the one to keep chosen
+ * afterwards; the DSpark blog, second layer: rejected draft paths discarded after
+ * verification).  Blocks
+ * no live handle can reach any more return to the free set.  The handle becomes
+ * stale (TKV_E_BADSEQ afterwards).  Host only; no device call. */
 int tkv_release(tkv_cache* c, tkv_seq s);
 
 /* Append ntok >= 1 tokens to s (DSpark blog, third layer: each new token's K and V
@@ -132,7 +136,12 @@ int tkv_truncate(tkv_cache* c, tkv_seq s, int64_t new_len);
 
 /* Device workspace needed by an attention call with these arguments (nq = NULL for
  * decode).  Builds (and caches) the call's plan.  *bytes may be 0.  nseq >= 1 (an
- * empty batch is TKV_E_INVAL here and in the attention calls). */
+ * empty batch is TKV_E_INVAL here and in the attention calls).  It takes the
+ * handles, not just their count and the query total, because the workspace holds
+ * the split-K partial records, whose number depends on how the batch's paths
+ * overlap and how long they are: the same (nseq, total queries) needs none for a
+ * batch of long independent paths cut one item per group and megabytes for a
+ * search tree cut into many chunks. */
 int tkv_workspace_size(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
                        size_t* bytes);
 
@@ -208,9 +217,15 @@ typedef struct tkv_counters {
 } tkv_counters;
 int tkv_get_counters(const tkv_cache* c, tkv_counters* out);
 
+/* Names of the kernels the last attention call on c launched, in launch order,
+ * "name<template arguments>" joined by ';' (e.g. the attention kernel and the
+ * merge), NUL-terminated into buf[cap].  TKV_E_RANGE if cap is too small (buf
+ * then holds as much as fits).  For naming measured kernels. */
+int tkv_last_kernels(const tkv_cache* c, char* buf, int32_t cap);
+
 /* Shape of the plan an attention call with these arguments uses (builds it). */
 typedef struct tkv_plan_info {
-  int32_t groups;          /* query groups (<= 64 rows each, one KV pass per group) */
+  int32_t groups;          /* query groups (<= TKV_OPT_MAX_ROWS rows each, one KV pass per group) */
   int32_t items;           /* work items; one workgroup per item and KV head */
   int32_t block_entries;   /* block visits summed over groups */
   int32_t unique_blocks;   /* distinct blocks the call reads */

@@ -2,8 +2,9 @@
 //
 // Dendrite article (ainews.cool, "technical deep dive"): a branch's query
 // attends over the keys and values of its shared ancestor path and then of its
-// own leaf path.  The planner has cut the batch into groups of up to 64 rows
-// (rows = the group's queries x the query heads that share one KV head) and
+// own leaf path.  The planner has cut the batch into groups of at most 128 rows
+// by default, 256 at most (rows = the group's queries x the query heads that
+// share one KV head) and
 // lists each group's blocks once, with a mask of which queries see each block.
 //
 // One workgroup (W = 2, 4 or 8 waves) runs one work item (a run of a group's
@@ -24,6 +25,8 @@
 // (m, l, acc) and attn_merge combines them (log-sum-exp, exp2 domain).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <cstdio>
 
 #include "attn_common.h"
 #include "kernels.h"
@@ -271,12 +274,19 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
   }
 }
 
+template <class P, int D, int T, int W, bool C>
+void note_partial() {
+  char nm[96];
+  snprintf(nm, sizeof nm, "attn_partial_kernel<%s, %d, %d, %d, %s>", P::kName, D, T, W, C ? "true" : "false");
+  launch_log_add(nm);
+}
+
 template <class P, int D, int W, bool C>
 hipError_t launch_t(int tiles, const AttnArgs& args, int32_t n_items, hipStream_t s) {
   const dim3 grid(n_items * args.hkv), block(64 * W);
   switch (tiles) {
-    case 1: hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, W, C>), grid, block, 0, s, args); break;
-    case 2: hipLaunchKernelGGL((attn_partial_kernel<P, D, 2, W, C>), grid, block, 0, s, args); break;
+    case 1: hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, W, C>), grid, block, 0, s, args); note_partial<P, D, 1, W, C>(); break;
+    case 2: hipLaunchKernelGGL((attn_partial_kernel<P, D, 2, W, C>), grid, block, 0, s, args); note_partial<P, D, 2, W, C>(); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -289,11 +299,13 @@ hipError_t launch_w(int tiles, int waves, const AttnArgs& args, int32_t n_items,
   if constexpr (kIsBF16<P> || D <= 64) {
     if (waves == 8 && tiles == 1) {
       hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, 8, C>), dim3(n_items * args.hkv), dim3(64 * 8), 0, s, args);
+      note_partial<P, D, 1, 8, C>();
       return hipGetLastError();
     }
   }
   if (waves == 2 && tiles == 1) {
     hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, 2, C>), dim3(n_items * args.hkv), dim3(64 * 2), 0, s, args);
+    note_partial<P, D, 1, 2, C>();
     return hipGetLastError();
   }
   return launch_t<P, D, 4, C>(tiles, args, n_items, s);

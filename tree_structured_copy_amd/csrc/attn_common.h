@@ -114,6 +114,7 @@ constexpr int rows_loads_per_wave() {
 // bf16 inputs: S^T and O^T via 16x16x32 bf16 MFMAs.
 struct BF16 {
   using elem = uint16_t;
+  static constexpr const char* kName = "BF16";
   template <int D>
   struct Frag {
     u32x4 v[D / 32];
@@ -202,6 +203,7 @@ struct BF16 {
 // fp32 inputs: 16x16x4 fp32 MFMAs (full fp32 products and sums).
 struct F32 {
   using elem = float;
+  static constexpr const char* kName = "F32";
   template <int D>
   struct Frag {
     f32x4 v[D / 16];

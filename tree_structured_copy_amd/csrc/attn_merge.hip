@@ -115,6 +115,7 @@ hipError_t launch_attn_merge(int head_dim, const MergeArgs& args, hipStream_t st
   if (head_dim == 128) hipLaunchKernelGGL((attn_merge_kernel<128>), grid, dim3(256), 0, stream, args);
   else if (head_dim == 64) hipLaunchKernelGGL((attn_merge_kernel<64>), grid, dim3(256), 0, stream, args);
   else return hipErrorInvalidValue;
+  launch_log_add(head_dim == 128 ? "attn_merge_kernel<128>" : "attn_merge_kernel<64>");
   return hipGetLastError();
 }
 

@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdio>
+
 #include "attn_common.h"
 #include "kernels.h"
 
@@ -359,6 +361,10 @@ hipError_t launch_one(const AttnArgs& args, int32_t n_items, hipStream_t s) {
   const size_t ents_bytes = sizeof(StagedBlock) * static_cast<size_t>(args.max_blocks > 0 ? args.max_blocks : 1);
   hipLaunchKernelGGL((attn_rows_kernel<P, D, TPW, W, HPW, NS, EARLY, MINW, C>), dim3(n_items * (args.hkv / HPW)),
                      dim3(64 * W * HPW), ents_bytes, s, args);
+  char nm[96];
+  snprintf(nm, sizeof nm, "attn_rows_kernel<%s, %d, %d, %d, %d, %d, %s, %d, %s>", P::kName, D, TPW, W, HPW, NS,
+           EARLY ? "true" : "false", MINW, C ? "true" : "false");
+  launch_log_add(nm);
   return hipGetLastError();
 }
 

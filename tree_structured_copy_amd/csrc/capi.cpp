@@ -16,6 +16,32 @@
 
 using namespace tkv;
 
+namespace tkv {
+
+namespace {
+constexpr size_t kLaunchLogBytes = 1024;
+thread_local char g_launch_log[kLaunchLogBytes];
+thread_local size_t g_launch_log_len = 0;
+}  // namespace
+
+void launch_log_reset() {
+  g_launch_log_len = 0;
+  g_launch_log[0] = '\0';
+}
+
+void launch_log_add(const char* name) {
+  const size_t n = std::strlen(name);
+  const size_t sep = g_launch_log_len ? 1 : 0;
+  if (g_launch_log_len + sep + n + 1 > kLaunchLogBytes) return;
+  if (sep) g_launch_log[g_launch_log_len++] = ';';
+  std::memcpy(g_launch_log + g_launch_log_len, name, n + 1);
+  g_launch_log_len += n;
+}
+
+const char* launch_log() { return g_launch_log; }
+
+}  // namespace tkv
+
 namespace {
 
 struct PlanSlot {
@@ -86,6 +112,8 @@ struct tkv_cache {
   hipStream_t aux[kKernelClasses - 1] = {};
   hipEvent_t fork_ev = nullptr;
   hipEvent_t join_ev[kKernelClasses - 1] = {};
+  // the kernels the last attention call launched (launch_log's format)
+  char last_kernels[1024] = {0};
   // profiling
   bool prof = false;
   std::vector<std::array<hipEvent_t, 3>> prof_used;
@@ -104,6 +132,15 @@ struct tkv_cache {
   }
   const char* vpool_layer(int layer) const {
     return static_cast<const char*>(cfg.v_pool) + layer * layer_elems() * elem_bytes();
+  }
+
+  // Back to the pool, or destroyed when the pool cannot grow.
+  void put_event(hipEvent_t e) {
+    try {
+      ev_pool.push_back(e);
+    } catch (const std::bad_alloc&) {
+      (void)hipEventDestroy(e);
+    }
   }
 
   hipEvent_t get_event() {
@@ -381,6 +418,7 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   if (need > 0 && (!ws || ws_bytes < need)) return TKV_E_WORKSPACE;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   DeviceGuard dg(c->device);
+  launch_log_reset();
   if (k_new) {
     if (int rc = prepare_new_tokens(c, s, layer, nseq, k_new, v_new, stream)) return rc;
   } else if (int rc = upload_plan(c, s, stream)) {
@@ -472,15 +510,22 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     m.scale_log2 = a.scale_log2;
     if (launch_attn_merge(c->cfg.head_dim, m, stream) != hipSuccess) return TKV_E_DEVICE;
   }
+  std::memcpy(c->last_kernels, launch_log(), std::strlen(launch_log()) + 1);
   if (c->prof) {
+    bool kept = false;
     if (ev[0] && ev[1] && ev[2]) {
       (void)hipEventRecord(ev[2], stream);
-      c->prof_used.push_back(ev);
-      ++c->prof_calls;
-    } else {
-      for (auto e : ev)
-        if (e) c->ev_pool.push_back(e);
+      try {
+        c->prof_used.push_back(ev);
+        ++c->prof_calls;
+        kept = true;
+      } catch (const std::bad_alloc&) {
+        // no room to keep this call's events: it goes untimed
+      }
     }
+    if (!kept)
+      for (auto e : ev)
+        if (e) c->put_event(e);
   }
   return TKV_OK;
 }
@@ -688,7 +733,13 @@ int tkv_gather(tkv_cache* c, tkv_seq s, int32_t layer, void* k_out, void* v_out,
   int32_t n = 0;
   int rc = c->tree.block_table(s, nullptr, nullptr, 0, &n);
   if (rc && rc != TKV_E_RANGE) return rc;
-  std::vector<int32_t> ids(n), valid(n);
+  std::vector<int32_t> ids, valid;
+  try {
+    ids.resize(n);
+    valid.resize(n);
+  } catch (const std::bad_alloc&) {
+    return TKV_E_NOMEM;
+  }
   if (n > 0 && (rc = c->tree.block_table(s, ids.data(), valid.data(), n, &n))) return rc;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   DeviceGuard dg(c->device);
@@ -728,6 +779,15 @@ int tkv_num_free(const tkv_cache* c, int32_t* n) {
   if (!c || !n) return TKV_E_INVAL;
   *n = c->tree.num_free();
   return TKV_OK;
+}
+
+int tkv_last_kernels(const tkv_cache* c, char* buf, int32_t cap) {
+  if (!c || !buf || cap < 1) return TKV_E_INVAL;
+  const size_t n = std::strlen(c->last_kernels);
+  const size_t k = std::min(n, static_cast<size_t>(cap) - 1);
+  std::memcpy(buf, c->last_kernels, k);
+  buf[k] = '\0';
+  return k == n ? TKV_OK : TKV_E_RANGE;
 }
 
 int tkv_get_counters(const tkv_cache* c, tkv_counters* out) {
@@ -830,7 +890,7 @@ int tkv_profile_read(tkv_cache* c, double* partial_ms, double* merge_ms, int64_t
         rc = TKV_E_DEVICE;
       pm += a;
       mm += b;
-      for (auto e : t) c->ev_pool.push_back(e);
+      for (auto e : t) c->put_event(e);
     }
   }
   c->prof_used.clear();

@@ -6,6 +6,13 @@
 
 namespace tkv {
 
+// Names of the kernels launched by this host thread since launch_log_reset(),
+// "name<template arguments>" joined by ';' (a fixed buffer: nothing is
+// allocated; names past its end are dropped).  The launchers below add theirs.
+void launch_log_reset();
+void launch_log_add(const char* name);
+const char* launch_log();
+
 // Partial attention over items [args.item0, args.item0 + n_items) whose groups
 // need `tiles` row tiles of 16; grid = n_items * Hkv workgroups of 64 * waves
 // threads (waves = 4 or 8).

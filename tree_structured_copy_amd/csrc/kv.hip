@@ -187,12 +187,14 @@ __global__ __launch_bounds__(512) void plan_patch_args_kernel(PatchArgs a) {
 hipError_t launch_plan_patch_args(const PatchArgs& args, hipStream_t stream) {
   if (args.n <= 0 || args.n > kPatchArgWords) return hipErrorInvalidValue;
   hipLaunchKernelGGL(plan_patch_args_kernel, dim3(1), dim3(512), 0, stream, args);
+  launch_log_add("plan_patch_args_kernel");
   return hipGetLastError();
 }
 
 hipError_t launch_plan_patch(int32_t* plan, const PlanWord* words, int32_t n, uint32_t limit, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(plan_patch_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, plan, words, n, limit);
+  launch_log_add("plan_patch_kernel");
   return hipGetLastError();
 }
 
@@ -218,6 +220,7 @@ hipError_t launch_decode_prep(int dtype, int head_dim, const DecodePrepArgs& arg
   else if (dtype == 0 && head_dim == 128) hipLaunchKernelGGL((decode_prep_kernel<4, 128>), grid, dim3(256), 0, stream, args);
   else if (dtype == 0 && head_dim == 64) hipLaunchKernelGGL((decode_prep_kernel<4, 64>), grid, dim3(256), 0, stream, args);
   else return hipErrorInvalidValue;
+  launch_log_add("decode_prep_kernel");
   return hipGetLastError();
 }
 

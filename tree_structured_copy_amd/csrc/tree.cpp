@@ -336,12 +336,17 @@ int Tree::block_table(tkv_seq s, int32_t* ids, int32_t* valid, int32_t cap, int3
 int Tree::block_refcounts(int32_t* rc) const {
   if (!rc) return TKV_E_INVAL;
   // handles in each node's subtree, accumulated bottom-up by depth
-  std::vector<int32_t> order;
+  std::vector<int32_t> order, sub;
+  try {
+    order.reserve(nodes_.size());
+    sub.assign(nodes_.size(), 0);
+  } catch (const std::bad_alloc&) {
+    return TKV_E_NOMEM;
+  }
   for (int32_t i = 0; i < (int32_t)nodes_.size(); ++i)
     if (nodes_[i].live) order.push_back(i);
   std::sort(order.begin(), order.end(),
             [&](int32_t a, int32_t b) { return nodes_[a].depth > nodes_[b].depth; });
-  std::vector<int32_t> sub(nodes_.size(), 0);
   for (int32_t id : order) {
     sub[id] += nodes_[id].nhandles;
     if (nodes_[id].parent >= 0) sub[nodes_[id].parent] += sub[id];

@@ -121,6 +121,7 @@ _SIGS = {
     "tkv_block_refcounts": [_P, _pI32],
     "tkv_num_free": [_P, _pI32],
     "tkv_get_counters": [_P, ctypes.POINTER(tkv_counters)],
+    "tkv_last_kernels": [_P, ctypes.c_char_p, _I32],
     "tkv_plan_info_get": [_P, _pU64, _pI32, _I32, ctypes.POINTER(tkv_plan_info)],
     "tkv_set_option": [_P, _I32, _I64],
     "tkv_get_option": [_P, _I32, ctypes.POINTER(_I64)],
@@ -297,6 +298,14 @@ def tkv_get_counters(c) -> dict:
     x = tkv_counters()
     _check(_lib.tkv_get_counters(c, ctypes.byref(x)), "tkv_get_counters")
     return {f: getattr(x, f) for f, _ in tkv_counters._fields_}
+
+
+def tkv_last_kernels(c) -> list:
+    """Names of the kernels the last attention call on c launched, in order."""
+    buf = ctypes.create_string_buffer(1024)
+    _check(_lib.tkv_last_kernels(c, buf, len(buf)), "tkv_last_kernels")
+    v = buf.value.decode()
+    return v.split(";") if v else []
 
 
 def tkv_plan_info_get(c, seqs, nq=None) -> dict:
