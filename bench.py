@@ -1,21 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark: tree-attention decode over a forked, copy-on-write KV cache on one MI355X.
 
-A step is one ``tkv_attend_decode`` call (plan lookup, split-K partial
-attention kernel, merge kernel) over the Llama-3-8B-shaped fork workload: 32
-requests, each a 4096-token prefix forked into 4 branches of 64 tokens, one
-decode query per branch (128 queries x 32 heads, GQA 32/8, head_dim 128, bf16).
-The tree is built first (fork + append, untimed); K/V are resident in HBM
-before the timed region.  Consecutive steps rotate over ``--copies``
-independent copies of the workload (disjoint pools) so that no step finds the
-previous step's KV in L2 or the 256 MB Infinity Cache.
+The headline step is one decode step of the 32-layer workload: 64 requests,
+each an 8192-token prefix forked into 16 branches of 256 tokens, one decode
+query per branch in every layer (32 layer calls of 1024 queries x 32 heads,
+GQA 32/8, head_dim 128, bf16; 103 GB of K/V resident in HBM).  The tree is
+built first (fork + append, untimed); K/V are resident before the timed
+region, and the 103 GB dwarf every cache, so no step finds the previous one's
+KV cached.
 
-Printed: one JSON line.  ``value`` is unique-KV GB/s: distinct (block, KV head)
-tiles the step must read, counted by valid token slots, K and V, divided by the
-wall time per step.  Also reported: branch-queries/s, the speculative-verify
-workload's verify tokens/s (64 requests x 3 draft paths x 8 drafts), the
-partial-attention kernel's roofline against 8 TB/s measured with HIP events,
-fork latency, and the CPU oracle timed on a sample of the same workload.
+Printed: one JSON line.  ``value`` is unique-KV GB/s: distinct (layer, block,
+KV head) tiles the step must read, counted by valid token slots, K and V,
+divided by the wall time per step.  ``roofline`` gives the dominant kernel's
+rate from HIP events against 8 TB/s, and ``cpu_baseline`` the float64 oracle
+on a sample of the same workload.  The other single-layer workloads (the
+fork workload, the speculative-verify batch and the search tree) are reported
+under ``workloads``, each with its own roofline and CPU baseline, beside the
+decode, speculative and search loops and the fork latency.
 """
 
 from __future__ import annotations
@@ -31,27 +32,28 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per launch of the decode kernel on llama_fork, from two rocprofv3
-# --pmc passes (FETCH_SIZE, then WRITE_SIZE) over `bench.py --counters`, each
-# scaled by the factor that makes the same counter read a plain 1 GiB copy
-# right.  Valid only for the kernel sources they were taken on (sha256 below);
-# after any change to them the bench line reports traffic as null.
-TRAFFIC_RECORD = {
-    "sources_sha256": "eeb46a9f0dd7e965c016df17018afb22ccbfcf619efd690b5ae671cebe0c6f48",
-    "fetch_kib_per_launch": 281858, "fetch_factor": 1.9999,   # 1 GiB read reads as 524309 KiB
-    "write_kib_per_launch": 2048, "write_factor": 1.0,        # 1 GiB written reads as 1048576 KiB
-    "hbm_bytes_per_launch": 577221744 + 2097152,
+# HBM bytes per launch of each workload's dominant attention kernel, from two
+# rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over `bench.py --counters
+# --counters-workload <name>`, each scaled by the factor that makes the same
+# counter read a plain 1 GiB copy right.  Valid only for the kernel sources
+# they were taken on (sha256 over the files listed); after any change to them
+# the line reports traffic as null.
+KERNEL_SOURCES = {
+    "attn_partial_kernel": ("attn.hip", "attn_common.h", "layout.h", "tkv_types.h"),
+    "attn_rows_kernel": ("attn_rows.hip", "attn_common.h", "layout.h", "tkv_types.h"),
 }
+TRAFFIC_RECORDS = {}
 
 
-def _kernel_sources_sha():
-    """sha256 of the decode kernel's sources with // comments and blank lines
-    removed, so that an edit of the comments alone keeps the recorded traffic."""
+def _kernel_sources_sha(kernel):
+    """sha256 of a kernel's sources with // comments and blank lines removed, so
+    that an edit of the comments alone keeps the recorded traffic."""
     import hashlib
     import re
+    base = kernel.split("<")[0]
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tree_structured_copy_amd", "csrc")
-    for f in ("attn.hip", "attn_common.h", "layout.h", "tkv_types.h"):
+    for f in KERNEL_SOURCES.get(base, ()):
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             for line in fh:
                 code = re.sub(r"//.*", "", line).rstrip()
@@ -60,11 +62,24 @@ def _kernel_sources_sha():
     return h.hexdigest()
 
 
-def _recorded_traffic():
-    rec = TRAFFIC_RECORD
-    if not rec or rec.get("sources_sha256") != _kernel_sources_sha():
+def _recorded_traffic(workload, kernel):
+    rec = TRAFFIC_RECORDS.get(workload)
+    if not rec or rec.get("kernel") != kernel or rec.get("sources_sha256") != _kernel_sources_sha(kernel):
         return None
     return rec["hbm_bytes_per_launch"]
+
+
+def _host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": model}
 
 
 class _Copy:
@@ -223,58 +238,75 @@ def _fork_sweep_ns():
     return {"summary": summary, "grid_prefix_depth_n": grid}
 
 
-def _cpu_baseline(requests: int, reps: int):
-    """The float64 oracle on the first ``requests`` requests of the fork workload:
-    materialise each branch's history and run textbook attention for all heads."""
-    import numpy as np
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    from oracle import attention
-    from oracle.cache import ArraySource, MaterializedCache
-    from workloads import gen, recipes
-    import workloads
-    full = recipes.llama_fork()
-    wl = recipes.fork_workload("llama_fork_sample", dtype="bf16", layers=1, q_heads=32, kv_heads=8, head_dim=128,
-                               requests=requests, prefix=4096, width=4, branch_tokens=64, seed=full.seed)
-    # inputs generated up front (not timed)
-    arrays = {}
-    for op in wl.ops:
-        if op[0] == "append":
-            _, h, ntok, call = op
-            arrays[call] = (workloads.kv_values(wl, call, ntok, gen.KIND_K),
-                            workloads.kv_values(wl, call, ntok, gen.KIND_V))
-    dec = wl.attend_ops()[0]
-    Q = workloads.q_values(wl, dec[-1], len(dec[2])).astype(np.float64)
-    times = []
-    for _ in range(reps):
+def _cpu_threads():
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _cpu_oracle(wl):
+    """The float64 oracle on workload ``wl`` (a benchmarked workload or a sample of
+    one): every append call's K/V generated up front (not timed), then, timed, the oracle's replay -- each branch's history
+    materialised (a fork copies it) and textbook attention for every query row
+    and head of every decode/verify call -- on T host threads with one BLAS
+    thread each (cores = T)."""
+    from threadpoolctl import threadpool_limits
+    from oracle.replay import OracleReplay, PreloadedArrays
+    threads = _cpu_threads()
+    arrays = PreloadedArrays(wl, threads)
+    rows = 0
+    with threadpool_limits(1):
         t0 = time.perf_counter()
-        mc = MaterializedCache()
-        names = {}
+        orc = OracleReplay(wl, with_alloc=False, threads=threads, arrays=arrays)
         for op in wl.ops:
-            if op[0] == "new":
-                names[op[1]] = mc.seq_new()
-            elif op[0] == "append":
-                mc.append(names[op[1]], ArraySource(*arrays[op[3]]))
-            elif op[0] == "fork":
-                for n, c in zip(op[3], mc.fork(names[op[1]], op[2])):
-                    names[n] = c
-            elif op[0] == "release":
-                mc.release(names.pop(op[1]))
-        for r, h in enumerate(dec[2]):
-            kv = [mc.kv(names[h], 0, g) for g in range(wl.kv_heads)]
-            for hq in range(wl.q_heads):
-                K, V = kv[attention.kv_head_of(hq, wl.q_heads, wl.kv_heads)]
-                attention.attend_one(K, V, Q[r, hq])
-        times.append(time.perf_counter() - t0)
-    t = sorted(times)[len(times) // 2]
-    unique = requests * (4096 + 4 * 64) * wl.kv_heads * wl.head_dim * 2 * 2
-    return {"value": unique / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d of 32 requests of the fork workload (%d decode queries x 32 heads), median of %d "
-                      "runs of %.2f s" % (requests, 4 * requests, reps, t),
-            "branch_queries_per_s": 4 * requests / t}
+            if op[0] in ("decode", "verify"):
+                orc.attend(op)
+                rows += sum(op[3]) if op[0] == "verify" else len(op[2])
+            orc.apply(op)
+        t = time.perf_counter() - t0
+    del arrays
+    return t, rows
+
+
+def _unique_kv_bytes_host(wl):
+    """Unique K/V bytes every attend call of wl reads, from a host-only replay of
+    its recipe through the library's planner (valid token slots of the distinct
+    blocks of each call, K and V, all KV heads)."""
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    lib = LibReplay(wl, None)
+    total = 0
+    try:
+        for op in wl.ops:
+            if op[0] in ("decode", "verify"):
+                nq = op[3] if op[0] == "verify" else None
+                info = tkv.tkv_plan_info_get(lib.c, lib.handles(op), nq)
+                total += info["unique_tokens"] * wl.kv_heads * wl.head_dim * wl.elem_bytes * 2
+            lib.apply(op)
+    finally:
+        lib.close()
+    return total
+
+
+def _cpu_baseline(name):
+    """The oracle timed on a bounded sample of workload ``name`` (all of it where
+    that takes seconds): rates in the GPU line's units."""
+    from workloads import recipes
+    full = recipes.STANDARD[name]()
+    if name == "full_depth":
+        wl = recipes.fork_workload("full_depth_sample", dtype="bf16", layers=32, q_heads=32, kv_heads=8,
+                                   head_dim=128, requests=1, prefix=8192, width=16, branch_tokens=256,
+                                   seed=full.seed)
+        scale = 64
+        sample = ("1 of the 64 requests (16 branches x 32 layers, 512 decode queries x 32 heads); the step's "
+                  "time extrapolated as 64 x the sample's")
+    else:
+        wl, scale = full, 1
+        sample = "the whole workload"
+    t, rows = _cpu_oracle(wl)
+    ubytes = _unique_kv_bytes_host(wl)
+    res = {"value": ubytes / t / 1e9, "unit": "GB/s", "cores": _cpu_threads(), "kind": "oracle",
+           "sample": sample + ", %.2f s" % t, "seconds": t, "queries_per_s": rows / t,
+           "extrapolated_ms_per_step": t * scale * 1e3 if scale > 1 else None}
+    return res
 
 
 def _native_loops():
@@ -371,23 +403,39 @@ def _time_generation_loop(copies, windows, patch, fused=False):
     return total / counted * 1e3, counters
 
 
+def _split_kernels(names):
+    """(attention kernels, merge kernel or None) from an attention call's launch list."""
+    attn = [n for n in names if n.startswith(("attn_partial_kernel", "attn_rows_kernel"))]
+    merge = [n for n in names if n.startswith("attn_merge_kernel")]
+    return attn, (merge[0] if merge else None)
+
+
 def measure(name, copies, steps, warmup, rebuild=False):
     """Wall time per step, kernel times and derived rates for one workload."""
     import torch
+    from tree_structured_copy_amd import tkv
     from workloads import recipes
     wl = recipes.STANDARD[name]()
     items = _prepare(wl, copies)
     ubytes, info = items[0].unique_bytes()
     queries = items[0].queries()
     ms = _time_wall(items, steps, warmup)
+    attn, merge = _split_kernels(tkv.tkv_last_kernels(items[0].lib.c))
     part_ms, merge_ms = _time_kernels(items, steps)
     ncalls = len(items[0].calls)
+    achieved = (ubytes / ncalls) / (part_ms / 1e3) / 1e9 if part_ms > 0 else None
+    kernel = attn[0] if len(attn) == 1 else (";".join(attn) if attn else None)
     res = {"workload": name, "ms_per_step": ms, "attend_calls_per_step": ncalls,
            "unique_kv_bytes": ubytes, "unique_kv_GBps": ubytes / (ms / 1e3) / 1e9,
+           "hbm_peak_frac": ubytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
            "queries_per_step": queries, "queries_per_s": queries / (ms / 1e3),
-           "partial_kernel_ms_per_call": part_ms, "merge_kernel_ms_per_call": merge_ms,
-           "partial_kernel_GBps": (ubytes / ncalls) / (part_ms / 1e3) / 1e9 if part_ms > 0 else None,
-           "plan": info, "copies_rotated": copies}
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": achieved / HBM_PEAK_GBS if achieved else None,
+                        "traffic": _recorded_traffic(name, kernel) if kernel else None,
+                        "kernel": kernel, "kernel_ms": part_ms, "launches_per_call": len(attn),
+                        "merge_kernel": merge, "merge_kernel_ms": merge_ms if merge else None,
+                        "timing": "HIP events around the attention launches of each call, on its stream"},
+           "plan": info, "copies_rotated": copies, "steps": steps, "warmup": warmup}
     if rebuild:
         res["ms_per_step_plan_rebuild"] = _time_rebuild(items, max(5, steps // 5))
     for it in items:
@@ -400,9 +448,10 @@ def measure(name, copies, steps, warmup, rebuild=False):
 def _counters_run(copies, workload="llama_fork"):
     """What the traffic figures are taken on: 3 launches of a plain streaming
     kernel over a 1 GiB buffer (dst = 2 * src: 1 GiB read + 1 GiB written per
-    launch), then 8 steps of the workload (by default the fork workload's decode
-    call), rotating over `copies` independent copies."""
+    launch), then a few steps of the workload (8 single-layer calls, or 2 steps
+    of the 32-layer workload), rotating over `copies` independent copies."""
     import torch
+    from tree_structured_copy_amd import tkv
     from workloads import recipes
     n = 1 << 30
     src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
@@ -410,42 +459,62 @@ def _counters_run(copies, workload="llama_fork"):
     for _ in range(3):
         torch.mul(src, 2, out=dst)
     torch.cuda.synchronize()
-    items = _prepare(recipes.STANDARD[workload](), copies)
+    del src, dst
+    wl = recipes.STANDARD[workload]()
+    copies = 1 if wl.layers > 1 else copies
+    steps = 2 if wl.layers > 1 else 8
+    items = _prepare(wl, copies)
     stream = torch.cuda.current_stream().cuda_stream
-    for i in range(8):
+    for i in range(steps):
         items[i % len(items)].step(stream)
     torch.cuda.synchronize()
     ubytes, _ = items[0].unique_bytes()
+    attn, merge = _split_kernels(tkv.tkv_last_kernels(items[0].lib.c))
     print(json.dumps({"counters_run": True, "workload": workload, "copy_bytes": n, "copy_launches": 3,
-                      "steps": 8, "unique_kv_bytes_per_call": ubytes, "sources_sha256": _kernel_sources_sha()}),
-          flush=True)
+                      "steps": steps, "attend_calls": steps * len(items[0].calls),
+                      "unique_kv_bytes_per_call": ubytes // len(items[0].calls), "kernels": attn,
+                      "merge_kernel": merge,
+                      "sources_sha256": {k: _kernel_sources_sha(k) for k in attn}}), flush=True)
+
+
+SUBS = {
+    "llama_fork": ("branch_queries_per_s",
+                   {"requests": 32, "prefix_tokens": 4096, "fork_width": 4, "branch_tokens": 64, "layers": 1,
+                    "decode_queries": 128}),
+    "spec_verify": ("verify_tokens_per_s",
+                    {"requests": 64, "prefix_tokens": 2048, "draft_paths": 3, "drafts_per_path": 8, "layers": 1,
+                     "verify_queries": 1536}),
+    "mcts_tree": ("branch_queries_per_s",
+                  {"root_tokens": 2048, "branching": 4, "depth": 12, "node_tokens": 16, "leaves": 256,
+                   "layers": 1, "decode_queries": 256}),
+}
+SHAPE = {"q_heads": 32, "kv_heads": 8, "head_dim": 128, "block_size": 16, "dtype": "bf16"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="timed steps of the 32-layer workload")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed steps of the 32-layer workload before them")
     # the clock ramps up from idle over the first tens of milliseconds of load:
-    # 300 warm-up steps (about 30 ms at these shapes) reach its steady state
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--copies", type=int, default=4)
-    ap.add_argument("--no-verify", action="store_true")
+    # 300 warm-up calls (about 30 ms at these shapes) reach its steady state
+    ap.add_argument("--sub-steps", type=int, default=200, help="timed calls of each single-layer workload")
+    ap.add_argument("--sub-warmup", type=int, default=300, help="untimed calls of each single-layer workload")
+    ap.add_argument("--copies", type=int, default=4, help="copies of each single-layer workload, rotated")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--all", action="store_true", help="also measure the 32-layer workload")
-    ap.add_argument("--cpu-requests", type=int, default=32)
-    ap.add_argument("--cpu-reps", type=int, default=7)
+    ap.add_argument("--no-loops", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="a short run for rocprofv3 --pmc passes: a plain 1 GiB streaming kernel (the "
-                         "counters' calibration), then 8 steps of --counters-workload")
-    ap.add_argument("--counters-workload", default="llama_fork",
-                    help="workload of the --counters run (llama_fork, spec_verify, mcts_tree, ...)")
+                         "counters' calibration), then a few steps of --counters-workload")
+    ap.add_argument("--counters-workload", default="full_depth",
+                    help="workload of the --counters run (full_depth, llama_fork, spec_verify, mcts_tree)")
     ap.add_argument("--only", default=None,
-                    help="measure just this workload (mcts_tree, spec_verify, full_depth, llama_fork, or "
+                    help="measure just this workload (full_depth, llama_fork, spec_verify, mcts_tree, or "
                          "generation_loop: the decode loop with batched appends) and print "
                          "its figures as one JSON line: a short run for a kernel trace of that workload alone")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the fork workload's requests are independent trees, so "
+        print("bench.py measures one GPU only: the 32-layer workload's requests are independent trees, so "
               "more GPUs would shard requests with no communication; --gpus %d is not supported" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
@@ -464,49 +533,54 @@ def main():
               flush=True)
         return
     if args.only:
-        copies = 1 if args.only == "full_depth" else args.copies
-        steps, warmup = (max(3, args.steps // 10), 1) if args.only == "full_depth" else (args.steps, args.warmup)
-        res = measure(args.only, copies, steps, warmup)
-        print(json.dumps({"only": args.only, "steps": steps, "warmup": warmup, **res}), flush=True)
+        if args.only == "full_depth":
+            res = measure("full_depth", 1, args.steps, args.warmup)
+        else:
+            res = measure(args.only, args.copies, args.sub_steps, args.sub_warmup)
+        print(json.dumps({"only": args.only, **res}), flush=True)
         return
 
-    main_res = measure("llama_fork", args.copies, args.steps, args.warmup, rebuild=True)
-    loop_ms, loop_counters = _time_generation_loop(args.copies, 8, 1)
-    loop_rebuild_ms, _ = _time_generation_loop(args.copies, 8, 0)
-    loop_fused_ms, _ = _time_generation_loop(args.copies, 8, 1, fused=True)
-    generation_loop = {
-        "steps_timed": 8 * 16 * args.copies,
-        "ms_per_step": loop_ms,
-        "ms_per_step_plans_rebuilt": loop_rebuild_ms,
-        "ms_per_step_token_written_in_decode_call": loop_fused_ms,
-        "branch_tokens_per_s": 128 / (loop_ms / 1e3),
-        "plans_built_patched_one_copy": [loop_counters["plans_built"], loop_counters["plans_patched"]],
-    }
-    ms = main_res["ms_per_step"]
-    ubytes = main_res["unique_kv_bytes"]
-    value = main_res["unique_kv_GBps"]
-    achieved = main_res["partial_kernel_GBps"]
-
-    verify = None
-    if not args.no_verify:
-        v = measure("spec_verify", args.copies, args.steps, args.warmup)
-        v["verify_tokens_per_s"] = v["queries_per_s"]
-        verify = v
-    # the search tree is part of every run; the 32-layer workload (103 GB of
-    # pools to build) only with --all
-    others = {"mcts_tree": measure("mcts_tree", args.copies, args.steps, args.warmup)}
-    others["mcts_tree"]["branch_queries_per_s"] = others["mcts_tree"]["queries_per_s"]
-    if args.all:
-        others["full_depth"] = measure("full_depth", 1, max(3, args.steps // 10), 1)
-        others["full_depth"]["branch_query_steps_per_s"] = 1024 / (others["full_depth"]["ms_per_step"] / 1e3)
+    # the headline: one decode step (32 layer calls) of the 32-layer workload
+    head = measure("full_depth", 1, args.steps, args.warmup)
+    print("[bench] full_depth: %.3f ms per step, %.0f GB/s" % (head["ms_per_step"], head["unique_kv_GBps"]),
+          file=sys.stderr, flush=True)
+    subs = {}
+    for name, (rate_key, cfg) in SUBS.items():
+        r = measure(name, args.copies, args.sub_steps, args.sub_warmup, rebuild=name == "llama_fork")
+        r[rate_key] = r["queries_per_s"]
+        r["config"] = dict(cfg, **SHAPE, copies_rotated=args.copies)
+        subs[name] = r
+        print("[bench] %s: %.1f us per call, %.0f GB/s" % (name, r["ms_per_step"] * 1e3, r["unique_kv_GBps"]),
+              file=sys.stderr, flush=True)
+    generation_loop = native = None
+    if not args.no_loops:
+        loop_ms, loop_counters = _time_generation_loop(args.copies, 8, 1)
+        loop_rebuild_ms, _ = _time_generation_loop(args.copies, 8, 0)
+        loop_fused_ms, fused_counters = _time_generation_loop(args.copies, 8, 1, fused=True)
+        generation_loop = {
+            "workload": "llama_fork decode loop: one token per branch per step",
+            "steps_timed": 8 * 16 * args.copies,
+            "ms_per_step": loop_ms,
+            "ms_per_step_plans_rebuilt": loop_rebuild_ms,
+            "ms_per_step_token_written_in_decode_call": loop_fused_ms,
+            "branch_tokens_per_s": 128 / (loop_ms / 1e3),
+            "plans_built_patched_one_copy": [loop_counters["plans_built"], loop_counters["plans_patched"]],
+            "fused_plans_built_patched_one_copy": [fused_counters["plans_built"], fused_counters["plans_patched"]],
+        }
+        native = _native_loops()
+        print("[bench] loops done", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
-        cpu = _cpu_baseline(args.cpu_requests, args.cpu_reps)
+        for name in SUBS:
+            subs[name]["cpu_baseline"] = _cpu_baseline(name)
+        cpu = _cpu_baseline("full_depth")
+        print("[bench] cpu baselines done", file=sys.stderr, flush=True)
 
+    ms = head["ms_per_step"]
     line = {
         "metric": "tree-attn decode unique-KV GB/s (% HBM peak) + branch-queries/s; verify tokens/s",
-        "value": value,
+        "value": head["unique_kv_GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -517,26 +591,22 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "llama_fork", "requests": 32, "prefix_tokens": 4096, "fork_width": 4,
-                   "branch_tokens": 64, "q_heads": 32, "kv_heads": 8, "head_dim": 128, "block_size": 16,
-                   "decode_queries": main_res["queries_per_step"], "copies_rotated": args.copies},
-        "hbm_peak_frac": value / HBM_PEAK_GBS,
-        "branch_queries_per_s": main_res["queries_per_s"],
-        "ms_per_step_plan_rebuild": main_res["ms_per_step_plan_rebuild"],
+        "config": dict({"workload": "full_depth", "layers": 32, "requests": 64, "prefix_tokens": 8192,
+                        "fork_width": 16, "branch_tokens": 256, "decode_queries_per_layer": 1024,
+                        "attend_calls_per_step": head["attend_calls_per_step"], "copies": 1}, **SHAPE),
+        "hbm_peak_frac": head["hbm_peak_frac"],
+        "branch_queries_per_s": head["queries_per_s"],
+        "branch_query_steps_per_s": 1024 / (ms / 1e3),
+        "unique_kv_bytes": head["unique_kv_bytes"],
+        "plan": head["plan"],
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "host": _host_info(),
+        "workloads": subs,
         "generation_loop": generation_loop,
-        "native_loops": _native_loops(),
-        "unique_kv_bytes": ubytes,
-        "plan": main_res["plan"],
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None, "traffic": _recorded_traffic(),
-                     "kernel": "attn_partial_kernel<BF16,128,1,2,false>",
-                     "kernel_ms": main_res["partial_kernel_ms_per_call"],
-                     "merge_kernel_ms": main_res["merge_kernel_ms_per_call"]},
-        "verify": verify,
-        "other_workloads": others or None,
+        "native_loops": native,
         "fork_latency_ns": _fork_sweep_ns(),
         "fork_latency_ns_ctypes": _fork_latency_ns(),
-        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

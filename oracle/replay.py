@@ -64,6 +64,34 @@ class _LayerArrays:
             return a
 
 
+class PreloadedArrays:
+    """Every append call's values generated up front (on ``threads`` threads), so
+    that a timed replay measures the oracle's own work and not the input
+    generator; ``get`` answers as ``_LayerArrays.get`` does."""
+
+    def __init__(self, wl, threads: int = 1):
+        self.wl = wl
+        gen_ = _LayerArrays(wl, threads)
+        self.arrays: Dict[tuple, np.ndarray] = {}
+        for op in wl.ops:
+            if op[0] == "append":
+                calls = [(op[3], op[2])]
+            elif op[0] in ("append_batch",):
+                calls = [(op[3], sum(op[2]))]
+            elif op[0] == "reserve_batch":
+                calls = [(op[2], len(op[1]))]
+            else:
+                continue
+            for call, total in calls:
+                per_layer = total * wl.kv_heads * wl.head_dim
+                for kind in (gen.KIND_K, gen.KIND_V):
+                    whole = gen_._generate(gen.stream_id(kind, call), 0, wl.layers * per_layer)
+                    self.arrays[(call, kind)] = whole.reshape(wl.layers, total, wl.kv_heads, wl.head_dim)
+
+    def get(self, call: int, ntok: int, kind: int, layer: int) -> np.ndarray:
+        return self.arrays[(call, kind)][layer]
+
+
 def _source_for(wl, call: int, ntok: int, arrays: Optional[_LayerArrays] = None):
     return _batch_source_for(wl, call, ntok, 0, ntok, arrays)
 
@@ -82,16 +110,17 @@ def _batch_source_for(wl, call: int, total: int, first: int, ntok: int, arrays: 
 class OracleReplay:
     """``threads`` > 1: append values are generated a whole layer of a call at a
     time (the same numbers) and ``attend`` works on several handles at once;
-    the arithmetic of each output is unchanged."""
+    the arithmetic of each output is unchanged.  ``arrays``: a
+    ``PreloadedArrays`` holding every call's values already."""
 
-    def __init__(self, wl, with_alloc: bool = True, threads: int = 1):
+    def __init__(self, wl, with_alloc: bool = True, threads: int = 1, arrays=None):
         self.wl = wl
         self.alloc = FlatAllocator(wl.num_blocks, wl.block_size) if with_alloc else None
         self.mat = MaterializedCache()
         self.h_alloc: Dict[int, int] = {}
         self.h_mat: Dict[int, int] = {}
         self.threads = max(1, threads)
-        self.arrays = _LayerArrays(wl, self.threads) if self.threads > 1 else None
+        self.arrays = arrays if arrays is not None else (_LayerArrays(wl, self.threads) if self.threads > 1 else None)
 
     # -- structural ops --------------------------------------------------------
     def apply(self, op) -> None:

@@ -302,3 +302,16 @@ def test_bulk_generated_replay_is_the_same_replay():
             np.testing.assert_array_equal(a.attend(op), b.attend(op))
         a.apply(op)
         b.apply(op)
+
+
+def test_preloaded_replay_is_the_same_replay():
+    """OracleReplay over values generated up front (PreloadedArrays) gives
+    bit-identical outputs."""
+    from oracle.replay import PreloadedArrays
+    wl = _wl()
+    a, b = OracleReplay(wl), OracleReplay(wl, threads=2, arrays=PreloadedArrays(wl, 2))
+    for op in wl.ops:
+        if op[0] in ("decode", "decode_new", "verify"):
+            np.testing.assert_array_equal(a.attend(op), b.attend(op))
+        a.apply(op)
+        b.apply(op)
