@@ -293,11 +293,11 @@ def _cpu_baseline(name):
     full = recipes.STANDARD[name]()
     if name == "full_depth":
         wl = recipes.fork_workload("full_depth_sample", dtype="bf16", layers=32, q_heads=32, kv_heads=8,
-                                   head_dim=128, requests=1, prefix=8192, width=16, branch_tokens=256,
+                                   head_dim=128, requests=4, prefix=8192, width=16, branch_tokens=256,
                                    seed=full.seed)
-        scale = 64
-        sample = ("1 of the 64 requests (16 branches x 32 layers, 512 decode queries x 32 heads); the step's "
-                  "time extrapolated as 64 x the sample's")
+        scale = 16
+        sample = ("4 of the 64 requests (64 branches x 32 layers: 2048 decode queries x 32 heads); the step's "
+                  "time extrapolated as 16 x the sample's")
     else:
         wl, scale = full, 1
         sample = "the whole workload"
