@@ -177,6 +177,22 @@ int tkv_attend_decode_new_token(tkv_cache* c, int32_t layer, const tkv_seq* seqs
                                 const void* k_new, const void* v_new, const void* q, float* out,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* tkv_attend_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same plan and kernels as tkv_attend_decode, with the plan and the split-K
+ * partial records in a fixed workspace the library holds on each device (a
+ * file-scope device array of 64 MiB, present from the first tkv_create on that
+ * device until the process ends), so no workspace argument is taken.  The plan
+ * is uploaded from pinned staging made at tkv_create (4 MiB at least).  The call
+ * makes no hipMalloc, hipFree, host-pinned allocation, stream or event.
+ * TKV_E_WORKSPACE if the plan and its partial records exceed the fixed
+ * workspace or the plan exceeds the staging; otherwise errors as
+ * tkv_attend_decode.  Every call on one GPU shares that GPU's workspace: calls
+ * that overlap on the device (different streams, or different caches, without
+ * ordering between them) race.  The profiling events are not recorded for it. */
+int tkv_attend_decode_noalloc(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t nseq,
+                              const void* q, float* out, void* stream);
+
 /* Verification attention (DSpark blog, second layer: a block of drafts checked in one
  * parallel pass).  The last nq[i] tokens of handle i (1 <= nq[i] <= L_i) are queries;
  * the query at absolute position p attends over positions 0..p of its own path.

@@ -36,7 +36,8 @@ ATTN_FLAGS = ["-fno-honor-nans"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
               "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]
 
-LIB_SOURCES = ["tree.cpp", "plan.cpp", "capi.cpp", "attn.hip", "attn_rows.hip", "attn_merge.hip", "kv.hip"]
+LIB_SOURCES = ["tree.cpp", "plan.cpp", "capi.cpp", "attn.hip", "attn_rows.hip", "attn_merge.hip", "kv.hip",
+               "static_ws.hip"]
 
 
 def _run(cmd, verbose):

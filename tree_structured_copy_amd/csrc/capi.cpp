@@ -62,6 +62,10 @@ struct PlanSlot {
 };
 
 constexpr int kPlanSlots = 4;
+// pinned staging made at tkv_create: the largest plan tkv_attend_decode_noalloc
+// can upload without allocating (the 32-layer workload's decode plan is about
+// 1.4 MiB)
+constexpr size_t kStaticPlanStagingBytes = size_t(4) << 20;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -381,9 +385,28 @@ int prepare_new_tokens(tkv_cache* c, PlanSlot* s, int32_t layer, int32_t nseq, c
   return TKV_OK;
 }
 
+// The plan of a tkv_attend_decode_noalloc call, copied into the fixed device
+// workspace `base` from the pinned staging made at tkv_create (no allocation:
+// a plan larger than that staging is refused).
+int upload_plan_fixed(tkv_cache* c, const Plan& P, char* base, hipStream_t stream) {
+  if (P.bytes > c->pinned_cap || !c->pinned_ev) return TKV_E_WORKSPACE;
+  if (c->pinned_busy) {
+    if (hipEventSynchronize(c->pinned_ev) != hipSuccess) return TKV_E_DEVICE;
+    c->pinned_busy = false;
+  }
+  P.serialise(c->pinned);
+  if (hipMemcpyAsync(base, c->pinned, P.bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return TKV_E_DEVICE;
+  if (hipEventRecord(c->pinned_ev, stream) != hipSuccess) return TKV_E_DEVICE;
+  c->pinned_busy = true;
+  return TKV_OK;
+}
+
+// fixed_ws: the call's plan and partial records go to the device's fixed
+// workspace (tkv_attend_decode_noalloc) instead of the cached plan's buffer
+// and the caller's workspace; nothing is allocated and no events are kept.
 int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
            const void* q, float* out, void* ws, size_t ws_bytes, void* stream_,
-           const void* k_new = nullptr, const void* v_new = nullptr) {
+           const void* k_new = nullptr, const void* v_new = nullptr, bool fixed_ws = false) {
   if (!c) return TKV_E_INVAL;
   if (!c->has_pools) return TKV_E_NODEVICE;
   if (layer < 0 || layer >= c->cfg.num_layers) return TKV_E_RANGE;
@@ -415,17 +438,27 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   if (int rc = find_plan(c, seqs, nq, nseq, &s)) return rc;
   const Plan& P = s->plan;
   const size_t need = partial_bytes(c, P);
-  if (need > 0 && (!ws || ws_bytes < need)) return TKV_E_WORKSPACE;
+  char* fixed = nullptr;
+  if (fixed_ws) {
+    fixed = static_cast<char*>(static_workspace(c->device));
+    if (!fixed) return TKV_E_DEVICE;
+    if (align256(P.bytes) + need > kStaticWorkspaceBytes) return TKV_E_WORKSPACE;
+    ws = fixed + align256(P.bytes);
+  } else if (need > 0 && (!ws || ws_bytes < need)) {
+    return TKV_E_WORKSPACE;
+  }
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   DeviceGuard dg(c->device);
   launch_log_reset();
-  if (k_new) {
+  if (fixed) {
+    if (int rc = upload_plan_fixed(c, P, fixed, stream)) return rc;
+  } else if (k_new) {
     if (int rc = prepare_new_tokens(c, s, layer, nseq, k_new, v_new, stream)) return rc;
   } else if (int rc = upload_plan(c, s, stream)) {
     return rc;
   }
 
-  const char* dev = static_cast<const char*>(s->dev);
+  const char* dev = fixed ? fixed : static_cast<const char*>(s->dev);
   AttnArgs a{};
   a.kpool = c->kpool_layer(layer);
   a.vpool = c->vpool_layer(layer);
@@ -446,7 +479,8 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(c->cfg.head_dim)));
 
   std::array<hipEvent_t, 3> ev{nullptr, nullptr, nullptr};
-  if (c->prof) {
+  const bool prof = c->prof && !fixed;
+  if (prof) {
     for (auto& e : ev) e = c->get_event();
     if (ev[0] && ev[1] && ev[2]) (void)hipEventRecord(ev[0], stream);
   }
@@ -458,7 +492,7 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   int ncls = 0;
   for (int cls = 0; cls < kKernelClasses; ++cls)
     if (P.bucket_begin[cls + 1] > P.bucket_begin[cls]) classes[ncls++] = cls;
-  const bool side = c->concurrent == 1 && ncls > 1;
+  const bool side = c->concurrent == 1 && ncls > 1 && !fixed;
   if (side) {
     if (!c->fork_ev && hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming) != hipSuccess) return TKV_E_DEVICE;
     for (int k = 0; k < ncls - 1; ++k) {
@@ -497,7 +531,7 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   if (side)
     for (int k = 1; k < ncls; ++k)
       if (hipStreamWaitEvent(stream, c->join_ev[k - 1], 0) != hipSuccess) return TKV_E_DEVICE;
-  if (c->prof && ev[1]) (void)hipEventRecord(ev[1], stream);
+  if (prof && ev[1]) (void)hipEventRecord(ev[1], stream);
   if (P.any_merge) {
     MergeArgs m{};
     m.parts = reinterpret_cast<const DevPart*>(dev + P.off_parts);
@@ -511,7 +545,7 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     if (launch_attn_merge(c->cfg.head_dim, m, stream) != hipSuccess) return TKV_E_DEVICE;
   }
   std::memcpy(c->last_kernels, launch_log(), std::strlen(launch_log()) + 1);
-  if (c->prof) {
+  if (prof) {
     bool kept = false;
     if (ev[0] && ev[1] && ev[2]) {
       (void)hipEventRecord(ev[2], stream);
@@ -577,6 +611,13 @@ int tkv_create(const tkv_config* cfg, tkv_cache** out) {
       return TKV_E_DEVICE;
     }
     if (cus > 0) cache->opt.target_wgs = cache->cus = cus;
+    // set-up for tkv_attend_decode_noalloc: this device's fixed workspace and
+    // the cache's pinned plan staging (later calls may grow the staging, never
+    // shrink it)
+    if (static_workspace_init(cache->device) || stage(cache, kStaticPlanStagingBytes)) {
+      tkv_destroy(cache);
+      return TKV_E_DEVICE;
+    }
   }
   *out = cache;
   return TKV_OK;
@@ -716,6 +757,11 @@ int tkv_attend_decode_new_token(tkv_cache* c, int32_t layer, const tkv_seq* seqs
                                 void* stream) {
   if (!k_new || !v_new) return TKV_E_INVAL;
   return attend(c, layer, seqs, nullptr, nseq, q, out, ws, ws_bytes, stream, k_new, v_new);
+}
+
+int tkv_attend_decode_noalloc(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t nseq, const void* q,
+                              float* out, void* stream) {
+  return attend(c, layer, seqs, nullptr, nseq, q, out, nullptr, 0, stream, nullptr, nullptr, true);
 }
 
 int tkv_attend_verify(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,

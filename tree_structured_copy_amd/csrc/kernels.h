@@ -6,6 +6,15 @@
 
 namespace tkv {
 
+// The fixed device workspace of tkv_attend_decode_noalloc (static_ws.hip): a
+// file-scope device array of this many bytes on every device the library runs
+// on.  static_workspace_init(device) looks its address up once per device
+// (with that device made current); static_workspace(device) returns it, or
+// nullptr before the init.  Nothing else may name the array.
+constexpr size_t kStaticWorkspaceBytes = size_t(64) << 20;
+int static_workspace_init(int device);
+void* static_workspace(int device);
+
 // Names of the kernels launched by this host thread since launch_log_reset(),
 // "name<template arguments>" joined by ';' (a fixed buffer: nothing is
 // allocated; names past its end are dropped).  The launchers below add theirs.

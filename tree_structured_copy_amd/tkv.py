@@ -114,6 +114,7 @@ _SIGS = {
     "tkv_attend_decode": [_P, _I32, _pU64, _I32, _P, _P, _P, _SZ, _P],
     "tkv_attend_verify": [_P, _I32, _pU64, _pI32, _I32, _P, _P, _P, _SZ, _P],
     "tkv_attend_decode_new_token": [_P, _I32, _pU64, _I32, _P, _P, _P, _P, _P, _SZ, _P],
+    "tkv_attend_decode_noalloc": [_P, _I32, _pU64, _I32, _P, _P, _P],
     "tkv_gather": [_P, _U64, _I32, _P, _P, _P],
     "tkv_seq_len": [_P, _U64, ctypes.POINTER(_I64)],
     "tkv_block_table": [_P, _U64, _pI32, _pI32, _I32, _pI32],
@@ -238,6 +239,12 @@ def tkv_attend_decode(c, layer: int, seqs, q, out, ws=None, ws_bytes: int = 0, s
     sa = seq_array(seqs)
     _check(_lib.tkv_attend_decode(c, layer, sa, len(sa), _ptr(q), _ptr(out), _ptr(ws), ws_bytes,
                                   _stream(stream)), "tkv_attend_decode")
+
+
+def tkv_attend_decode_noalloc(c, layer: int, seqs, q, out, stream=None) -> None:
+    sa = seq_array(seqs)
+    _check(_lib.tkv_attend_decode_noalloc(c, layer, sa, len(sa), _ptr(q), _ptr(out), _stream(stream)),
+           "tkv_attend_decode_noalloc")
 
 
 def tkv_attend_decode_new_token(c, layer: int, seqs, k_new, v_new, q, out, ws=None, ws_bytes: int = 0,
