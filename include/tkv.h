@@ -166,10 +166,15 @@ int tkv_attend_decode(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t 
  * handle i (each at most once), its last token -- which must lie in the handle's
  * own tip node, e.g. reserved for all layers by tkv_append_batch with k = v = NULL
  * -- gets K = k_new[i], V = v_new[i] for `layer` (device [nseq][Hkv][head_dim], cache
- * dtype), then the call is tkv_attend_decode over the paths that include it.  The
- * tokens are written in the same launch as the plan's in-place update (one launch
- * per 128 tokens) before the attention kernels, on `stream`.  A token that opened
- * its block is written with zeros in the block's other slots.  Errors as
+ * dtype), then the call is tkv_attend_decode over the paths that include it.  With up
+ * to 224 handles, and no change to the cached plan since its last use other than
+ * these tokens (the usual decode step after tkv_append_batch reserved them), the
+ * attention launch itself writes each token -- the workgroup that reads its block
+ * writes it first -- and the block's valid count in the plan: one launch per step
+ * (TKV_OPT_FUSED_NEW_TOKEN).  Otherwise a preparation launch (one per 128 tokens)
+ * writes them and the plan's changed words before the attention kernels, on
+ * `stream`.  A token that opened its block is written with zeros in the block's
+ * other slots.  Errors as
  * tkv_attend_decode, plus TKV_E_INVAL for a handle given twice or a null k_new /
  * v_new, and TKV_E_SHARED when a handle's last token is shared with other branches
  * (its tip node was forked, or it has no tokens of its own). */
@@ -266,11 +271,15 @@ enum {
   TKV_OPT_CONCURRENT = 7,   /* how a call's kernel classes run: 0 = one after another on the call's
                                stream (default); 1 = at once, on side streams of the library's own
                                forked from and joined back to the call's stream */
-  TKV_OPT_PLAN_PATCH = 8    /* 1 = a cached plan made before appends that each fitted in their tip
+  TKV_OPT_PLAN_PATCH = 8,   /* 1 = a cached plan made before appends that each fitted in their tip
                                node's last block (no new block, node, fork, release or truncation
                                since) is updated in place: the changed block counts and query
                                positions are written into its device copy by a small kernel
                                (default); 0 = such a plan is rebuilt and uploaded whole */
+  TKV_OPT_FUSED_NEW_TOKEN = 9 /* 1 = tkv_attend_decode_new_token writes its tokens (and their blocks'
+                               valid counts in the plan) from the attention launch itself when it
+                               can: one launch per step (default); 0 = always by a preparation
+                               launch first */
 };
 int tkv_set_option(tkv_cache* c, int32_t key, int64_t value);
 int tkv_get_option(const tkv_cache* c, int32_t key, int64_t* value);

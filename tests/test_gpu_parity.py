@@ -426,21 +426,25 @@ def test_loop_recipes_match_oracle(kind):
     assert_close(res, wl.dtype)
 
 
+@pytest.mark.parametrize("one_launch", [1, 0])
 @pytest.mark.parametrize("dtype,layers,head_dim", [("bf16", 1, 128), ("bf16", 2, 128), ("f32", 1, 64),
                                                    ("bf16", 1, 64), ("f32", 2, 128)])
-def test_decode_with_new_token_written_in_the_call(dtype, layers, head_dim):
+def test_decode_with_new_token_written_in_the_call(dtype, layers, head_dim, one_launch):
     """The fused decode step: each round reserves one token per branch
     (tkv_append_batch without K/V), then per layer tkv_attend_decode_new_token
-    writes that layer's K/V of the token and decodes.  Every call matches the
-    oracle; outputs and pool contents equal, bit for bit, those of the same
-    loop run as a batched append with K/V followed by tkv_attend_decode."""
+    writes that layer's K/V of the token and decodes -- from the attention
+    launch itself (one_launch = 1: TKV_OPT_FUSED_NEW_TOKEN, every call launches
+    only attention kernels) or from a preparation launch first.  Every call
+    matches the oracle; outputs and pool contents equal, bit for bit, those of
+    the same loop run as a batched append with K/V followed by
+    tkv_attend_decode."""
     torch = need_gpu()
     from tree_structured_copy_amd import tkv
     from tree_structured_copy_amd.replay import LibReplay
     import dataclasses
     wl = recipes.decode_loop_workload("fused_%s_%d_%d" % (dtype, layers, head_dim), dtype=dtype, layers=layers,
                                       head_dim=head_dim, rounds=14, fused=True, seed=81)
-    assert_close(run_both(wl), wl.dtype)
+    assert_close(run_both(wl, options={tkv.TKV_OPT_FUSED_NEW_TOKEN: one_launch}), wl.dtype)
     plain_ops = []
     for op in wl.ops:
         if op[0] == "reserve_batch":
@@ -453,11 +457,21 @@ def test_decode_with_new_token_written_in_the_call(dtype, layers, head_dim):
     outs, pools = {}, {}
     for key, w in (("fused", wl), ("plain", plain)):
         lib = LibReplay(w)
+        tkv.tkv_set_option(lib.c, tkv.TKV_OPT_FUSED_NEW_TOKEN, one_launch)
         try:
             got = []
             for op in w.ops:
                 if op[0] in ("decode", "decode_new"):
                     got.append(lib.attend(op).cpu())
+                    if op[0] == "decode_new":
+                        names = tkv.tkv_last_kernels(lib.c)
+                        attn = [n for n in names if n.startswith(("attn_partial_kernel", "attn_rows_kernel"))]
+                        prep = [n for n in names if n.startswith(("decode_prep_kernel", "plan_patch"))]
+                        assert attn, names
+                        if one_launch:
+                            assert not prep and all("NewTokens" in n for n in attn), names
+                        else:
+                            assert prep and not any("NewTokens" in n for n in attn), names
                 lib.apply(op)
             torch.cuda.synchronize()
             outs[key] = got
@@ -515,14 +529,19 @@ def test_decode_with_new_token_refusals():
         tkv.tkv_destroy(c)
 
 
-def test_decode_with_new_token_more_than_128_handles():
-    """135 branches in one fused decode call: its tokens are written by two
-    preparation launches (128 + 7), the first also carrying the plan's changed
-    words.  Every call matches the oracle."""
-    wl = recipes.decode_loop_workload("fused_wide", requests=45, width=3, branch_tokens=14, rounds=4, fused=True,
-                                      seed=83)
-    assert len(wl.attend_ops()[0][2]) == 135
-    assert_close(run_both(wl), wl.dtype)
+@pytest.mark.parametrize("requests,one_launch", [(45, 0), (45, 1), (80, 1)])
+def test_decode_with_new_token_more_than_128_handles(requests, one_launch):
+    """135 branches in one fused decode call: its tokens are written by the
+    attention launch (one_launch = 1, up to 224 tokens) or by two preparation
+    launches (128 + 7), the first also carrying the plan's changed words; 240
+    branches are more than one attention launch carries, so preparation
+    launches write them even with one_launch = 1.  Every call matches the
+    oracle."""
+    from tree_structured_copy_amd import tkv
+    wl = recipes.decode_loop_workload("fused_wide_%d" % requests, requests=requests, width=3, branch_tokens=14,
+                                      rounds=4, fused=True, seed=83)
+    assert len(wl.attend_ops()[0][2]) == 3 * requests
+    assert_close(run_both(wl, options={tkv.TKV_OPT_FUSED_NEW_TOKEN: one_launch}), wl.dtype)
 
 
 @pytest.mark.parametrize("concurrent", [0, 1])

@@ -36,8 +36,10 @@ namespace {
 
 using namespace attn;
 
-template <class P, int D, int T, int W, bool CAUSAL>
-__global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
+// X = NewTokens: the launch first writes a decode step's new tokens that lie
+// in its items' blocks (write_new_tokens); X = NoNewTokens: it writes none.
+template <class P, int D, int T, int W, bool CAUSAL, class X>
+__global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
   using E = typename P::elem;
   using F = typename P::template Frag<D>;
   constexpr int NDT = D / 16;
@@ -48,6 +50,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
   const int g = lane >> 4, r = lane & 15;
   const int kvh = blockIdx.x % a.hkv;
   const DevItem it = a.items[a.item0 + blockIdx.x / a.hkv];
+  if constexpr (X::kActive) write_new_tokens<P, D>(x, it, kvh, 1, a.hkv, tid, NT);
   const int nb = it.blk_count;
   const int nsb = (nb + 1) >> 1;
   // super-blocks of this wave: a contiguous share of the item (two waves
@@ -274,58 +277,56 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a) {
   }
 }
 
-template <class P, int D, int T, int W, bool C>
+template <class P, int D, int T, int W, bool C, class X>
 void note_partial() {
-  char nm[96];
-  snprintf(nm, sizeof nm, "attn_partial_kernel<%s, %d, %d, %d, %s>", P::kName, D, T, W, C ? "true" : "false");
+  char nm[112];
+  snprintf(nm, sizeof nm, "attn_partial_kernel<%s, %d, %d, %d, %s%s>", P::kName, D, T, W, C ? "true" : "false",
+           X::kActive ? ", NewTokens" : "");
   launch_log_add(nm);
 }
 
-template <class P, int D, int W, bool C>
-hipError_t launch_t(int tiles, const AttnArgs& args, int32_t n_items, hipStream_t s) {
-  const dim3 grid(n_items * args.hkv), block(64 * W);
-  switch (tiles) {
-    case 1: hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, W, C>), grid, block, 0, s, args); note_partial<P, D, 1, W, C>(); break;
-    case 2: hipLaunchKernelGGL((attn_partial_kernel<P, D, 2, W, C>), grid, block, 0, s, args); note_partial<P, D, 2, W, C>(); break;
-    default: return hipErrorInvalidValue;
-  }
+template <class P, int D, int T, int W, bool C, class X>
+hipError_t launch_one(const AttnArgs& args, const X& x, int32_t n_items, hipStream_t s) {
+  hipLaunchKernelGGL((attn_partial_kernel<P, D, T, W, C, X>), dim3(n_items * args.hkv), dim3(64 * W), 0, s, args, x);
+  note_partial<P, D, T, W, C, X>();
   return hipGetLastError();
 }
 
 // Eight waves only at one tile and not for fp32 at d = 128 (more fragments per
-// wave than eight waves leave registers for).
-template <class P, int D, bool C>
-hipError_t launch_w(int tiles, int waves, const AttnArgs& args, int32_t n_items, hipStream_t s) {
+// wave than eight waves leave registers for); two waves at one tile; four
+// otherwise.
+template <class P, int D, bool C, class X>
+hipError_t launch_w(int tiles, int waves, const AttnArgs& args, const X& x, int32_t n_items, hipStream_t s) {
   if constexpr (kIsBF16<P> || D <= 64) {
-    if (waves == 8 && tiles == 1) {
-      hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, 8, C>), dim3(n_items * args.hkv), dim3(64 * 8), 0, s, args);
-      note_partial<P, D, 1, 8, C>();
-      return hipGetLastError();
-    }
+    if (waves == 8 && tiles == 1) return launch_one<P, D, 1, 8, C, X>(args, x, n_items, s);
   }
-  if (waves == 2 && tiles == 1) {
-    hipLaunchKernelGGL((attn_partial_kernel<P, D, 1, 2, C>), dim3(n_items * args.hkv), dim3(64 * 2), 0, s, args);
-    note_partial<P, D, 1, 2, C>();
-    return hipGetLastError();
-  }
-  return launch_t<P, D, 4, C>(tiles, args, n_items, s);
+  if (waves == 2 && tiles == 1) return launch_one<P, D, 1, 2, C, X>(args, x, n_items, s);
+  if (tiles == 1) return launch_one<P, D, 1, 4, C, X>(args, x, n_items, s);
+  if (tiles == 2) return launch_one<P, D, 2, 4, C, X>(args, x, n_items, s);
+  return hipErrorInvalidValue;
 }
 
 template <class P, int D>
-hipError_t launch_c(int tiles, int waves, bool causal, const AttnArgs& args, int32_t n_items, hipStream_t s) {
-  return causal ? launch_w<P, D, true>(tiles, waves, args, n_items, s) : launch_w<P, D, false>(tiles, waves, args, n_items, s);
+hipError_t launch_c(int tiles, int waves, bool causal, const AttnArgs& args, const NewTokens* nt, int32_t n_items,
+                    hipStream_t s) {
+  if (nt) {
+    if (causal) return hipErrorInvalidValue;
+    return launch_w<P, D, false, NewTokens>(tiles, waves, args, *nt, n_items, s);
+  }
+  return causal ? launch_w<P, D, true, NoNewTokens>(tiles, waves, args, NoNewTokens{}, n_items, s)
+                : launch_w<P, D, false, NoNewTokens>(tiles, waves, args, NoNewTokens{}, n_items, s);
 }
 
 }  // namespace
 
 hipError_t launch_attn_partial(int dtype, int head_dim, int tiles, int waves, bool causal, const AttnArgs& args,
-                               int32_t n_items, hipStream_t stream) {
+                               int32_t n_items, hipStream_t stream, const NewTokens* nt) {
   if (n_items <= 0) return hipSuccess;
   if (waves != 2 && waves != 4 && waves != 8) return hipErrorInvalidValue;
-  if (dtype == 1 && head_dim == 128) return launch_c<BF16, 128>(tiles, waves, causal, args, n_items, stream);
-  if (dtype == 1 && head_dim == 64) return launch_c<BF16, 64>(tiles, waves, causal, args, n_items, stream);
-  if (dtype == 0 && head_dim == 128) return launch_c<F32, 128>(tiles, waves, causal, args, n_items, stream);
-  if (dtype == 0 && head_dim == 64) return launch_c<F32, 64>(tiles, waves, causal, args, n_items, stream);
+  if (dtype == 1 && head_dim == 128) return launch_c<BF16, 128>(tiles, waves, causal, args, nt, n_items, stream);
+  if (dtype == 1 && head_dim == 64) return launch_c<BF16, 64>(tiles, waves, causal, args, nt, n_items, stream);
+  if (dtype == 0 && head_dim == 128) return launch_c<F32, 128>(tiles, waves, causal, args, nt, n_items, stream);
+  if (dtype == 0 && head_dim == 64) return launch_c<F32, 64>(tiles, waves, causal, args, nt, n_items, stream);
   return hipErrorInvalidValue;
 }
 

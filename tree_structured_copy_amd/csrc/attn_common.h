@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "layout.h"
 #include "tkv_types.h"
 
 namespace tkv {
@@ -279,6 +280,85 @@ struct SBMeta {
 
 template <class P>
 constexpr bool kIsBF16 = sizeof(typename P::elem) == 2;
+
+// A decode step's new tokens that lie in this work item's blocks (plan entries
+// [it.blk_begin, it.blk_begin + it.blk_count)) are written into the pool tiles
+// of KV heads [h0, h0 + nh) -- a block the token opens (slot 0) whole, with
+// zeros in its other slots -- and their blocks' valid counts (slot + 1) into
+// the plan's block list (every KV head's workgroup writes the same value);
+// then both are made visible to the workgroup's later reads.  Every thread of
+// the workgroup calls this before any of them reads the pool or the plan's
+// block entries.  Only this workgroup reads these tiles and entries in the
+// launch: an unfrozen tip block appears once in a plan.
+template <class P, int D>
+__device__ void write_new_tokens(const NewTokens& x, const DevItem& it, int h0, int nh, int hkv, int tid,
+                                 int nthreads) {
+  using E = typename P::elem;
+  constexpr int EB = static_cast<int>(sizeof(E));
+  using L = Layout<EB>;
+  constexpr int PC = L::kPerChunk;
+  constexpr int NCH = 16 * D / PC;
+  using Chunk = u32x4;
+  const int lane = tid & 63;
+  bool any = false;
+  for (int base = 0; base < x.n; base += 64) {
+    const int k = base + lane;
+    const int e = k < x.n ? x.tok[k].entry : -1;
+    const bool mine = e >= it.blk_begin && e < it.blk_begin + it.blk_count;
+    uint64_t m = __ballot(mine);
+    while (m) {
+      const int j = __builtin_ctzll(m);
+      m &= m - 1;
+      any = true;
+      const NewTok t = x.tok[base + j];
+      const bool fresh = t.slot == 0;
+      const int units = fresh ? 2 * NCH : D / PC + D;  // per head
+      for (int u = tid; u < nh * units; u += nthreads) {
+        const int hh = u / units, w = u - hh * units;
+        const int h = h0 + hh;
+        const size_t tile = (static_cast<size_t>(t.blk) * hkv + h) * (16 * D);
+        E* kt = static_cast<E*>(x.kpool) + tile;
+        E* vt = static_cast<E*>(x.vpool) + tile;
+        const E* sk = static_cast<const E*>(x.k) + (static_cast<size_t>(t.src) * hkv + h) * D;
+        const E* sv = static_cast<const E*>(x.v) + (static_cast<size_t>(t.src) * hkv + h) * D;
+        if (fresh) {
+          // chunk w % NCH of K (w < NCH) or of V: the token in slot 0, zeros elsewhere
+          const bool isk = w < NCH;
+          const int ch = isk ? w : w - NCH;
+          E vals[PC];
+#pragma unroll
+          for (int el = 0; el < PC; ++el) {
+            int tok, d;
+            if (isk) L::k_coord(ch, el, tok, d);
+            else L::v_coord(ch, el, tok, d);
+            vals[el] = tok == 0 ? (isk ? sk[d] : sv[d]) : E(0);
+          }
+          *reinterpret_cast<Chunk*>((isk ? kt : vt) + ch * PC) = *reinterpret_cast<const Chunk*>(vals);
+        } else if (w < D / PC) {
+          // K: chunk w of the token's row (PC consecutive d), one 16-byte store
+          int ch;
+          if constexpr (EB == 2) ch = w * 16 + t.slot;
+          else ch = (w >> 2) * 64 + (w & 3) * 16 + t.slot;
+          *reinterpret_cast<Chunk*>(kt + ch * PC) = *reinterpret_cast<const Chunk*>(sk + w * PC);
+        } else {
+          // V: element d of the token, inside the unit (bf16) or chunk (fp32)
+          // that holds tokens 4 (slot / 4) .. + 3 at that d
+          const int d = w - D / PC;
+          const int at = ((d >> 4) * 64 + (t.slot >> 2) * 16 + (d & 15)) * 4 + (t.slot & 3);
+          vt[at] = sv[d];
+        }
+      }
+      if (tid == 0) x.blocks[t.entry].valid = t.slot + 1;
+    }
+  }
+  if (any) {
+    // every store of the workgroup acknowledged (in L2) before any wave loads
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+}
 
 }  // namespace attn
 }  // namespace tkv

@@ -52,8 +52,10 @@ struct StagedBlock {
 };
 constexpr uint32_t kStagedIdMask = (1u << 27) - 1;
 
-template <class P, int D, int TPW, int W, int HPW, int NS, bool EARLY, int MINW, bool CAUSAL>
-__global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs a) {
+// X = NewTokens: the launch first writes a decode step's new tokens that lie
+// in its items' blocks (write_new_tokens); X = NoNewTokens: it writes none.
+template <class P, int D, int TPW, int W, int HPW, int NS, bool EARLY, int MINW, bool CAUSAL, class X>
+__global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs a, X x) {
   using E = typename P::elem;
   using F = typename P::template Frag<D>;
   constexpr int NDT = D / 16;
@@ -80,6 +82,7 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
   const int kvh0 = (blockIdx.x % hgroups) * HPW;
   const int kvh = kvh0 + hsel;
   const DevItem it = a.items[a.item0 + blockIdx.x / hgroups];
+  if constexpr (X::kActive) write_new_tokens<P, D>(x, it, kvh0, HPW, a.hkv, tid, 64 * W * HPW);
   const int nb = it.blk_count;
   const int nsb = (nb + 1) >> 1;
   const DevBlock* bl = a.blocks + it.blk_begin;
@@ -356,14 +359,14 @@ constexpr int ring_slots() {
   return (BUDGET_KB * 1024 / stage) < 8 ? (BUDGET_KB * 1024 / stage) : 8;
 }
 
-template <class P, int D, int TPW, int W, int HPW, int NS, bool EARLY, int MINW, bool C>
-hipError_t launch_one(const AttnArgs& args, int32_t n_items, hipStream_t s) {
+template <class P, int D, int TPW, int W, int HPW, int NS, bool EARLY, int MINW, bool C, class X>
+hipError_t launch_one(const AttnArgs& args, const X& x, int32_t n_items, hipStream_t s) {
   const size_t ents_bytes = sizeof(StagedBlock) * static_cast<size_t>(args.max_blocks > 0 ? args.max_blocks : 1);
-  hipLaunchKernelGGL((attn_rows_kernel<P, D, TPW, W, HPW, NS, EARLY, MINW, C>), dim3(n_items * (args.hkv / HPW)),
-                     dim3(64 * W * HPW), ents_bytes, s, args);
-  char nm[96];
-  snprintf(nm, sizeof nm, "attn_rows_kernel<%s, %d, %d, %d, %d, %d, %s, %d, %s>", P::kName, D, TPW, W, HPW, NS,
-           EARLY ? "true" : "false", MINW, C ? "true" : "false");
+  hipLaunchKernelGGL((attn_rows_kernel<P, D, TPW, W, HPW, NS, EARLY, MINW, C, X>), dim3(n_items * (args.hkv / HPW)),
+                     dim3(64 * W * HPW), ents_bytes, s, args, x);
+  char nm[112];
+  snprintf(nm, sizeof nm, "attn_rows_kernel<%s, %d, %d, %d, %d, %d, %s, %d, %s%s>", P::kName, D, TPW, W, HPW, NS,
+           EARLY ? "true" : "false", MINW, C ? "true" : "false", X::kActive ? ", NewTokens" : "");
   launch_log_add(nm);
   return hipGetLastError();
 }
@@ -383,54 +386,59 @@ constexpr int shallow_slots() {
 // workgroups fit a CU; with no more workgroups than CUs the ring is filled
 // deeper, as one workgroup then has the CU's loads in flight alone.  fp32 at
 // d = 128 needs the registers of one workgroup per CU.
-template <class P, int D, bool C>
-hipError_t launch_shape(int tiles, const AttnArgs& args, int32_t n_items, hipStream_t s, int cus) {
+template <class P, int D, bool C, class X>
+hipError_t launch_shape(int tiles, const AttnArgs& args, const X& x, int32_t n_items, hipStream_t s, int cus) {
   constexpr bool kSmall = kIsBF16<P> || D <= 64;
   if (tiles <= 4) {
     if constexpr (kSmall) {
       if (static_cast<int64_t>(n_items) * args.hkv > cus)
-        return launch_one<P, D, 1, 4, 1, shallow_slots<P, D, 1>(), false, 2, C>(args, n_items, s);
-      return launch_one<P, D, 1, 4, 1, ring_slots<P, D, 1, 64>(), false, 2, C>(args, n_items, s);
+        return launch_one<P, D, 1, 4, 1, shallow_slots<P, D, 1>(), false, 2, C, X>(args, x, n_items, s);
+      return launch_one<P, D, 1, 4, 1, ring_slots<P, D, 1, 64>(), false, 2, C, X>(args, x, n_items, s);
     } else {
-      return launch_one<P, D, 1, 4, 1, ring_slots<P, D, 1, 128>(), false, 1, C>(args, n_items, s);
+      return launch_one<P, D, 1, 4, 1, ring_slots<P, D, 1, 128>(), false, 1, C, X>(args, x, n_items, s);
     }
   }
   if (tiles <= 6) {
     // two heads per workgroup where the head count allows, so that its 12 waves
     // spread evenly over the CU's four SIMDs (6 waves would sit 2, 2, 1, 1)
     if constexpr (kSmall) {
-      if (args.hkv % 2 == 0) return launch_one<P, D, 1, 6, 2, shallow_slots<P, D, 2>(), false, 3, C>(args, n_items, s);
-      return launch_one<P, D, 1, 6, 1, shallow_slots<P, D, 1>(), false, 3, C>(args, n_items, s);
+      if (args.hkv % 2 == 0) return launch_one<P, D, 1, 6, 2, shallow_slots<P, D, 2>(), false, 3, C, X>(args, x, n_items, s);
+      return launch_one<P, D, 1, 6, 1, shallow_slots<P, D, 1>(), false, 3, C, X>(args, x, n_items, s);
     } else {
-      return launch_one<P, D, 1, 6, 1, ring_slots<P, D, 1, 128>(), false, 2, C>(args, n_items, s);
+      return launch_one<P, D, 1, 6, 1, ring_slots<P, D, 1, 128>(), false, 2, C, X>(args, x, n_items, s);
     }
   }
   if (tiles <= 8) {
-    if constexpr (kSmall) return launch_one<P, D, 1, 8, 1, shallow_slots<P, D, 1>(), false, 4, C>(args, n_items, s);
-    else return launch_one<P, D, 1, 8, 1, ring_slots<P, D, 1, 128>(), false, 2, C>(args, n_items, s);
+    if constexpr (kSmall) return launch_one<P, D, 1, 8, 1, shallow_slots<P, D, 1>(), false, 4, C, X>(args, x, n_items, s);
+    else return launch_one<P, D, 1, 8, 1, ring_slots<P, D, 1, 128>(), false, 2, C, X>(args, x, n_items, s);
   }
   if (tiles <= 16) {
-    if constexpr (kSmall) return launch_one<P, D, 1, 16, 1, shallow_slots<P, D, 1>(), false, 4, C>(args, n_items, s);
-    else return launch_one<P, D, 2, 8, 1, ring_slots<P, D, 1, 128>(), false, 2, C>(args, n_items, s);
+    if constexpr (kSmall) return launch_one<P, D, 1, 16, 1, shallow_slots<P, D, 1>(), false, 4, C, X>(args, x, n_items, s);
+    else return launch_one<P, D, 2, 8, 1, ring_slots<P, D, 1, 128>(), false, 2, C, X>(args, x, n_items, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <class P, int D>
-hipError_t launch_c(int tiles, bool causal, const AttnArgs& args, int32_t n_items, hipStream_t s, int cus) {
-  return causal ? launch_shape<P, D, true>(tiles, args, n_items, s, cus)
-                : launch_shape<P, D, false>(tiles, args, n_items, s, cus);
+hipError_t launch_c(int tiles, bool causal, const AttnArgs& args, const NewTokens* nt, int32_t n_items, hipStream_t s,
+                    int cus) {
+  if (nt) {
+    if (causal) return hipErrorInvalidValue;
+    return launch_shape<P, D, false, NewTokens>(tiles, args, *nt, n_items, s, cus);
+  }
+  return causal ? launch_shape<P, D, true, NoNewTokens>(tiles, args, NoNewTokens{}, n_items, s, cus)
+                : launch_shape<P, D, false, NoNewTokens>(tiles, args, NoNewTokens{}, n_items, s, cus);
 }
 
 }  // namespace
 
 hipError_t launch_attn_rows(int dtype, int head_dim, int tiles, bool causal, const AttnArgs& args, int32_t n_items,
-                            hipStream_t stream, int cus) {
+                            hipStream_t stream, int cus, const NewTokens* nt) {
   if (n_items <= 0) return hipSuccess;
-  if (dtype == 1 && head_dim == 128) return launch_c<BF16, 128>(tiles, causal, args, n_items, stream, cus);
-  if (dtype == 1 && head_dim == 64) return launch_c<BF16, 64>(tiles, causal, args, n_items, stream, cus);
-  if (dtype == 0 && head_dim == 128) return launch_c<F32, 128>(tiles, causal, args, n_items, stream, cus);
-  if (dtype == 0 && head_dim == 64) return launch_c<F32, 64>(tiles, causal, args, n_items, stream, cus);
+  if (dtype == 1 && head_dim == 128) return launch_c<BF16, 128>(tiles, causal, args, nt, n_items, stream, cus);
+  if (dtype == 1 && head_dim == 64) return launch_c<BF16, 64>(tiles, causal, args, nt, n_items, stream, cus);
+  if (dtype == 0 && head_dim == 128) return launch_c<F32, 128>(tiles, causal, args, nt, n_items, stream, cus);
+  if (dtype == 0 && head_dim == 64) return launch_c<F32, 64>(tiles, causal, args, nt, n_items, stream, cus);
   return hipErrorInvalidValue;
 }
 

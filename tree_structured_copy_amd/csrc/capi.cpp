@@ -92,6 +92,11 @@ struct tkv_cache {
   uint64_t opt_epoch = 1;
   bool plan_cache = true;
   bool plan_patch = true;  // TKV_OPT_PLAN_PATCH
+  bool fuse_new = true;    // TKV_OPT_FUSED_NEW_TOKEN
+  // a decode step's new tokens for the attention launch's arguments, and
+  // tree node -> its tail entry in the call's plan (-1 between calls)
+  NewTokens fused{};
+  std::vector<int32_t> node_entry;
   int32_t waves = 0;
   int32_t cus = 256;  // compute units of the device (set at create when pools are given)
   int32_t concurrent = 0;  // TKV_OPT_CONCURRENT
@@ -385,6 +390,64 @@ int prepare_new_tokens(tkv_cache* c, PlanSlot* s, int32_t layer, int32_t nseq, c
   return TKV_OK;
 }
 
+// A decode step whose new tokens the attention launch writes itself: possible
+// when there are at most kFusedMaxTokens of them, each in its handle's tip
+// block as listed by the plan, and the plan's device copy is either uploaded
+// whole first or differs from the host plan only in those blocks' valid
+// counts (which the launch writes too).  Fills c->fused and uploads the plan
+// if needed; returns false (nothing done) when the preparation launch must
+// write them instead.
+bool prepare_fused(tkv_cache* c, PlanSlot* s, int32_t layer, const tkv_seq* seqs, int32_t nseq, const void* k_new,
+                   const void* v_new, int* rc) {
+  *rc = TKV_OK;
+  if (!c->fuse_new || nseq > kFusedMaxTokens) return false;
+  const Plan& P = s->plan;
+  try {
+    if (c->node_entry.size() < static_cast<size_t>(c->tree.node_capacity()))
+      c->node_entry.resize(c->tree.node_capacity(), -1);
+  } catch (const std::bad_alloc&) {
+    return false;
+  }
+  for (size_t t = 0; t < P.tail_entry.size(); ++t) c->node_entry[P.tail_node[t]] = P.tail_entry[t];
+  bool ok = true;
+  NewTokens& x = c->fused;
+  for (int32_t i = 0; i < nseq && ok; ++i) {
+    int32_t tip = -1;
+    const AppendEntry& a = c->app_ents[i];
+    if (c->tree.resolve(seqs[i], &tip) != TKV_OK) {
+      ok = false;
+      break;
+    }
+    const int32_t e = c->node_entry[tip];
+    if (e < 0 || P.blocks[e].id != a.blk || P.blocks[e].valid != a.slot + 1) {
+      ok = false;
+      break;
+    }
+    x.tok[i] = NewTok{e, a.blk, a.slot, i};
+  }
+  for (size_t t = 0; t < P.tail_entry.size(); ++t) c->node_entry[P.tail_node[t]] = -1;
+  if (!ok) return false;
+  if (s->uploaded && !s->pending.empty()) {
+    // every changed word must be one the launch writes: a new token's valid count
+    const uint32_t v0 = static_cast<uint32_t>((P.off_blocks + offsetof(DevBlock, valid)) / 4);
+    const uint32_t per = sizeof(DevBlock) / 4;
+    for (const PlanWord& w : s->pending) {
+      bool covered = false;
+      if (w.word >= v0 && (w.word - v0) % per == 0) {
+        const int32_t e = static_cast<int32_t>((w.word - v0) / per);
+        for (int32_t i = 0; i < nseq && !covered; ++i) covered = x.tok[i].entry == e && w.value == x.tok[i].slot + 1;
+      }
+      if (!covered) return false;
+    }
+  }
+  x.k = k_new;
+  x.v = v_new;
+  x.kpool = const_cast<char*>(c->kpool_layer(layer));
+  x.vpool = const_cast<char*>(c->vpool_layer(layer));
+  x.n = nseq;
+  return true;
+}
+
 // The plan of a tkv_attend_decode_noalloc call, copied into the fixed device
 // workspace `base` from the pinned staging made at tkv_create (no allocation:
 // a plan larger than that staging is refused).
@@ -450,15 +513,28 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   DeviceGuard dg(c->device);
   launch_log_reset();
+  NewTokens* nt = nullptr;
   if (fixed) {
     if (int rc = upload_plan_fixed(c, P, fixed, stream)) return rc;
   } else if (k_new) {
-    if (int rc = prepare_new_tokens(c, s, layer, nseq, k_new, v_new, stream)) return rc;
+    int rc = TKV_OK;
+    if (prepare_fused(c, s, layer, seqs, nseq, k_new, v_new, &rc)) {
+      // the plan's device copy: whole if it was never uploaded; otherwise it
+      // differs only in the valid counts the launch writes
+      if (!s->uploaded) {
+        if (int rc2 = upload_plan(c, s, stream)) return rc2;
+      }
+      s->pending.clear();
+      nt = &c->fused;
+    } else if (int rc2 = prepare_new_tokens(c, s, layer, nseq, k_new, v_new, stream)) {
+      return rc2;
+    }
   } else if (int rc = upload_plan(c, s, stream)) {
     return rc;
   }
 
   const char* dev = fixed ? fixed : static_cast<const char*>(s->dev);
+  if (nt) nt->blocks = reinterpret_cast<DevBlock*>(const_cast<char*>(dev) + P.off_blocks);
   AttnArgs a{};
   a.kpool = c->kpool_layer(layer);
   a.vpool = c->vpool_layer(layer);
@@ -516,14 +592,14 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
       // large batch of sequences): the LDS-staged kernel's 4-tile shape,
       // whose shallow ring with two workgroups per CU streams these faster
       // than the register kernel
-      e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, 1, P.causal, a, n, st, c->cus);
+      e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, 1, P.causal, a, n, st, c->cus, nt);
     } else if (cls < 2) {
       // One tile otherwise: two waves, i.e. few long streams of loads per CU,
       // which HBM serves faster than more, shorter ones; two tiles: four.
       const int w = c->waves ? c->waves : (cls == 0 ? 2 : 4);
-      e = launch_attn_partial(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], w, P.causal, a, n, st);
+      e = launch_attn_partial(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], w, P.causal, a, n, st, nt);
     } else {
-      e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], P.causal, a, n, st, c->cus);
+      e = launch_attn_rows(c->cfg.dtype, c->cfg.head_dim, P.bucket_tiles[cls], P.causal, a, n, st, c->cus, nt);
     }
     if (e != hipSuccess) return TKV_E_DEVICE;
     if (st != stream && hipEventRecord(c->join_ev[k - 1], st) != hipSuccess) return TKV_E_DEVICE;
@@ -893,6 +969,10 @@ int tkv_set_option(tkv_cache* c, int32_t key, int64_t value) {
       if (value != 0 && value != 1) return TKV_E_RANGE;
       c->plan_patch = value != 0;
       break;
+    case TKV_OPT_FUSED_NEW_TOKEN:
+      if (value != 0 && value != 1) return TKV_E_RANGE;
+      c->fuse_new = value != 0;
+      break;
     default:
       return TKV_E_INVAL;
   }
@@ -911,6 +991,7 @@ int tkv_get_option(const tkv_cache* c, int32_t key, int64_t* value) {
     case TKV_OPT_CASCADE: *value = c->opt.cascade; break;
     case TKV_OPT_CONCURRENT: *value = c->concurrent; break;
     case TKV_OPT_PLAN_PATCH: *value = c->plan_patch ? 1 : 0; break;
+    case TKV_OPT_FUSED_NEW_TOKEN: *value = c->fuse_new ? 1 : 0; break;
     default: return TKV_E_INVAL;
   }
   return TKV_OK;

@@ -25,14 +25,15 @@ const char* launch_log();
 // Partial attention over items [args.item0, args.item0 + n_items) whose groups
 // need `tiles` row tiles of 16; grid = n_items * Hkv workgroups of 64 * waves
 // threads (waves = 4 or 8).
+// nt (decode only): the launch first writes these new tokens (write_new_tokens).
 hipError_t launch_attn_partial(int dtype, int head_dim, int tiles, int waves, bool causal, const AttnArgs& args,
-                               int32_t n_items, hipStream_t stream);
+                               int32_t n_items, hipStream_t stream, const NewTokens* nt = nullptr);
 
 // Partial attention for groups of 3..16 row tiles with K/V staged in LDS;
 // grid = n_items * Hkv / (heads per workgroup) workgroups.  cus = the device's
 // compute units (the ring depth depends on workgroups per CU).
 hipError_t launch_attn_rows(int dtype, int head_dim, int tiles, bool causal, const AttnArgs& args, int32_t n_items,
-                            hipStream_t stream, int cus);
+                            hipStream_t stream, int cus, const NewTokens* nt = nullptr);
 
 // Log-sum-exp merge of each query's partial records into out; one wave per
 // (query, query head), four per workgroup.

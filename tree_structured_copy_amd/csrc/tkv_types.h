@@ -103,6 +103,35 @@ struct AttnArgs {
   int32_t max_blocks;    // the longest block list among this launch's items
 };
 
+// The new token of one branch in a decode step, written by the attention
+// launch itself (tkv_attend_decode_new_token in one launch): plan block entry
+// `entry` (an index into the plan's block list) is the token's block `blk`,
+// which takes the token at `slot` from row `src` of the call's K/V arrays.
+struct NewTok {
+  int32_t entry;
+  int32_t blk;
+  int32_t slot;
+  int32_t src;
+};
+// Up to this many new tokens travel in an attention launch's arguments (with
+// AttnArgs, within the 4 KiB kernel-argument limit).
+constexpr int kFusedMaxTokens = 224;
+struct NewTokens {
+  static constexpr bool kActive = true;
+  const void* k;     // [rows][Hkv][D] of the call's layer
+  const void* v;
+  void* kpool;       // the layer's base
+  void* vpool;
+  DevBlock* blocks;  // the plan's block list: the tokens' valid counts are written here
+  int32_t n;
+  int32_t pad;
+  NewTok tok[kFusedMaxTokens];
+};
+// A launch that writes no token (an empty argument).
+struct NoNewTokens {
+  static constexpr bool kActive = false;
+};
+
 struct MergeArgs {
   const DevPart* parts;
   const DevMerge* merge;

@@ -39,6 +39,7 @@ TKV_OPT_WAVES = 5
 TKV_OPT_CASCADE = 6
 TKV_OPT_CONCURRENT = 7
 TKV_OPT_PLAN_PATCH = 8
+TKV_OPT_FUSED_NEW_TOKEN = 9
 
 STATUS_NAMES = {
     TKV_E_INVAL: "inval", TKV_E_NOMEM: "nomem", TKV_E_BADSEQ: "badseq", TKV_E_SHARED: "shared",
