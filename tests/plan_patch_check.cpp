@@ -1,6 +1,9 @@
 // Host check of the planner's in-place update (patch_plan), run by
-// tests/test_host_core.py: for seeded random sessions of forks, appends,
-// truncations and releases, build the plan of a decode or verify batch, then
+// tests/test_host_core.py (also under AddressSanitizer and
+// UndefinedBehaviorSanitizer): for seeded random sessions of forks, appends,
+// truncations and releases, and planner options drawn per session (row limit
+// 16..256, one-tile subgroups on or off, 1..16 query heads per KV head, chunk
+// floors and workgroup targets), build the plan of a decode or verify batch, then
 // repeatedly append tokens that fit in tip nodes' last blocks, patch the plan,
 // and require (1) the patched plan to equal a fresh build byte for byte and
 // (2) the changed words, written over the previous serialisation, to give the
@@ -89,10 +92,14 @@ int main(int argc, char** argv) {
       nq.push_back(1 + r.below(static_cast<int32_t>(len < 12 ? len : 12)));
     }
     if (seqs.empty()) continue;
-    const int32_t qpk = sess % 3 == 0 ? 16 : 4, hkv = 2;
+    static const int32_t kQpk[] = {1, 2, 4, 8, 16};
+    static const int32_t kRows[] = {16, 32, 64, 128, 256};
+    const int32_t qpk = kQpk[r.below(5)], hkv = 2;
     PlanOptions opt;
     opt.min_chunk = 1 + r.below(32);
     opt.target_wgs = 2 + r.below(600);
+    opt.max_rows = kRows[r.below(5)];
+    opt.cascade = r.below(2);
     PlanScratch scratch;
     Plan live_plan, fresh;
     const int32_t* nqp = verify ? nq.data() : nullptr;

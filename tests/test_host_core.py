@@ -283,29 +283,62 @@ def test_fork_bench_flat_over_prefix_and_depth():
         assert max(vals) < 3 * min(vals) + 50, (n, min(vals), max(vals))
 
 
-def test_plan_update_in_place_equals_rebuild(tmp_path):
-    """The planner's in-place update after appends that fit in tip blocks
-    (patch_plan): over 60 seeded random fork/append/truncate/release sessions,
-    12 rounds each of such appends, the updated plan equals a fresh build byte
-    for byte, and its list of changed words, written over the previous bytes
-    (what the device copy receives), gives the same bytes
-    (tests/plan_patch_check.cpp, compiled here against the library's host
-    sources)."""
+def _host_check(tmp_path, src, sanitize):
+    """Compile a host checker against the library's host sources (tree.cpp,
+    plan.cpp), with g++ alone, optionally under AddressSanitizer and
+    UndefinedBehaviorSanitizer (any report aborts)."""
     import shutil
     import subprocess
-    cxx = shutil.which("g++") or shutil.which("clang++")
+    cxx = shutil.which("g++")
     if cxx is None:
         pytest.skip("no host C++ compiler")
     csrc = os.path.join(ROOT, "tree_structured_copy_amd", "csrc")
-    exe = str(tmp_path / "plan_patch_check")
-    subprocess.run([cxx, "-O1", "-std=c++17", "-I" + csrc, "-I" + os.path.join(ROOT, "include"),
-                    os.path.join(ROOT, "tests", "plan_patch_check.cpp"), os.path.join(csrc, "tree.cpp"),
-                    os.path.join(csrc, "plan.cpp"), "-o", exe], check=True, timeout=300)
-    r = subprocess.run([exe, "60"], capture_output=True, text=True, timeout=120)
-    assert r.returncode == 0, r.stdout[-2000:]
+    exe = str(tmp_path / (os.path.splitext(src)[0] + ("_san" if sanitize else "")))
+    flags = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+             "-fno-omit-frame-pointer"] if sanitize else ["-O1"]
+    subprocess.run([cxx] + flags + ["-std=c++17", "-I" + csrc, "-I" + os.path.join(ROOT, "include"),
+                                    os.path.join(ROOT, "tests", src), os.path.join(csrc, "tree.cpp"),
+                                    os.path.join(csrc, "plan.cpp"), "-o", exe], check=True, timeout=300)
+    return exe
+
+
+@pytest.mark.parametrize("sanitize", [False, True])
+def test_plan_update_in_place_equals_rebuild(tmp_path, sanitize):
+    """The planner's in-place update after appends that fit in tip blocks
+    (patch_plan): over 60 seeded random fork/append/truncate/release sessions
+    with random planner options, 12 rounds each of such appends, the updated
+    plan equals a fresh build byte for byte, and its list of changed words,
+    written over the previous bytes (what the device copy receives), gives the
+    same bytes (tests/plan_patch_check.cpp); also built with ASan + UBSan."""
+    import subprocess
+    exe = _host_check(tmp_path, "plan_patch_check.cpp", sanitize)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe, "60"], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-3000:])
     assert "all sessions ok: 720 rounds" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
     words = int(re.search(r"(\d+) changed words", r.stdout).group(1))
     assert words > 1000
+
+
+@pytest.mark.parametrize("sanitize", [False, True])
+def test_plan_means_what_the_tree_says(tmp_path, sanitize):
+    """What the planner's output means, checked from the tree alone over 120
+    seeded random sessions with random planner options (row limit 16..256,
+    one-tile subgroups on or off, 1..16 query heads per KV head, chunk floors,
+    workgroup targets): every query sees exactly its own path's (block, slot)
+    pairs up to its position once; items cover their groups' lists; each
+    query's output is written directly once or merged from one record per
+    item at that item's slot, no slot shared; the layout's sections are
+    disjoint (tests/plan_semantics_check.cpp); also built with ASan + UBSan."""
+    import subprocess
+    exe = _host_check(tmp_path, "plan_semantics_check.cpp", sanitize)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe, "120"], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-3000:])
+    assert "all sessions ok" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
+    assert sum("cascade 1 ok" in line for line in r.stdout.splitlines()) > 20
 
 
 def test_shape_epoch_only_moves_on_structural_change():

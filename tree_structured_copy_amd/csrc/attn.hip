@@ -36,8 +36,9 @@ namespace {
 
 using namespace attn;
 
-// X = NewTokens: the launch first writes a decode step's new tokens that lie
-// in its items' blocks (write_new_tokens); X = NoNewTokens: it writes none.
+// X = NewTokens: the launch also writes a decode step's new tokens that lie
+// in its items' blocks, each by the wave that reads it, before reading it;
+// X = NoNewTokens: it writes none.
 template <class P, int D, int T, int W, bool CAUSAL, class X>
 __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
   using E = typename P::elem;
@@ -50,7 +51,6 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
   const int g = lane >> 4, r = lane & 15;
   const int kvh = blockIdx.x % a.hkv;
   const DevItem it = a.items[a.item0 + blockIdx.x / a.hkv];
-  if constexpr (X::kActive) write_new_tokens<P, D>(x, it, kvh, 1, a.hkv, tid, NT);
   const int nb = it.blk_count;
   const int nsb = (nb + 1) >> 1;
   // super-blocks of this wave: a contiguous share of the item (two waves
@@ -69,6 +69,23 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
   int e_id = -1, e_valid = 0, e_pos = 0;
   uint32_t e_mlo = 0, e_mhi = 0;
   int cur_batch = -1;
+  // X = NewTokens: the item's new-token records (tail blocks [tk0, tk0 + tkc),
+  // at most 64); each wave keeps their (entry, valid count) pairs in LDS
+  const int tk0 = X::kActive ? (it.tails & 0xffff) : 0, tkc = X::kActive ? (it.tails >> 16) : 0;
+  __shared__ int2 s_tok[X::kActive ? W : 1][X::kActive ? 64 : 1];
+  bool tk_loaded = false;
+  // a block this launch writes a new token into holds one more token than the
+  // plan's copy may say: the valid counts of the loaded batch, corrected
+  auto correct_valid = [&]() {
+    if constexpr (X::kActive) {
+      if (!tk_loaded || cur_batch < 0) return;
+      const int b = 2 * (start_w + 32 * cur_batch + (lane >> 1)) + (lane & 1);
+      for (int i = 0; i < tkc; ++i) {
+        const int2 ev = s_tok[wave][i];
+        if (ev.x >= 0 && ev.x == it.blk_begin + b) e_valid = ev.y;
+      }
+    }
+  };
   // (the entry is selected by value and stored once: branches that each store
   // the fields let the compiler merge their last stores through a selected
   // pointer, which puts these registers on the stack)
@@ -83,6 +100,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
     e_mlo = static_cast<uint32_t>(e.mask);
     e_mhi = static_cast<uint32_t>(e.mask >> 32);
     cur_batch = batch;
+    correct_valid();
   };
   auto meta = [&](int k) {
     if ((k >> 5) != cur_batch) load_entries(k >> 5);
@@ -115,9 +133,103 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
   F kA0, kA1, kB0, kB1;
   VP vA, vB;
   SBMeta mA, mB;
+  // A decode step's new tokens in this wave's blocks are written by the wave
+  // itself.  The first super-block's loads go out first; then the item's
+  // token records (one load per lane), the values of the wave's tokens and
+  // their stores.  If the first super-block holds a written block it is loaded
+  // again once the stores have landed; otherwise the wave waits for them
+  // before loading its first super-block that holds one.
   if (nmine > 0) {
     mA = meta(0);
     load_sb(kA0, kA1, vA, mA);
+  }
+  int tok_sb = 0x7fffffff;  // index in this wave's share of its first super-block that gets a token
+  if constexpr (X::kActive) {
+    using TU = TokUnits<P, D>;
+    if (tkc > 0) {
+      int tk_entry = -1, tk_blk = 0, tk_slot = 0, tk_src = 0;
+      if (lane < tkc) {
+        const NewTok t = x.tok[tk0 + lane];
+        tk_entry = t.entry;
+        tk_blk = t.blk;
+        tk_slot = t.slot;
+        tk_src = t.src;
+        s_tok[wave][lane] = int2{t.entry, t.slot + 1};
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done (a wave reads only its own)
+      tk_loaded = true;
+      correct_valid();
+      if (nmine > 0) mA = meta(0);
+      const int my_lo = it.blk_begin + 2 * start_w, my_hi = it.blk_begin + 2 * (start_w + nmine);
+      const bool own = tk_entry >= my_lo && tk_entry < my_hi;
+      uint64_t mine = __ballot(own);
+      if (mine) {
+        const int first = __builtin_ctzll(mine);
+        tok_sb = ((__builtin_amdgcn_readlane(tk_entry, first) - it.blk_begin) >> 1) - start_w;
+        auto rec = [&](int i) {
+          return NewTok{__builtin_amdgcn_readlane(tk_entry, i), __builtin_amdgcn_readlane(tk_blk, i),
+                        __builtin_amdgcn_readlane(tk_slot, i), __builtin_amdgcn_readlane(tk_src, i)};
+        };
+        // tokens that open their block (rare: whole tiles), then the others, a
+        // few at a time with all their values' loads in flight together
+        uint64_t fresh = __ballot(own && tk_slot == 0);
+        while (fresh) {
+          const NewTok t = rec(__builtin_ctzll(fresh));
+          fresh &= fresh - 1;
+          for (int u0 = lane; u0 < TU::kFresh; u0 += 4 * 64) {
+            u32x4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (u0 + 64 * k < TU::kFresh) v[k] = TU::value(x, t, kvh, a.hkv, u0 + 64 * k);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (u0 + 64 * k < TU::kFresh) TU::store(x, t, kvh, a.hkv, u0 + 64 * k, v[k]);
+          }
+          if (lane == 0) x.blocks[t.entry].valid = 1;
+        }
+        uint64_t plain = __ballot(own && tk_slot != 0);
+        constexpr int RPT = (TU::kPlain + 63) / 64;  // 64-unit rows per token
+        constexpr int MAXT = 4;                      // tokens whose values are in flight at once
+        while (plain) {
+          NewTok t[MAXT];
+          int nt = 0;
+#pragma unroll
+          for (int j = 0; j < MAXT; ++j) {
+            t[j] = NewTok{-1, 0, 0, 0};
+            if (plain) {
+              t[j] = rec(__builtin_ctzll(plain));
+              plain &= plain - 1;
+              nt = j + 1;
+            }
+          }
+          u32x4 v[MAXT][RPT];
+#pragma unroll
+          for (int j = 0; j < MAXT; ++j) {
+            if (j >= nt) break;
+#pragma unroll
+            for (int rr = 0; rr < RPT; ++rr)
+              if (rr * 64 + lane < TU::kPlain) v[j][rr] = TU::value(x, t[j], kvh, a.hkv, rr * 64 + lane);
+          }
+          // the values, and the first super-block issued before them, have
+          // landed: the stores then go out after every load the loop's first
+          // step needs, so nothing waits for their acknowledgement until the
+          // super-block that reads them
+          __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+          for (int j = 0; j < MAXT; ++j) {
+            if (j >= nt) break;
+#pragma unroll
+            for (int rr = 0; rr < RPT; ++rr)
+              if (rr * 64 + lane < TU::kPlain) TU::store(x, t[j], kvh, a.hkv, rr * 64 + lane, v[j][rr]);
+            if (lane == 0) x.blocks[t[j].entry].valid = t[j].slot + 1;
+          }
+        }
+        if (tok_sb == 0) {
+          __builtin_amdgcn_s_waitcnt(0);
+          load_sb(kA0, kA1, vA, mA);
+        }
+      }
+    }
   }
 
   // queries: row R = 16 t + r of the group is query R / G, head kvh * G + R % G
@@ -212,10 +324,16 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
   if (nmine > 0) {
     for (int k = 0; k < nmine; k += 2) {
       mB = meta(min(k + 1, nmine - 1));
+      if constexpr (X::kActive) {
+        if (k + 1 == tok_sb) __builtin_amdgcn_s_waitcnt(0);
+      }
       load_sb(kB0, kB1, vB, mB);
       process(kA0, kA1, vA, mA);
       if (k + 1 >= nmine) break;
       mA = meta(min(k + 2, nmine - 1));
+      if constexpr (X::kActive) {
+        if (k + 2 == tok_sb) __builtin_amdgcn_s_waitcnt(0);
+      }
       load_sb(kA0, kA1, vA, mA);
       process(kB0, kB1, vB, mB);
     }

@@ -281,83 +281,153 @@ struct SBMeta {
 template <class P>
 constexpr bool kIsBF16 = sizeof(typename P::elem) == 2;
 
-// A decode step's new tokens that lie in this work item's blocks (plan entries
-// [it.blk_begin, it.blk_begin + it.blk_count)) are written into the pool tiles
-// of KV heads [h0, h0 + nh) -- a block the token opens (slot 0) whole, with
-// zeros in its other slots -- and their blocks' valid counts (slot + 1) into
-// the plan's block list (every KV head's workgroup writes the same value);
-// then both are made visible to the workgroup's later reads.  Every thread of
-// the workgroup calls this before any of them reads the pool or the plan's
-// block entries.  Only this workgroup reads these tiles and entries in the
-// launch: an unfrozen tip block appears once in a plan.
+// Writing a decode step's new tokens from the attention launch itself.
+// Work unit w of one token and KV head:
+//   * the token opens its block (slot 0): the whole tile is written, the
+//     token in slot 0 and zeros elsewhere; units [0, 2 NCH) are the K then V
+//     chunks (kFresh);
+//   * otherwise only the token (kPlain): unit w < D / PC is the 16-byte K chunk
+//     holding d = PC w .. PC w + PC - 1 of the token, unit D / PC + d its V
+//     element d (inside the bf16 8-byte unit, or fp32 chunk, of tokens
+//     4 (slot / 4) .. + 3).
+// value() loads a unit's contents (so that several units' loads can be in
+// flight together), store() writes them.
+template <class P, int D>
+struct TokUnits {
+  using E = typename P::elem;
+  static constexpr int EB = static_cast<int>(sizeof(E));
+  using L = Layout<EB>;
+  static constexpr int PC = L::kPerChunk;
+  static constexpr int NCH = 16 * D / PC;
+  static constexpr int kFresh = 2 * NCH;
+  static constexpr int kPlain = D / PC + D;
+  __device__ static int units(const NewTok& t) { return t.slot == 0 ? kFresh : kPlain; }
+  __device__ static size_t tile(const NewTok& t, int h, int hkv) {
+    return (static_cast<size_t>(t.blk) * hkv + h) * (16 * D);
+  }
+  __device__ static u32x4 value(const NewTokens& x, const NewTok& t, int h, int hkv, int w) {
+    const E* sk = static_cast<const E*>(x.k) + (static_cast<size_t>(t.src) * hkv + h) * D;
+    const E* sv = static_cast<const E*>(x.v) + (static_cast<size_t>(t.src) * hkv + h) * D;
+    if (t.slot == 0) {
+      const bool isk = w < NCH;
+      const int ch = isk ? w : w - NCH;
+      E vals[PC];
+#pragma unroll
+      for (int el = 0; el < PC; ++el) {
+        int tok, d;
+        if (isk) L::k_coord(ch, el, tok, d);
+        else L::v_coord(ch, el, tok, d);
+        vals[el] = tok == 0 ? (isk ? sk[d] : sv[d]) : E(0);
+      }
+      return bitcast<u32x4>(vals);
+    }
+    if (w < D / PC) return *reinterpret_cast<const u32x4*>(sk + w * PC);
+    u32x4 r{0u, 0u, 0u, 0u};
+    const E e = sv[w - D / PC];
+    __builtin_memcpy(&r, &e, sizeof(E));
+    return r;
+  }
+  __device__ static void store(const NewTokens& x, const NewTok& t, int h, int hkv, int w, const u32x4& v) {
+    const size_t tl = tile(t, h, hkv);
+    E* kt = static_cast<E*>(x.kpool) + tl;
+    E* vt = static_cast<E*>(x.vpool) + tl;
+    // nontemporal: the lines go out without staying dirty in L2 until the
+    // kernel's end (3 us of a decode step on the fork workload, measured)
+    if (t.slot == 0) {
+      const bool isk = w < NCH;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>((isk ? kt : vt) + (isk ? w : w - NCH) * PC));
+    } else if (w < D / PC) {
+      int ch;
+      if constexpr (EB == 2) ch = w * 16 + t.slot;
+      else ch = (w >> 2) * 64 + (w & 3) * 16 + t.slot;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(kt + ch * PC));
+    } else {
+      const int d = w - D / PC;
+      E e;
+      __builtin_memcpy(&e, &v, sizeof(E));
+      __builtin_nontemporal_store(e, vt + ((d >> 4) * 64 + (t.slot >> 2) * 16 + (d & 15)) * 4 + (t.slot & 3));
+    }
+  }
+};
+
+// The decode step's new tokens in this work item's blocks (DevItem::tails, at
+// most 64), written by the whole workgroup for its KV heads [h0, h0 + nh)
+// before any of its threads reads the pool or the plan's block entries: the
+// tiles (a block the token opens whole, with zeros in its other slots) and each
+// block's valid count in the plan (every KV head's workgroup writes the same
+// value).  Each wave holds the item's token records in its lanes (one load);
+// the units of up to four tokens at a time are spread over the workgroup's
+// threads with all their loads in flight together.  Only this workgroup reads
+// these tiles and entries in the launch: an unfrozen tip block appears once in
+// a plan.
 template <class P, int D>
 __device__ void write_new_tokens(const NewTokens& x, const DevItem& it, int h0, int nh, int hkv, int tid,
                                  int nthreads) {
-  using E = typename P::elem;
-  constexpr int EB = static_cast<int>(sizeof(E));
-  using L = Layout<EB>;
-  constexpr int PC = L::kPerChunk;
-  constexpr int NCH = 16 * D / PC;
-  using Chunk = u32x4;
+  using TU = TokUnits<P, D>;
+  const int tk0 = it.tails & 0xffff, tkc = it.tails >> 16;
+  if (tkc == 0) return;
   const int lane = tid & 63;
-  bool any = false;
-  for (int base = 0; base < x.n; base += 64) {
-    const int k = base + lane;
-    const int e = k < x.n ? x.tok[k].entry : -1;
-    const bool mine = e >= it.blk_begin && e < it.blk_begin + it.blk_count;
-    uint64_t m = __ballot(mine);
-    while (m) {
-      const int j = __builtin_ctzll(m);
-      m &= m - 1;
-      any = true;
-      const NewTok t = x.tok[base + j];
-      const bool fresh = t.slot == 0;
-      const int units = fresh ? 2 * NCH : D / PC + D;  // per head
-      for (int u = tid; u < nh * units; u += nthreads) {
-        const int hh = u / units, w = u - hh * units;
-        const int h = h0 + hh;
-        const size_t tile = (static_cast<size_t>(t.blk) * hkv + h) * (16 * D);
-        E* kt = static_cast<E*>(x.kpool) + tile;
-        E* vt = static_cast<E*>(x.vpool) + tile;
-        const E* sk = static_cast<const E*>(x.k) + (static_cast<size_t>(t.src) * hkv + h) * D;
-        const E* sv = static_cast<const E*>(x.v) + (static_cast<size_t>(t.src) * hkv + h) * D;
-        if (fresh) {
-          // chunk w % NCH of K (w < NCH) or of V: the token in slot 0, zeros elsewhere
-          const bool isk = w < NCH;
-          const int ch = isk ? w : w - NCH;
-          E vals[PC];
+  int te = -1, tbk = 0, ts = 0, tsr = 0;
+  if (lane < tkc) {
+    const NewTok t = x.tok[tk0 + lane];
+    te = t.entry;
+    tbk = t.blk;
+    ts = t.slot;
+    tsr = t.src;
+  }
+  auto rec = [&](int i) {
+    return NewTok{__builtin_amdgcn_readlane(te, i), __builtin_amdgcn_readlane(tbk, i),
+                  __builtin_amdgcn_readlane(ts, i), __builtin_amdgcn_readlane(tsr, i)};
+  };
+  uint64_t todo = __ballot(te >= 0);
+  if (!todo) return;
+  constexpr int MAXT = 4;
+  while (todo) {
+    NewTok t[MAXT];
+    int nt = 0;
 #pragma unroll
-          for (int el = 0; el < PC; ++el) {
-            int tok, d;
-            if (isk) L::k_coord(ch, el, tok, d);
-            else L::v_coord(ch, el, tok, d);
-            vals[el] = tok == 0 ? (isk ? sk[d] : sv[d]) : E(0);
-          }
-          *reinterpret_cast<Chunk*>((isk ? kt : vt) + ch * PC) = *reinterpret_cast<const Chunk*>(vals);
-        } else if (w < D / PC) {
-          // K: chunk w of the token's row (PC consecutive d), one 16-byte store
-          int ch;
-          if constexpr (EB == 2) ch = w * 16 + t.slot;
-          else ch = (w >> 2) * 64 + (w & 3) * 16 + t.slot;
-          *reinterpret_cast<Chunk*>(kt + ch * PC) = *reinterpret_cast<const Chunk*>(sk + w * PC);
-        } else {
-          // V: element d of the token, inside the unit (bf16) or chunk (fp32)
-          // that holds tokens 4 (slot / 4) .. + 3 at that d
-          const int d = w - D / PC;
-          const int at = ((d >> 4) * 64 + (t.slot >> 2) * 16 + (d & 15)) * 4 + (t.slot & 3);
-          vt[at] = sv[d];
-        }
+    for (int j = 0; j < MAXT; ++j) {
+      t[j] = NewTok{-1, 0, 0, 0};
+      if (todo) {
+        t[j] = rec(__builtin_ctzll(todo));
+        todo &= todo - 1;
+        nt = j + 1;
       }
-      if (tid == 0) x.blocks[t.entry].valid = t.slot + 1;
+    }
+    // units of these tokens, thread-strided; a thread's share of one token's
+    // units is at most ceil(nh * units / nthreads) <= 4 for every shape here
+    constexpr int R = 4;
+    u32x4 v[MAXT][R];
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) {
+      if (j >= nt) break;
+      const int per = TU::units(t[j]), total = nh * per;
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int u = tid + k * nthreads;
+        if (u < total) v[j][k] = TU::value(x, t[j], h0 + u / per, hkv, u % per);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) {
+      if (j >= nt) break;
+      const int per = TU::units(t[j]), total = nh * per;
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const int u = tid + k * nthreads;
+        if (u < total) TU::store(x, t[j], h0 + u / per, hkv, u % per, v[j][k]);
+      }
+      // a thread past R * nthreads units: the rest of this token, one at a time
+      for (int u = tid + R * nthreads; u < total; u += nthreads)
+        TU::store(x, t[j], h0 + u / per, hkv, u % per, TU::value(x, t[j], h0 + u / per, hkv, u % per));
+      if (tid == 0) x.blocks[t[j].entry].valid = t[j].slot + 1;
     }
   }
-  if (any) {
-    // every store of the workgroup acknowledged (in L2) before any wave loads
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  }
+  // every store of the workgroup acknowledged (in L2) before any wave loads
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 }  // namespace attn

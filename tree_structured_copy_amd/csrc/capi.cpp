@@ -400,17 +400,25 @@ int prepare_new_tokens(tkv_cache* c, PlanSlot* s, int32_t layer, int32_t nseq, c
 bool prepare_fused(tkv_cache* c, PlanSlot* s, int32_t layer, const tkv_seq* seqs, int32_t nseq, const void* k_new,
                    const void* v_new, int* rc) {
   *rc = TKV_OK;
-  if (!c->fuse_new || nseq > kFusedMaxTokens) return false;
   const Plan& P = s->plan;
+  // the launch's token list is indexed by the plan's tail blocks (DevItem::tails)
+  const int32_t ntail = static_cast<int32_t>(P.tail_entry.size());
+  if (!c->fuse_new || ntail > kFusedMaxTokens) return false;
+  // a workgroup holds its item's token records in one wave's lanes
+  for (const DevItem& it : P.items)
+    if ((it.tails >> 16) > 64) return false;
   try {
     if (c->node_entry.size() < static_cast<size_t>(c->tree.node_capacity()))
       c->node_entry.resize(c->tree.node_capacity(), -1);
   } catch (const std::bad_alloc&) {
     return false;
   }
-  for (size_t t = 0; t < P.tail_entry.size(); ++t) c->node_entry[P.tail_node[t]] = P.tail_entry[t];
-  bool ok = true;
   NewTokens& x = c->fused;
+  for (int32_t t = 0; t < ntail; ++t) {
+    c->node_entry[P.tail_node[t]] = t;
+    x.tok[t] = NewTok{-1, 0, 0, 0};
+  }
+  bool ok = true;
   for (int32_t i = 0; i < nseq && ok; ++i) {
     int32_t tip = -1;
     const AppendEntry& a = c->app_ents[i];
@@ -418,14 +426,15 @@ bool prepare_fused(tkv_cache* c, PlanSlot* s, int32_t layer, const tkv_seq* seqs
       ok = false;
       break;
     }
-    const int32_t e = c->node_entry[tip];
-    if (e < 0 || P.blocks[e].id != a.blk || P.blocks[e].valid != a.slot + 1) {
+    const int32_t t = c->node_entry[tip];
+    const int32_t e = t >= 0 ? P.tail_entry[t] : -1;
+    if (e < 0 || P.blocks[e].id != a.blk || P.blocks[e].valid != a.slot + 1 || x.tok[t].entry >= 0) {
       ok = false;
       break;
     }
-    x.tok[i] = NewTok{e, a.blk, a.slot, i};
+    x.tok[t] = NewTok{e, a.blk, a.slot, i};
   }
-  for (size_t t = 0; t < P.tail_entry.size(); ++t) c->node_entry[P.tail_node[t]] = -1;
+  for (int32_t t = 0; t < ntail; ++t) c->node_entry[P.tail_node[t]] = -1;
   if (!ok) return false;
   if (s->uploaded && !s->pending.empty()) {
     // every changed word must be one the launch writes: a new token's valid count
@@ -435,7 +444,7 @@ bool prepare_fused(tkv_cache* c, PlanSlot* s, int32_t layer, const tkv_seq* seqs
       bool covered = false;
       if (w.word >= v0 && (w.word - v0) % per == 0) {
         const int32_t e = static_cast<int32_t>((w.word - v0) / per);
-        for (int32_t i = 0; i < nseq && !covered; ++i) covered = x.tok[i].entry == e && w.value == x.tok[i].slot + 1;
+        for (int32_t t = 0; t < ntail && !covered; ++t) covered = x.tok[t].entry == e && w.value == x.tok[t].slot + 1;
       }
       if (!covered) return false;
     }
@@ -444,7 +453,7 @@ bool prepare_fused(tkv_cache* c, PlanSlot* s, int32_t layer, const tkv_seq* seqs
   x.v = v_new;
   x.kpool = const_cast<char*>(c->kpool_layer(layer));
   x.vpool = const_cast<char*>(c->vpool_layer(layer));
-  x.n = nseq;
+  x.n = ntail;
   return true;
 }
 

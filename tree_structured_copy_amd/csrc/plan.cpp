@@ -24,14 +24,25 @@ void Plan::layout() {
   bytes = o;
 }
 
+namespace {
+
+// memcpy of a list that may be empty (an empty vector's data() may be null,
+// which memcpy may not be given even for zero bytes)
+template <class T>
+void put(char* dst, const std::vector<T>& v) {
+  if (!v.empty()) std::memcpy(dst, v.data(), v.size() * sizeof(T));
+}
+
+}  // namespace
+
 void Plan::serialise(void* dst) const {
   char* p = static_cast<char*>(dst);
-  std::memcpy(p + off_items, items.data(), items.size() * sizeof(DevItem));
-  std::memcpy(p + off_gq, gq.data(), gq.size() * sizeof(int32_t));
-  std::memcpy(p + off_gqpos, gqpos.data(), gqpos.size() * sizeof(int32_t));
-  std::memcpy(p + off_blocks, blocks.data(), blocks.size() * sizeof(DevBlock));
-  std::memcpy(p + off_parts, parts.data(), parts.size() * sizeof(DevPart));
-  std::memcpy(p + off_merge, merge.data(), merge.size() * sizeof(DevMerge));
+  put(p + off_items, items);
+  put(p + off_gq, gq);
+  put(p + off_gqpos, gqpos);
+  put(p + off_blocks, blocks);
+  put(p + off_parts, parts);
+  put(p + off_merge, merge);
 }
 
 void Plan::reset() {
@@ -446,7 +457,7 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
         t.it.q_begin = P.groups[gi].q_begin;
         t.it.nq = P.groups[gi].nq;
         t.it.min_pos = P.groups[gi].min_pos;
-        t.it.pad = 0;
+        t.it.tails = 0;
         if (nc == 1 && !S.go_partials[gi]) {
           t.it.part_base = -1;
         } else {
@@ -494,6 +505,14 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     for (const auto& x : tmp) {
       P.bucket_max_blocks[x.tiles] = std::max(P.bucket_max_blocks[x.tiles], x.it.blk_count);
       P.bucket_blocks[x.tiles] += x.it.blk_count;
+    }
+    // each item's range of tail blocks (tail_entry is in block-list order)
+    for (int32_t k = 0; k < nitems; ++k) {
+      DevItem& it = P.items[k];
+      const auto b = std::lower_bound(P.tail_entry.begin(), P.tail_entry.end(), it.blk_begin);
+      const auto e = std::lower_bound(b, P.tail_entry.end(), it.blk_begin + it.blk_count);
+      const int64_t lo = b - P.tail_entry.begin(), cnt = e - b;
+      it.tails = (cnt > 0 && lo < 0x10000 && cnt < 0x8000) ? static_cast<int32_t>(lo | (cnt << 16)) : 0;
     }
     // merge records: every partial of a query, in the order its groups were made
     P.merge.resize(total_q);

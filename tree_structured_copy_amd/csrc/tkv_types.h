@@ -31,6 +31,10 @@ struct DevGroup {
 // part_base < 0: the item covers its group's whole list and writes normalised
 // outputs directly; otherwise it writes fp32 partial records (m, l, acc) at
 // slots part_base + j * Hq + h.
+// tails: the item's blocks that end an unfrozen node (a branch's tip block,
+// where a decode step's new token goes) are the plan's tail blocks
+// [tails & 0xffff, + (tails >> 16)) in block-list order; 0 when there are
+// none or the indices do not fit 16 bits.
 struct DevItem {
   int32_t group;
   int32_t blk_begin;
@@ -39,7 +43,7 @@ struct DevItem {
   int32_t q_begin;
   int32_t nq;
   int32_t min_pos;
-  int32_t pad;
+  int32_t tails;
 };
 
 // One block on a group's path list.  mask bit j = group query j can see the
@@ -107,6 +111,8 @@ struct AttnArgs {
 // launch itself (tkv_attend_decode_new_token in one launch): plan block entry
 // `entry` (an index into the plan's block list) is the token's block `blk`,
 // which takes the token at `slot` from row `src` of the call's K/V arrays.
+// The launch's list is indexed by the plan's tail blocks (DevItem::tails);
+// entry = -1 where a tail block takes no token in this call.
 struct NewTok {
   int32_t entry;
   int32_t blk;
@@ -123,7 +129,7 @@ struct NewTokens {
   void* kpool;       // the layer's base
   void* vpool;
   DevBlock* blocks;  // the plan's block list: the tokens' valid counts are written here
-  int32_t n;
+  int32_t n;         // tail blocks listed (tok[0 .. n))
   int32_t pad;
   NewTok tok[kFusedMaxTokens];
 };
