@@ -439,6 +439,34 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       nc = std::max<int64_t>(nc, (nb + kRowsMaxItemBlocks - 1) / kRowsMaxItemBlocks);
       return static_cast<int32_t>(std::max<int64_t>(nc, 1));
     };
+    // The LDS-staged kernels spend, on a block, its memory time plus the math
+    // of every row tile with a query that sees it (a wave skips a block none
+    // of its rows sees).  A group whose blocks are seen by different numbers
+    // of row tiles -- a search tree's shared root and its private leaves -- is
+    // cut into chunks of equal cost rather than equal length:
+    // cost = kBlockCost + (row tiles that see the block - 1), which keeps the
+    // chunks of a widely shared root short.
+    constexpr int64_t kBlockCost = kPlanBlockCost;
+    // tile bits of the queries of one byte of a visibility mask, by byte position
+    auto& tile_of_byte = S.tile_of_byte;
+    tile_of_byte.assign(8 * 256, 0);
+    for (int32_t pb = 0; pb < 8; ++pb)
+      for (int32_t v = 1; v < 256; ++v) {
+        uint32_t t = 0;
+        for (int32_t bit = 0; bit < 8; ++bit)
+          if ((v >> bit) & 1) {
+            const int32_t j = 8 * pb + bit;
+            if (j * q_per_kv >= kMaxRows) break;  // no group holds query j
+            for (int32_t tl = (j * q_per_kv) >> 4; tl <= (j * q_per_kv + q_per_kv - 1) >> 4; ++tl) t |= 1u << tl;
+          }
+        tile_of_byte[pb * 256 + v] = t;
+      }
+    auto tiles_seeing = [&](uint64_t m) {
+      uint32_t t = 0;
+      for (int32_t pb = 0; m; ++pb, m >>= 8) t |= tile_of_byte[pb * 256 + static_cast<int32_t>(m & 0xff)];
+      return __builtin_popcount(t);
+    };
+    auto& cut = S.cut;
     auto& tmp = S.tmp;
     tmp.clear();
     int64_t slots = 0;
@@ -447,9 +475,36 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       if (nb == 0) continue;
       const int32_t nc = chunks_of(gi);
       const int32_t tiles = class_of(gi);
+      // chunk c is blocks [cut[c], cut[c + 1]) of the group's list
+      cut.assign(nc + 1, nb);
+      cut[0] = 0;
+      bool weighted = false;
+      if (tiles >= 2 && nc > 1) {
+        const DevBlock* gb = P.blocks.data() + S.go_begin[gi];
+        const uint64_t full = P.groups[gi].nq >= 64 ? ~0ull : ((1ull << P.groups[gi].nq) - 1);
+        for (int32_t b = 0; b < nb && !weighted; ++b) weighted = gb[b].mask != full;
+        if (weighted) {
+          int64_t total = 0;
+          for (int32_t b = 0; b < nb; ++b) total += kBlockCost + tiles_seeing(gb[b].mask) - 1;
+          int64_t acc = 0;
+          int32_t c = 1;
+          for (int32_t b = 0; b < nb && c < nc; ++b) {
+            acc += kBlockCost + tiles_seeing(gb[b].mask) - 1;
+            // close chunk c - 1 after block b once it holds its share of the
+            // cost, leaving at least one block for each chunk still to come
+            if (acc * nc >= total * c && nb - (b + 1) >= nc - c) cut[c++] = b + 1;
+          }
+          for (; c < nc; ++c) cut[c] = nb - (nc - c);
+          // no chunk longer than a staged block list
+          for (int32_t k = 0; k < nc && weighted; ++k)
+            if (cut[k + 1] - cut[k] > kRowsMaxItemBlocks) weighted = false;
+        }
+      }
+      if (!weighted)
+        for (int32_t c = 0; c < nc; ++c) cut[c + 1] = cut[c] + nb / nc + (c < nb % nc ? 1 : 0);
       int32_t at = 0;
       for (int32_t c = 0; c < nc; ++c) {
-        const int32_t cnt = nb / nc + (c < nb % nc ? 1 : 0);
+        const int32_t cnt = cut[c + 1] - cut[c];
         PlanItemTmp t;
         t.it.group = gi;
         t.it.blk_begin = S.go_begin[gi] + at;

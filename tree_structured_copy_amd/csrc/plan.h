@@ -23,6 +23,13 @@
 
 namespace tkv {
 
+// Cost of a block's memory time in the planner's chunking of LDS-staged
+// groups, in units of one more row tile's work on it.  Measured on the search
+// tree (2048-token root, 256 leaves; 8-tile groups cut into 6 chunks each):
+// 56.0 us per call with equal-length chunks; 69.6, 58.0, 52.7, 51.6, 51.4,
+// 52.2 and 54.9 us at 2, 4, 8, 16, 24, 32 and 64.
+constexpr int64_t kPlanBlockCost = 20;
+
 struct PlanOptions {
   int32_t target_wgs = 256;
   int32_t min_chunk = 32;
@@ -112,6 +119,8 @@ struct PlanScratch {
   std::vector<int8_t> gclass;
   std::vector<PlanItemTmp> tmp;
   std::vector<int32_t> ibeg, ilist;
+  std::vector<uint32_t> tile_of_byte;
+  std::vector<int32_t> cut;
 };
 
 // Which kernel runs a group of `tiles` row tiles of 16: 0, 1 = attn.hip with 1
