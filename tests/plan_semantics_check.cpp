@@ -10,8 +10,9 @@
 //   2. each group's items cover its block list exactly, in order, with the
 //      group's queries, position minimum and the list's tail blocks;
 //   3. a query's output is written directly by exactly one item or assembled
-//      by the merge from one partial record per item of its groups, at the
-//      slot that item writes for it, and no two records share a slot;
+//      by the merge from one partial record per item of its groups that holds
+//      a block the query sees (the item's query mask), at the slot that item
+//      writes for it, and no two records share a slot;
 //   4. the serialised layout's sections are disjoint, aligned and inside the
 //      buffer, and kernel classes and their longest items agree with the items.
 // Prints one line per session and exits non-zero on the first violation.
@@ -197,8 +198,11 @@ int main(int argc, char** argv) {
       for (auto [g, j] : seen[q]) {
         for (int32_t k : items_of[g]) {
           const DevItem& it = P.items[k];
+          uint64_t om = 0;
+          for (int32_t b = it.blk_begin; b < it.blk_begin + it.blk_count; ++b) om |= P.blocks[b].mask;
+          if (om != it.qmask) return fail(sess, "item query mask is not the OR of its blocks' masks");
           if (it.part_base < 0) ++direct;
-          else {
+          else if ((it.qmask >> j) & 1ull) {
             ++partial;
             const int64_t slot0 = static_cast<int64_t>(it.part_base) + static_cast<int64_t>(j) * qpk * hkv;
             expected_slots.insert(static_cast<int32_t>(slot0));

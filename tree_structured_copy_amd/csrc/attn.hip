@@ -382,7 +382,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
       if (it.part_base < 0) {
         const int qi = a.gq[it.q_begin + j];
         a.out[(static_cast<size_t>(qi) * a.hq + h) * D + d] = as / ls;
-      } else {
+      } else if ((it.qmask >> j) & 1ull) {
         const size_t slot = static_cast<size_t>(it.part_base) + static_cast<size_t>(j) * a.hq + h;
         a.part_acc[slot * D + d] = as;
         if (d == 0) {

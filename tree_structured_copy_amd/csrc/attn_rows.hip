@@ -338,7 +338,7 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
         *reinterpret_cast<f32x4*>(o + 16 * dt + 4 * g) = acc[t][dt] / lt;
-    } else {
+    } else if ((it.qmask >> j) & 1ull) {
       const size_t slot = static_cast<size_t>(it.part_base) + static_cast<size_t>(j) * a.hq + h;
       float* o = a.part_acc + slot * D;
 #pragma unroll

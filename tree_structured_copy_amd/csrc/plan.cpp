@@ -513,6 +513,9 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
         t.it.nq = P.groups[gi].nq;
         t.it.min_pos = P.groups[gi].min_pos;
         t.it.tails = 0;
+        t.it.qmask = 0;
+        t.it.pad0 = t.it.pad1 = 0;
+        for (int32_t b = 0; b < cnt; ++b) t.it.qmask |= P.blocks[S.go_begin[gi] + at + b].mask;
         if (nc == 1 && !S.go_partials[gi]) {
           t.it.part_base = -1;
         } else {
@@ -583,6 +586,7 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
             ++direct;
             continue;
           }
+          if (!((P.items[item].qmask >> j) & 1ull)) continue;  // sees none of the item's blocks
           P.parts.push_back({P.items[item].part_base + j * q_per_kv * num_kv_heads, item});
         }
       }

@@ -30,11 +30,14 @@ struct DevGroup {
 // a workgroup needs no group record before it can load its queries).
 // part_base < 0: the item covers its group's whole list and writes normalised
 // outputs directly; otherwise it writes fp32 partial records (m, l, acc) at
-// slots part_base + j * Hq + h.
+// slots part_base + j * Hq + h for the queries j in qmask.
 // tails: the item's blocks that end an unfrozen node (a branch's tip block,
 // where a decode step's new token goes) are the plan's tail blocks
 // [tails & 0xffff, + (tails >> 16)) in block-list order; 0 when there are
 // none or the indices do not fit 16 bits.
+// qmask: the group queries that see at least one of the item's blocks; an
+// item with partial records writes records for these queries only (the
+// merge lists no record of an item for a query that sees none of its blocks).
 struct DevItem {
   int32_t group;
   int32_t blk_begin;
@@ -44,6 +47,9 @@ struct DevItem {
   int32_t nq;
   int32_t min_pos;
   int32_t tails;
+  uint64_t qmask;
+  int32_t pad0;
+  int32_t pad1;
 };
 
 // One block on a group's path list.  mask bit j = group query j can see the
