@@ -167,7 +167,7 @@ int tkv_attend_decode(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t 
  * own tip node, e.g. reserved for all layers by tkv_append_batch with k = v = NULL
  * -- gets K = k_new[i], V = v_new[i] for `layer` (device [nseq][Hkv][head_dim], cache
  * dtype), then the call is tkv_attend_decode over the paths that include it.  With up
- * to 224 handles, and no change to the cached plan since its last use other than
+ * to 160 handles, and no change to the cached plan since its last use other than
  * these tokens (the usual decode step after tkv_append_batch reserved them), the
  * attention launch itself writes each token -- the workgroup that reads its block
  * writes it first -- and the block's valid count in the plan: one launch per step
@@ -234,7 +234,11 @@ typedef struct tkv_counters {
   int64_t block_ids_copied;   /* block-table entries copied by any operation (fork: none) */
   int64_t plans_built;
   int64_t plans_uploaded;     /* whole plans copied to the device */
-  int64_t plans_patched;      /* cached plans updated in place after appends (TKV_OPT_PLAN_PATCH) */
+  int64_t plans_patched;      /* device copies updated in place instead of uploaded whole (TKV_OPT_PLAN_PATCH):
+                                 after appends inside tip blocks, and plans_reused */
+  int64_t plans_reused;       /* plans built for a new batch that took over the device copy of a cached plan
+                                 of the same shape differing only in block ids (the next attention launch
+                                 rewrites those ids); also counted in plans_built and plans_patched */
 } tkv_counters;
 int tkv_get_counters(const tkv_cache* c, tkv_counters* out);
 

@@ -30,12 +30,13 @@ def oracle_threads():
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-def run_both(wl, sample=None, options=None, extra_blocks=0, check_tables=True, threads=1):
+def run_both(wl, sample=None, options=None, extra_blocks=0, check_tables=True, threads=1, counters=None):
     """Replay wl on the library (GPU) and the oracle; compare every attend op.
 
     sample: None = every row and head, or a function (op, nrows) -> [(row, head)]
     (or None for every row and head of that op, or [] for none of it).  threads: the oracle's
-    (OracleReplay) for large checks.
+    (OracleReplay) for large checks.  counters: a dict to receive the
+    library's tkv_get_counters at the end.
     Returns a list of (op, max_abs_err, n_compared).
     """
     torch = need_gpu()
@@ -81,6 +82,8 @@ def run_both(wl, sample=None, options=None, extra_blocks=0, check_tables=True, t
             orc.apply(op)
         if check_tables:
             assert tkv.tkv_num_free(lib.c) == orc.alloc.num_free()
+        if counters is not None:
+            counters.update(tkv.tkv_get_counters(lib.c))
     finally:
         lib.close()
         del lib

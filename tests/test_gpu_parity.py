@@ -426,6 +426,32 @@ def test_loop_recipes_match_oracle(kind):
     assert_close(res, wl.dtype)
 
 
+@pytest.mark.parametrize("route", ["register_kernel", "lds_kernel", "off"])
+def test_search_loop_reuses_device_plans_of_the_same_shape(route):
+    """A tree-search loop (60 simulations: descend, fork into 3, append a
+    node to each child, decode the new leaves): each decode is a new batch,
+    and a plan whose device copy differs from a cached one of the same shape
+    only in block ids takes that copy over; the ids are rewritten by the
+    attention launch (register kernel) or by the patch kernel with the other
+    changed words (when the call runs the LDS-staged kernel).  Every call
+    matches the oracle, tables bit-exact; with TKV_OPT_PLAN_PATCH = 0 no plan
+    is reused."""
+    from tree_structured_copy_amd import tkv
+    wl = recipes.mcts_loop_workload("mcts_loop_reuse", q_heads=8, kv_heads=2, root_tokens=40, branching=3,
+                                    depth=4, iterations=60, node_tokens=5, seed=4)
+    opts = {"register_kernel": {}, "lds_kernel": {tkv.TKV_OPT_TARGET_WGS: 4096},
+            "off": {tkv.TKV_OPT_PLAN_PATCH: 0}}[route]
+    counters = {}
+    res = run_both(wl, options=opts, counters=counters)
+    assert len(res) == len(wl.attend_ops())
+    assert_close(res, wl.dtype)
+    if route == "off":
+        assert counters["plans_reused"] == 0
+    else:
+        assert counters["plans_reused"] > 10, counters
+        assert counters["plans_uploaded"] + counters["plans_reused"] >= counters["plans_built"]
+
+
 @pytest.mark.parametrize("one_launch", [1, 0])
 @pytest.mark.parametrize("dtype,layers,head_dim", [("bf16", 1, 128), ("bf16", 2, 128), ("f32", 1, 64),
                                                    ("bf16", 1, 64), ("f32", 2, 128)])
@@ -532,7 +558,7 @@ def test_decode_with_new_token_refusals():
 @pytest.mark.parametrize("requests,one_launch", [(45, 0), (45, 1), (80, 1)])
 def test_decode_with_new_token_more_than_128_handles(requests, one_launch):
     """135 branches in one fused decode call: its tokens are written by the
-    attention launch (one_launch = 1, up to 224 tokens) or by two preparation
+    attention launch (one_launch = 1, up to 160 tokens) or by two preparation
     launches (128 + 7), the first also carrying the plan's changed words; 240
     branches are more than one attention launch carries, so preparation
     launches write them even with one_launch = 1.  Every call matches the

@@ -74,6 +74,20 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
   const int tk0 = X::kActive ? (it.tails & 0xffff) : 0, tkc = X::kActive ? (it.tails >> 16) : 0;
   __shared__ int2 s_tok[X::kActive ? W : 1][X::kActive ? 64 : 1];
   bool tk_loaded = false;
+  // X = NewTokens with id patches: the (entry, id) pairs of this item, in LDS
+  // (the same list for every wave)
+  __shared__ int2 s_ids[X::kActive ? kMaxIdPatches : 1];
+  int nids = 0;
+  auto correct_id = [&]() {
+    if constexpr (X::kActive) {
+      if (nids == 0 || cur_batch < 0) return;
+      const int b = 2 * (start_w + 32 * cur_batch + (lane >> 1)) + (lane & 1);
+      for (int i = 0; i < nids; ++i) {
+        const int2 ei = s_ids[i];
+        if (ei.x == it.blk_begin + b && e_id >= 0) e_id = ei.y;
+      }
+    }
+  };
   // a block this launch writes a new token into holds one more token than the
   // plan's copy may say: the valid counts of the loaded batch, corrected
   auto correct_valid = [&]() {
@@ -101,6 +115,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
     e_mhi = static_cast<uint32_t>(e.mask >> 32);
     cur_batch = batch;
     correct_valid();
+    correct_id();
   };
   auto meta = [&](int k) {
     if ((k >> 5) != cur_batch) load_entries(k >> 5);
@@ -139,6 +154,27 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
   // their stores.  If the first super-block holds a written block it is loaded
   // again once the stores have landed; otherwise the wave waits for them
   // before loading its first super-block that holds one.
+  if constexpr (X::kActive) {
+    if (x.nid > 0) {
+      // a reused plan's new block ids: this item's are written into the plan
+      // (every KV head's workgroup writes the same values) and read from LDS
+      // wherever the old ids were loaded; the first loads wait for them
+      IdPatch pch{-1, 0};
+      if (lane < x.nid) pch = x.ids[lane];
+      const bool mine = pch.entry >= it.blk_begin && pch.entry < it.blk_begin + nb;
+      const uint64_t m = __ballot(mine);
+      nids = __popcll(m);
+      if (mine) {
+        const int k = __popcll(m & ((1ull << lane) - 1));
+        if (wave == 0) {
+          s_ids[k] = int2{pch.entry, pch.id};
+          __builtin_nontemporal_store(pch.id, &x.blocks[pch.entry].id);
+        }
+      }
+      __syncthreads();
+      correct_id();
+    }
+  }
   if (nmine > 0) {
     mA = meta(0);
     load_sb(kA0, kA1, vA, mA);
@@ -149,7 +185,10 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
     if (tkc > 0) {
       int tk_entry = -1, tk_blk = 0, tk_slot = 0, tk_src = 0;
       if (lane < tkc) {
-        const NewTok t = x.tok[tk0 + lane];
+        // records past x.n are not this launch's (a launch with id patches
+        // and no tokens lists none)
+        NewTok t{-1, 0, 0, 0};
+        if (tk0 + lane < x.n) t = x.tok[tk0 + lane];
         tk_entry = t.entry;
         tk_blk = t.blk;
         tk_slot = t.slot;

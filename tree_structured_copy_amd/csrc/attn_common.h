@@ -368,7 +368,7 @@ __device__ void write_new_tokens(const NewTokens& x, const DevItem& it, int h0, 
   if (tkc == 0) return;
   const int lane = tid & 63;
   int te = -1, tbk = 0, ts = 0, tsr = 0;
-  if (lane < tkc) {
+  if (lane < tkc && tk0 + lane < x.n) {
     const NewTok t = x.tok[tk0 + lane];
     te = t.entry;
     tbk = t.blk;

@@ -58,8 +58,18 @@ struct PlanSlot {
   bool uploaded = false;  // dev holds the plan as of the last upload
   // words changed by patch_plan since that upload (uploaded == true only)
   std::vector<PlanWord> pending;
+  // the device copy's words as the host last left them (small plans only;
+  // empty = unknown): what a plan of the same shape for another batch is
+  // compared with
+  std::vector<uint32_t> shadow;
+  // block ids the next attention launch on this plan writes into the device
+  // copy (a reused device copy, see adopt_plan)
+  std::vector<IdPatch> id_patches;
   uint64_t stamp = 0;
 };
+
+// Plans up to this size keep a host copy of their device words (PlanSlot::shadow).
+constexpr size_t kShadowBytes = 64 << 10;
 
 constexpr int kPlanSlots = 4;
 // pinned staging made at tkv_create: the largest plan tkv_attend_decode_noalloc
@@ -102,6 +112,8 @@ struct tkv_cache {
   int32_t concurrent = 0;  // TKV_OPT_CONCURRENT
   PlanSlot slots[kPlanSlots];
   PlanScratch scratch;
+  Plan spare;                  // a plan is built here, then swapped into its slot
+  std::vector<uint32_t> ser;   // the built plan's words, to compare with a shadow
   // tkv_append_batch's working lists, kept so a call of a familiar size
   // allocates nothing; seen[slot] == seen_stamp marks a handle of the batch
   std::vector<Placement> app_pl;
@@ -178,6 +190,60 @@ void drop_position_words(const Plan& p, std::vector<PlanWord>* words) {
   words->erase(std::remove_if(words->begin(), words->end(), position), words->end());
 }
 
+void shadow_apply(PlanSlot* s, const PlanWord* w, size_t n) {
+  if (s->shadow.empty()) return;
+  for (size_t i = 0; i < n; ++i) {
+    if (w[i].word >= s->shadow.size()) {
+      s->shadow.clear();
+      return;
+    }
+    s->shadow[w[i].word] = static_cast<uint32_t>(w[i].value);
+  }
+}
+
+// A plan just built for a batch that no slot holds (c->spare) takes over the
+// device copy of a cached plan of the same shape when the two differ only in
+// block ids (the leaves under a search node at the depth of an earlier one):
+// the slot then holds the new plan, and its next attention launch rewrites
+// those ids in the device copy before reading them (id_patches) instead of
+// the plan being uploaded.  Returns the slot, or nullptr.
+PlanSlot* adopt_plan(tkv_cache* c) {
+  const Plan& N = c->spare;
+  if (!c->plan_patch || N.bytes > kShadowBytes || N.bytes % 4) return nullptr;
+  const size_t nw = N.bytes / 4;
+  try {
+    c->ser.resize(nw);
+  } catch (const std::bad_alloc&) {
+    return nullptr;
+  }
+  std::memset(c->ser.data(), 0, N.bytes);
+  N.serialise(c->ser.data());
+  const uint32_t b0 = static_cast<uint32_t>(N.off_blocks / 4), per = sizeof(DevBlock) / 4;
+  const uint32_t b1 = b0 + static_cast<uint32_t>(N.blocks.size()) * per;
+  for (auto& s : c->slots) {
+    const Plan& O = s.plan;
+    if (!s.valid || !s.uploaded || !s.pending.empty() || !s.id_patches.empty() || s.shadow.size() != nw) continue;
+    if (O.off_items != N.off_items || O.off_gq != N.off_gq || O.off_gqpos != N.off_gqpos ||
+        O.off_blocks != N.off_blocks || O.off_parts != N.off_parts || O.off_merge != N.off_merge)
+      continue;
+    bool ok = true;
+    s.id_patches.clear();
+    for (size_t w = 0; w < nw && ok; ++w) {
+      if (c->ser[w] == s.shadow[w]) continue;
+      const uint32_t word = static_cast<uint32_t>(w);
+      ok = word >= b0 && word < b1 && (word - b0) % per == 0 &&
+           s.id_patches.size() < static_cast<size_t>(kMaxIdPatches);
+      if (ok) s.id_patches.push_back(IdPatch{static_cast<int32_t>((word - b0) / per), static_cast<int32_t>(c->ser[w])});
+    }
+    if (!ok) {
+      s.id_patches.clear();
+      continue;
+    }
+    return &s;
+  }
+  return nullptr;
+}
+
 int find_plan(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq, PlanSlot** out) {
   const bool verify = nq != nullptr;
   const uint64_t ep = c->tree.epoch(), shape = c->tree.shape_epoch();
@@ -218,20 +284,26 @@ int find_plan(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq
       return TKV_OK;
     }
   }
-  // build into the least recently used slot (a slot with stale contents first)
-  PlanSlot* victim = &c->slots[0];
-  for (auto& s : c->slots) {
-    const bool stale = !s.valid || s.epoch != ep || s.opt_epoch != c->opt_epoch;
-    const bool vstale = !victim->valid || victim->epoch != ep || victim->opt_epoch != c->opt_epoch;
-    if (stale && !vstale) victim = &s;
-    else if (stale == vstale && s.stamp < victim->stamp) victim = &s;
-  }
-  // rebuilt in place: the slot's lists and the planner's scratch keep their
-  // memory, so a rebuild of a familiar size allocates nothing
-  victim->valid = false;
+  // build (the spare plan, the planner's scratch and every slot's lists keep
+  // their memory, so a build of a familiar size allocates nothing), then take
+  // over a cached device copy of the same shape, or the least recently used
+  // slot (a slot with stale contents first)
   const int32_t gsize = c->cfg.num_q_heads / c->cfg.num_kv_heads;
-  if (int rc = build_plan(c->tree, seqs, nq, nseq, gsize, c->cfg.num_kv_heads, c->opt, &victim->plan, &c->scratch))
+  if (int rc = build_plan(c->tree, seqs, nq, nseq, gsize, c->cfg.num_kv_heads, c->opt, &c->spare, &c->scratch))
     return rc;
+  PlanSlot* victim = c->plan_cache ? adopt_plan(c) : nullptr;
+  const bool adopted = victim != nullptr;
+  if (!adopted) {
+    victim = &c->slots[0];
+    for (auto& s : c->slots) {
+      const bool stale = !s.valid || s.epoch != ep || s.opt_epoch != c->opt_epoch;
+      const bool vstale = !victim->valid || victim->epoch != ep || victim->opt_epoch != c->opt_epoch;
+      if (stale && !vstale) victim = &s;
+      else if (stale == vstale && s.stamp < victim->stamp) victim = &s;
+    }
+  }
+  victim->valid = false;
+  std::swap(victim->plan, c->spare);
   try {
     victim->seqs.assign(seqs, seqs + nseq);
     if (verify) victim->nq.assign(nq, nq + nseq);
@@ -245,9 +317,17 @@ int find_plan(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq
   victim->pending.clear();
   victim->opt_epoch = c->opt_epoch;
   victim->valid = true;
-  victim->uploaded = false;
   victim->stamp = ++c->stamp;
   ++c->tree.counters.plans_built;
+  if (adopted) {
+    // the device copy stays; its block ids change with the next launch
+    ++c->tree.counters.plans_patched;
+    ++c->tree.counters.plans_reused;
+  } else {
+    victim->uploaded = false;
+    victim->id_patches.clear();
+    victim->shadow.clear();
+  }
   *out = victim;
   return TKV_OK;
 }
@@ -280,6 +360,7 @@ int stage(tkv_cache* c, size_t bytes) {
 int upload_patch(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
   const size_t n = s->pending.size();
   const size_t at = align256(s->plan.bytes);
+  shadow_apply(s, s->pending.data(), n);
   const size_t bytes = n * sizeof(PlanWord);
   const uint32_t limit = static_cast<uint32_t>(s->plan.bytes / 4);
   for (const PlanWord& w : s->pending)
@@ -334,7 +415,19 @@ int upload_plan(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
     s->dev_cap = cap;
   }
   if (int rc = stage(c, std::max<size_t>(s->plan.bytes, 256))) return rc;
+  const bool keep = s->plan.bytes <= kShadowBytes && s->plan.bytes % 4 == 0;
+  if (keep) std::memset(c->pinned, 0, s->plan.bytes);  // the gaps between sections too, as the shadow has them
   s->plan.serialise(c->pinned);
+  s->id_patches.clear();
+  s->shadow.clear();
+  if (keep) {
+    try {
+      const uint32_t* w = static_cast<const uint32_t*>(c->pinned);
+      s->shadow.assign(w, w + s->plan.bytes / 4);
+    } catch (const std::bad_alloc&) {
+      s->shadow.clear();
+    }
+  }
   if (hipMemcpyAsync(s->dev, c->pinned, s->plan.bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
     return TKV_E_DEVICE;
   if (hipEventRecord(c->pinned_ev, stream) != hipSuccess) return TKV_E_DEVICE;
@@ -383,6 +476,7 @@ int prepare_new_tokens(tkv_cache* c, PlanSlot* s, int32_t layer, int32_t nseq, c
         if (w.word >= limit) return TKV_E_INVAL;
       a.npatch = static_cast<int32_t>(s->pending.size());
       std::memcpy(a.patch, s->pending.data(), s->pending.size() * sizeof(PlanWord));
+      shadow_apply(s, s->pending.data(), s->pending.size());
     }
     if (launch_decode_prep(c->cfg.dtype, c->cfg.head_dim, a, stream) != hipSuccess) return TKV_E_DEVICE;
   }
@@ -523,23 +617,73 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   DeviceGuard dg(c->device);
   launch_log_reset();
   NewTokens* nt = nullptr;
+  // block ids of a reused device copy (adopt_plan): written by the attention
+  // launch when every kernel of the call is the register kernel, else by the
+  // patch kernel with the other changed words
+  const uint32_t b0 = static_cast<uint32_t>(P.off_blocks / 4), per = sizeof(DevBlock) / 4;
+  bool ids_in_launch = false;
+  if (!fixed && !s->id_patches.empty()) {
+    ids_in_launch = true;
+    for (int cls = 0; cls < kKernelClasses; ++cls) {
+      if (P.bucket_begin[cls + 1] == P.bucket_begin[cls]) continue;
+      const int64_t wgs = static_cast<int64_t>(P.bucket_begin[cls + 1] - P.bucket_begin[cls]) * c->cfg.num_kv_heads;
+      if (cls >= 2 || (cls == 0 && !c->waves && wgs > c->cus)) ids_in_launch = false;
+    }
+    if (!ids_in_launch) {
+      try {
+        for (const IdPatch& ip : s->id_patches)
+          s->pending.push_back(PlanWord{b0 + static_cast<uint32_t>(ip.entry) * per, ip.id});
+      } catch (const std::bad_alloc&) {
+        s->uploaded = false;  // uploaded whole instead
+        s->pending.clear();
+      }
+      s->id_patches.clear();
+    }
+  }
   if (fixed) {
     if (int rc = upload_plan_fixed(c, P, fixed, stream)) return rc;
   } else if (k_new) {
     int rc = TKV_OK;
     if (prepare_fused(c, s, layer, seqs, nseq, k_new, v_new, &rc)) {
       // the plan's device copy: whole if it was never uploaded; otherwise it
-      // differs only in the valid counts the launch writes
+      // differs only in the valid counts (and block ids) the launch writes
       if (!s->uploaded) {
         if (int rc2 = upload_plan(c, s, stream)) return rc2;
       }
+      shadow_apply(s, s->pending.data(), s->pending.size());
       s->pending.clear();
       nt = &c->fused;
-    } else if (int rc2 = prepare_new_tokens(c, s, layer, nseq, k_new, v_new, stream)) {
-      return rc2;
+      nt->nid = 0;
+    } else {
+      if (ids_in_launch) {
+        // the preparation launch carries the ids with the other changed words
+        try {
+          for (const IdPatch& ip : s->id_patches)
+            s->pending.push_back(PlanWord{b0 + static_cast<uint32_t>(ip.entry) * per, ip.id});
+        } catch (const std::bad_alloc&) {
+          s->uploaded = false;
+          s->pending.clear();
+        }
+        s->id_patches.clear();
+        ids_in_launch = false;
+      }
+      if (int rc2 = prepare_new_tokens(c, s, layer, nseq, k_new, v_new, stream)) return rc2;
     }
   } else if (int rc = upload_plan(c, s, stream)) {
     return rc;
+  }
+  if (ids_in_launch && !s->id_patches.empty()) {
+    if (!nt) {
+      nt = &c->fused;
+      nt->n = 0;
+    }
+    nt->nid = static_cast<int32_t>(s->id_patches.size());
+    std::memcpy(nt->ids, s->id_patches.data(), s->id_patches.size() * sizeof(IdPatch));
+    for (const IdPatch& ip : s->id_patches)
+      if (!s->shadow.empty()) s->shadow[b0 + static_cast<uint32_t>(ip.entry) * per] = static_cast<uint32_t>(ip.id);
+    s->id_patches.clear();
+  } else if (nt) {
+    nt->nid = 0;
   }
 
   const char* dev = fixed ? fixed : static_cast<const char*>(s->dev);

@@ -125,19 +125,29 @@ struct NewTok {
   int32_t slot;
   int32_t src;
 };
-// Up to this many new tokens travel in an attention launch's arguments (with
-// AttnArgs, within the 4 KiB kernel-argument limit).
-constexpr int kFusedMaxTokens = 224;
+// A block id of a plan's device copy that the attention launch rewrites
+// before reading it: a cached plan's device copy reused for another batch of
+// the same shape (a search step's new leaves under a node at the depth of an
+// earlier one), whose only differences are the block ids.
+struct IdPatch {
+  int32_t entry;  // index into the plan's block list
+  int32_t id;
+};
+// Up to this many new tokens and id patches travel in an attention launch's
+// arguments (with AttnArgs, within the 4 KiB kernel-argument limit).
+constexpr int kFusedMaxTokens = 160;
+constexpr int kMaxIdPatches = 64;
 struct NewTokens {
   static constexpr bool kActive = true;
   const void* k;     // [rows][Hkv][D] of the call's layer
   const void* v;
   void* kpool;       // the layer's base
   void* vpool;
-  DevBlock* blocks;  // the plan's block list: the tokens' valid counts are written here
-  int32_t n;         // tail blocks listed (tok[0 .. n))
-  int32_t pad;
+  DevBlock* blocks;  // the plan's block list: the tokens' valid counts and patched ids are written here
+  int32_t n;         // tail blocks listed (tok[0 .. n)), 0 = no tokens
+  int32_t nid;       // id patches (ids[0 .. nid)), 0 = none
   NewTok tok[kFusedMaxTokens];
+  IdPatch ids[kMaxIdPatches];
 };
 // A launch that writes no token (an empty argument).
 struct NoNewTokens {

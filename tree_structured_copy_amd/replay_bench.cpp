@@ -30,7 +30,7 @@
 //                                 over all layers, K and V;
 //   full_copy_bytes   what copying the parent's whole path at every fork would
 //                     have allocated (the design the article compares with);
-//   plans_built, plans_patched    from the counters.
+//   plans_built, plans_patched, plans_uploaded, plans_reused    from the counters.
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -243,6 +243,7 @@ class Replayer {
       st.counters.plans_built -= base.plans_built;
       st.counters.plans_patched -= base.plans_patched;
       st.counters.plans_uploaded -= base.plans_uploaded;
+      st.counters.plans_reused -= base.plans_reused;
     }
     // empty the cache for the next pass: release every live handle
     for (tkv_seq x : h)
@@ -311,12 +312,13 @@ int main(int argc, char** argv) {
   printf("{\"wall_ms\": %.4f, \"attend_calls\": %lld, \"decode_queries\": %lld, \"verify_tokens\": %lld, "
          "\"attend_kernel_ms\": %.4f, \"merge_kernel_ms\": %.4f, \"forks\": %lld, \"fork_ns\": %.1f, "
          "\"appended_tokens\": %lld, \"peak_blocks\": %lld, \"cow_peak_bytes\": %lld, \"full_copy_bytes\": %lld, "
-         "\"plans_built\": %lld, \"plans_patched\": %lld, \"plans_uploaded\": %lld}\n",
+         "\"plans_built\": %lld, \"plans_patched\": %lld, \"plans_uploaded\": %lld, \"plans_reused\": %lld}\n",
          s.wall_ms, static_cast<long long>(s.attend_calls), static_cast<long long>(s.decode_queries),
          static_cast<long long>(s.verify_tokens), s.attend_ms + s.merge_ms, s.merge_ms,
          static_cast<long long>(s.forks), s.forks ? s.fork_ns / s.forks : 0.0, static_cast<long long>(s.appended),
          static_cast<long long>(s.peak_blocks), static_cast<long long>(s.peak_blocks * block_bytes),
          static_cast<long long>(s.full_copy_tokens * tb), static_cast<long long>(s.counters.plans_built),
-         static_cast<long long>(s.counters.plans_patched), static_cast<long long>(s.counters.plans_uploaded));
+         static_cast<long long>(s.counters.plans_patched), static_cast<long long>(s.counters.plans_uploaded),
+         static_cast<long long>(s.counters.plans_reused));
   return 0;
 }

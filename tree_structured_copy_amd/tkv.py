@@ -66,7 +66,7 @@ class tkv_config(ctypes.Structure):
 class tkv_counters(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("blocks_taken", "blocks_freed", "nodes_created",
                                               "nodes_freed", "block_ids_copied", "plans_built",
-                                              "plans_uploaded", "plans_patched")]
+                                              "plans_uploaded", "plans_patched", "plans_reused")]
 
 
 class tkv_plan_info(ctypes.Structure):
