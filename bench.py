@@ -42,7 +42,25 @@ KERNEL_SOURCES = {
     "attn_partial_kernel": ("attn.hip", "attn_common.h", "layout.h", "tkv_types.h"),
     "attn_rows_kernel": ("attn_rows.hip", "attn_common.h", "layout.h", "tkv_types.h"),
 }
-TRAFFIC_RECORDS = {}
+TRAFFIC_RECORDS = {
+    "full_depth": {"kernel": "attn_rows_kernel<BF16, 128, 1, 4, 1, 2, false, 2, false>",
+                   "sources_sha256": "da1af918a419d879bb7a9f8f4ad053bab832bc1a8417b65ea9ca4375f7bb2245",
+                   "fetch_kib_per_launch": 1581692.25, "fetch_factor": 1.99992, "write_kib_per_launch": 16384.0,
+                   "write_factor": 1.0, "hbm_bytes_per_launch": 3255953201},
+    "llama_fork": {"kernel": "attn_partial_kernel<BF16, 128, 1, 2, false>",
+                   "sources_sha256": "573c338ca8a8682597ffd9f11cf15fdebb086d025c0331f145c70d45ee74e21b",
+                   "fetch_kib_per_launch": 281785.40625, "fetch_factor": 1.99992, "write_kib_per_launch": 2048.0,
+                   "write_factor": 1.0, "hbm_bytes_per_launch": 579170550},
+    "spec_verify": {"kernel": "attn_rows_kernel<BF16, 128, 1, 6, 2, 2, false, 3, true>",
+                    "sources_sha256": "da1af918a419d879bb7a9f8f4ad053bab832bc1a8417b65ea9ca4375f7bb2245",
+                    "fetch_kib_per_launch": 275009.75, "fetch_factor": 1.99992, "write_kib_per_launch": 24576.0,
+                    "write_factor": 1.0, "hbm_bytes_per_launch": 588363234},
+    # the attention kernel alone; its merge kernel adds 19.5 MB fetched and 4.2 MB written
+    "mcts_tree": {"kernel": "attn_rows_kernel<BF16, 128, 1, 8, 1, 2, false, 4, false>",
+                  "sources_sha256": "da1af918a419d879bb7a9f8f4ad053bab832bc1a8417b65ea9ca4375f7bb2245",
+                  "fetch_kib_per_launch": 85328.25, "fetch_factor": 1.99992, "write_kib_per_launch": 18053.75,
+                  "write_factor": 1.0, "hbm_bytes_per_launch": 193232297},
+}
 
 
 def _kernel_sources_sha(kernel):
