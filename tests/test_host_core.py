@@ -341,6 +341,44 @@ def test_plan_means_what_the_tree_says(tmp_path, sanitize):
     assert sum("cascade 1 ok" in line for line in r.stdout.splitlines()) > 20
 
 
+_PLANTED_PLANNER_MISTAKES = [
+    # a block's first position off by one
+    ("out[b].pos = pos0 + 16 * b;", "out[b].pos = pos0 + 16 * b + 1;"),
+    # a tip block counted full
+    ("if (nb > 0) out[nb - 1].valid = nd.tail_valid();", "if (nb > 0) out[nb - 1].valid = 16;"),
+    # a merge record's slot without the KV-head stride
+    ("P.parts.push_back({P.items[item].part_base + j * q_per_kv * num_kv_heads, item});",
+     "P.parts.push_back({P.items[item].part_base + j * q_per_kv, item});"),
+    # a visibility bit given to the wrong query of a pair
+    ("mask[k] |= 1ull << j;", "mask[k] |= 1ull << (j / 2 * 2);"),
+]
+
+
+@pytest.mark.parametrize("planted", range(len(_PLANTED_PLANNER_MISTAKES)))
+def test_plan_checker_catches_planted_mistakes(tmp_path, planted):
+    """The planner checker has the power to fail: each mistake planted in a
+    copy of plan.cpp (a block position off by one, a tip block counted full,
+    a merge slot without the KV-head stride, a visibility bit on the wrong
+    query) makes tests/plan_semantics_check.cpp report a failure."""
+    import shutil
+    import subprocess
+    cxx = shutil.which("g++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    csrc = os.path.join(ROOT, "tree_structured_copy_amd", "csrc")
+    src = open(os.path.join(csrc, "plan.cpp")).read()
+    old, new = _PLANTED_PLANNER_MISTAKES[planted]
+    assert src.count(old) == 1, old
+    mutated = tmp_path / "plan_planted.cpp"
+    mutated.write_text(src.replace(old, new))
+    exe = str(tmp_path / "psc_planted")
+    subprocess.run([cxx, "-O1", "-std=c++17", "-I" + csrc, "-I" + os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "plan_semantics_check.cpp"), os.path.join(csrc, "tree.cpp"),
+                    str(mutated), "-o", exe], check=True, timeout=300)
+    r = subprocess.run([exe, "100"], capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 or "all sessions ok" not in r.stdout, r.stdout[-1000:]
+
+
 def test_shape_epoch_only_moves_on_structural_change():
     """Appends that fit in the tip node's last block leave the tree's shape
     unchanged, so a cached plan is updated rather than rebuilt; a new block, a
