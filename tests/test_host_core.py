@@ -718,10 +718,13 @@ def test_plan_cascade_shapes():
 
 
 def test_plan_classes_fill_one_round():
-    """Each kernel class is cut to fill the GPU on its own, in one round of
-    workgroups (two per CU for the 4- and 8-tile shapes): the shared groups of the search tree become 30 items (240
-    workgroups for 256 CUs); groups that already give one workgroup per CU,
-    or that cannot be cut below the chunk floor, are left whole (the 32-layer
+    """Each kernel class is cut to fill the GPU on its own, in exactly one
+    round of workgroups where its groups can be cut that fine (two per CU for
+    the 4- and 8-tile shapes): the search tree's 10 groups become 64 items
+    (512 workgroups for 256 CUs; shared by cost, the leftovers of rounding
+    down going to the largest remainders); with 16-tile groups, 32 shared items
+    (256 workgroups); groups that already give one workgroup per CU, or that
+    cannot be cut below the chunk floor, are left whole (the 32-layer
     workload's 768-block lists fit one item each)."""
     expect = {"llama_fork": [32, 0, 0, 0, 0, 0], "spec_verify": [0, 0, 0, 64, 0, 0],
               "full_depth": [0, 0, 64, 0, 0, 0]}
@@ -732,15 +735,15 @@ def test_plan_classes_fill_one_round():
     # launch of the 8-tile shape, cut to two workgroups per CU
     info = _host_plan(recipes.mcts_tree(), [(tkv.TKV_OPT_TARGET_WGS, 256)])
     ipk = info["items_per_kernel"]
-    assert ipk == [0, 0, 0, 0, 60, 0], info
-    assert ipk[4] * 8 <= 2 * 256
-    # with 16-tile groups and the cascade: 30 shared items (240 workgroups) plus
+    assert ipk == [0, 0, 0, 0, 64, 0], info
+    assert ipk[4] * 8 == 2 * 256
+    # with 16-tile groups and the cascade: 32 shared items (256 workgroups) plus
     # the one-tile subgroups
     big = [(tkv.TKV_OPT_MAX_ROWS, 256), (tkv.TKV_OPT_CASCADE, 1)]
     info = _host_plan(recipes.mcts_tree(), [(tkv.TKV_OPT_TARGET_WGS, 256)] + big)
     ipk = info["items_per_kernel"]
-    assert ipk[0] == 65 and ipk[5] == 30 and sum(ipk[1:5]) == 0, info
-    assert ipk[5] * 8 <= 256
+    assert ipk[0] == 65 and ipk[5] == 32 and sum(ipk[1:5]) == 0, info
+    assert ipk[5] * 8 == 256
     # twice the workgroups asked for: the shared groups are cut about twice as
     # fine, still within one round
     info2 = _host_plan(recipes.mcts_tree(), [(tkv.TKV_OPT_TARGET_WGS, 512)] + big)

@@ -95,6 +95,32 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
   const int G = a.gsize;
   const int nrows = it.nq * G;
 
+  // rows of this wave: tiles lw, lw + W, ... of head kvh; their query
+  // indices load beside the ring's first block ids, so that the queries
+  // themselves go out right behind the ring's first loads
+  const uint64_t gmask = it.nq >= 64 ? ~0ull : ((1ull << it.nq) - 1);
+  int qi[TPW], qj[TPW], qlim[TPW];
+  uint64_t my_q = 0;  // group queries with a row in this wave's tiles
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int tile = lw + W * t;
+    const int R = 16 * tile + r;
+    if (16 * tile < nrows) {
+      const int j0 = (16 * tile) / G, j1 = min(nrows - 1, 16 * tile + 15) / G;
+      for (int j = j0; j <= j1; ++j) my_q |= 1ull << j;
+    }
+    if (R < nrows) {
+      const int j = R / G;
+      qi[t] = a.gq[it.q_begin + j];
+      qj[t] = j;
+      qlim[t] = CAUSAL ? a.gqpos[it.q_begin + j] : 0;
+    } else {
+      qi[t] = -1;
+      qj[t] = 0;
+      qlim[t] = 0x7fffffff;
+    }
+  }
+
   // Issue this wave's share of super-block sp's loads into ring slot `slot`.
   // The ids of the first 64 blocks come straight from global memory, so the
   // ring's first super-blocks are in flight before the block list and the
@@ -132,39 +158,7 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
   for (int sp = 0; sp < AHEAD; ++sp)
     if (sp < nsb) issue(sp, sp);
 
-  // rows of this wave: tiles lw, lw + W, ... of head kvh; their query
-  // indices load beside the block list
-  const uint64_t gmask = it.nq >= 64 ? ~0ull : ((1ull << it.nq) - 1);
-  int qi[TPW], qj[TPW], qlim[TPW];
-  uint64_t my_q = 0;  // group queries with a row in this wave's tiles
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int tile = lw + W * t;
-    const int R = 16 * tile + r;
-    if (16 * tile < nrows) {
-      const int j0 = (16 * tile) / G, j1 = min(nrows - 1, 16 * tile + 15) / G;
-      for (int j = j0; j <= j1; ++j) my_q |= 1ull << j;
-    }
-    if (R < nrows) {
-      const int j = R / G;
-      qi[t] = a.gq[it.q_begin + j];
-      qj[t] = j;
-      qlim[t] = CAUSAL ? a.gqpos[it.q_begin + j] : 0;
-    } else {
-      qi[t] = -1;
-      qj[t] = 0;
-      qlim[t] = 0x7fffffff;
-    }
-  }
-
-  // the item's block list, staged once; waves read it 64 entries at a time
-  // (lane k holds entry base + k) and take each super-block's fields with
-  // v_readlane, so no LDS round trip sits on the per-super-block path
-  for (int k = tid; k < nb; k += 64 * W * HPW) {
-    const DevBlock e = bl[k];
-    ents[k] = StagedBlock{static_cast<uint32_t>(e.id) | (static_cast<uint32_t>(e.valid) << 27), e.pos, e.mask};
-  }
-
+  // the queries, right behind the ring's first loads
   F qf[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
@@ -176,6 +170,14 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
       P::zero(qf[t]);
     }
   }
+  // the item's block list, staged once; waves read it 64 entries at a time
+  // (lane k holds entry base + k) and take each super-block's fields with
+  // v_readlane, so no LDS round trip sits on the per-super-block path
+  for (int k = tid; k < nb; k += 64 * W * HPW) {
+    const DevBlock e = bl[k];
+    ents[k] = StagedBlock{static_cast<uint32_t>(e.id) | (static_cast<uint32_t>(e.valid) << 27), e.pos, e.mask};
+  }
+
   float m[TPW], l[TPW];
   f32x4 acc[TPW][NDT];
 #pragma unroll
@@ -208,6 +210,7 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
     else wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     if constexpr (!EARLY) {
+      // (super-block NS - 1 went out with the prologue)
       if (s + NS - 1 < nsb) issue(s + NS - 1, (s + NS - 1) % NS);
     }
 

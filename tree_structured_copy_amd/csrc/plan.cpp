@@ -395,9 +395,9 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     // 5. split-K chunking and items.  The kernel classes of a call do not
     //    share the GPU well (a class's workgroups take whole CUs' registers or
     //    LDS, and side-stream joins cost more than the overlap gains), so each
-    //    class is cut to fill the GPU on its own: about target_wgs / Hkv items,
-    //    shared among its groups in proportion to their blocks, rounded down
-    //    so that one round of workgroups holds them all.  A chunk stays long
+    //    class is cut to fill the GPU on its own: about target_wgs / Hkv items
+    //    (one round of workgroups), shared among its groups in proportion to
+    //    their cost (below).  A chunk stays long
     //    next to its partial record: at least min_chunk blocks for the
     //    register-tile classes, whose time is their memory time, and a quarter
     //    of that for the LDS-staged classes (3+ row tiles), whose time per
@@ -419,33 +419,13 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     if (top > 2)
       for (int32_t gi = 0; gi < ngroups; ++gi)
         if (gclass[gi] >= 2 && gclass[gi] < top && class_work[gclass[gi]] < class_work[top]) gclass[gi] = top;
-    int64_t class_blocks[kKernelClasses] = {0, 0, 0, 0, 0, 0};
     auto class_of = [&](int32_t gi) { return static_cast<int>(gclass[gi]); };
-    for (int32_t gi = 0; gi < ngroups; ++gi) class_blocks[class_of(gi)] += S.go_count[gi];
-    const int64_t class_items = std::max<int64_t>(1, std::max<int32_t>(1, opt.target_wgs) / num_kv_heads);
-    auto chunks_of = [&](int32_t gi) -> int32_t {
-      const int cls = class_of(gi);
-      const int64_t nb = S.go_count[gi];
-      // the 4- and 8-tile LDS-staged shapes fit two workgroups per CU, and
-      // two per CU stream faster than one with a deeper ring: twice the items
-      const int64_t want = (cls == 2 || cls == 4) ? 2 * class_items : class_items;
-      // a class too small to give every item its floor of blocks (a few
-      // queries over a few thousand tokens) is latency-bound, not
-      // bandwidth-bound: its floor drops to what fills the GPU, at least 4
-      const int64_t base = std::max<int32_t>(1, cls < 2 ? opt.min_chunk : opt.min_chunk / 4);
-      const int64_t floor = std::max<int64_t>(1, std::min(base, std::max<int64_t>(4, class_blocks[cls] / want)));
-      int64_t nc = nb * want / class_blocks[cls];
-      nc = std::min(nc, nb / floor);
-      nc = std::max<int64_t>(nc, (nb + kRowsMaxItemBlocks - 1) / kRowsMaxItemBlocks);
-      return static_cast<int32_t>(std::max<int64_t>(nc, 1));
-    };
     // The LDS-staged kernels spend, on a block, its memory time plus the math
     // of every row tile with a query that sees it (a wave skips a block none
-    // of its rows sees).  A group whose blocks are seen by different numbers
-    // of row tiles -- a search tree's shared root and its private leaves -- is
-    // cut into chunks of equal cost rather than equal length:
-    // cost = kBlockCost + (row tiles that see the block - 1), which keeps the
-    // chunks of a widely shared root short.
+    // of its rows sees).  Their groups are chunked by cost,
+    // kBlockCost + (row tiles that see the block - 1) per block, so that a
+    // chunk of a widely shared root is shorter than one of private leaves,
+    // and a group's share of its class's items follows its cost.
     constexpr int64_t kBlockCost = kPlanBlockCost;
     // tile bits of the queries of one byte of a visibility mask, by byte position
     auto& tile_of_byte = S.tile_of_byte;
@@ -466,6 +446,72 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       for (int32_t pb = 0; m; ++pb, m >>= 8) t |= tile_of_byte[pb * 256 + static_cast<int32_t>(m & 0xff)];
       return __builtin_popcount(t);
     };
+    auto block_cost = [&](const DevBlock& b) -> int64_t { return kBlockCost + tiles_seeing(b.mask) - 1; };
+    auto& gcost = S.gcost;
+    gcost.assign(ngroups, 0);
+    int64_t class_cost[kKernelClasses] = {0, 0, 0, 0, 0, 0};
+    int64_t class_blocks[kKernelClasses] = {0, 0, 0, 0, 0, 0};
+    for (int32_t gi = 0; gi < ngroups; ++gi) {
+      const int cls = class_of(gi);
+      const int32_t nb = S.go_count[gi];
+      if (cls >= 2) {
+        const DevBlock* gb = P.blocks.data() + S.go_begin[gi];
+        for (int32_t b = 0; b < nb; ++b) gcost[gi] += block_cost(gb[b]);
+      } else {
+        gcost[gi] = nb;
+      }
+      class_cost[cls] += gcost[gi];
+      class_blocks[cls] += nb;
+    }
+    const int64_t class_items = std::max<int64_t>(1, std::max<int32_t>(1, opt.target_wgs) / num_kv_heads);
+    auto want_of = [&](int cls) -> int64_t {
+      // the 4- and 8-tile LDS-staged shapes fit two workgroups per CU, and
+      // two per CU stream faster than one with a deeper ring: twice the items
+      return (cls == 2 || cls == 4) ? 2 * class_items : class_items;
+    };
+    auto most_of = [&](int32_t gi) -> int64_t {
+      const int cls = class_of(gi);
+      // a class too small to give every item its floor of blocks (a few
+      // queries over a few thousand tokens) is latency-bound, not
+      // bandwidth-bound: its floor drops to what fills the GPU, at least 4
+      const int64_t base = std::max<int32_t>(1, cls < 2 ? opt.min_chunk : opt.min_chunk / 4);
+      const int64_t floor =
+          std::max<int64_t>(1, std::min(base, std::max<int64_t>(4, class_blocks[cls] / want_of(cls))));
+      return std::max<int64_t>(1, S.go_count[gi] / floor);
+    };
+    // Chunks per group: the group's share of its class's items by cost,
+    // rounded down; the items that leaves go one each to the groups with the
+    // largest remainders, so that a class fills one round of workgroups.  A
+    // chunk stays at least the floor above and at most kRowsMaxItemBlocks.
+    auto& gchunks = S.gchunks;
+    auto& gfrac = S.gfrac;
+    gchunks.assign(ngroups, 1);
+    gfrac.assign(ngroups, -1.0);
+    int64_t class_chunks[kKernelClasses] = {0, 0, 0, 0, 0, 0};
+    for (int32_t gi = 0; gi < ngroups; ++gi) {
+      const int cls = class_of(gi);
+      const int64_t nb = S.go_count[gi];
+      if (nb == 0) continue;
+      const double ideal = static_cast<double>(gcost[gi]) * static_cast<double>(want_of(cls)) /
+                           static_cast<double>(std::max<int64_t>(1, class_cost[cls]));
+      const int64_t most = most_of(gi);
+      const int64_t least = (nb + kRowsMaxItemBlocks - 1) / kRowsMaxItemBlocks;
+      int64_t nc = std::min(static_cast<int64_t>(ideal), most);
+      nc = std::max<int64_t>(std::max<int64_t>(nc, least), 1);
+      gchunks[gi] = static_cast<int32_t>(nc);
+      if (nc < most && static_cast<double>(nc) < ideal) gfrac[gi] = ideal - static_cast<double>(nc);
+      class_chunks[cls] += nc;
+    }
+    for (int cls = 0; cls < kKernelClasses; ++cls) {
+      for (int64_t left = want_of(cls) - class_chunks[cls]; left > 0; --left) {
+        int32_t best = -1;
+        for (int32_t gi = 0; gi < ngroups; ++gi)
+          if (class_of(gi) == cls && gfrac[gi] > 0.0 && (best < 0 || gfrac[gi] > gfrac[best])) best = gi;
+        if (best < 0) break;
+        ++gchunks[best];
+        gfrac[best] = -1.0;  // one extra chunk per group
+      }
+    }
     auto& cut = S.cut;
     auto& tmp = S.tmp;
     tmp.clear();
@@ -473,7 +519,7 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     for (int32_t gi = 0; gi < ngroups; ++gi) {
       const int32_t nb = S.go_count[gi];
       if (nb == 0) continue;
-      const int32_t nc = chunks_of(gi);
+      const int32_t nc = gchunks[gi];
       const int32_t tiles = class_of(gi);
       // chunk c is blocks [cut[c], cut[c + 1]) of the group's list
       cut.assign(nc + 1, nb);
@@ -485,11 +531,11 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
         for (int32_t b = 0; b < nb && !weighted; ++b) weighted = gb[b].mask != full;
         if (weighted) {
           int64_t total = 0;
-          for (int32_t b = 0; b < nb; ++b) total += kBlockCost + tiles_seeing(gb[b].mask) - 1;
+          for (int32_t b = 0; b < nb; ++b) total += block_cost(gb[b]);
           int64_t acc = 0;
           int32_t c = 1;
           for (int32_t b = 0; b < nb && c < nc; ++b) {
-            acc += kBlockCost + tiles_seeing(gb[b].mask) - 1;
+            acc += block_cost(gb[b]);
             // close chunk c - 1 after block b once it holds its share of the
             // cost, leaving at least one block for each chunk still to come
             if (acc * nc >= total * c && nb - (b + 1) >= nc - c) cut[c++] = b + 1;

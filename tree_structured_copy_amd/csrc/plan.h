@@ -121,6 +121,9 @@ struct PlanScratch {
   std::vector<int32_t> ibeg, ilist;
   std::vector<uint32_t> tile_of_byte;
   std::vector<int32_t> cut;
+  std::vector<int64_t> gcost;  // per group: blocks (register classes) or chunking cost (LDS-staged)
+  std::vector<int32_t> gchunks;
+  std::vector<double> gfrac;
 };
 
 // Which kernel runs a group of `tiles` row tiles of 16: 0, 1 = attn.hip with 1
