@@ -276,7 +276,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
   const int nrows = it.nq * G;
   const uint64_t gmask = it.nq >= 64 ? ~0ull : ((1ull << it.nq) - 1);
   F qf[T];
-  int qj[T], qlim[T];
+  int qj[T], qlim[T], qix[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int R = 16 * t + r;
@@ -286,10 +286,12 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
       const int qi = a.gq[it.q_begin + j];
       P::load_q(qf[t], static_cast<const E*>(a.q) + (static_cast<size_t>(qi) * a.hq + h) * D, g);
       qj[t] = j;
+      qix[t] = qi;
       qlim[t] = CAUSAL ? a.gqpos[it.q_begin + j] : 0;
     } else {
       P::zero(qf[t]);
       qj[t] = 0;
+      qix[t] = 0;
       qlim[t] = 0x7fffffff;
     }
   }
@@ -385,46 +387,54 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
     l[t] += __shfl_xor(l[t], 32);
   }
 
-  // merge the W waves' states through LDS, one row tile at a time
+  // merge the W waves' states through LDS, one row tile at a time: each wave
+  // puts its rows there row-major (16-byte runs, as the MFMA leaves them),
+  // then every thread finishes four consecutive elements of a row at a time,
+  // the row's maximum and wave weights formed once per piece, so that a
+  // wave's stores cover whole rows
+  constexpr int RS = D + 4;  // LDS row stride in floats
+  constexpr int P4 = D / 4;  // four-element pieces per row
   __shared__ float s_m[W][16];
   __shared__ float s_l[W][16];
-  __shared__ float s_acc[W][D][17];
+  __shared__ int s_qi[16];
+  __shared__ __attribute__((aligned(16))) float s_acc[W][16][RS];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     if (16 * t >= nrows) break;
     if (g == 0) {
       s_m[wave][r] = m[t];
       s_l[wave][r] = l[t];
+      if (wave == 0) s_qi[r] = qix[t];
     }
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_acc[wave][16 * dt + 4 * g + i][r] = acc[t][dt][i];
+    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(&s_acc[wave][r][16 * dt + 4 * g]) = acc[t][dt];
     __syncthreads();
-    for (int o = tid; o < 16 * D; o += NT) {
-      const int rr = o / D, d = o - rr * D;
+    for (int pc = tid; pc < 16 * P4; pc += NT) {
+      const int rr = pc / P4, c4 = pc - rr * P4;
       const int R = 16 * t + rr;
-      if (R >= nrows) continue;
+      if (R >= nrows) break;  // pieces go row by row: the rest are past the group too
       float M = s_m[0][rr];
 #pragma unroll
       for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w][rr]);
-      float ls = 0.f, as = 0.f;
+      float ls = 0.f;
+      f32x4 as = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < W; ++w) {
         const float mw = s_m[w][rr];
         const float f = (mw == kNegInf) ? 0.f : fast_exp2((mw - M) * sl2);
         ls += s_l[w][rr] * f;
-        as += s_acc[w][d][rr] * f;
+        as += *reinterpret_cast<const f32x4*>(&s_acc[w][rr][4 * c4]) * f;
       }
       const int j = R / G;
       const int h = kvh * G + (R - j * G);
       if (it.part_base < 0) {
-        const int qi = a.gq[it.q_begin + j];
-        a.out[(static_cast<size_t>(qi) * a.hq + h) * D + d] = as / ls;
+        // divided, not multiplied by 1 / l: a single visible key then gives
+        // its value exactly
+        *reinterpret_cast<f32x4*>(a.out + (static_cast<size_t>(s_qi[rr]) * a.hq + h) * D + 4 * c4) = as / ls;
       } else if ((it.qmask >> j) & 1ull) {
         const size_t slot = static_cast<size_t>(it.part_base) + static_cast<size_t>(j) * a.hq + h;
-        a.part_acc[slot * D + d] = as;
-        if (d == 0) {
+        *reinterpret_cast<f32x4*>(a.part_acc + slot * D + 4 * c4) = as;
+        if (c4 == 0) {
           a.part_ml[2 * slot] = M;
           a.part_ml[2 * slot + 1] = ls;
         }
