@@ -44,22 +44,22 @@ KERNEL_SOURCES = {
 }
 TRAFFIC_RECORDS = {
     "full_depth": {"kernel": "attn_rows_kernel<BF16, 128, 1, 4, 1, 2, false, 2, false>",
-                   "sources_sha256": "da1af918a419d879bb7a9f8f4ad053bab832bc1a8417b65ea9ca4375f7bb2245",
-                   "fetch_kib_per_launch": 1581692.25, "fetch_factor": 1.99992, "write_kib_per_launch": 16384.0,
-                   "write_factor": 1.0, "hbm_bytes_per_launch": 3255953201},
+                   "sources_sha256": "ccf7845f53c0dc476804e28766bba45b3db5cff32a0157aaaa0bcee254d10413",
+                   "fetch_kib_per_launch": 1581695.28125, "fetch_factor": 1.99992, "write_kib_per_launch": 16384.0,
+                   "write_factor": 1.0, "hbm_bytes_per_launch": 3255959409},
     "llama_fork": {"kernel": "attn_partial_kernel<BF16, 128, 1, 2, false>",
-                   "sources_sha256": "573c338ca8a8682597ffd9f11cf15fdebb086d025c0331f145c70d45ee74e21b",
-                   "fetch_kib_per_launch": 281785.40625, "fetch_factor": 1.99992, "write_kib_per_launch": 2048.0,
-                   "write_factor": 1.0, "hbm_bytes_per_launch": 579170550},
+                   "sources_sha256": "fab2b9b84f2ef060120d32d5f53726192f352a30f6ab797bec8f42019a70eece",
+                   "fetch_kib_per_launch": 281812.71875, "fetch_factor": 1.99992, "write_kib_per_launch": 2048.0,
+                   "write_factor": 1.0, "hbm_bytes_per_launch": 579226483},
     "spec_verify": {"kernel": "attn_rows_kernel<BF16, 128, 1, 6, 2, 2, false, 3, true>",
-                    "sources_sha256": "da1af918a419d879bb7a9f8f4ad053bab832bc1a8417b65ea9ca4375f7bb2245",
-                    "fetch_kib_per_launch": 275009.75, "fetch_factor": 1.99992, "write_kib_per_launch": 24576.0,
-                    "write_factor": 1.0, "hbm_bytes_per_launch": 588363234},
-    # the attention kernel alone; its merge kernel adds 19.5 MB fetched and 4.2 MB written
+                    "sources_sha256": "ccf7845f53c0dc476804e28766bba45b3db5cff32a0157aaaa0bcee254d10413",
+                    "fetch_kib_per_launch": 275006.78125, "fetch_factor": 1.99992, "write_kib_per_launch": 24576.0,
+                    "write_factor": 1.0, "hbm_bytes_per_launch": 588357154},
+    # the attention kernel alone; its merge kernel adds 20.2 MB fetched and 4.2 MB written
     "mcts_tree": {"kernel": "attn_rows_kernel<BF16, 128, 1, 8, 1, 2, false, 4, false>",
-                  "sources_sha256": "da1af918a419d879bb7a9f8f4ad053bab832bc1a8417b65ea9ca4375f7bb2245",
-                  "fetch_kib_per_launch": 85328.25, "fetch_factor": 1.99992, "write_kib_per_launch": 18053.75,
-                  "write_factor": 1.0, "hbm_bytes_per_launch": 193232297},
+                  "sources_sha256": "ccf7845f53c0dc476804e28766bba45b3db5cff32a0157aaaa0bcee254d10413",
+                  "fetch_kib_per_launch": 87150.65625, "fetch_factor": 1.99992, "write_kib_per_launch": 18703.75,
+                  "write_factor": 1.0, "hbm_bytes_per_launch": 197630035},
 }
 
 
