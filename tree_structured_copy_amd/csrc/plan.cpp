@@ -427,20 +427,25 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     // chunk of a widely shared root is shorter than one of private leaves,
     // and a group's share of its class's items follows its cost.
     constexpr int64_t kBlockCost = kPlanBlockCost;
-    // tile bits of the queries of one byte of a visibility mask, by byte position
+    // tile bits of the queries of one byte of a visibility mask, by byte
+    // position (made once per query heads per KV head: the scratch keeps it)
     auto& tile_of_byte = S.tile_of_byte;
-    tile_of_byte.assign(8 * 256, 0);
-    for (int32_t pb = 0; pb < 8; ++pb)
-      for (int32_t v = 1; v < 256; ++v) {
-        uint32_t t = 0;
-        for (int32_t bit = 0; bit < 8; ++bit)
-          if ((v >> bit) & 1) {
-            const int32_t j = 8 * pb + bit;
-            if (j * q_per_kv >= kMaxRows) break;  // no group holds query j
-            for (int32_t tl = (j * q_per_kv) >> 4; tl <= (j * q_per_kv + q_per_kv - 1) >> 4; ++tl) t |= 1u << tl;
-          }
-        tile_of_byte[pb * 256 + v] = t;
-      }
+    if (S.tile_of_byte_qpk != q_per_kv) {
+      tile_of_byte.assign(8 * 256, 0);
+      for (int32_t pb = 0; pb < 8; ++pb)
+        for (int32_t v = 1; v < 256; ++v) {
+          uint32_t t = 0;
+          for (int32_t bit = 0; bit < 8; ++bit)
+            if ((v >> bit) & 1) {
+              const int32_t j = 8 * pb + bit;
+              if (j * q_per_kv >= kMaxRows) break;  // no group holds query j
+              for (int32_t tl = (j * q_per_kv) >> 4; tl <= (j * q_per_kv + q_per_kv - 1) >> 4; ++tl)
+                t |= 1u << tl;
+            }
+          tile_of_byte[pb * 256 + v] = t;
+        }
+      S.tile_of_byte_qpk = q_per_kv;
+    }
     auto tiles_seeing = [&](uint64_t m) {
       uint32_t t = 0;
       for (int32_t pb = 0; m; ++pb, m >>= 8) t |= tile_of_byte[pb * 256 + static_cast<int32_t>(m & 0xff)];
@@ -455,8 +460,12 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       const int cls = class_of(gi);
       const int32_t nb = S.go_count[gi];
       if (cls >= 2) {
+        // (a block every query of the group sees -- most of a shared prefix --
+        // costs the same for all: no table lookups for it)
         const DevBlock* gb = P.blocks.data() + S.go_begin[gi];
-        for (int32_t b = 0; b < nb; ++b) gcost[gi] += block_cost(gb[b]);
+        const uint64_t full = P.groups[gi].nq >= 64 ? ~0ull : ((1ull << P.groups[gi].nq) - 1);
+        const int64_t full_cost = kBlockCost + (P.groups[gi].nq * q_per_kv + 15) / 16 - 1;
+        for (int32_t b = 0; b < nb; ++b) gcost[gi] += gb[b].mask == full ? full_cost : block_cost(gb[b]);
       } else {
         gcost[gi] = nb;
       }

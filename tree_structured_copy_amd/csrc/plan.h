@@ -120,6 +120,7 @@ struct PlanScratch {
   std::vector<PlanItemTmp> tmp;
   std::vector<int32_t> ibeg, ilist;
   std::vector<uint32_t> tile_of_byte;
+  int32_t tile_of_byte_qpk = 0;  // the query heads per KV head tile_of_byte was made for
   std::vector<int32_t> cut;
   std::vector<int64_t> gcost;  // per group: blocks (register classes) or chunking cost (LDS-staged)
   std::vector<int32_t> gchunks;

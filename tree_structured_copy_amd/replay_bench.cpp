@@ -16,8 +16,9 @@
 // against the oracle.
 //
 // With --host the cache is host-only: appends reserve slots, attention calls
-// are counted but not run, and no HIP call is made (the block and fork
-// figures still hold).
+// have their plans built (the host work a loop needs per call) but are not
+// run, and no HIP call is made (the block and fork figures still hold; wall_ms
+// is then the loop's tree and planner time).
 //
 // Output: one JSON object on stdout with, for the measured part,
 //   wall_ms         wall time;
@@ -209,9 +210,9 @@ class Replayer {
         const int32_t* nq = verify ? counts.data() : nullptr;
         ++st.attend_calls;
         (verify ? st.verify_tokens : st.decode_queries) += rows;
-        if (host_) continue;
         size_t need = 0;
         check(tkv_workspace_size(cache, seqs.data(), nq, n, &need), "tkv_workspace_size");
+        if (host_) continue;
         if (need > ws_cap_) {
           // only the first pass grows it, outside any timed region
           if (ws_) hip_check(hipStreamSynchronize(stream_), "hipStreamSynchronize");
