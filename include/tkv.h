@@ -182,6 +182,21 @@ int tkv_attend_decode_new_token(tkv_cache* c, int32_t layer, const tkv_seq* seqs
                                 const void* k_new, const void* v_new, const void* q, float* out,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* As tkv_attend_decode_new_token, with ntok[i] new tokens for handle i (1 <= ntok[i]
+ * <= 16): its last ntok[i] tokens, which must all lie in its last block and its own tip
+ * node -- e.g. a node of ntok[i] tokens reserved for every layer by tkv_append_batch
+ * with k = v = NULL after a fork, as a tree search expands a node (Dendrite demo tape,
+ * "MCTS demo": each expansion forks and extends the children before evaluating them).
+ * Their K and V for `layer` are rows [r_i, r_i + ntok[i]) of k_new / v_new (device
+ * [sum ntok][Hkv][head_dim], cache dtype), r_i = ntok[0] + ... + ntok[i-1].  One launch
+ * per call under the same conditions as tkv_attend_decode_new_token (the records are
+ * per tail block: a node opened by the tokens is written whole, zeros after them).
+ * TKV_E_RANGE if some ntok[i] is outside 1..16 or the tokens would reach into an
+ * earlier block; otherwise errors as tkv_attend_decode_new_token. */
+int tkv_attend_decode_new_tokens(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* ntok,
+                                 int32_t nseq, const void* k_new, const void* v_new, const void* q,
+                                 float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* tkv_attend_decode for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
  * same plan and kernels as tkv_attend_decode, with the plan and the split-K
@@ -280,7 +295,7 @@ enum {
                                since) is updated in place: the changed block counts and query
                                positions are written into its device copy by a small kernel
                                (default); 0 = such a plan is rebuilt and uploaded whole */
-  TKV_OPT_FUSED_NEW_TOKEN = 9 /* 1 = tkv_attend_decode_new_token writes its tokens (and their blocks'
+  TKV_OPT_FUSED_NEW_TOKEN = 9 /* 1 = tkv_attend_decode_new_token(s) writes its tokens (and their blocks'
                                valid counts in the plan) from the attention launch itself when it
                                can: one launch per step (default); 0 = always by a preparation
                                launch first */

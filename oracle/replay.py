@@ -79,7 +79,7 @@ class PreloadedArrays:
             elif op[0] in ("append_batch",):
                 calls = [(op[3], sum(op[2]))]
             elif op[0] == "reserve_batch":
-                calls = [(op[2], len(op[1]))]
+                calls = [(op[2], sum(op[3]) if len(op) > 3 else len(op[1]))]
             else:
                 continue
             for call, total in calls:
@@ -144,10 +144,12 @@ class OracleReplay:
                 self.mat.append(self.h_mat[h], _batch_source_for(self.wl, call, total, first, n, self.arrays))
                 first += n
         elif kind == "reserve_batch":
-            # one token per handle whose K/V (every layer) are those of batched
-            # append `call`, written later by the decode_new ops
-            _, hs, call = op
-            self.apply(("append_batch", hs, [1] * len(hs), call))
+            # ntok[i] tokens (default one) for handle i whose K/V (every layer)
+            # are those of batched append `call`, written later by the
+            # decode_new ops
+            hs, call = op[1], op[2]
+            ns = list(op[3]) if len(op) > 3 else [1] * len(hs)
+            self.apply(("append_batch", hs, ns, call))
         elif kind == "fork":
             _, h, n, kids = op
             if self.alloc is not None:

@@ -408,19 +408,21 @@ def test_generation_loop_plan_update(kind, layers):
     assert counters[1]["plans_built"] < counters[0]["plans_built"]
 
 
-@pytest.mark.parametrize("kind", ["spec_loop", "mcts_loop"])
+@pytest.mark.parametrize("kind", ["spec_loop", "mcts_loop", "mcts_loop_one_launch"])
 def test_loop_recipes_match_oracle(kind):
     """The multi-round speculative loop (6 rounds of forking at unaligned
     lengths, drafts in fresh blocks, verify, rollback by truncation, a bonus
     token) and the tree-search loop (60 simulations with terminal
-    re-evaluations), replayed through the library: every attention call
+    re-evaluations; also with each expansion's new nodes reserved and written
+    by the decode call), replayed through the library: every attention call
     matches the oracle; tables and free blocks are bit-exact."""
     if kind == "spec_loop":
         wl = recipes.spec_loop_workload("spec_loop_small", q_heads=8, kv_heads=2, requests=5, prefix=40, paths=3,
                                         drafts=5, rounds=6, seed=3)
     else:
         wl = recipes.mcts_loop_workload("mcts_loop_small", q_heads=8, kv_heads=2, root_tokens=40, branching=3,
-                                        depth=4, iterations=60, node_tokens=5, seed=4)
+                                        depth=4, iterations=60, node_tokens=5, seed=4,
+                                        one_launch=kind == "mcts_loop_one_launch")
     res = run_both(wl)
     assert len(res) == len(wl.attend_ops())
     assert_close(res, wl.dtype)
@@ -521,6 +523,146 @@ def test_decode_with_new_token_written_in_the_call(dtype, layers, head_dim, one_
     for k in pools["fused"]:
         assert torch.equal(pools["fused"][k][0], pools["plain"][k][0])
         assert torch.equal(pools["fused"][k][1], pools["plain"][k][1])
+
+
+def _multi_new_token_workload(name, dtype, layers, head_dim, rounds, seed):
+    """3 requests (a 37-token prefix forked 3 ways, 6 tokens per branch), then
+    ``rounds`` rounds of: every third round the first leaf forks into two
+    (their tokens open blocks in new nodes); every leaf reserves n tokens, n
+    cycling over 1, 2, 3, 5, 16 but at most what its last block still holds (16
+    when its next token opens a block); then per layer one decode_new with
+    those counts."""
+    ops, nxt, call = [], [0], 0
+
+    def nm():
+        nxt[0] += 1
+        return nxt[0] - 1
+    leaves, free = [], {}
+    for _ in range(3):
+        p = nm()
+        ops += [("new", p), ("append", p, 37, call)]
+        call += 1
+        kids = [nm() for _ in range(3)]
+        ops += [("fork", p, 3, kids), ("release", p)]
+        for c in kids:
+            ops.append(("append", c, 6, call))
+            call += 1
+            free[c] = 10
+        leaves += kids
+    cycle, qcall = [1, 2, 3, 5, 16], 0
+    for rnd in range(rounds):
+        if rnd % 3 == 1:
+            h, kids = leaves[0], [nm(), nm()]
+            ops += [("fork", h, 2, kids), ("release", h)]
+            leaves = kids + leaves[1:]
+            for c in kids:
+                free[c] = 16
+        ns = []
+        for i, h in enumerate(leaves):
+            n = min(cycle[(rnd + i) % len(cycle)], free[h])
+            ns.append(n)
+            free[h] = free[h] - n or 16
+        ops.append(("reserve_batch", list(leaves), call, ns))
+        for layer in range(layers):
+            ops.append(("decode_new", layer, list(leaves), call, ns, qcall))
+            qcall += 1
+        call += 1
+    return recipes.Workload(name=name, dtype=dtype, layers=layers, q_heads=8, kv_heads=2, head_dim=head_dim,
+                            num_blocks=1024, ops=ops, seed=seed)
+
+
+@pytest.mark.parametrize("one_launch", [1, 0])
+@pytest.mark.parametrize("dtype,layers,head_dim", [("bf16", 1, 128), ("bf16", 2, 64), ("f32", 2, 128)])
+def test_decode_with_several_new_tokens_written_in_the_call(dtype, layers, head_dim, one_launch):
+    """tkv_attend_decode_new_tokens: each round every branch reserves 1 to 16
+    tokens (a partly filled block, a block they fill, or a new node's block
+    after a fork), and per layer the decode call writes them -- from the
+    attention launch itself (one_launch = 1) or from a preparation launch.
+    Every call matches the oracle; outputs and pool contents equal, bit for
+    bit, those of the same rounds run as a batched append with K/V followed by
+    tkv_attend_decode."""
+    torch = need_gpu()
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    import dataclasses
+    wl = _multi_new_token_workload("multi_%s_%d_%d" % (dtype, layers, head_dim), dtype, layers, head_dim, 12, 82)
+    assert_close(run_both(wl, options={tkv.TKV_OPT_FUSED_NEW_TOKEN: one_launch}), wl.dtype)
+    plain_ops = []
+    for op in wl.ops:
+        if op[0] == "reserve_batch":
+            plain_ops.append(("append_batch", op[1], op[3], op[2]))
+        elif op[0] == "decode_new":
+            plain_ops.append(("decode", op[1], op[2], op[-1]))
+        else:
+            plain_ops.append(op)
+    plain = dataclasses.replace(wl, ops=plain_ops)
+    outs, pools = {}, {}
+    for key, w in (("fused", wl), ("plain", plain)):
+        lib = LibReplay(w)
+        tkv.tkv_set_option(lib.c, tkv.TKV_OPT_FUSED_NEW_TOKEN, one_launch)
+        try:
+            got = []
+            for op in w.ops:
+                if op[0] in ("decode", "decode_new"):
+                    got.append(lib.attend(op).cpu())
+                    if op[0] == "decode_new":
+                        names = tkv.tkv_last_kernels(lib.c)
+                        attn = [n for n in names if n.startswith(("attn_partial_kernel", "attn_rows_kernel"))]
+                        prep = [n for n in names if n.startswith(("decode_prep_kernel", "plan_patch"))]
+                        assert attn, names
+                        if one_launch:
+                            assert not prep and all("NewTokens" in n for n in attn), names
+                        else:
+                            assert prep and not any("NewTokens" in n for n in attn), names
+                lib.apply(op)
+            torch.cuda.synchronize()
+            outs[key] = got
+            views = {}
+            for name in sorted(lib.h):
+                L = tkv.tkv_seq_len(lib.c, lib.h[name])
+                for layer in range(w.layers):
+                    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+                    ko = torch.empty((L, w.kv_heads, w.head_dim), dtype=dt, device="cuda")
+                    vo = torch.empty_like(ko)
+                    tkv.tkv_gather(lib.c, lib.h[name], layer, ko, vo, torch.cuda.current_stream())
+                    views[(name, layer)] = (ko.cpu(), vo.cpu())
+            torch.cuda.synchronize()
+            pools[key] = views
+        finally:
+            lib.close()
+    assert len(outs["fused"]) == 12 * layers
+    for a, b in zip(outs["fused"], outs["plain"]):
+        assert torch.equal(a, b)
+    assert pools["fused"].keys() == pools["plain"].keys()
+    for k in pools["fused"]:
+        assert torch.equal(pools["fused"][k][0], pools["plain"][k][0])
+        assert torch.equal(pools["fused"][k][1], pools["plain"][k][1])
+
+
+def test_decode_with_several_new_tokens_refusals():
+    """tkv_attend_decode_new_tokens refuses, before any launch, a count outside
+    1..16 and tokens that would reach into an earlier block (TKV_E_RANGE)."""
+    torch = need_gpu()
+    from tree_structured_copy_amd import tkv
+    n = 1 * 64 * 2 * 16 * 64
+    kp = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    c = tkv.tkv_create(1, 8, 2, 64, 64, tkv.TKV_BF16, kp, vp)
+    try:
+        st = torch.cuda.current_stream()
+        root = tkv.tkv_seq_new(c)
+        tkv.tkv_append(c, root, 22)  # slots 0..5 of its second block
+        k = torch.zeros((20, 2, 64), dtype=torch.bfloat16, device="cuda")
+        q = torch.zeros((1, 8, 64), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((1, 8, 64), dtype=torch.float32, device="cuda")
+        for cnt in (0, 17, 7):
+            with pytest.raises(tkv.TkvError) as e:
+                tkv.tkv_attend_decode_new_tokens(c, 0, [root], [cnt], k, k, q, out, None, 0, st)
+            assert e.value.code == tkv.TKV_E_RANGE, cnt
+        tkv.tkv_attend_decode_new_tokens(c, 0, [root], [6], k, k, q, out, None, 0, st)
+        torch.cuda.synchronize()
+    finally:
+        tkv.tkv_destroy(c)
 
 
 def test_decode_with_new_token_refusals():

@@ -50,6 +50,8 @@ def _wl():
         ("truncate", 1, 6),
         ("append_batch", [1, 3], [2, 1], 5),
         ("verify", 0, [1, 3], [2, 2], 106),
+        ("reserve_batch", [3, 1], 6, [2, 3]),
+        ("decode_new", 1, [3, 1], 6, [2, 3], 107),
     ]
     return recipes.Workload(name="replay_pin", dtype="f32", layers=LAYERS, q_heads=HQ, kv_heads=HKV, head_dim=D,
                             num_blocks=64, ops=ops, seed=11, block_size=4)
@@ -95,6 +97,10 @@ def _expected_cases(wl):
     h1 = _cat(P, _rows(B5, 0, 2))                      # truncated to the prefix, then 2 more
     h3 = _cat(h3, _rows(B5, 2, 3))
     cases[106] = ([(1, 6), (1, 7), (3, 9), (3, 10)], {1: h1, 3: h3})
+    R6 = _call(wl, 6, 5)      # reserved with counts [2, 3] in batch order [3, 1]: h3 rows 0..1, h1 rows 2..4
+    h3 = _cat(h3, _rows(R6, 0, 2))
+    h1 = _cat(h1, _rows(R6, 2, 5))
+    cases[107] = ([(3, 12), (1, 10)], {1: h1, 3: h3})
     return cases
 
 
@@ -151,7 +157,7 @@ def test_replay_tables_follow_the_recipe():
     orc = OracleReplay(wl)
     for op in wl.ops:
         orc.apply(op)
-    lens = {1: 8, 2: 9, 3: 11}
+    lens = {1: 11, 2: 9, 3: 13}
     used = set()
     for h, L in lens.items():
         tab = orc.alloc.table(orc.h_alloc[h])
@@ -280,6 +286,17 @@ def test_pins_catch_transposed_generator_index(monkeypatch):
             * np.uint64(wl.head_dim) + d
         return gen.values(wl.seed, gen.stream_id(kind, call), idx.reshape(-1), wl.dtype).reshape(t1 - t0, wl.head_dim)
     monkeypatch.setattr(workloads, "kv_slice", bad_slice)
+    assert _caught() > 0
+
+
+def test_pins_catch_reservation_counts_ignored(monkeypatch):
+    orig = OracleReplay.apply
+
+    def apply(self, op):
+        if op[0] == "reserve_batch":
+            op = op[:3]  # one token per handle whatever the counts
+        orig(self, op)
+    monkeypatch.setattr(OracleReplay, "apply", apply)
     assert _caught() > 0
 
 

@@ -183,17 +183,18 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
   if constexpr (X::kActive) {
     using TU = TokUnits<P, D>;
     if (tkc > 0) {
-      int tk_entry = -1, tk_blk = 0, tk_slot = 0, tk_src = 0;
+      int tk_entry = -1, tk_blk = 0, tk_slot = 0, tk_n = 0, tk_src = 0;
       if (lane < tkc) {
         // records past x.n are not this launch's (a launch with id patches
         // and no tokens lists none)
-        NewTok t{-1, 0, 0, 0};
+        NewTok t{-1, 0, 0, 0, 0};
         if (tk0 + lane < x.n) t = x.tok[tk0 + lane];
         tk_entry = t.entry;
         tk_blk = t.blk;
         tk_slot = t.slot;
+        tk_n = t.n;
         tk_src = t.src;
-        s_tok[wave][lane] = int2{t.entry, t.slot + 1};
+        s_tok[wave][lane] = int2{t.entry, t.slot + t.n};
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done (a wave reads only its own)
       tk_loaded = true;
@@ -207,26 +208,30 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
         tok_sb = ((__builtin_amdgcn_readlane(tk_entry, first) - it.blk_begin) >> 1) - start_w;
         auto rec = [&](int i) {
           return NewTok{__builtin_amdgcn_readlane(tk_entry, i), __builtin_amdgcn_readlane(tk_blk, i),
-                        __builtin_amdgcn_readlane(tk_slot, i), __builtin_amdgcn_readlane(tk_src, i)};
+                        static_cast<int16_t>(__builtin_amdgcn_readlane(tk_slot, i)),
+                        static_cast<int16_t>(__builtin_amdgcn_readlane(tk_n, i)), __builtin_amdgcn_readlane(tk_src, i)};
         };
-        // tokens that open their block (rare: whole tiles), then the others, a
-        // few at a time with all their values' loads in flight together
-        uint64_t fresh = __ballot(own && tk_slot == 0);
+        // records that open their block (rare in a decode step: whole tiles)
+        // and records of several tokens in a block that has others, one at a
+        // time; then single tokens, a few at a time with all their values'
+        // loads in flight together
+        uint64_t fresh = __ballot(own && (tk_slot == 0 || tk_n > 1));
         while (fresh) {
           const NewTok t = rec(__builtin_ctzll(fresh));
           fresh &= fresh - 1;
-          for (int u0 = lane; u0 < TU::kFresh; u0 += 4 * 64) {
+          const int nu = TU::units(t);
+          for (int u0 = lane; u0 < nu; u0 += 4 * 64) {
             u32x4 v[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-              if (u0 + 64 * k < TU::kFresh) v[k] = TU::value(x, t, kvh, a.hkv, u0 + 64 * k);
+              if (u0 + 64 * k < nu) v[k] = TU::value(x, t, kvh, a.hkv, u0 + 64 * k);
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-              if (u0 + 64 * k < TU::kFresh) TU::store(x, t, kvh, a.hkv, u0 + 64 * k, v[k]);
+              if (u0 + 64 * k < nu) TU::store(x, t, kvh, a.hkv, u0 + 64 * k, v[k]);
           }
-          if (lane == 0) x.blocks[t.entry].valid = 1;
+          if (lane == 0) x.blocks[t.entry].valid = t.slot + t.n;
         }
-        uint64_t plain = __ballot(own && tk_slot != 0);
+        uint64_t plain = __ballot(own && tk_slot != 0 && tk_n == 1);
         constexpr int RPT = (TU::kPlain + 63) / 64;  // 64-unit rows per token
         constexpr int MAXT = 4;                      // tokens whose values are in flight at once
         while (plain) {
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
           int nt = 0;
 #pragma unroll
           for (int j = 0; j < MAXT; ++j) {
-            t[j] = NewTok{-1, 0, 0, 0};
+            t[j] = NewTok{-1, 0, 0, 0, 0};
             if (plain) {
               t[j] = rec(__builtin_ctzll(plain));
               plain &= plain - 1;
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
 #pragma unroll
             for (int rr = 0; rr < RPT; ++rr)
               if (rr * 64 + lane < TU::kPlain) TU::store(x, t[j], kvh, a.hkv, rr * 64 + lane, v[j][rr]);
-            if (lane == 0) x.blocks[t[j].entry].valid = t[j].slot + 1;
+            if (lane == 0) x.blocks[t[j].entry].valid = t[j].slot + t[j].n;
           }
         }
         if (tok_sb == 0) {

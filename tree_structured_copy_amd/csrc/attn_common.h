@@ -282,14 +282,14 @@ template <class P>
 constexpr bool kIsBF16 = sizeof(typename P::elem) == 2;
 
 // Writing a decode step's new tokens from the attention launch itself.
-// Work unit w of one token and KV head:
-//   * the token opens its block (slot 0): the whole tile is written, the
-//     token in slot 0 and zeros elsewhere; units [0, 2 NCH) are the K then V
-//     chunks (kFresh);
-//   * otherwise only the token (kPlain): unit w < D / PC is the 16-byte K chunk
-//     holding d = PC w .. PC w + PC - 1 of the token, unit D / PC + d its V
-//     element d (inside the bf16 8-byte unit, or fp32 chunk, of tokens
-//     4 (slot / 4) .. + 3).
+// Work unit w of one record (n tokens of one block) and KV head:
+//   * the tokens open their block (slot 0): the whole tile is written, the
+//     tokens in slots 0 .. n - 1 and zeros elsewhere; units [0, 2 NCH) are the
+//     K then V chunks (kFresh);
+//   * otherwise only the tokens, kPlain units each: unit i kPlain + u of token
+//     slot + i is, for u < D / PC, the 16-byte K chunk holding
+//     d = PC u .. PC u + PC - 1, else its V element d = u - D / PC (inside the
+//     bf16 8-byte unit, or fp32 chunk, of tokens 4 (slot / 4) .. + 3).
 // value() loads a unit's contents (so that several units' loads can be in
 // flight together), store() writes them.
 template <class P, int D>
@@ -301,13 +301,14 @@ struct TokUnits {
   static constexpr int NCH = 16 * D / PC;
   static constexpr int kFresh = 2 * NCH;
   static constexpr int kPlain = D / PC + D;
-  __device__ static int units(const NewTok& t) { return t.slot == 0 ? kFresh : kPlain; }
+  __device__ static int units(const NewTok& t) { return t.slot == 0 ? kFresh : t.n * kPlain; }
   __device__ static size_t tile(const NewTok& t, int h, int hkv) {
     return (static_cast<size_t>(t.blk) * hkv + h) * (16 * D);
   }
   __device__ static u32x4 value(const NewTokens& x, const NewTok& t, int h, int hkv, int w) {
     const E* sk = static_cast<const E*>(x.k) + (static_cast<size_t>(t.src) * hkv + h) * D;
     const E* sv = static_cast<const E*>(x.v) + (static_cast<size_t>(t.src) * hkv + h) * D;
+    const size_t row = static_cast<size_t>(hkv) * D;  // one token's row
     if (t.slot == 0) {
       const bool isk = w < NCH;
       const int ch = isk ? w : w - NCH;
@@ -317,13 +318,14 @@ struct TokUnits {
         int tok, d;
         if (isk) L::k_coord(ch, el, tok, d);
         else L::v_coord(ch, el, tok, d);
-        vals[el] = tok == 0 ? (isk ? sk[d] : sv[d]) : E(0);
+        vals[el] = tok < t.n ? (isk ? sk[tok * row + d] : sv[tok * row + d]) : E(0);
       }
       return bitcast<u32x4>(vals);
     }
-    if (w < D / PC) return *reinterpret_cast<const u32x4*>(sk + w * PC);
+    const int i = w / kPlain, u = w - i * kPlain;
+    if (u < D / PC) return *reinterpret_cast<const u32x4*>(sk + i * row + u * PC);
     u32x4 r{0u, 0u, 0u, 0u};
-    const E e = sv[w - D / PC];
+    const E e = sv[i * row + (u - D / PC)];
     __builtin_memcpy(&r, &e, sizeof(E));
     return r;
   }
@@ -336,16 +338,20 @@ struct TokUnits {
     if (t.slot == 0) {
       const bool isk = w < NCH;
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>((isk ? kt : vt) + (isk ? w : w - NCH) * PC));
-    } else if (w < D / PC) {
+      return;
+    }
+    const int i = w / kPlain, u = w - i * kPlain;
+    const int slot = t.slot + i;
+    if (u < D / PC) {
       int ch;
-      if constexpr (EB == 2) ch = w * 16 + t.slot;
-      else ch = (w >> 2) * 64 + (w & 3) * 16 + t.slot;
+      if constexpr (EB == 2) ch = u * 16 + slot;
+      else ch = (u >> 2) * 64 + (u & 3) * 16 + slot;
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(kt + ch * PC));
     } else {
-      const int d = w - D / PC;
+      const int d = u - D / PC;
       E e;
       __builtin_memcpy(&e, &v, sizeof(E));
-      __builtin_nontemporal_store(e, vt + ((d >> 4) * 64 + (t.slot >> 2) * 16 + (d & 15)) * 4 + (t.slot & 3));
+      __builtin_nontemporal_store(e, vt + ((d >> 4) * 64 + (slot >> 2) * 16 + (d & 15)) * 4 + (slot & 3));
     }
   }
 };
@@ -356,7 +362,7 @@ struct TokUnits {
 // tiles (a block the token opens whole, with zeros in its other slots) and each
 // block's valid count in the plan (every KV head's workgroup writes the same
 // value).  Each wave holds the item's token records in its lanes (one load);
-// the units of up to four tokens at a time are spread over the workgroup's
+// the units of up to four records at a time are spread over the workgroup's
 // threads with all their loads in flight together.  Only this workgroup reads
 // these tiles and entries in the launch: an unfrozen tip block appears once in
 // a plan.
@@ -367,17 +373,19 @@ __device__ void write_new_tokens(const NewTokens& x, const DevItem& it, int h0, 
   const int tk0 = it.tails & 0xffff, tkc = it.tails >> 16;
   if (tkc == 0) return;
   const int lane = tid & 63;
-  int te = -1, tbk = 0, ts = 0, tsr = 0;
+  int te = -1, tbk = 0, ts = 0, tn = 0, tsr = 0;
   if (lane < tkc && tk0 + lane < x.n) {
     const NewTok t = x.tok[tk0 + lane];
     te = t.entry;
     tbk = t.blk;
     ts = t.slot;
+    tn = t.n;
     tsr = t.src;
   }
   auto rec = [&](int i) {
     return NewTok{__builtin_amdgcn_readlane(te, i), __builtin_amdgcn_readlane(tbk, i),
-                  __builtin_amdgcn_readlane(ts, i), __builtin_amdgcn_readlane(tsr, i)};
+                  static_cast<int16_t>(__builtin_amdgcn_readlane(ts, i)),
+                  static_cast<int16_t>(__builtin_amdgcn_readlane(tn, i)), __builtin_amdgcn_readlane(tsr, i)};
   };
   uint64_t todo = __ballot(te >= 0);
   if (!todo) return;
@@ -387,15 +395,16 @@ __device__ void write_new_tokens(const NewTokens& x, const DevItem& it, int h0, 
     int nt = 0;
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
-      t[j] = NewTok{-1, 0, 0, 0};
+      t[j] = NewTok{-1, 0, 0, 0, 0};
       if (todo) {
         t[j] = rec(__builtin_ctzll(todo));
         todo &= todo - 1;
         nt = j + 1;
       }
     }
-    // units of these tokens, thread-strided; a thread's share of one token's
-    // units is at most ceil(nh * units / nthreads) <= 4 for every shape here
+    // units of these records, thread-strided; a thread's share of one
+    // record's units is at most ceil(nh * units / nthreads) <= 4 for every
+    // shape here when it holds one token or opens its block (the rest, below)
     constexpr int R = 4;
     u32x4 v[MAXT][R];
 #pragma unroll
@@ -420,7 +429,7 @@ __device__ void write_new_tokens(const NewTokens& x, const DevItem& it, int h0, 
       // a thread past R * nthreads units: the rest of this token, one at a time
       for (int u = tid + R * nthreads; u < total; u += nthreads)
         TU::store(x, t[j], h0 + u / per, hkv, u % per, TU::value(x, t[j], h0 + u / per, hkv, u % per));
-      if (tid == 0) x.blocks[t[j].entry].valid = t[j].slot + 1;
+      if (tid == 0) x.blocks[t[j].entry].valid = t[j].slot + t[j].n;
     }
   }
   // every store of the workgroup acknowledged (in L2) before any wave loads

@@ -462,7 +462,8 @@ int prepare_new_tokens(tkv_cache* c, PlanSlot* s, int32_t layer, int32_t nseq, c
   a.app.kpool = const_cast<char*>(c->kpool_layer(layer));
   a.app.vpool = const_cast<char*>(c->vpool_layer(layer));
   a.app.layer_stride = 0;
-  a.app.ntok = nseq;
+  a.app.ntok = 0;
+  for (int32_t i = 0; i < nseq; ++i) a.app.ntok += c->app_ents[i].cnt;
   a.app.hkv = c->cfg.num_kv_heads;
   a.plan = static_cast<int32_t*>(s->dev);
   a.limit = limit;
@@ -485,10 +486,11 @@ int prepare_new_tokens(tkv_cache* c, PlanSlot* s, int32_t layer, int32_t nseq, c
 }
 
 // A decode step whose new tokens the attention launch writes itself: possible
-// when there are at most kFusedMaxTokens of them, each in its handle's tip
-// block as listed by the plan, and the plan's device copy is either uploaded
-// whole first or differs from the host plan only in those blocks' valid
-// counts (which the launch writes too).  Fills c->fused and uploads the plan
+// when the plan lists at most kFusedMaxTokens tail blocks (one token record
+// each), every handle's new tokens lie in its tip block as listed by the
+// plan, and the plan's device copy is either uploaded whole first or differs
+// from the host plan only in those blocks' valid counts (which the launch
+// writes too).  Fills c->fused and uploads the plan
 // if needed; returns false (nothing done) when the preparation launch must
 // write them instead.
 bool prepare_fused(tkv_cache* c, PlanSlot* s, int32_t layer, const tkv_seq* seqs, int32_t nseq, const void* k_new,
@@ -510,7 +512,7 @@ bool prepare_fused(tkv_cache* c, PlanSlot* s, int32_t layer, const tkv_seq* seqs
   NewTokens& x = c->fused;
   for (int32_t t = 0; t < ntail; ++t) {
     c->node_entry[P.tail_node[t]] = t;
-    x.tok[t] = NewTok{-1, 0, 0, 0};
+    x.tok[t] = NewTok{-1, 0, 0, 0, 0};
   }
   bool ok = true;
   for (int32_t i = 0; i < nseq && ok; ++i) {
@@ -522,11 +524,11 @@ bool prepare_fused(tkv_cache* c, PlanSlot* s, int32_t layer, const tkv_seq* seqs
     }
     const int32_t t = c->node_entry[tip];
     const int32_t e = t >= 0 ? P.tail_entry[t] : -1;
-    if (e < 0 || P.blocks[e].id != a.blk || P.blocks[e].valid != a.slot + 1 || x.tok[t].entry >= 0) {
+    if (e < 0 || P.blocks[e].id != a.blk || P.blocks[e].valid != a.slot + a.cnt || x.tok[t].entry >= 0) {
       ok = false;
       break;
     }
-    x.tok[t] = NewTok{e, a.blk, a.slot, i};
+    x.tok[t] = NewTok{e, a.blk, static_cast<int16_t>(a.slot), static_cast<int16_t>(a.cnt), a.src};
   }
   for (int32_t t = 0; t < ntail; ++t) c->node_entry[P.tail_node[t]] = -1;
   if (!ok) return false;
@@ -538,7 +540,8 @@ bool prepare_fused(tkv_cache* c, PlanSlot* s, int32_t layer, const tkv_seq* seqs
       bool covered = false;
       if (w.word >= v0 && (w.word - v0) % per == 0) {
         const int32_t e = static_cast<int32_t>((w.word - v0) / per);
-        for (int32_t t = 0; t < ntail && !covered; ++t) covered = x.tok[t].entry == e && w.value == x.tok[t].slot + 1;
+        for (int32_t t = 0; t < ntail && !covered; ++t)
+          covered = x.tok[t].entry == e && w.value == x.tok[t].slot + x.tok[t].n;
       }
       if (!covered) return false;
     }
@@ -572,7 +575,8 @@ int upload_plan_fixed(tkv_cache* c, const Plan& P, char* base, hipStream_t strea
 // and the caller's workspace; nothing is allocated and no events are kept.
 int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
            const void* q, float* out, void* ws, size_t ws_bytes, void* stream_,
-           const void* k_new = nullptr, const void* v_new = nullptr, bool fixed_ws = false) {
+           const void* k_new = nullptr, const void* v_new = nullptr, bool fixed_ws = false,
+           const int32_t* ntok = nullptr) {
   if (!c) return TKV_E_INVAL;
   if (!c->has_pools) return TKV_E_NODEVICE;
   if (layer < 0 || layer >= c->cfg.num_layers) return TKV_E_RANGE;
@@ -591,13 +595,19 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
       return TKV_E_NOMEM;
     }
     const uint64_t stamp = ++c->seen_stamp;
+    int32_t row = 0;
     for (int32_t i = 0; i < nseq; ++i) {
+      // the handle's last n tokens: all in its last block, in its own tip node
+      const int32_t n = ntok ? ntok[i] : 1;
+      if (n < 1 || n > 16) return TKV_E_RANGE;
       int32_t blk, slot;
       if (int rc = c->tree.own_last_token(seqs[i], &blk, &slot)) return rc;
+      if (slot - n + 1 < 0) return TKV_E_RANGE;
       uint64_t& mark = c->seen[Tree::slot_of(seqs[i])];
       if (mark == stamp) return TKV_E_INVAL;
       mark = stamp;
-      c->app_ents[i] = {blk, slot, i, 1};
+      c->app_ents[i] = {blk, slot - n + 1, row, n};
+      row += n;
     }
   }
   PlanSlot* s = nullptr;
@@ -986,6 +996,13 @@ int tkv_attend_decode_new_token(tkv_cache* c, int32_t layer, const tkv_seq* seqs
                                 void* stream) {
   if (!k_new || !v_new) return TKV_E_INVAL;
   return attend(c, layer, seqs, nullptr, nseq, q, out, ws, ws_bytes, stream, k_new, v_new);
+}
+
+int tkv_attend_decode_new_tokens(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* ntok,
+                                 int32_t nseq, const void* k_new, const void* v_new, const void* q, float* out,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (!k_new || !v_new || !ntok) return TKV_E_INVAL;
+  return attend(c, layer, seqs, nullptr, nseq, q, out, ws, ws_bytes, stream, k_new, v_new, false, ntok);
 }
 
 int tkv_attend_decode_noalloc(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t nseq, const void* q,

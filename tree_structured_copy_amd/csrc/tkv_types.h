@@ -113,16 +113,18 @@ struct AttnArgs {
   int32_t max_blocks;    // the longest block list among this launch's items
 };
 
-// The new token of one branch in a decode step, written by the attention
-// launch itself (tkv_attend_decode_new_token in one launch): plan block entry
-// `entry` (an index into the plan's block list) is the token's block `blk`,
-// which takes the token at `slot` from row `src` of the call's K/V arrays.
-// The launch's list is indexed by the plan's tail blocks (DevItem::tails);
-// entry = -1 where a tail block takes no token in this call.
+// The new tokens of one branch in a decode step, written by the attention
+// launch itself (tkv_attend_decode_new_token(s) in one launch): plan block
+// entry `entry` (an index into the plan's block list) is the tokens' block
+// `blk`, which takes `n` tokens at slots slot .. slot + n - 1 from rows
+// src .. src + n - 1 of the call's K/V arrays.  The launch's list is indexed by
+// the plan's tail blocks (DevItem::tails); entry = -1 where a tail block takes
+// no token in this call.
 struct NewTok {
   int32_t entry;
   int32_t blk;
-  int32_t slot;
+  int16_t slot;
+  int16_t n;
   int32_t src;
 };
 // A block id of a plan's device copy that the attention launch rewrites

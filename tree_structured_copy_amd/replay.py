@@ -72,8 +72,9 @@ class LibReplay:
                 v = wdev.kv_tensor(self.wl, call, total, gen.KIND_V, self.device)
                 tkv.tkv_append_batch(self.c, seqs, ns, k, v, torch.cuda.current_stream())
         elif kind == "reserve_batch":
-            _, hs, call = op
-            tkv.tkv_append_batch(self.c, [self.h[h] for h in hs], [1] * len(hs))
+            hs = op[1]
+            ns = list(op[3]) if len(op) > 3 else [1] * len(hs)
+            tkv.tkv_append_batch(self.c, [self.h[h] for h in hs], ns)
         elif kind == "fork":
             _, h, n, kids = op
             for name, s in zip(kids, tkv.tkv_fork(self.c, self.h[h], n)):
@@ -129,9 +130,14 @@ class LibReplay:
         elif op[0] == "decode_new":
             # the reserved tokens' K/V of this layer: rows of batched append call op[3]
             from workloads import gen
-            k = wdev.kv_tensor(wl, op[3], rows, gen.KIND_K, self.device)[op[1]].contiguous()
-            v = wdev.kv_tensor(wl, op[3], rows, gen.KIND_V, self.device)[op[1]].contiguous()
-            tkv.tkv_attend_decode_new_token(self.c, op[1], self.handles(op), k, v, q, out, ws, need, stream)
+            ns = list(op[4]) if len(op) > 5 else [1] * rows
+            total = sum(ns)
+            k = wdev.kv_tensor(wl, op[3], total, gen.KIND_K, self.device)[op[1]].contiguous()
+            v = wdev.kv_tensor(wl, op[3], total, gen.KIND_V, self.device)[op[1]].contiguous()
+            if len(op) > 5:
+                tkv.tkv_attend_decode_new_tokens(self.c, op[1], self.handles(op), ns, k, v, q, out, ws, need, stream)
+            else:
+                tkv.tkv_attend_decode_new_token(self.c, op[1], self.handles(op), k, v, q, out, ws, need, stream)
         else:
             tkv.tkv_attend_verify(self.c, op[1], self.handles(op), op[3], q, out, ws, need, stream)
         return out

@@ -87,12 +87,12 @@ class Replayer {
     int64_t max_src = 1, max_rows = 1, max_name = 0;
     for (const Op& op : ops) {
       if (op.kind == "append") max_src = std::max(max_src, op.a[1]);
-      if (op.kind == "append_batch") {
+      if (op.kind == "append_batch" || op.kind == "reserve_batch") {
         int64_t t = 0;
         for (int64_t i = 0; i < op.a[0]; ++i) t += op.a[2 + 2 * i];
         max_src = std::max(max_src, t);
       }
-      if (op.kind == "decode") max_rows = std::max(max_rows, op.a[1]);
+      if (op.kind == "decode" || op.kind == "decode_new") max_rows = std::max(max_rows, op.a[1]);
       if (op.kind == "verify") {
         int64_t t = 0;
         for (int64_t i = 0; i < op.a[1]; ++i) t += op.a[3 + 2 * i];
@@ -180,6 +180,42 @@ class Replayer {
                                stream_),
               "tkv_append_batch");
         sample_blocks();
+      } else if (op.kind == "reserve_batch") {
+        // slots only: the decode_new call that follows writes their K/V
+        seqs.clear();
+        counts.clear();
+        for (int64_t i = 0; i < a[0]; ++i) {
+          seqs.push_back(h[a[1 + 2 * i]]);
+          counts.push_back(static_cast<int32_t>(a[2 + 2 * i]));
+          st.appended += a[2 + 2 * i];
+        }
+        check(tkv_append_batch(cache, seqs.data(), counts.data(), static_cast<int32_t>(seqs.size()), nullptr,
+                               nullptr, stream_),
+              "tkv_append_batch");
+        sample_blocks();
+      } else if (op.kind == "decode_new") {
+        seqs.clear();
+        counts.clear();
+        for (int64_t i = 0; i < a[1]; ++i) {
+          seqs.push_back(h[a[2 + 2 * i]]);
+          counts.push_back(static_cast<int32_t>(a[3 + 2 * i]));
+        }
+        const int32_t n = static_cast<int32_t>(seqs.size());
+        ++st.attend_calls;
+        st.decode_queries += n;
+        size_t need = 0;
+        check(tkv_workspace_size(cache, seqs.data(), nullptr, n, &need), "tkv_workspace_size");
+        if (host_) continue;
+        if (need > ws_cap_) {
+          if (ws_) hip_check(hipStreamSynchronize(stream_), "hipStreamSynchronize");
+          if (ws_) (void)hipFree(ws_);
+          ws_cap_ = need + need / 4;
+          hip_check(hipMalloc(&ws_, ws_cap_), "hipMalloc");
+        }
+        // the tokens' K/V of this layer: the constant-filled source rows
+        check(tkv_attend_decode_new_tokens(cache, static_cast<int32_t>(a[0]), seqs.data(), counts.data(), n, ksrc_,
+                                           vsrc_, q_, static_cast<float*>(out_), ws_, ws_cap_, stream_),
+              "tkv_attend_decode_new_tokens");
       } else if (op.kind == "fork") {
         const int32_t n = static_cast<int32_t>(a[1]);
         int64_t len = 0;

@@ -18,11 +18,14 @@ Operations:
 * ``("fork", h, n, [c0, ..., c(n-1)])``   -- n children of ``h``; ``h`` stays live
 * ``("release", h)``
 * ``("truncate", h, new_len)``
-* ``("reserve_batch", [h...], call)``     -- one token per (distinct) handle, slots only;
-  its K/V are those of a batched append ``call`` of one token per handle, written
-  layer by layer by the ``decode_new`` ops that follow
-* ``("decode_new", layer, [h...], call, qcall)`` -- write layer ``layer`` of those
-  tokens' K/V and decode, in one call (``tkv_attend_decode_new_token``)
+* ``("reserve_batch", [h...], call[, [ntok...]])`` -- ``ntok[i]`` tokens (default 1)
+  per (distinct) handle, slots only; their K/V are those of a batched append
+  ``call`` of those counts, written layer by layer by the ``decode_new`` ops that
+  follow
+* ``("decode_new", layer, [h...], call, qcall)`` or
+  ``("decode_new", layer, [h...], call, [ntok...], qcall)`` -- write layer
+  ``layer`` of those tokens' K/V and decode, in one call
+  (``tkv_attend_decode_new_token``, or ``tkv_attend_decode_new_tokens`` with counts)
 * ``("time_begin",)``                     -- no effect on the cache: where a timed
   replay of a loop starts (after its set-up)
 * ``("decode", layer, [h...], qcall)``    -- one query per handle; Q from stream
@@ -326,7 +329,7 @@ def spec_loop_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_
 def mcts_loop_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_heads: int = 8,
                        head_dim: int = 128, root_tokens: int = 2048, branching: int = 4, depth: int = 12,
                        iterations: int = 500, node_tokens: int = 16, seed: int = 0,
-                       description: str = "") -> Workload:
+                       one_launch: bool = False, description: str = "") -> Workload:
     """A tree search run as ``iterations`` simulations (the Dendrite demo tape's
     MCTS run: 500 simulations, branching 4, depth 12, head_dim 128): root = new;
     append(root, root_tokens).  A simulation descends from the root, taking at
@@ -335,7 +338,9 @@ def mcts_loop_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_
     handle decodes one query.  Any other is expanded: forked into ``branching``
     children and released (the children keep its path), one append_batch gives
     every child ``node_tokens`` tokens, and one decode evaluates the new
-    children."""
+    children.  With ``one_launch`` the children's tokens are reserved instead
+    (``reserve_batch``) and written by the decode call itself (``decode_new``):
+    the same cache contents and outputs, one launch fewer."""
     nm = _Names()
     ops: List[tuple] = []
     call = 0
@@ -360,8 +365,13 @@ def mcts_loop_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_
         kids = [nm() for _ in range(branching)]
         ops.append(("fork", h, branching, kids))
         ops.append(("release", h))
-        ops.append(("append_batch", list(kids), [node_tokens] * branching, call)); call += 1
-        ops.append(("decode", 0, list(kids), qcall)); qcall += 1
+        if one_launch:
+            ns = [node_tokens] * branching
+            ops.append(("reserve_batch", list(kids), call, ns))
+            ops.append(("decode_new", 0, list(kids), call, ns, qcall)); call += 1; qcall += 1
+        else:
+            ops.append(("append_batch", list(kids), [node_tokens] * branching, call)); call += 1
+            ops.append(("decode", 0, list(kids), qcall)); qcall += 1
         children[h] = kids
         for c in kids:
             level[c] = level[h] + 1
@@ -379,7 +389,8 @@ def ops_text(wl: Workload) -> str:
     ``config layers q_heads kv_heads head_dim num_blocks dtype(0 f32, 1 bf16)``,
     ``new h``, ``append h ntok``, ``append_batch n h1 n1 ... hn nn``,
     ``fork h n c1 ... cn``, ``release h``, ``truncate h len``, ``time_begin``,
-    ``decode layer n h1 ... hn``, ``verify layer n h1 q1 ... hn qn``.  K/V/Q
+    ``decode layer n h1 ... hn``, ``verify layer n h1 q1 ... hn qn``,
+    ``reserve_batch n h1 n1 ... hn nn``, ``decode_new layer n h1 n1 ... hn nn``.  K/V/Q
     values are not carried: the replayer measures time and memory, while the
     parity tests replay the same recipe against the oracle."""
     out = ["config %d %d %d %d %d %d" % (wl.layers, wl.q_heads, wl.kv_heads, wl.head_dim, wl.num_blocks,
@@ -404,6 +415,12 @@ def ops_text(wl: Workload) -> str:
             out.append("decode %d %d %s" % (op[1], len(op[2]), " ".join(str(h) for h in op[2])))
         elif k == "verify":
             out.append("verify %d %d %s" % (op[1], len(op[2]), " ".join("%d %d" % x for x in zip(op[2], op[3]))))
+        elif k == "reserve_batch":
+            ns = op[3] if len(op) > 3 else [1] * len(op[1])
+            out.append("reserve_batch %d %s" % (len(op[1]), " ".join("%d %d" % x for x in zip(op[1], ns))))
+        elif k == "decode_new":
+            ns = op[4] if len(op) > 5 else [1] * len(op[2])
+            out.append("decode_new %d %d %s" % (op[1], len(op[2]), " ".join("%d %d" % x for x in zip(op[2], ns))))
         else:
             raise ValueError(k)
     return "\n".join(out) + "\n"
