@@ -334,14 +334,17 @@ def _native_loops():
       paths of 8 tokens) through 8 rounds of fork, draft, verify, accept or
       roll back and a bonus token;
     * search_loop: 500 tree-search simulations, branching 4, depth 12, a
-      2048-token root and 16 tokens per node (GQA 32/8, d = 128, bf16)."""
+      2048-token root and 16 tokens per node (GQA 32/8, d = 128, bf16);
+    * search_loop_one_launch: the same, each expansion's new nodes reserved and
+      written by its decode call (tkv_attend_decode_new_tokens)."""
     import subprocess
     import tempfile
     from workloads import recipes
     exe = os.path.join(ROOT, "tree_structured_copy_amd", "replay_bench")
     res = {}
     for key, wl in (("spec_loop", recipes.spec_loop_workload("spec_loop", rounds=8)),
-                    ("search_loop", recipes.mcts_loop_workload("search_loop"))):
+                    ("search_loop", recipes.mcts_loop_workload("search_loop")),
+                    ("search_loop_one_launch", recipes.mcts_loop_workload("search_loop", one_launch=True))):
         with tempfile.NamedTemporaryFile("w", suffix=".ops", delete=False) as f:
             f.write(recipes.ops_text(wl))
             path = f.name

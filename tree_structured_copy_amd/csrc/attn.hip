@@ -70,8 +70,18 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
   uint32_t e_mlo = 0, e_mhi = 0;
   int cur_batch = -1;
   // X = NewTokens: the item's new-token records (tail blocks [tk0, tk0 + tkc),
-  // at most 64); each wave keeps their (entry, valid count) pairs in LDS
-  const int tk0 = X::kActive ? (it.tails & 0xffff) : 0, tkc = X::kActive ? (it.tails >> 16) : 0;
+  // at most 64); each wave keeps their (entry, valid count) pairs in LDS.
+  // When some record of the launch holds several tokens (a node the step
+  // opens: whole tiles), the whole workgroup writes the item's records first,
+  // before anything is loaded, and the owning waves write none.
+  if constexpr (X::kActive) {
+    if (x.multi) write_new_tokens<P, D, NT, 1>(x, it, kvh, a.hkv, tid);
+  }
+  const int tk0 = X::kActive ? (it.tails & 0xffff) : 0;
+  const int tkc = [&]() {
+    if constexpr (X::kActive) return x.multi ? 0 : (it.tails >> 16);
+    else return 0;
+  }();
   __shared__ int2 s_tok[X::kActive ? W : 1][X::kActive ? 64 : 1];
   bool tk_loaded = false;
   // X = NewTokens with id patches: the (entry, id) pairs of this item, in LDS

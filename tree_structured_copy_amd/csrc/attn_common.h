@@ -291,7 +291,8 @@ constexpr bool kIsBF16 = sizeof(typename P::elem) == 2;
 //     d = PC u .. PC u + PC - 1, else its V element d = u - D / PC (inside the
 //     bf16 8-byte unit, or fp32 chunk, of tokens 4 (slot / 4) .. + 3).
 // value() loads a unit's contents (so that several units' loads can be in
-// flight together), store() writes them.
+// flight together: it only loads, a bf16 V chunk of a whole tile as four raw
+// 32-bit parts), store() arranges and writes them.
 template <class P, int D>
 struct TokUnits {
   using E = typename P::elem;
@@ -310,17 +311,27 @@ struct TokUnits {
     const E* sv = static_cast<const E*>(x.v) + (static_cast<size_t>(t.src) * hkv + h) * D;
     const size_t row = static_cast<size_t>(hkv) * D;  // one token's row
     if (t.slot == 0) {
-      const bool isk = w < NCH;
-      const int ch = isk ? w : w - NCH;
-      E vals[PC];
-#pragma unroll
-      for (int el = 0; el < PC; ++el) {
+      if (w < NCH) {
+        // a K chunk is PC consecutive elements of one token's row: one load
         int tok, d;
-        if (isk) L::k_coord(ch, el, tok, d);
-        else L::v_coord(ch, el, tok, d);
-        vals[el] = tok < t.n ? (isk ? sk[tok * row + d] : sv[tok * row + d]) : E(0);
+        L::k_coord(w, 0, tok, d);
+        if (tok >= t.n) return u32x4{0u, 0u, 0u, 0u};
+        return *reinterpret_cast<const u32x4*>(sk + tok * row + d);
       }
-      return bitcast<u32x4>(vals);
+      // a V chunk is element d (fp32), or elements d and d + 1 (bf16), of
+      // four consecutive tokens: one load per token
+      int tok0, d;
+      L::v_coord(w - NCH, 0, tok0, d);
+      uint32_t part[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        part[i] = 0u;
+        if (tok0 + i < t.n) {
+          if constexpr (EB == 2) part[i] = *reinterpret_cast<const uint32_t*>(sv + (tok0 + i) * row + d);
+          else part[i] = __builtin_bit_cast(uint32_t, sv[(tok0 + i) * row + d]);
+        }
+      }
+      return u32x4{part[0], part[1], part[2], part[3]};
     }
     const int i = w / kPlain, u = w - i * kPlain;
     if (u < D / PC) return *reinterpret_cast<const u32x4*>(sk + i * row + u * PC);
@@ -329,15 +340,33 @@ struct TokUnits {
     __builtin_memcpy(&r, &e, sizeof(E));
     return r;
   }
+  // NT: nontemporal stores, whose lines go out without staying dirty in L2
+  // until the kernel's end (3 us of a decode step on the fork workload,
+  // measured, where each wave writes its own tokens and waits for them only
+  // before the super-block that reads them); plain stores where the writers
+  // wait for their acknowledgement at once
+  template <bool NT, class T>
+  __device__ static void put(T v, T* p) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+  }
+  template <bool NT = true>
   __device__ static void store(const NewTokens& x, const NewTok& t, int h, int hkv, int w, const u32x4& v) {
     const size_t tl = tile(t, h, hkv);
     E* kt = static_cast<E*>(x.kpool) + tl;
     E* vt = static_cast<E*>(x.vpool) + tl;
-    // nontemporal: the lines go out without staying dirty in L2 until the
-    // kernel's end (3 us of a decode step on the fork workload, measured)
     if (t.slot == 0) {
-      const bool isk = w < NCH;
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>((isk ? kt : vt) + (isk ? w : w - NCH) * PC));
+      if (w < NCH) {
+        put<NT>(v, reinterpret_cast<u32x4*>(kt + w * PC));
+      } else if constexpr (EB == 2) {
+        // the raw parts hold elements d, d + 1 of tokens tok0 .. tok0 + 3; the
+        // chunk is d of the four tokens, then d + 1 of them
+        const u32x4 c{(v[0] & 0xffffu) | (v[1] << 16), (v[2] & 0xffffu) | (v[3] << 16),
+                      (v[0] >> 16) | (v[1] & 0xffff0000u), (v[2] >> 16) | (v[3] & 0xffff0000u)};
+        put<NT>(c, reinterpret_cast<u32x4*>(vt + (w - NCH) * PC));
+      } else {
+        put<NT>(v, reinterpret_cast<u32x4*>(vt + (w - NCH) * PC));
+      }
       return;
     }
     const int i = w / kPlain, u = w - i * kPlain;
@@ -346,30 +375,112 @@ struct TokUnits {
       int ch;
       if constexpr (EB == 2) ch = u * 16 + slot;
       else ch = (u >> 2) * 64 + (u & 3) * 16 + slot;
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(kt + ch * PC));
+      put<NT>(v, reinterpret_cast<u32x4*>(kt + ch * PC));
     } else {
       const int d = u - D / PC;
       E e;
       __builtin_memcpy(&e, &v, sizeof(E));
-      __builtin_nontemporal_store(e, vt + ((d >> 4) * 64 + (slot >> 2) * 16 + (d & 15)) * 4 + (slot & 3));
+      put<NT>(e, vt + ((d >> 4) * 64 + (slot >> 2) * 16 + (d & 15)) * 4 + (slot & 3));
     }
   }
 };
 
-// The decode step's new tokens in this work item's blocks (DevItem::tails, at
-// most 64), written by the whole workgroup for its KV heads [h0, h0 + nh)
-// before any of its threads reads the pool or the plan's block entries: the
-// tiles (a block the token opens whole, with zeros in its other slots) and each
-// block's valid count in the plan (every KV head's workgroup writes the same
-// value).  Each wave holds the item's token records in its lanes (one load);
-// the units of up to four records at a time are spread over the workgroup's
-// threads with all their loads in flight together.  Only this workgroup reads
-// these tiles and entries in the launch: an unfrozen tip block appears once in
-// a plan.
-template <class P, int D>
-__device__ void write_new_tokens(const NewTokens& x, const DevItem& it, int h0, int nh, int hkv, int tid,
-                                 int nthreads) {
+// Whole tiles of up to four token records that open their blocks (slot 0),
+// for KV heads [h0, h0 + NH), by NTH threads together, every load of every
+// record in flight before the first store:
+//   * K: job j is piece j % PR (PC consecutive elements) of token row
+//     (j / PR) % 16 of head h0 + j / (16 PR), PR = D / PC: one 16-byte load,
+//     16 lanes reading one token's row, then a store to the piece's chunk of
+//     the tile;
+//   * V: job j is chunk j % NCH of head h0 + j / NCH: element d (fp32), or
+//     elements d and d + 1 (bf16), of four consecutive tokens, four 32-bit
+//     loads.
+// A row past the record's tokens is read from its last token and zeroed
+// (no branch per chunk: the compiler waited for the loads at each join).
+template <class P, int D, int NTH, int NH, bool NT>
+__device__ void write_fresh_tiles(const NewTokens& x, const NewTok* t, int nt, int h0, int hkv, int tid) {
   using TU = TokUnits<P, D>;
+  using E = typename P::elem;
+  constexpr int EB = TU::EB;
+  using L = typename TU::L;
+  constexpr int PC = TU::PC, NCH = TU::NCH, PR = D / PC;
+  constexpr int JOBS = NH * NCH;  // per kind (K or V) and record
+  constexpr int JPT = (JOBS + NTH - 1) / NTH;
+  constexpr int MAXT = 4;
+  const size_t row = static_cast<size_t>(hkv) * D;
+  u32x4 kp[MAXT][JPT];
+  uint32_t vp[MAXT][JPT][4];
+#pragma unroll
+  for (int r = 0; r < MAXT; ++r) {
+    if (r >= nt) break;
+#pragma unroll
+    for (int q = 0; q < JPT; ++q) {
+      const int j = tid + q * NTH;
+      if (JOBS % NTH != 0 && j >= JOBS) break;
+      const int h = h0 + j / NCH, c = j % NCH;
+      const E* kb = static_cast<const E*>(x.k) + (static_cast<size_t>(t[r].src) * hkv + h) * D;
+      const E* vb = static_cast<const E*>(x.v) + (static_cast<size_t>(t[r].src) * hkv + h) * D;
+      const int ktok = c / PR, piece = c % PR;
+      kp[r][q] = *reinterpret_cast<const u32x4*>(kb + min(ktok, t[r].n - 1) * row + piece * PC);
+      int tok, d;
+      L::v_coord(c, 0, tok, d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vp[r][q][i] = *reinterpret_cast<const uint32_t*>(vb + min(tok + i, t[r].n - 1) * row + d);
+    }
+  }
+  // every load issued before the first store
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < MAXT; ++r) {
+    if (r >= nt) break;
+#pragma unroll
+    for (int q = 0; q < JPT; ++q) {
+      const int j = tid + q * NTH;
+      if (JOBS % NTH != 0 && j >= JOBS) break;
+      const int h = h0 + j / NCH, c = j % NCH;
+      const size_t tl = TU::tile(t[r], h, hkv);
+      // K: piece `piece` of token ktok is chunk (piece, ktok) of the tile
+      const int ktok = c / PR, piece = c % PR;
+      int kch;
+      if constexpr (EB == 2) kch = piece * 16 + ktok;
+      else kch = (piece >> 2) * 64 + (piece & 3) * 16 + ktok;
+      const u32x4 kv = ktok < t[r].n ? kp[r][q] : u32x4{0u, 0u, 0u, 0u};
+      TU::template put<NT>(kv, reinterpret_cast<u32x4*>(static_cast<E*>(x.kpool) + tl + kch * PC));
+      int tok, d;
+      L::v_coord(c, 0, tok, d);
+      uint32_t p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = tok + i < t[r].n ? vp[r][q][i] : 0u;
+      u32x4 v;
+      if constexpr (EB == 2) {
+        // the parts hold elements d, d + 1 of the four tokens; the chunk is d
+        // of the four tokens, then d + 1 of them
+        v = u32x4{(p[0] & 0xffffu) | (p[1] << 16), (p[2] & 0xffffu) | (p[3] << 16), (p[0] >> 16) | (p[1] & 0xffff0000u),
+                  (p[2] >> 16) | (p[3] & 0xffff0000u)};
+      } else {
+        v = u32x4{p[0], p[1], p[2], p[3]};
+      }
+      TU::template put<NT>(v, reinterpret_cast<u32x4*>(static_cast<E*>(x.vpool) + tl + c * PC));
+    }
+  }
+}
+
+// The decode step's new tokens in this work item's blocks (DevItem::tails, at
+// most 64), written by the whole workgroup (NTH threads) for its KV heads
+// [h0, h0 + NH) before any of its threads reads the pool or the plan's block
+// entries: the tiles (a block the tokens open whole, with zeros after them)
+// and each block's valid count in the plan (every KV head's workgroup writes
+// the same value).  Each wave holds the item's token records in its lanes
+// (one load); whole tiles go four records at a time (write_fresh_tiles), the
+// units of records in partly filled blocks four records at a time spread over
+// the threads, with all their loads in flight together.  Only this workgroup
+// reads these tiles and entries in the launch: an unfrozen tip block appears
+// once in a plan.
+template <class P, int D, int NTH, int NH>
+__device__ void write_new_tokens(const NewTokens& x, const DevItem& it, int h0, int hkv, int tid) {
+  using TU = TokUnits<P, D>;
+  constexpr int nh = NH, nthreads = NTH;
   const int tk0 = it.tails & 0xffff, tkc = it.tails >> 16;
   if (tkc == 0) return;
   const int lane = tid & 63;
@@ -387,9 +498,27 @@ __device__ void write_new_tokens(const NewTokens& x, const DevItem& it, int h0, 
                   static_cast<int16_t>(__builtin_amdgcn_readlane(ts, i)),
                   static_cast<int16_t>(__builtin_amdgcn_readlane(tn, i)), __builtin_amdgcn_readlane(tsr, i)};
   };
-  uint64_t todo = __ballot(te >= 0);
-  if (!todo) return;
   constexpr int MAXT = 4;
+  uint64_t whole = __ballot(te >= 0 && ts == 0);
+  uint64_t todo = __ballot(te >= 0 && ts != 0);
+  if (!whole && !todo) return;
+  while (whole) {
+    NewTok t[MAXT];
+    int nt = 0;
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) {
+      t[j] = NewTok{-1, 0, 0, 0, 0};
+      if (whole) {
+        t[j] = rec(__builtin_ctzll(whole));
+        whole &= whole - 1;
+        nt = j + 1;
+      }
+    }
+    write_fresh_tiles<P, D, NTH, NH, false>(x, t, nt, h0, hkv, tid);
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j)  // (unrolled: a runtime index would put t on the stack)
+      if (j < nt && tid == 0) x.blocks[t[j].entry].valid = t[j].slot + t[j].n;
+  }
   while (todo) {
     NewTok t[MAXT];
     int nt = 0;
@@ -402,9 +531,9 @@ __device__ void write_new_tokens(const NewTokens& x, const DevItem& it, int h0, 
         nt = j + 1;
       }
     }
-    // units of these records, thread-strided; a thread's share of one
-    // record's units is at most ceil(nh * units / nthreads) <= 4 for every
-    // shape here when it holds one token or opens its block (the rest, below)
+    // units of these records, thread-strided; a thread's share of a
+    // one-token record's units is at most ceil(nh * units / nthreads) <= 4
+    // for every shape here (the rest, below)
     constexpr int R = 4;
     u32x4 v[MAXT][R];
 #pragma unroll
@@ -424,11 +553,12 @@ __device__ void write_new_tokens(const NewTokens& x, const DevItem& it, int h0, 
 #pragma unroll
       for (int k = 0; k < R; ++k) {
         const int u = tid + k * nthreads;
-        if (u < total) TU::store(x, t[j], h0 + u / per, hkv, u % per, v[j][k]);
+        if (u < total) TU::template store<false>(x, t[j], h0 + u / per, hkv, u % per, v[j][k]);
       }
-      // a thread past R * nthreads units: the rest of this token, one at a time
+      // a thread past R * nthreads units: the rest of this record, one at a time
       for (int u = tid + R * nthreads; u < total; u += nthreads)
-        TU::store(x, t[j], h0 + u / per, hkv, u % per, TU::value(x, t[j], h0 + u / per, hkv, u % per));
+        TU::template store<false>(x, t[j], h0 + u / per, hkv, u % per,
+                                  TU::value(x, t[j], h0 + u / per, hkv, u % per));
       if (tid == 0) x.blocks[t[j].entry].valid = t[j].slot + t[j].n;
     }
   }

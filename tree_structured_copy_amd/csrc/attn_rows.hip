@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
   const int kvh0 = (blockIdx.x % hgroups) * HPW;
   const int kvh = kvh0 + hsel;
   const DevItem it = a.items[a.item0 + blockIdx.x / hgroups];
-  if constexpr (X::kActive) write_new_tokens<P, D>(x, it, kvh0, HPW, a.hkv, tid, 64 * W * HPW);
+  if constexpr (X::kActive) write_new_tokens<P, D, 64 * W * HPW, HPW>(x, it, kvh0, a.hkv, tid);
   const int nb = it.blk_count;
   const int nsb = (nb + 1) >> 1;
   const DevBlock* bl = a.blocks + it.blk_begin;

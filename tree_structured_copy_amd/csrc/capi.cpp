@@ -546,6 +546,8 @@ bool prepare_fused(tkv_cache* c, PlanSlot* s, int32_t layer, const tkv_seq* seqs
       if (!covered) return false;
     }
   }
+  x.multi = 0;
+  for (int32_t t = 0; t < ntail; ++t) x.multi |= x.tok[t].n > 1 ? 1 : 0;
   x.k = k_new;
   x.v = v_new;
   x.kpool = const_cast<char*>(c->kpool_layer(layer));
@@ -686,6 +688,7 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     if (!nt) {
       nt = &c->fused;
       nt->n = 0;
+      nt->multi = 0;
     }
     nt->nid = static_cast<int32_t>(s->id_patches.size());
     std::memcpy(nt->ids, s->id_patches.data(), s->id_patches.size() * sizeof(IdPatch));

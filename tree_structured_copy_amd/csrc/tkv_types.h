@@ -148,6 +148,7 @@ struct NewTokens {
   DevBlock* blocks;  // the plan's block list: the tokens' valid counts and patched ids are written here
   int32_t n;         // tail blocks listed (tok[0 .. n)), 0 = no tokens
   int32_t nid;       // id patches (ids[0 .. nid)), 0 = none
+  int32_t multi;     // 1: some record holds several tokens (each workgroup writes its records together first)
   NewTok tok[kFusedMaxTokens];
   IdPatch ids[kMaxIdPatches];
 };
