@@ -345,7 +345,7 @@ _PLANTED_PLANNER_MISTAKES = [
     # a block's first position off by one
     ("out[b].pos = pos0 + 16 * b;", "out[b].pos = pos0 + 16 * b + 1;"),
     # a tip block counted full
-    ("if (nb > 0) out[nb - 1].valid = nd.tail_valid();", "if (nb > 0) out[nb - 1].valid = 16;"),
+    ("out[nb - 1].valid = nd.tail_valid();", "out[nb - 1].valid = 16;"),
     # a merge record's slot without the KV-head stride
     ("P.parts.push_back({P.items[item].part_base + j * q_per_kv * num_kv_heads, item});",
      "P.parts.push_back({P.items[item].part_base + j * q_per_kv, item});"),

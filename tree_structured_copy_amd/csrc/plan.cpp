@@ -28,8 +28,8 @@ namespace {
 
 // memcpy of a list that may be empty (an empty vector's data() may be null,
 // which memcpy may not be given even for zero bytes)
-template <class T>
-void put(char* dst, const std::vector<T>& v) {
+template <class T, class A>
+void put(char* dst, const std::vector<T, A>& v) {
   if (!v.empty()) std::memcpy(dst, v.data(), v.size() * sizeof(T));
 }
 
@@ -251,6 +251,38 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     //    queries: a large group costs row-tile work on every block it reads,
     //    a one-tile group about its memory time.  A query then has partial
     //    records in both groups, merged afterwards.
+    // The LDS-staged kernels spend, on a block, its memory time plus the math
+    // of every row tile with a query that sees it (a wave skips a block none
+    // of its rows sees).  Their groups are chunked by cost,
+    // kBlockCost + (row tiles that see the block - 1) per block, so that a
+    // chunk of a widely shared root is shorter than one of private leaves,
+    // and a group's share of its class's items follows its cost.
+    constexpr int64_t kBlockCost = kPlanBlockCost;
+    // tile bits of the queries of one byte of a visibility mask, by byte
+    // position (made once per query heads per KV head: the scratch keeps it)
+    auto& tile_of_byte = S.tile_of_byte;
+    if (S.tile_of_byte_qpk != q_per_kv) {
+      tile_of_byte.assign(8 * 256, 0);
+      for (int32_t pb = 0; pb < 8; ++pb)
+        for (int32_t v = 1; v < 256; ++v) {
+          uint32_t t = 0;
+          for (int32_t bit = 0; bit < 8; ++bit)
+            if ((v >> bit) & 1) {
+              const int32_t j = 8 * pb + bit;
+              if (j * q_per_kv >= kMaxRows) break;  // no group holds query j
+              for (int32_t tl = (j * q_per_kv) >> 4; tl <= (j * q_per_kv + q_per_kv - 1) >> 4; ++tl)
+                t |= 1u << tl;
+            }
+          tile_of_byte[pb * 256 + v] = t;
+        }
+      S.tile_of_byte_qpk = q_per_kv;
+    }
+    auto tiles_seeing = [&](uint64_t m) {
+      uint32_t t = 0;
+      for (int32_t pb = 0; m; ++pb, m >>= 8) t |= tile_of_byte[pb * 256 + static_cast<int32_t>(m & 0xff)];
+      return __builtin_popcount(t);
+    };
+    auto block_cost = [&](const DevBlock& b) -> int64_t { return kBlockCost + tiles_seeing(b.mask) - 1; };
     Plan& P = *out;
     P.reset();
     P.nqueries = static_cast<int32_t>(total_q);
@@ -260,6 +292,8 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     S.go_count.clear();
     S.go_root.clear();
     S.go_partials.clear();
+    S.go_cost.clear();
+    S.go_mask.clear();
     // the (group, index in group) of each query's at most two groups: its own
     // and possibly one cascade subgroup of it
     S.qm_n.assign(total_q, 0);
@@ -299,6 +333,8 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       S.go_count.push_back(0);
       S.go_root.push_back(root);
       S.go_partials.push_back(partials ? 1 : 0);
+      S.go_cost.push_back(0);
+      S.go_mask.push_back(0);
     };
     // a node's blocks, once per group that reads it; the statistics count each node once
     auto emit_node = [&](int32_t k, uint64_t m) {
@@ -316,7 +352,12 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
         out[b].pad = 0;
         out[b].mask = m;
       }
-      if (nb > 0) out[nb - 1].valid = nd.tail_valid();
+      if (nb > 0) {
+        out[nb - 1].valid = nd.tail_valid();
+        // the group's cost and query mask, one lookup per node (its blocks share the mask)
+        S.go_cost.back() += static_cast<int64_t>(nb) * (kBlockCost + tiles_seeing(m) - 1);
+        S.go_mask.back() |= m;
+      }
       if (!nd.frozen && nb > 0) {
         P.tail_entry.push_back(static_cast<int32_t>(P.blocks.size()) - 1);
         P.tail_node.push_back(S.lnode[k]);
@@ -420,38 +461,6 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       for (int32_t gi = 0; gi < ngroups; ++gi)
         if (gclass[gi] >= 2 && gclass[gi] < top && class_work[gclass[gi]] < class_work[top]) gclass[gi] = top;
     auto class_of = [&](int32_t gi) { return static_cast<int>(gclass[gi]); };
-    // The LDS-staged kernels spend, on a block, its memory time plus the math
-    // of every row tile with a query that sees it (a wave skips a block none
-    // of its rows sees).  Their groups are chunked by cost,
-    // kBlockCost + (row tiles that see the block - 1) per block, so that a
-    // chunk of a widely shared root is shorter than one of private leaves,
-    // and a group's share of its class's items follows its cost.
-    constexpr int64_t kBlockCost = kPlanBlockCost;
-    // tile bits of the queries of one byte of a visibility mask, by byte
-    // position (made once per query heads per KV head: the scratch keeps it)
-    auto& tile_of_byte = S.tile_of_byte;
-    if (S.tile_of_byte_qpk != q_per_kv) {
-      tile_of_byte.assign(8 * 256, 0);
-      for (int32_t pb = 0; pb < 8; ++pb)
-        for (int32_t v = 1; v < 256; ++v) {
-          uint32_t t = 0;
-          for (int32_t bit = 0; bit < 8; ++bit)
-            if ((v >> bit) & 1) {
-              const int32_t j = 8 * pb + bit;
-              if (j * q_per_kv >= kMaxRows) break;  // no group holds query j
-              for (int32_t tl = (j * q_per_kv) >> 4; tl <= (j * q_per_kv + q_per_kv - 1) >> 4; ++tl)
-                t |= 1u << tl;
-            }
-          tile_of_byte[pb * 256 + v] = t;
-        }
-      S.tile_of_byte_qpk = q_per_kv;
-    }
-    auto tiles_seeing = [&](uint64_t m) {
-      uint32_t t = 0;
-      for (int32_t pb = 0; m; ++pb, m >>= 8) t |= tile_of_byte[pb * 256 + static_cast<int32_t>(m & 0xff)];
-      return __builtin_popcount(t);
-    };
-    auto block_cost = [&](const DevBlock& b) -> int64_t { return kBlockCost + tiles_seeing(b.mask) - 1; };
     auto& gcost = S.gcost;
     gcost.assign(ngroups, 0);
     int64_t class_cost[kKernelClasses] = {0, 0, 0, 0, 0, 0};
@@ -459,16 +468,7 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     for (int32_t gi = 0; gi < ngroups; ++gi) {
       const int cls = class_of(gi);
       const int32_t nb = S.go_count[gi];
-      if (cls >= 2) {
-        // (a block every query of the group sees -- most of a shared prefix --
-        // costs the same for all: no table lookups for it)
-        const DevBlock* gb = P.blocks.data() + S.go_begin[gi];
-        const uint64_t full = P.groups[gi].nq >= 64 ? ~0ull : ((1ull << P.groups[gi].nq) - 1);
-        const int64_t full_cost = kBlockCost + (P.groups[gi].nq * q_per_kv + 15) / 16 - 1;
-        for (int32_t b = 0; b < nb; ++b) gcost[gi] += gb[b].mask == full ? full_cost : block_cost(gb[b]);
-      } else {
-        gcost[gi] = nb;
-      }
+      gcost[gi] = cls >= 2 ? S.go_cost[gi] : nb;
       class_cost[cls] += gcost[gi];
       class_blocks[cls] += nb;
     }
@@ -539,12 +539,17 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
         const uint64_t full = P.groups[gi].nq >= 64 ? ~0ull : ((1ull << P.groups[gi].nq) - 1);
         for (int32_t b = 0; b < nb && !weighted; ++b) weighted = gb[b].mask != full;
         if (weighted) {
-          int64_t total = 0;
-          for (int32_t b = 0; b < nb; ++b) total += block_cost(gb[b]);
+          const int64_t total = gcost[gi];
           int64_t acc = 0;
           int32_t c = 1;
+          uint64_t run_mask = gb[0].mask;
+          int64_t run_cost = block_cost(gb[0]);
           for (int32_t b = 0; b < nb && c < nc; ++b) {
-            acc += block_cost(gb[b]);
+            if (gb[b].mask != run_mask) {
+              run_mask = gb[b].mask;
+              run_cost = block_cost(gb[b]);
+            }
+            acc += run_cost;
             // close chunk c - 1 after block b once it holds its share of the
             // cost, leaving at least one block for each chunk still to come
             if (acc * nc >= total * c && nb - (b + 1) >= nc - c) cut[c++] = b + 1;
@@ -570,7 +575,11 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
         t.it.tails = 0;
         t.it.qmask = 0;
         t.it.pad0 = t.it.pad1 = 0;
-        for (int32_t b = 0; b < cnt; ++b) t.it.qmask |= P.blocks[S.go_begin[gi] + at + b].mask;
+        if (nc == 1) {
+          t.it.qmask = S.go_mask[gi];
+        } else {
+          for (int32_t b = 0; b < cnt; ++b) t.it.qmask |= P.blocks[S.go_begin[gi] + at + b].mask;
+        }
         if (nc == 1 && !S.go_partials[gi]) {
           t.it.part_base = -1;
         } else {

@@ -16,6 +16,9 @@
 #pragma once
 #include <stdint.h>
 
+#include <memory>
+#include <new>
+#include <utility>
 #include <vector>
 
 #include "tkv_types.h"
@@ -29,6 +32,29 @@ namespace tkv {
 // 56.0 us per call with equal-length chunks; 69.6, 58.0, 52.7, 51.6, 51.4,
 // 52.2 and 54.9 us at 2, 4, 8, 16, 24, 32 and 64.
 constexpr int64_t kPlanBlockCost = 20;
+
+// An allocator whose resize() leaves new elements uninitialised: the planner
+// writes every field of each block entry it appends, and value-initialising
+// them first was a second pass over the block list (half of its time on a
+// 49 152-block plan).
+template <class T>
+struct NoInitAlloc : std::allocator<T> {
+  template <class U>
+  struct rebind {
+    using other = NoInitAlloc<U>;
+  };
+  NoInitAlloc() = default;
+  template <class U>
+  NoInitAlloc(const NoInitAlloc<U>&) noexcept {}
+  template <class U>
+  void construct(U* p) noexcept {
+    ::new (static_cast<void*>(p)) U;
+  }
+  template <class U, class... A>
+  void construct(U* p, A&&... a) {
+    ::new (static_cast<void*>(p)) U(std::forward<A>(a)...);
+  }
+};
 
 struct PlanOptions {
   int32_t target_wgs = 256;
@@ -54,7 +80,7 @@ struct Plan {
   std::vector<DevGroup> groups;
   std::vector<int32_t> gq;
   std::vector<int32_t> gqpos;
-  std::vector<DevBlock> blocks;
+  std::vector<DevBlock, NoInitAlloc<DevBlock>> blocks;  // each entry written in full by the planner
   std::vector<DevPart> parts;
   std::vector<DevMerge> merge;
   int32_t nqueries = 0;
@@ -114,6 +140,8 @@ struct PlanScratch {
   std::vector<uint8_t> emitted;
   std::vector<int32_t> go_begin, go_count, go_root;
   std::vector<uint8_t> go_partials;
+  std::vector<int64_t> go_cost;   // per group: chunking cost of its blocks (see kPlanBlockCost)
+  std::vector<uint64_t> go_mask;  // per group: the queries that see any of its blocks
   std::vector<uint8_t> qm_n;
   std::vector<int32_t> qm_g, qm_j;
   std::vector<int8_t> gclass;
