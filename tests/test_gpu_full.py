@@ -156,3 +156,48 @@ def test_loops_at_full_shape_sampled(kind):
     res = run_both(wl, sample=s)
     assert len(res) == len(wl.attend_ops())
     assert_close(res, wl.dtype)
+
+
+def test_queued_plan_copies_wait_for_the_launches_before_them():
+    """Six verify calls on the verify workload's handles (64 requests x
+    2048-token prefix, 3 draft paths of 8 tokens), each over the handles in
+    another order, so each builds its own plan of about 200 KB: a plan that
+    large is copied on the cache's copy stream.  All six are queued behind a
+    spin kernel, so the host queues them before the first runs, and the four
+    plan slots are reused: the copy of the fifth and sixth plans into a slot
+    must wait for the launch that reads that slot's earlier plan.  Every output
+    must be bit-identical to that of the same call made on an idle GPU."""
+    import torch
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    from workloads import device as wdev
+
+    wl = recipes.STANDARD["spec_verify"]()
+    lib = LibReplay(wl)
+    try:
+        op = wl.ops[lib.build()]
+        hs = lib.handles(op)
+        nq = list(op[3])
+        rows = sum(nq)
+        q = wdev.q_tensor(wl, op[-1], rows, "cuda")
+        batches = [hs[24 * k:] + hs[:24 * k] for k in range(6)]
+        outs = [torch.full((rows, wl.q_heads, wl.head_dim), float("nan"), device="cuda") for _ in batches]
+        refs = [torch.full((rows, wl.q_heads, wl.head_dim), float("nan"), device="cuda") for _ in batches]
+        sizes = [tkv.tkv_workspace_size(lib.c, b, nq) for b in batches]
+        ws = [torch.empty(max(n, 1), dtype=torch.uint8, device="cuda") for n in sizes]
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        before = tkv.tkv_get_counters(lib.c)["plans_uploaded"]
+        torch.cuda._sleep(20_000_000)
+        for b, o, w, n in zip(batches, outs, ws, sizes):
+            tkv.tkv_attend_verify(lib.c, 0, b, nq, q, o, w, n, stream)
+        torch.cuda.synchronize()
+        assert tkv.tkv_get_counters(lib.c)["plans_uploaded"] - before == 6
+        for b, o, w, n in zip(batches, refs, ws, sizes):
+            tkv.tkv_attend_verify(lib.c, 0, b, nq, q, o, w, n, stream)
+            torch.cuda.synchronize()
+        for k in range(6):
+            assert not torch.isnan(outs[k]).any(), k
+            assert torch.equal(outs[k], refs[k]), k
+    finally:
+        lib.close()

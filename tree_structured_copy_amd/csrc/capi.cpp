@@ -44,6 +44,15 @@ const char* launch_log() { return g_launch_log; }
 
 namespace {
 
+// A pinned host buffer a plan (or a list of changed words) is copied from;
+// ev is recorded behind that copy, busy until it has been waited for.
+struct Staging {
+  void* p = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool busy = false;
+};
+
 struct PlanSlot {
   std::vector<tkv_seq> seqs;
   std::vector<int32_t> nq;
@@ -66,12 +75,28 @@ struct PlanSlot {
   // copy (a reused device copy, see adopt_plan)
   std::vector<IdPatch> id_patches;
   uint64_t stamp = 0;
+  // read_ev is recorded behind the launches of a call on a large plan
+  // (read_rec: ever recorded); read_dirty: a call has queued work on dev that
+  // no read_ev follows (a small plan's, or one that failed part-way), so the
+  // next plan is copied into dev in stream order
+  hipEvent_t read_ev = nullptr;
+  bool read_rec = false;
+  bool read_dirty = false;
+  bool copy_side = false;  // this call may copy a whole plan on the copy stream
+  hipEvent_t up_ev = nullptr;  // behind that copy
 };
 
 // Plans up to this size keep a host copy of their device words (PlanSlot::shadow).
 constexpr size_t kShadowBytes = 64 << 10;
 
 constexpr int kPlanSlots = 4;
+// pinned staging buffers used in turn by plan uploads: a call waits only for
+// the copy kStagings uploads back, so the host may run that far ahead of the GPU
+constexpr int kStagings = 4;
+// a whole plan at least this large is copied on the cache's copy stream, where
+// the copy overlaps the kernels queued before it (a smaller one is copied in
+// the caller's stream, where it costs less than the cross-stream waits)
+constexpr size_t kSideCopyBytes = 64 << 10;
 // pinned staging made at tkv_create: the largest plan tkv_attend_decode_noalloc
 // can upload without allocating (the 32-layer workload's decode plan is about
 // 1.4 MiB)
@@ -122,11 +147,12 @@ struct tkv_cache {
   std::vector<uint64_t> seen;
   uint64_t seen_stamp = 0;
   uint64_t stamp = 0;
-  // pinned staging for plan uploads
-  void* pinned = nullptr;
-  size_t pinned_cap = 0;
-  hipEvent_t pinned_ev = nullptr;
-  bool pinned_busy = false;
+  // pinned staging for plan uploads: a ring, and the noalloc path's own
+  // buffer (made at tkv_create, never grown)
+  Staging stg[kStagings];
+  int stg_next = 0;
+  Staging fixed_stg;
+  hipStream_t copy_stream = nullptr;  // default priority, made on first use
   // side streams (default priority) on which the kernel classes of one call
   // after the first run concurrently, forked from and joined back to the
   // caller's stream with events
@@ -332,25 +358,40 @@ int find_plan(tkv_cache* c, const tkv_seq* seqs, const int32_t* nq, int32_t nseq
   return TKV_OK;
 }
 
-// Pinned staging of at least `bytes`, once the copy that last read it is done.
-int stage(tkv_cache* c, size_t bytes) {
-  if (c->pinned_busy) {
-    if (hipEventSynchronize(c->pinned_ev) != hipSuccess) return TKV_E_DEVICE;
-    c->pinned_busy = false;
+// `g` holding at least `bytes`, once the copy that last read it is done.
+int take_staging(Staging* g, size_t bytes) {
+  if (g->busy) {
+    if (hipEventSynchronize(g->ev) != hipSuccess) return TKV_E_DEVICE;
+    g->busy = false;
   }
-  if (c->pinned_cap < bytes) {
-    if (c->pinned) (void)hipHostFree(c->pinned);
-    c->pinned = nullptr;
-    c->pinned_cap = 0;
+  if (g->cap < bytes) {
+    if (g->p) (void)hipHostFree(g->p);
+    g->p = nullptr;
+    g->cap = 0;
     const size_t cap = align256(bytes + bytes / 4);
-    if (hipHostMalloc(&c->pinned, cap, hipHostMallocDefault) != hipSuccess) {
-      c->pinned = nullptr;
+    if (hipHostMalloc(&g->p, cap, hipHostMallocDefault) != hipSuccess) {
+      g->p = nullptr;
       return TKV_E_NOMEM;
     }
-    c->pinned_cap = cap;
+    g->cap = cap;
   }
-  if (!c->pinned_ev && hipEventCreateWithFlags(&c->pinned_ev, hipEventDisableTiming) != hipSuccess)
-    return TKV_E_DEVICE;
+  if (!g->ev && hipEventCreateWithFlags(&g->ev, hipEventDisableTiming) != hipSuccess) return TKV_E_DEVICE;
+  return TKV_OK;
+}
+
+// The next staging buffer of the ring, holding at least `bytes`.
+int stage(tkv_cache* c, size_t bytes, Staging** out) {
+  Staging* g = &c->stg[c->stg_next];
+  if (int rc = take_staging(g, bytes)) return rc;
+  c->stg_next = (c->stg_next + 1) % kStagings;
+  *out = g;
+  return TKV_OK;
+}
+
+// Marks `g` as read by the copy just queued on `stream`.
+int staged_copy_queued(Staging* g, hipStream_t stream) {
+  if (hipEventRecord(g->ev, stream) != hipSuccess) return TKV_E_DEVICE;
+  g->busy = true;
   return TKV_OK;
 }
 
@@ -379,11 +420,11 @@ int upload_patch(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
     s->pending.clear();
     return TKV_OK;
   }
-  if (int rc = stage(c, bytes)) return rc;
-  std::memcpy(c->pinned, s->pending.data(), bytes);
-  if (hipMemcpyAsync(dev + at, c->pinned, bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return TKV_E_DEVICE;
-  if (hipEventRecord(c->pinned_ev, stream) != hipSuccess) return TKV_E_DEVICE;
-  c->pinned_busy = true;
+  Staging* g = nullptr;
+  if (int rc = stage(c, bytes, &g)) return rc;
+  std::memcpy(g->p, s->pending.data(), bytes);
+  if (hipMemcpyAsync(dev + at, g->p, bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return TKV_E_DEVICE;
+  if (int rc = staged_copy_queued(g, stream)) return rc;
   if (launch_plan_patch(reinterpret_cast<int32_t*>(dev), reinterpret_cast<const PlanWord*>(dev + at),
                         static_cast<int32_t>(n), limit, stream) != hipSuccess)
     return TKV_E_DEVICE;
@@ -401,8 +442,9 @@ int upload_plan(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
   s->uploaded = false;
   if (s->dev_cap < bytes) {
     if (s->dev) {
-      // the old buffer may still be read by queued kernels
+      // the old buffer may still be read by queued kernels or written by a copy
       if (hipStreamSynchronize(stream) != hipSuccess) return TKV_E_DEVICE;
+      if (c->copy_stream && hipStreamSynchronize(c->copy_stream) != hipSuccess) return TKV_E_DEVICE;
       (void)hipFree(s->dev);
       s->dev = nullptr;
       s->dev_cap = 0;
@@ -414,24 +456,38 @@ int upload_plan(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
     }
     s->dev_cap = cap;
   }
-  if (int rc = stage(c, std::max<size_t>(s->plan.bytes, 256))) return rc;
+  Staging* g = nullptr;
+  if (int rc = stage(c, std::max<size_t>(s->plan.bytes, 256), &g)) return rc;
   const bool keep = s->plan.bytes <= kShadowBytes && s->plan.bytes % 4 == 0;
-  if (keep) std::memset(c->pinned, 0, s->plan.bytes);  // the gaps between sections too, as the shadow has them
-  s->plan.serialise(c->pinned);
+  if (keep) std::memset(g->p, 0, s->plan.bytes);  // the gaps between sections too, as the shadow has them
+  s->plan.serialise(g->p);
   s->id_patches.clear();
   s->shadow.clear();
   if (keep) {
     try {
-      const uint32_t* w = static_cast<const uint32_t*>(c->pinned);
+      const uint32_t* w = static_cast<const uint32_t*>(g->p);
       s->shadow.assign(w, w + s->plan.bytes / 4);
     } catch (const std::bad_alloc&) {
       s->shadow.clear();
     }
   }
-  if (hipMemcpyAsync(s->dev, c->pinned, s->plan.bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
-    return TKV_E_DEVICE;
-  if (hipEventRecord(c->pinned_ev, stream) != hipSuccess) return TKV_E_DEVICE;
-  c->pinned_busy = true;
+  if (s->copy_side && s->plan.bytes >= kSideCopyBytes) {
+    // on the copy stream, after the last launches that read dev; the caller's
+    // stream waits for it
+    if (!c->copy_stream && hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking) != hipSuccess)
+      return TKV_E_DEVICE;
+    if (!s->up_ev && hipEventCreateWithFlags(&s->up_ev, hipEventDisableTiming) != hipSuccess) return TKV_E_DEVICE;
+    if (s->read_rec && hipStreamWaitEvent(c->copy_stream, s->read_ev, 0) != hipSuccess) return TKV_E_DEVICE;
+    if (hipMemcpyAsync(s->dev, g->p, s->plan.bytes, hipMemcpyHostToDevice, c->copy_stream) != hipSuccess)
+      return TKV_E_DEVICE;
+    if (int rc = staged_copy_queued(g, c->copy_stream)) return rc;
+    if (hipEventRecord(s->up_ev, c->copy_stream) != hipSuccess || hipStreamWaitEvent(stream, s->up_ev, 0) != hipSuccess)
+      return TKV_E_DEVICE;
+  } else {
+    if (hipMemcpyAsync(s->dev, g->p, s->plan.bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+      return TKV_E_DEVICE;
+    if (int rc = staged_copy_queued(g, stream)) return rc;
+  }
   s->uploaded = true;
   ++c->tree.counters.plans_uploaded;
   return TKV_OK;
@@ -557,19 +613,15 @@ bool prepare_fused(tkv_cache* c, PlanSlot* s, int32_t layer, const tkv_seq* seqs
 }
 
 // The plan of a tkv_attend_decode_noalloc call, copied into the fixed device
-// workspace `base` from the pinned staging made at tkv_create (no allocation:
-// a plan larger than that staging is refused).
+// workspace `base` from the pinned staging made for it at tkv_create (no
+// allocation: a plan larger than that staging is refused).
 int upload_plan_fixed(tkv_cache* c, const Plan& P, char* base, hipStream_t stream) {
-  if (P.bytes > c->pinned_cap || !c->pinned_ev) return TKV_E_WORKSPACE;
-  if (c->pinned_busy) {
-    if (hipEventSynchronize(c->pinned_ev) != hipSuccess) return TKV_E_DEVICE;
-    c->pinned_busy = false;
-  }
-  P.serialise(c->pinned);
-  if (hipMemcpyAsync(base, c->pinned, P.bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return TKV_E_DEVICE;
-  if (hipEventRecord(c->pinned_ev, stream) != hipSuccess) return TKV_E_DEVICE;
-  c->pinned_busy = true;
-  return TKV_OK;
+  Staging* g = &c->fixed_stg;
+  if (P.bytes > g->cap || !g->ev) return TKV_E_WORKSPACE;
+  if (int rc = take_staging(g, P.bytes)) return rc;
+  P.serialise(g->p);
+  if (hipMemcpyAsync(base, g->p, P.bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return TKV_E_DEVICE;
+  return staged_copy_queued(g, stream);
 }
 
 // fixed_ws: the call's plan and partial records go to the device's fixed
@@ -628,6 +680,10 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   DeviceGuard dg(c->device);
   launch_log_reset();
+  if (!fixed) {
+    s->copy_side = !s->read_dirty;
+    s->read_dirty = true;
+  }
   NewTokens* nt = nullptr;
   // block ids of a reused device copy (adopt_plan): written by the attention
   // launch when every kernel of the call is the register kernel, else by the
@@ -786,6 +842,14 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     m.scale_log2 = a.scale_log2;
     if (launch_attn_merge(c->cfg.head_dim, m, stream) != hipSuccess) return TKV_E_DEVICE;
   }
+  if (!fixed && P.bytes >= kSideCopyBytes) {
+    // (an event behind a small plan's launches costs more than copying the
+    // slot's next plan in stream order, which its absence leads to)
+    if (!s->read_ev && hipEventCreateWithFlags(&s->read_ev, hipEventDisableTiming) != hipSuccess) return TKV_E_DEVICE;
+    if (hipEventRecord(s->read_ev, stream) != hipSuccess) return TKV_E_DEVICE;
+    s->read_rec = true;
+    s->read_dirty = false;
+  }
   std::memcpy(c->last_kernels, launch_log(), std::strlen(launch_log()) + 1);
   if (prof) {
     bool kept = false;
@@ -854,9 +918,8 @@ int tkv_create(const tkv_config* cfg, tkv_cache** out) {
     }
     if (cus > 0) cache->opt.target_wgs = cache->cus = cus;
     // set-up for tkv_attend_decode_noalloc: this device's fixed workspace and
-    // the cache's pinned plan staging (later calls may grow the staging, never
-    // shrink it)
-    if (static_workspace_init(cache->device) || stage(cache, kStaticPlanStagingBytes)) {
+    // the cache's pinned staging for its plans
+    if (static_workspace_init(cache->device) || take_staging(&cache->fixed_stg, kStaticPlanStagingBytes)) {
       tkv_destroy(cache);
       return TKV_E_DEVICE;
     }
@@ -870,10 +933,18 @@ int tkv_destroy(tkv_cache* c) {
   if (c->has_pools) {
     DeviceGuard dg(c->device);
     (void)hipDeviceSynchronize();
-    for (auto& s : c->slots)
+    for (auto& s : c->slots) {
       if (s.dev) (void)hipFree(s.dev);
-    if (c->pinned) (void)hipHostFree(c->pinned);
-    if (c->pinned_ev) (void)hipEventDestroy(c->pinned_ev);
+      if (s.read_ev) (void)hipEventDestroy(s.read_ev);
+      if (s.up_ev) (void)hipEventDestroy(s.up_ev);
+    }
+    if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+    auto free_staging = [](Staging& g) {
+      if (g.p) (void)hipHostFree(g.p);
+      if (g.ev) (void)hipEventDestroy(g.ev);
+    };
+    for (Staging& g : c->stg) free_staging(g);
+    free_staging(c->fixed_stg);
     for (auto& t : c->prof_used)
       for (auto e : t) (void)hipEventDestroy(e);
     for (auto e : c->ev_pool) (void)hipEventDestroy(e);
