@@ -44,10 +44,12 @@ const char* launch_log() { return g_launch_log; }
 
 namespace {
 
-// A pinned host buffer a plan (or a list of changed words) is copied from;
-// ev is recorded behind that copy, busy until it has been waited for.
+// A pinned host buffer a plan (or a list of changed words) is read from (p on
+// the host, dp on the device); ev is recorded behind the launch or copy that
+// reads it, busy until it has been waited for.
 struct Staging {
   void* p = nullptr;
+  void* dp = nullptr;
   size_t cap = 0;
   hipEvent_t ev = nullptr;
   bool busy = false;
@@ -75,15 +77,6 @@ struct PlanSlot {
   // copy (a reused device copy, see adopt_plan)
   std::vector<IdPatch> id_patches;
   uint64_t stamp = 0;
-  // read_ev is recorded behind the launches of a call on a large plan
-  // (read_rec: ever recorded); read_dirty: a call has queued work on dev that
-  // no read_ev follows (a small plan's, or one that failed part-way), so the
-  // next plan is copied into dev in stream order
-  hipEvent_t read_ev = nullptr;
-  bool read_rec = false;
-  bool read_dirty = false;
-  bool copy_side = false;  // this call may copy a whole plan on the copy stream
-  hipEvent_t up_ev = nullptr;  // behind that copy
 };
 
 // Plans up to this size keep a host copy of their device words (PlanSlot::shadow).
@@ -93,10 +86,6 @@ constexpr int kPlanSlots = 4;
 // pinned staging buffers used in turn by plan uploads: a call waits only for
 // the copy kStagings uploads back, so the host may run that far ahead of the GPU
 constexpr int kStagings = 4;
-// a whole plan at least this large is copied on the cache's copy stream, where
-// the copy overlaps the kernels queued before it (a smaller one is copied in
-// the caller's stream, where it costs less than the cross-stream waits)
-constexpr size_t kSideCopyBytes = 64 << 10;
 // pinned staging made at tkv_create: the largest plan tkv_attend_decode_noalloc
 // can upload without allocating (the 32-layer workload's decode plan is about
 // 1.4 MiB)
@@ -152,7 +141,6 @@ struct tkv_cache {
   Staging stg[kStagings];
   int stg_next = 0;
   Staging fixed_stg;
-  hipStream_t copy_stream = nullptr;  // default priority, made on first use
   // side streams (default priority) on which the kernel classes of one call
   // after the first run concurrently, forked from and joined back to the
   // caller's stream with events
@@ -366,12 +354,17 @@ int take_staging(Staging* g, size_t bytes) {
   }
   if (g->cap < bytes) {
     if (g->p) (void)hipHostFree(g->p);
-    g->p = nullptr;
+    g->p = g->dp = nullptr;
     g->cap = 0;
     const size_t cap = align256(bytes + bytes / 4);
-    if (hipHostMalloc(&g->p, cap, hipHostMallocDefault) != hipSuccess) {
+    if (hipHostMalloc(&g->p, cap, hipHostMallocMapped) != hipSuccess) {
       g->p = nullptr;
       return TKV_E_NOMEM;
+    }
+    if (hipHostGetDevicePointer(&g->dp, g->p, 0) != hipSuccess) {
+      (void)hipHostFree(g->p);
+      g->p = g->dp = nullptr;
+      return TKV_E_DEVICE;
     }
     g->cap = cap;
   }
@@ -400,7 +393,6 @@ int staged_copy_queued(Staging* g, hipStream_t stream) {
 // kernels that read the plan before.
 int upload_patch(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
   const size_t n = s->pending.size();
-  const size_t at = align256(s->plan.bytes);
   shadow_apply(s, s->pending.data(), n);
   const size_t bytes = n * sizeof(PlanWord);
   const uint32_t limit = static_cast<uint32_t>(s->plan.bytes / 4);
@@ -420,31 +412,28 @@ int upload_patch(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
     s->pending.clear();
     return TKV_OK;
   }
+  // a longer one is read by the patch kernel from pinned staging
   Staging* g = nullptr;
   if (int rc = stage(c, bytes, &g)) return rc;
   std::memcpy(g->p, s->pending.data(), bytes);
-  if (hipMemcpyAsync(dev + at, g->p, bytes, hipMemcpyHostToDevice, stream) != hipSuccess) return TKV_E_DEVICE;
-  if (int rc = staged_copy_queued(g, stream)) return rc;
-  if (launch_plan_patch(reinterpret_cast<int32_t*>(dev), reinterpret_cast<const PlanWord*>(dev + at),
-                        static_cast<int32_t>(n), limit, stream) != hipSuccess)
+  if (launch_plan_patch(reinterpret_cast<int32_t*>(dev), static_cast<const PlanWord*>(g->dp), static_cast<int32_t>(n),
+                        limit, stream) != hipSuccess)
     return TKV_E_DEVICE;
+  if (int rc = staged_copy_queued(g, stream)) return rc;
   s->pending.clear();
   return TKV_OK;
 }
 
 int upload_plan(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
   if (s->uploaded && s->pending.empty()) return TKV_OK;
-  // room behind the plan for the longest list of changed words a patch can make
-  const size_t words = s->plan.tail_entry.size() + s->plan.gq.size() + s->plan.items.size();
-  const size_t bytes = align256(std::max<size_t>(s->plan.bytes, 256)) + align256(words * sizeof(PlanWord));
+  const size_t bytes = align256(std::max<size_t>(s->plan.bytes, 256));
   if (s->uploaded && s->dev_cap >= bytes) return upload_patch(c, s, stream);
   s->pending.clear();
   s->uploaded = false;
   if (s->dev_cap < bytes) {
     if (s->dev) {
-      // the old buffer may still be read by queued kernels or written by a copy
+      // the old buffer may still be read by queued kernels
       if (hipStreamSynchronize(stream) != hipSuccess) return TKV_E_DEVICE;
-      if (c->copy_stream && hipStreamSynchronize(c->copy_stream) != hipSuccess) return TKV_E_DEVICE;
       (void)hipFree(s->dev);
       s->dev = nullptr;
       s->dev_cap = 0;
@@ -471,23 +460,11 @@ int upload_plan(tkv_cache* c, PlanSlot* s, hipStream_t stream) {
       s->shadow.clear();
     }
   }
-  if (s->copy_side && s->plan.bytes >= kSideCopyBytes) {
-    // on the copy stream, after the last launches that read dev; the caller's
-    // stream waits for it
-    if (!c->copy_stream && hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking) != hipSuccess)
-      return TKV_E_DEVICE;
-    if (!s->up_ev && hipEventCreateWithFlags(&s->up_ev, hipEventDisableTiming) != hipSuccess) return TKV_E_DEVICE;
-    if (s->read_rec && hipStreamWaitEvent(c->copy_stream, s->read_ev, 0) != hipSuccess) return TKV_E_DEVICE;
-    if (hipMemcpyAsync(s->dev, g->p, s->plan.bytes, hipMemcpyHostToDevice, c->copy_stream) != hipSuccess)
-      return TKV_E_DEVICE;
-    if (int rc = staged_copy_queued(g, c->copy_stream)) return rc;
-    if (hipEventRecord(s->up_ev, c->copy_stream) != hipSuccess || hipStreamWaitEvent(stream, s->up_ev, 0) != hipSuccess)
-      return TKV_E_DEVICE;
-  } else {
-    if (hipMemcpyAsync(s->dev, g->p, s->plan.bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
-      return TKV_E_DEVICE;
-    if (int rc = staged_copy_queued(g, stream)) return rc;
-  }
+  // copied by a kernel in the caller's stream, which reads the staging over the
+  // host link: the attention launch after it then starts without waiting for
+  // a copy engine
+  if (launch_plan_copy(s->dev, g->dp, s->plan.bytes, stream) != hipSuccess) return TKV_E_DEVICE;
+  if (int rc = staged_copy_queued(g, stream)) return rc;
   s->uploaded = true;
   ++c->tree.counters.plans_uploaded;
   return TKV_OK;
@@ -680,10 +657,6 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   DeviceGuard dg(c->device);
   launch_log_reset();
-  if (!fixed) {
-    s->copy_side = !s->read_dirty;
-    s->read_dirty = true;
-  }
   NewTokens* nt = nullptr;
   // block ids of a reused device copy (adopt_plan): written by the attention
   // launch when every kernel of the call is the register kernel, else by the
@@ -842,14 +815,6 @@ int attend(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, 
     m.scale_log2 = a.scale_log2;
     if (launch_attn_merge(c->cfg.head_dim, m, stream) != hipSuccess) return TKV_E_DEVICE;
   }
-  if (!fixed && P.bytes >= kSideCopyBytes) {
-    // (an event behind a small plan's launches costs more than copying the
-    // slot's next plan in stream order, which its absence leads to)
-    if (!s->read_ev && hipEventCreateWithFlags(&s->read_ev, hipEventDisableTiming) != hipSuccess) return TKV_E_DEVICE;
-    if (hipEventRecord(s->read_ev, stream) != hipSuccess) return TKV_E_DEVICE;
-    s->read_rec = true;
-    s->read_dirty = false;
-  }
   std::memcpy(c->last_kernels, launch_log(), std::strlen(launch_log()) + 1);
   if (prof) {
     bool kept = false;
@@ -933,12 +898,8 @@ int tkv_destroy(tkv_cache* c) {
   if (c->has_pools) {
     DeviceGuard dg(c->device);
     (void)hipDeviceSynchronize();
-    for (auto& s : c->slots) {
+    for (auto& s : c->slots)
       if (s.dev) (void)hipFree(s.dev);
-      if (s.read_ev) (void)hipEventDestroy(s.read_ev);
-      if (s.up_ev) (void)hipEventDestroy(s.up_ev);
-    }
-    if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
     auto free_staging = [](Staging& g) {
       if (g.p) (void)hipHostFree(g.p);
       if (g.ev) (void)hipEventDestroy(g.ev);

@@ -43,6 +43,11 @@ hipError_t launch_attn_merge(int head_dim, const MergeArgs& args, hipStream_t st
 hipError_t launch_append(int dtype, int head_dim, int32_t layers, const AppendArgs& args,
                          hipStream_t stream);
 
+// Copy `bytes` (a multiple of 4; both pointers 16-byte aligned) from src, a
+// device-visible pointer to pinned host memory, to dst in device memory;
+// at most 1024 workgroups of 256.
+hipError_t launch_plan_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
 // Write words[i].value at 32-bit word words[i].word of plan, for i < n, skipping
 // words >= limit; grid = ceil(n / 256) workgroups of 256.
 hipError_t launch_plan_patch(int32_t* plan, const PlanWord* words, int32_t n, uint32_t limit, hipStream_t stream);

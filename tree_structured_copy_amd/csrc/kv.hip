@@ -9,6 +9,9 @@
 // uninitialised bits; a block that continues keeps its earlier slots.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cstdint>
+
 #include "kernels.h"
 #include "layout.h"
 
@@ -174,6 +177,17 @@ __global__ __launch_bounds__(256) void plan_patch_kernel(int32_t* __restrict__ p
   if (w.word < limit) plan[w.word] = w.value;
 }
 
+// Copies a serialised plan from pinned host memory into its device buffer:
+// 16 bytes per thread and step (the loads cross the host link, all of a
+// thread's in flight at once), then the last n4 4-byte words.
+__global__ __launch_bounds__(256) void plan_copy_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                                        int64_t n16, int32_t n4) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+  if (blockIdx.x == 0 && static_cast<int32_t>(threadIdx.x) < n4)
+    reinterpret_cast<int32_t*>(dst + n16)[threadIdx.x] = reinterpret_cast<const int32_t*>(src + n16)[threadIdx.x];
+}
+
 // The same with the words in the kernel arguments.
 __global__ __launch_bounds__(512) void plan_patch_args_kernel(PatchArgs a) {
   const int32_t i = static_cast<int32_t>(threadIdx.x);
@@ -188,6 +202,18 @@ hipError_t launch_plan_patch_args(const PatchArgs& args, hipStream_t stream) {
   if (args.n <= 0 || args.n > kPatchArgWords) return hipErrorInvalidValue;
   hipLaunchKernelGGL(plan_patch_args_kernel, dim3(1), dim3(512), 0, stream, args);
   launch_log_add("plan_patch_args_kernel");
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_copy(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  if (bytes % 4 || (reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) % 16) return hipErrorInvalidValue;
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  const int32_t n4 = static_cast<int32_t>((bytes % 16) / 4);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n16 + 255) / 256, 1024));
+  hipLaunchKernelGGL(plan_copy_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                     static_cast<uint4*>(dst), static_cast<const uint4*>(src), n16, n4);
+  launch_log_add("plan_copy_kernel");
   return hipGetLastError();
 }
 
