@@ -161,12 +161,12 @@ def test_loops_at_full_shape_sampled(kind):
 def test_queued_plan_copies_wait_for_the_launches_before_them():
     """Six verify calls on the verify workload's handles (64 requests x
     2048-token prefix, 3 draft paths of 8 tokens), each over the handles in
-    another order, so each builds its own plan of about 200 KB: a plan that
-    large is copied on the cache's copy stream.  All six are queued behind a
-    spin kernel, so the host queues them before the first runs, and the four
-    plan slots are reused: the copy of the fifth and sixth plans into a slot
-    must wait for the launch that reads that slot's earlier plan.  Every output
-    must be bit-identical to that of the same call made on an idle GPU."""
+    another order, so each builds its own plan of about 200 KB.  All six are
+    queued behind a spin kernel, so the host queues them before the first runs:
+    the four plan slots are reused (the fifth and sixth plans are copied into
+    slots whose earlier plans are still to be read) and the ring of pinned
+    staging buffers wraps.  Every output must be bit-identical to that of the
+    same call made on an idle GPU."""
     import torch
     from tree_structured_copy_amd import tkv
     from tree_structured_copy_amd.replay import LibReplay
