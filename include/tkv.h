@@ -203,7 +203,8 @@ int tkv_attend_decode_new_tokens(tkv_cache* c, int32_t layer, const tkv_seq* seq
  * partial records in a fixed workspace the library holds on each device (a
  * file-scope device array of 64 MiB, present from the first tkv_create on that
  * device until the process ends), so no workspace argument is taken.  The plan
- * is uploaded from pinned staging made at tkv_create (4 MiB at least).  The call
+ * is uploaded from a pinned staging buffer of 4 MiB made for it at tkv_create
+ * (never grown; other calls use staging of their own).  The call
  * makes no hipMalloc, hipFree, host-pinned allocation, stream or event.
  * TKV_E_WORKSPACE if the plan and its partial records exceed the fixed
  * workspace or the plan exceeds the staging; otherwise errors as
