@@ -76,11 +76,24 @@ def test_mcts_cascade(cascade, dtype, hq, hkv, d):
 def test_concurrent_modes(mode):
     """The kernel classes of one call run one after another (0) or on side
     streams (1): the same outputs against the oracle in both modes, on a plan
-    with one-tile, 8-tile and 16-tile items and a merge."""
+    with one-tile and 16-tile items and a merge (256-row groups with the
+    cascade)."""
     from tree_structured_copy_amd import tkv
     wl = recipes.mcts_workload("mcts_modes", dtype="bf16", q_heads=8, kv_heads=2, head_dim=128, root_tokens=70,
                                branching=4, depth=5, leaves=64, node_tokens=9, seed=43)
-    assert_close(run_both(wl, options={tkv.TKV_OPT_CONCURRENT: mode}), "bf16")
+    opts = {tkv.TKV_OPT_MAX_ROWS: 256, tkv.TKV_OPT_CASCADE: 1, tkv.TKV_OPT_CONCURRENT: mode}
+    from tree_structured_copy_amd.replay import LibReplay
+    need_gpu()
+    lib = LibReplay(wl)
+    try:
+        for k, v in opts.items():
+            tkv.tkv_set_option(lib.c, k, v)
+        op = wl.ops[lib.build()]
+        ipk = tkv.tkv_plan_info_get(lib.c, lib.handles(op), None)["items_per_kernel"]
+        assert ipk[0] > 0 and ipk[5] > 0, ipk
+    finally:
+        lib.close()
+    assert_close(run_both(wl, options=opts), "bf16")
 
 
 @pytest.mark.parametrize("waves", [2, 4, 8])
@@ -118,8 +131,10 @@ def test_every_kernel_class(max_rows, cls, kind):
     """Group size decides the kernel: 1-2 row tiles in registers (attn.hip), 3-16
     row tiles with K/V staged in LDS (attn_rows.hip).  Each class against the oracle."""
     if kind == "decode":
+        # 64 branches per request: groups of 4, 8, 16, 24 (24, 20, 20 after the
+        # last two are balanced), 32 and 64 queries for the six row limits
         wl = recipes.fork_workload("classes", dtype="bf16", layers=1, q_heads=16, kv_heads=4, head_dim=128,
-                                   requests=2, prefix=333, width=40, branch_tokens=5, seed=17)
+                                   requests=2, prefix=333, width=64, branch_tokens=5, seed=17)
     else:
         wl = recipes.verify_workload("classes_v", dtype="bf16", q_heads=16, kv_heads=4, head_dim=128,
                                      requests=2, prefix=333, paths=8, drafts=7, seed=19)

@@ -874,6 +874,9 @@ int tkv_create(const tkv_config* cfg, tkv_cache** out) {
     return TKV_E_NOMEM;
   }
   cache->has_pools = c.k_pool != nullptr;
+  // the LDS-staged shapes' workgroups per CU (attn_rows.hip): fp32 at d = 128
+  // takes a CU's registers with one
+  cache->opt.two_per_cu = (c.dtype == TKV_BF16 || c.head_dim <= 64) ? 1 : 0;
   if (cache->has_pools) {
     int cus = 0;
     if (hipGetDevice(&cache->device) != hipSuccess ||

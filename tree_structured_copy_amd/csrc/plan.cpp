@@ -224,6 +224,7 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
           }
         }
         // unit u of this tree = uq[ub[u] .. ub[u + 1]), the last one ending at uq.size()
+        const size_t g_first = S.gbeg.size();
         int32_t cur_begin = 0, cur_size = 0;
         for (size_t u = 0; u < ub.size(); ++u) {
           const int32_t usz = (u + 1 < ub.size() ? ub[u + 1] : static_cast<int32_t>(uq.size())) - ub[u];
@@ -240,6 +241,24 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
           S.gbeg.push_back(cur_begin);
           S.gsize.push_back(cur_size);
           S.groot.push_back(static_cast<int32_t>(r));
+        }
+        // The packing leaves the tree's last group with what remains (a
+        // 40-way fork: 32 queries, then 8).  The last two groups take the unit
+        // boundary that splits their queries most evenly instead (20 and 20):
+        // the same row tiles in all, and groups of one size run in one kernel
+        // class rather than an 8-tile launch and a 2-tile one.
+        const size_t ng = S.gbeg.size();
+        if (ng >= g_first + 2) {
+          const int32_t a = S.gbeg[ng - 2], end = S.gbeg[ng - 1] + S.gsize[ng - 1];
+          int32_t best = S.gbeg[ng - 1];
+          for (size_t u = 0; u < ub.size(); ++u) {
+            const int32_t cut = ub[u];
+            if (cut <= a || cut >= end || cut - a > qg || end - cut > qg) continue;
+            if (std::max(cut - a, end - cut) < std::max(best - a, end - best)) best = cut;
+          }
+          S.gsize[ng - 2] = best - a;
+          S.gbeg[ng - 1] = best;
+          S.gsize[ng - 1] = end - best;
         }
       }
     }
@@ -443,9 +462,13 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     //    register-tile classes, whose time is their memory time, and a quarter
     //    of that for the LDS-staged classes (3+ row tiles), whose time per
     //    block is several times longer; and at most kRowsMaxItemBlocks.
-    //    An LDS-staged class whose work (blocks x row tiles) is smaller than
-    //    that of the largest LDS-staged class present runs in that class's
-    //    kernel instead (its extra waves idle): one launch and one ramp fewer.
+    //    With groups of at most 8 row tiles, every LDS-staged class below the
+    //    largest one present runs in that class's kernel (its extra waves
+    //    idle): one launch, one ramp and one tail instead of several, each
+    //    class filling the GPU alone (a search tree whose groups came out of
+    //    6 and 8 tiles: 60 -> 37 us).  Below a 16-tile class (groups of up to
+    //    256 rows) only a class with less work (blocks x row tiles) than that
+    //    class joins it: a 16-tile workgroup holds a CU alone.
     auto& gclass = S.gclass;
     gclass.resize(ngroups);
     int64_t class_work[kKernelClasses] = {0, 0, 0, 0, 0, 0};
@@ -459,7 +482,8 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       if (class_work[c] > 0) top = c;
     if (top > 2)
       for (int32_t gi = 0; gi < ngroups; ++gi)
-        if (gclass[gi] >= 2 && gclass[gi] < top && class_work[gclass[gi]] < class_work[top]) gclass[gi] = top;
+        if (gclass[gi] >= 2 && gclass[gi] < top && (top <= 4 || class_work[gclass[gi]] < class_work[top]))
+          gclass[gi] = top;
     auto class_of = [&](int32_t gi) { return static_cast<int>(gclass[gi]); };
     auto& gcost = S.gcost;
     gcost.assign(ngroups, 0);
@@ -475,8 +499,10 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
     const int64_t class_items = std::max<int64_t>(1, std::max<int32_t>(1, opt.target_wgs) / num_kv_heads);
     auto want_of = [&](int cls) -> int64_t {
       // the 4- and 8-tile LDS-staged shapes fit two workgroups per CU, and
-      // two per CU stream faster than one with a deeper ring: twice the items
-      return (cls == 2 || cls == 4) ? 2 * class_items : class_items;
+      // two per CU stream faster than one with a deeper ring; the 6-tile
+      // shape's workgroups pair two KV heads: twice the items either way
+      // (a 24-branch fork's 6-tile groups: 122 -> 83 us)
+      return (opt.two_per_cu && cls >= 2 && cls <= 4) ? 2 * class_items : class_items;
     };
     auto most_of = [&](int32_t gi) -> int64_t {
       const int cls = class_of(gi);

@@ -67,6 +67,11 @@ struct PlanOptions {
   // tried, and the same on the fork and verify workloads.
   int32_t max_rows = 128;
   int32_t cascade = 0;  // split narrow blocks of large groups into one-tile subgroups
+  // 1: a CU holds two workgroups of the 4- and 8-tile LDS-staged shapes, and
+  // the 6-tile shape's workgroups hold two KV heads (or two fit a CU), so
+  // one round of those classes is twice target_wgs / Hkv items (bf16, or
+  // d <= 64); 0: one workgroup of one KV head per CU (fp32 at d = 128)
+  int32_t two_per_cu = 1;
 };
 
 struct Plan {
