@@ -8,8 +8,8 @@
 // lists each group's blocks once, with a mask of which queries see each block.
 //
 // One workgroup (W = 2, 4 or 8 waves) runs one work item (a run of a group's
-// block list) for one KV head.  Each wave takes every W-th super-block (two
-// blocks) of the item and keeps, for all of the group's rows, a
+// block list) for one KV head.  Each wave takes a contiguous share of the
+// item's super-blocks (two blocks each) and keeps, for all of the group's rows, a
 // flash-decoding state (running max m, sum l, output accumulator) in
 // registers:
 //   * a block's K tile arrives with four contiguous 1 KiB wave loads already in
