@@ -153,6 +153,37 @@ def test_every_kernel_class(max_rows, cls, kind):
     assert_close(run_both(wl, options={3: max_rows}), "bf16")
 
 
+@pytest.mark.parametrize("case", ["tree_deep_nodes", "tree_short_nodes", "fork24"])
+def test_promoted_classes_and_six_tile_items(case):
+    """Groups of different sizes in one launch, and the 6-tile class cut to
+    twice the items: a search tree's 64 leaves packed into three groups of
+    4-8 row tiles all run in the 8-tile kernel (the smaller groups with idle
+    waves); a 24-branch fork's 6-tile groups are cut into 64 items (16 per
+    group, merged).  Every output against the oracle."""
+    if case == "fork24":
+        wl = recipes.fork_workload("fork24", dtype="bf16", layers=1, q_heads=32, kv_heads=8, head_dim=128,
+                                   requests=4, prefix=1024, width=24, branch_tokens=40, seed=61)
+        want = [0, 0, 0, 64, 0, 0]
+    else:
+        node = 64 if case == "tree_deep_nodes" else 16
+        wl = recipes.mcts_workload(case, leaves=64, node_tokens=node, root_tokens=512,
+                                   depth=6 if node == 64 else 12, seed=0 if node == 64 else 2)
+        want = [0, 0, 0, 0, 64, 0]
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    need_gpu()
+    lib = LibReplay(wl)
+    try:
+        tkv.tkv_set_option(lib.c, tkv.TKV_OPT_TARGET_WGS, 256)
+        op = wl.ops[lib.build()]
+        info = tkv.tkv_plan_info_get(lib.c, lib.handles(op), None)
+        say("plan %s" % info)
+        assert info["items_per_kernel"] == want and info["groups"] >= 3, info
+    finally:
+        lib.close()
+    assert_close(run_both(wl, options={tkv.TKV_OPT_TARGET_WGS: 256}), "bf16")
+
+
 @pytest.mark.parametrize("dtype,hkv,d", [("bf16", 3, 128), ("bf16", 2, 64), ("f32", 2, 64), ("f32", 2, 128)])
 def test_six_tile_shapes(dtype, hkv, d):
     """Groups of 6 row tiles run two KV heads per workgroup where the head count
