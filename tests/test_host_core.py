@@ -350,7 +350,7 @@ _PLANTED_PLANNER_MISTAKES = [
     ("P.parts.push_back({P.items[item].part_base + j * q_per_kv * num_kv_heads, item});",
      "P.parts.push_back({P.items[item].part_base + j * q_per_kv, item});"),
     # a visibility bit given to the wrong query of a pair
-    ("mask[k] |= 1ull << j;", "mask[k] |= 1ull << (j / 2 * 2);"),
+    ("bits |= 1ull << j1;", "bits |= 1ull << (j1 / 2 * 2);"),
 ]
 
 

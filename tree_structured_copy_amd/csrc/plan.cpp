@@ -399,11 +399,19 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       const PlanQuery* qs = uq.data() + S.gbeg[g0];
       const int32_t n = S.gsize[g0];
       touched.clear();
-      for (int32_t j = 0; j < n; ++j)
-        for (int32_t k = loc[S.tip[qs[j].handle]]; k >= 0; k = S.lparent[k]) {
+      for (int32_t j = 0; j < n;) {
+        // a handle's queries are consecutive and see the same nodes: one walk
+        // up its path per handle, with all their bits
+        const int32_t h = qs[j].handle;
+        uint64_t bits = 0;
+        int32_t j1 = j;
+        for (; j1 < n && qs[j1].handle == h; ++j1) bits |= 1ull << j1;
+        for (int32_t k = loc[S.tip[h]]; k >= 0; k = S.lparent[k]) {
           if (!mask[k]) touched.push_back(k);
-          mask[k] |= 1ull << j;
+          mask[k] |= bits;
         }
+        j = j1;
+      }
       std::sort(touched.begin(), touched.end(), [&](int32_t a, int32_t b) { return S.pre[a] < S.pre[b]; });
       bool cascade = false;
       const int32_t ntouch = static_cast<int32_t>(touched.size());
@@ -662,28 +670,35 @@ int build_plan(const Tree& tree, const tkv_seq* seqs, const int32_t* nq, int32_t
       const int64_t lo = b - P.tail_entry.begin(), cnt = e - b;
       it.tails = (cnt > 0 && lo < 0x10000 && cnt < 0x8000) ? static_cast<int32_t>(lo | (cnt << 16)) : 0;
     }
-    // merge records: every partial of a query, in the order its groups were made
+    // merge records: every partial of a query, in the order its groups were
+    // made.  With no partial records at all, every group is one item writing
+    // its queries' outputs itself (a cascade subgroup always writes partials),
+    // so each query has one direct item and an empty record.
     P.merge.resize(total_q);
-    for (int64_t q = 0; q < total_q; ++q) {
-      DevMerge m;
-      m.p_begin = static_cast<int32_t>(P.parts.size());
-      int32_t direct = 0;
-      for (int32_t x = 0; x < S.qm_n[q]; ++x) {
-        const int32_t g = S.qm_g[2 * q + x], j = S.qm_j[2 * q + x];
-        for (int32_t y = S.ibeg[g]; y < S.ibeg[g + 1]; ++y) {
-          const int32_t item = S.ilist[y];
-          if (P.items[item].part_base < 0) {
-            ++direct;
-            continue;
+    if (slots == 0) {
+      std::fill(P.merge.begin(), P.merge.end(), DevMerge{0, 0});
+    } else {
+      for (int64_t q = 0; q < total_q; ++q) {
+        DevMerge m;
+        m.p_begin = static_cast<int32_t>(P.parts.size());
+        int32_t direct = 0;
+        for (int32_t x = 0; x < S.qm_n[q]; ++x) {
+          const int32_t g = S.qm_g[2 * q + x], j = S.qm_j[2 * q + x];
+          for (int32_t y = S.ibeg[g]; y < S.ibeg[g + 1]; ++y) {
+            const int32_t item = S.ilist[y];
+            if (P.items[item].part_base < 0) {
+              ++direct;
+              continue;
+            }
+            if (!((P.items[item].qmask >> j) & 1ull)) continue;  // sees none of the item's blocks
+            P.parts.push_back({P.items[item].part_base + j * q_per_kv * num_kv_heads, item});
           }
-          if (!((P.items[item].qmask >> j) & 1ull)) continue;  // sees none of the item's blocks
-          P.parts.push_back({P.items[item].part_base + j * q_per_kv * num_kv_heads, item});
         }
+        m.p_count = static_cast<int32_t>(P.parts.size()) - m.p_begin;
+        if (direct + m.p_count == 0 || (direct > 0 && (direct > 1 || m.p_count > 0))) return TKV_E_INVAL;
+        P.merge[q] = m;
+        if (m.p_count) P.any_merge = true;
       }
-      m.p_count = static_cast<int32_t>(P.parts.size()) - m.p_begin;
-      if (direct + m.p_count == 0 || (direct > 0 && (direct > 1 || m.p_count > 0))) return TKV_E_INVAL;
-      P.merge[q] = m;
-      if (m.p_count) P.any_merge = true;
     }
     P.layout();
   } catch (const std::bad_alloc&) {
