@@ -618,7 +618,7 @@ def _multi_new_token_workload(name, dtype, layers, head_dim, rounds, seed):
 
 
 @pytest.mark.parametrize("one_launch", [1, 0])
-@pytest.mark.parametrize("dtype,layers,head_dim", [("bf16", 1, 128), ("bf16", 2, 64), ("f32", 2, 128)])
+@pytest.mark.parametrize("dtype,layers,head_dim", [("bf16", 1, 128), ("bf16", 2, 64), ("f32", 2, 128), ("f32", 1, 64)])
 def test_decode_with_several_new_tokens_written_in_the_call(dtype, layers, head_dim, one_launch):
     """tkv_attend_decode_new_tokens: each round every branch reserves 1 to 16
     tokens (a partly filled block, a block they fill, or a new node's block
