@@ -103,6 +103,7 @@ int main(int argc, char** argv) {
     opt.cascade = r.below(2);
     opt.min_chunk = 1 + r.below(40);
     opt.target_wgs = 1 + r.below(800);
+    opt.two_per_cu = r.below(2);
     const int32_t* nqp = verify ? nq.data() : nullptr;
     const int32_t nseq = static_cast<int32_t>(seqs.size());
     PlanScratch scratch;
