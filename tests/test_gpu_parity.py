@@ -153,6 +153,21 @@ def test_every_kernel_class(max_rows, cls, kind):
     assert_close(run_both(wl, options={3: max_rows}), "bf16")
 
 
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (16, 2), (8, 8)])
+@pytest.mark.parametrize("kind", ["decode", "verify"])
+def test_query_heads_per_kv_head(hq, hkv, kind):
+    """GQA ratios 2, 8 and 1 (the other tests use 4, and 16 in random
+    sessions): a fork of 12 branches per request and a verify batch of 3
+    draft paths x 6 tokens per request, against the oracle on every output."""
+    if kind == "decode":
+        wl = recipes.fork_workload("gqa_fork", dtype="bf16", layers=1, q_heads=hq, kv_heads=hkv, head_dim=128,
+                                   requests=3, prefix=300, width=12, branch_tokens=21, seed=71 + hq + hkv)
+    else:
+        wl = recipes.verify_workload("gqa_verify", dtype="bf16", q_heads=hq, kv_heads=hkv, head_dim=128,
+                                     requests=3, prefix=300, paths=3, drafts=6, seed=73 + hq + hkv)
+    assert_close(run_both(wl), "bf16")
+
+
 @pytest.mark.parametrize("case", ["tree_deep_nodes", "tree_short_nodes", "fork24"])
 def test_promoted_classes_and_six_tile_items(case):
     """Groups of different sizes in one launch, and the 6-tile class cut to
