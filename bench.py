@@ -333,6 +333,8 @@ def _native_loops():
     * spec_loop: the verify workload's 64 requests (2048-token prefixes, 3 draft
       paths of 8 tokens) through 8 rounds of fork, draft, verify, accept or
       roll back and a bonus token;
+    * spec_loop_one_launch: the same, each round's drafts reserved and written
+      by the verify call (tkv_attend_verify_new_tokens);
     * search_loop: 500 tree-search simulations, branching 4, depth 12, a
       2048-token root and 16 tokens per node (GQA 32/8, d = 128, bf16);
     * search_loop_one_launch: the same, each expansion's new nodes reserved and
@@ -343,6 +345,7 @@ def _native_loops():
     exe = os.path.join(ROOT, "tree_structured_copy_amd", "replay_bench")
     res = {}
     for key, wl in (("spec_loop", recipes.spec_loop_workload("spec_loop", rounds=8)),
+                    ("spec_loop_one_launch", recipes.spec_loop_workload("spec_loop", rounds=8, one_launch=True)),
                     ("search_loop", recipes.mcts_loop_workload("search_loop")),
                     ("search_loop_one_launch", recipes.mcts_loop_workload("search_loop", one_launch=True))):
         with tempfile.NamedTemporaryFile("w", suffix=".ops", delete=False) as f:
@@ -356,7 +359,7 @@ def _native_loops():
             raise RuntimeError("replay_bench failed on %s: %s" % (key, r.stderr[-2000:]))
         d = json.loads(r.stdout)
         sec = d["wall_ms"] / 1e3
-        if key == "spec_loop":
+        if key.startswith("spec_loop"):
             d["rounds"] = 8
             d["verify_tokens_per_s"] = d["verify_tokens"] / sec
             d["ms_per_round"] = d["wall_ms"] / 8

@@ -167,7 +167,7 @@ int tkv_attend_decode(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t 
  * own tip node, e.g. reserved for all layers by tkv_append_batch with k = v = NULL
  * -- gets K = k_new[i], V = v_new[i] for `layer` (device [nseq][Hkv][head_dim], cache
  * dtype), then the call is tkv_attend_decode over the paths that include it.  With up
- * to 160 handles, and no change to the cached plan since its last use other than
+ * to 192 handles, and no change to the cached plan since its last use other than
  * these tokens (the usual decode step after tkv_append_batch reserved them), the
  * attention launch itself writes each token -- the workgroup that reads its block
  * writes it first -- and the block's valid count in the plan: one launch per step
@@ -196,6 +196,23 @@ int tkv_attend_decode_new_token(tkv_cache* c, int32_t layer, const tkv_seq* seqs
 int tkv_attend_decode_new_tokens(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* ntok,
                                  int32_t nseq, const void* k_new, const void* v_new, const void* q,
                                  float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* tkv_attend_verify whose verified tokens are new: handle i's last nq[i] tokens
+ * (1 <= nq[i] <= 16), which must all lie in its last block and its own tip node --
+ * the draft tokens of a speculative step, reserved for every layer by
+ * tkv_append_batch with k = v = NULL after the fork into draft paths -- get their K
+ * and V for `layer` from rows [r_i, r_i + nq[i]) of k_new / v_new (device
+ * [sum nq][Hkv][head_dim], cache dtype), r_i = nq[0] + ... + nq[i-1], and are
+ * verified in the same call: the target model computes each layer's K/V for the
+ * drafts in the pass that verifies them, and they stay in the cache for the
+ * accepted ones (DSpark blog, second layer: verify the drafts in parallel; third
+ * layer: each token's K/V is computed once and kept).  One launch per call under the
+ * conditions of tkv_attend_decode_new_token (at most 192 handles, the cached plan
+ * changed only by these tokens); otherwise a preparation launch writes them first.
+ * Errors as tkv_attend_verify and tkv_attend_decode_new_tokens. */
+int tkv_attend_verify_new_tokens(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
+                                 const void* k_new, const void* v_new, const void* q, float* out, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /* tkv_attend_decode for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The

@@ -166,7 +166,7 @@ class OracleReplay:
             if self.alloc is not None:
                 self.alloc.truncate(self.h_alloc[h], L)
             self.mat.truncate(self.h_mat[h], L)
-        elif kind in ("decode", "decode_new", "verify", "time_begin"):
+        elif kind in ("decode", "decode_new", "verify", "verify_new", "time_begin"):
             pass
         else:
             raise ValueError(kind)

@@ -53,7 +53,7 @@ def run_both(wl, sample=None, options=None, extra_blocks=0, check_tables=True, t
     results = []
     try:
         for op in wl.ops:
-            if op[0] in ("decode", "decode_new", "verify"):
+            if op[0] in ("decode", "decode_new", "verify", "verify_new"):
                 out = lib.attend(op)
                 torch.cuda.synchronize()
                 rows = lib.nrows(op)

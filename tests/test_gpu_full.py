@@ -138,16 +138,18 @@ def test_fork_workload_decode_loop_sampled(fused):
     assert_close(res, wl.dtype)
 
 
-@pytest.mark.parametrize("kind", ["spec_loop", "search_loop", "search_loop_one_launch"])
+@pytest.mark.parametrize("kind", ["spec_loop", "spec_loop_one_launch", "search_loop", "search_loop_one_launch"])
 def test_loops_at_full_shape_sampled(kind):
     """The loops bench.py times, at their full shapes: the speculative loop on
     the verify workload's 64 requests (2048-token prefixes, 3 paths of 8
-    drafts) for 2 rounds, and 40 tree-search simulations (2048-token root,
-    branching 4, depth 12, 16 tokens per node), with each expansion's nodes
-    appended then decoded or reserved and written by the decode call.
+    drafts) for 2 rounds, with the drafts appended then verified or reserved
+    and written by the verify call, and 40 tree-search simulations
+    (2048-token root, branching 4, depth 12, 16 tokens per node), with each
+    expansion's nodes appended then decoded or reserved and written by the
+    decode call.
     Sampled against the oracle; tables bit-exact."""
-    if kind == "spec_loop":
-        wl = recipes.spec_loop_workload("spec_loop_full", rounds=2, seed=5)
+    if kind.startswith("spec_loop"):
+        wl = recipes.spec_loop_workload("spec_loop_full", rounds=2, seed=5, one_launch=kind == "spec_loop_one_launch")
         per_op = 64
     else:
         wl = recipes.mcts_loop_workload("search_loop_full", iterations=40, seed=6,

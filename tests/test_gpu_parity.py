@@ -469,17 +469,18 @@ def test_generation_loop_plan_update(kind, layers):
     assert counters[1]["plans_built"] < counters[0]["plans_built"]
 
 
-@pytest.mark.parametrize("kind", ["spec_loop", "mcts_loop", "mcts_loop_one_launch"])
+@pytest.mark.parametrize("kind", ["spec_loop", "spec_loop_one_launch", "mcts_loop", "mcts_loop_one_launch"])
 def test_loop_recipes_match_oracle(kind):
     """The multi-round speculative loop (6 rounds of forking at unaligned
     lengths, drafts in fresh blocks, verify, rollback by truncation, a bonus
-    token) and the tree-search loop (60 simulations with terminal
-    re-evaluations; also with each expansion's new nodes reserved and written
-    by the decode call), replayed through the library: every attention call
-    matches the oracle; tables and free blocks are bit-exact."""
-    if kind == "spec_loop":
+    token; also with the drafts reserved and written by the verify call) and
+    the tree-search loop (60 simulations with terminal re-evaluations; also
+    with each expansion's new nodes reserved and written by the decode call),
+    replayed through the library: every attention call matches the oracle;
+    tables and free blocks are bit-exact."""
+    if kind.startswith("spec_loop"):
         wl = recipes.spec_loop_workload("spec_loop_small", q_heads=8, kv_heads=2, requests=5, prefix=40, paths=3,
-                                        drafts=5, rounds=6, seed=3)
+                                        drafts=5, rounds=6, seed=3, one_launch=kind == "spec_loop_one_launch")
     else:
         wl = recipes.mcts_loop_workload("mcts_loop_small", q_heads=8, kv_heads=2, root_tokens=40, branching=3,
                                         depth=4, iterations=60, node_tokens=5, seed=4,
@@ -700,6 +701,124 @@ def test_decode_with_several_new_tokens_written_in_the_call(dtype, layers, head_
         assert torch.equal(pools["fused"][k][1], pools["plain"][k][1])
 
 
+def _draft_verify_workload(name, dtype, layers, head_dim, rounds, seed):
+    """3 requests (prefixes of 37, 50 and 70 tokens); each round every request's
+    head forks into 2 or 3 draft paths (alternating by request and round), each
+    path reserves n drafts (n cycling over 1, 3, 8, 16, 5; a path's drafts open
+    a block of its new node) and per layer one verify_new verifies them; then
+    each request keeps its first path truncated to its head's length plus
+    n // 2 + 1 drafts, releases the others and appends one bonus token (with
+    K/V)."""
+    ops, nxt, call, qcall = [], [0], 0, 0
+
+    def nm():
+        nxt[0] += 1
+        return nxt[0] - 1
+    heads, lens = [], []
+    for L in (37, 50, 70):
+        h = nm()
+        ops += [("new", h), ("append", h, L, call)]
+        call += 1
+        heads.append(h)
+        lens.append(L)
+    cycle = [1, 3, 8, 16, 5]
+    for rnd in range(rounds):
+        paths, ns, kids_of = [], [], []
+        for r, h in enumerate(heads):
+            kids = [nm() for _ in range(2 + (rnd + r) % 2)]
+            ops += [("fork", h, len(kids), kids), ("release", h)]
+            kids_of.append(kids)
+            for i, c in enumerate(kids):
+                paths.append(c)
+                ns.append(cycle[(rnd + r + i) % len(cycle)])
+        ops.append(("reserve_batch", list(paths), call, list(ns)))
+        for layer in range(layers):
+            ops.append(("verify_new", layer, list(paths), list(ns), call, qcall))
+            qcall += 1
+        call += 1
+        at = 0
+        for r, kids in enumerate(kids_of):
+            keep = ns[at] // 2 + 1
+            ops.append(("truncate", kids[0], lens[r] + keep))
+            lens[r] += keep + 1
+            for c in kids[1:]:
+                ops.append(("release", c))
+            heads[r] = kids[0]
+            at += len(kids)
+        ops.append(("append_batch", list(heads), [1] * len(heads), call))
+        call += 1
+    return recipes.Workload(name=name, dtype=dtype, layers=layers, q_heads=8, kv_heads=2, head_dim=head_dim,
+                            num_blocks=1024, ops=ops, seed=seed)
+
+
+@pytest.mark.parametrize("one_launch", [1, 0])
+@pytest.mark.parametrize("dtype,layers,head_dim", [("bf16", 1, 128), ("bf16", 2, 64), ("f32", 2, 128), ("f32", 1, 64)])
+def test_verify_with_new_tokens_written_in_the_call(dtype, layers, head_dim, one_launch):
+    """tkv_attend_verify_new_tokens: each round the draft paths reserve 1 to 16
+    tokens and per layer the verify call writes their K/V -- from the attention
+    launch itself (one_launch = 1) or from a preparation launch -- and verifies
+    them; then accept or roll back by truncation and a bonus token.  Every
+    call matches the oracle; outputs and pool contents equal, bit for bit,
+    those of the same rounds run as a batched append with K/V followed by
+    tkv_attend_verify."""
+    torch = need_gpu()
+    from tree_structured_copy_amd import tkv
+    from tree_structured_copy_amd.replay import LibReplay
+    import dataclasses
+    wl = _draft_verify_workload("drafts_%s_%d_%d" % (dtype, layers, head_dim), dtype, layers, head_dim, 8, 86)
+    assert_close(run_both(wl, options={tkv.TKV_OPT_FUSED_NEW_TOKEN: one_launch}), wl.dtype)
+    plain_ops = []
+    for op in wl.ops:
+        if op[0] == "reserve_batch":
+            plain_ops.append(("append_batch", op[1], op[3], op[2]))
+        elif op[0] == "verify_new":
+            plain_ops.append(("verify", op[1], op[2], op[3], op[-1]))
+        else:
+            plain_ops.append(op)
+    plain = dataclasses.replace(wl, ops=plain_ops)
+    outs, pools = {}, {}
+    for key, w in (("fused", wl), ("plain", plain)):
+        lib = LibReplay(w)
+        tkv.tkv_set_option(lib.c, tkv.TKV_OPT_FUSED_NEW_TOKEN, one_launch)
+        try:
+            got = []
+            for op in w.ops:
+                if op[0] in ("verify", "verify_new"):
+                    got.append(lib.attend(op).cpu())
+                    if op[0] == "verify_new":
+                        names = tkv.tkv_last_kernels(lib.c)
+                        attn = [n for n in names if n.startswith(("attn_partial_kernel", "attn_rows_kernel"))]
+                        prep = [n for n in names if n.startswith(("decode_prep_kernel", "plan_patch"))]
+                        assert attn, names
+                        if one_launch:
+                            assert not prep and all("NewTokens" in n for n in attn), names
+                        else:
+                            assert prep and not any("NewTokens" in n for n in attn), names
+                lib.apply(op)
+            torch.cuda.synchronize()
+            outs[key] = got
+            views = {}
+            for name in sorted(lib.h):
+                L = tkv.tkv_seq_len(lib.c, lib.h[name])
+                for layer in range(w.layers):
+                    ko = torch.empty((L, w.kv_heads, w.head_dim), dtype=torch.bfloat16 if w.dtype == "bf16"
+                                     else torch.float32, device="cuda")
+                    vo = torch.empty_like(ko)
+                    tkv.tkv_gather(lib.c, lib.h[name], layer, ko, vo, torch.cuda.current_stream())
+                    views[(name, layer)] = (ko.cpu(), vo.cpu())
+            torch.cuda.synchronize()
+            pools[key] = views
+        finally:
+            lib.close()
+    assert len(outs["fused"]) == 8 * layers
+    for a, b in zip(outs["fused"], outs["plain"]):
+        assert torch.equal(a, b)
+    assert pools["fused"].keys() == pools["plain"].keys()
+    for k in pools["fused"]:
+        assert torch.equal(pools["fused"][k][0], pools["plain"][k][0])
+        assert torch.equal(pools["fused"][k][1], pools["plain"][k][1])
+
+
 def test_decode_with_several_new_tokens_refusals():
     """tkv_attend_decode_new_tokens refuses, before any launch, a count outside
     1..16 and tokens that would reach into an earlier block (TKV_E_RANGE)."""
@@ -761,7 +880,7 @@ def test_decode_with_new_token_refusals():
 @pytest.mark.parametrize("requests,one_launch", [(45, 0), (45, 1), (80, 1)])
 def test_decode_with_new_token_more_than_128_handles(requests, one_launch):
     """135 branches in one fused decode call: its tokens are written by the
-    attention launch (one_launch = 1, up to 160 tokens) or by two preparation
+    attention launch (one_launch = 1, up to 192 tokens) or by two preparation
     launches (128 + 7), the first also carrying the plan's changed words; 240
     branches are more than one attention launch carries, so preparation
     launches write them even with one_launch = 1.  Every call matches the

@@ -484,9 +484,11 @@ def test_append_batch_refusals_change_nothing():
         tkv.tkv_destroy(c)
 
 
-@pytest.mark.parametrize("kind", ["spec_loop", "mcts_loop"])
+@pytest.mark.parametrize("kind", ["spec_loop", "spec_loop_one_launch", "mcts_loop", "mcts_loop_one_launch"])
 def test_replay_bench_host_mode_matches_the_oracle(kind, tmp_path):
-    """The native replayer (replay_bench), run host-only on the loop recipes:
+    """The native replayer (replay_bench), run host-only on the loop recipes
+    (with the new tokens appended before the attention calls, or reserved and
+    written by them):
     its block high-water mark after time_begin equals the oracle allocator's
     over the same operations, its call, query, token and fork counts equal the
     recipe's, and its full-copy figure is the sum over forks of n x the
@@ -495,11 +497,13 @@ def test_replay_bench_host_mode_matches_the_oracle(kind, tmp_path):
     exe = os.path.join(ROOT, "tree_structured_copy_amd", "replay_bench")
     if not os.path.exists(exe):
         pytest.skip("replay_bench not built")
-    if kind == "spec_loop":
-        wl = recipes.spec_loop_workload("s", requests=5, prefix=40, paths=3, drafts=5, rounds=6, seed=3)
+    one = kind.endswith("one_launch")
+    if kind.startswith("spec_loop"):
+        wl = recipes.spec_loop_workload("s", requests=5, prefix=40, paths=3, drafts=5, rounds=6, seed=3,
+                                        one_launch=one)
     else:
         wl = recipes.mcts_loop_workload("m", root_tokens=40, branching=3, depth=4, iterations=60,
-                                        node_tokens=5, seed=4)
+                                        node_tokens=5, seed=4, one_launch=one)
     path = tmp_path / "ops.txt"
     path.write_text(recipes.ops_text(wl))
     r = subprocess.run([exe, str(path), "--host"], capture_output=True, text=True, timeout=120)
@@ -521,10 +525,11 @@ def test_replay_bench_host_mode_matches_the_oracle(kind, tmp_path):
         elif k == "append":
             o.append(names[op[1]], op[2])
             appended += op[2] if timed else 0
-        elif k == "append_batch":
-            for h, n in zip(op[1], op[2]):
+        elif k in ("append_batch", "reserve_batch"):
+            ns = op[2] if k == "append_batch" else (op[3] if len(op) > 3 else [1] * len(op[1]))
+            for h, n in zip(op[1], ns):
                 o.append(names[h], n)
-            appended += sum(op[2]) if timed else 0
+            appended += sum(ns) if timed else 0
         elif k == "fork":
             if timed:
                 full_copy += op[2] * o.length(names[op[1]])
@@ -535,10 +540,10 @@ def test_replay_bench_host_mode_matches_the_oracle(kind, tmp_path):
             o.release(names.pop(op[1]))
         elif k == "truncate":
             o.truncate(names[op[1]], op[2])
-        elif k == "decode":
+        elif k in ("decode", "decode_new"):
             calls += 1
             queries += len(op[2])
-        elif k == "verify":
+        elif k in ("verify", "verify_new"):
             calls += 1
             vtokens += sum(op[3])
         if timed:

@@ -52,6 +52,8 @@ def _wl():
         ("verify", 0, [1, 3], [2, 2], 106),
         ("reserve_batch", [3, 1], 6, [2, 3]),
         ("decode_new", 1, [3, 1], 6, [2, 3], 107),
+        ("reserve_batch", [1, 3], 7, [2, 1]),
+        ("verify_new", 0, [1, 3], [2, 1], 7, 108),
     ]
     return recipes.Workload(name="replay_pin", dtype="f32", layers=LAYERS, q_heads=HQ, kv_heads=HKV, head_dim=D,
                             num_blocks=64, ops=ops, seed=11, block_size=4)
@@ -101,6 +103,10 @@ def _expected_cases(wl):
     h3 = _cat(h3, _rows(R6, 0, 2))
     h1 = _cat(h1, _rows(R6, 2, 5))
     cases[107] = ([(3, 12), (1, 10)], {1: h1, 3: h3})
+    R7 = _call(wl, 7, 3)      # reserved with counts [2, 1] in batch order [1, 3], then verified
+    h1 = _cat(h1, _rows(R7, 0, 2))
+    h3 = _cat(h3, _rows(R7, 2, 3))
+    cases[108] = ([(1, 11), (1, 12), (3, 13)], {1: h1, 3: h3})
     return cases
 
 
@@ -127,7 +133,7 @@ def pin_replay_outputs():
     orc = OracleReplay(wl)
     seen = 0
     for op in wl.ops:
-        if op[0] in ("decode", "decode_new", "verify"):
+        if op[0] in ("decode", "decode_new", "verify", "verify_new"):
             qcall = op[-1]
             rows, hist = cases[qcall]
             assert orc.query_rows(op) == rows, (qcall, orc.query_rows(op))
@@ -157,7 +163,7 @@ def test_replay_tables_follow_the_recipe():
     orc = OracleReplay(wl)
     for op in wl.ops:
         orc.apply(op)
-    lens = {1: 11, 2: 9, 3: 13}
+    lens = {1: 13, 2: 9, 3: 14}
     used = set()
     for h, L in lens.items():
         tab = orc.alloc.table(orc.h_alloc[h])

@@ -491,10 +491,9 @@ hipError_t launch_w(int tiles, int waves, const AttnArgs& args, const X& x, int3
 template <class P, int D>
 hipError_t launch_c(int tiles, int waves, bool causal, const AttnArgs& args, const NewTokens* nt, int32_t n_items,
                     hipStream_t s) {
-  if (nt) {
-    if (causal) return hipErrorInvalidValue;
-    return launch_w<P, D, false, NewTokens>(tiles, waves, args, *nt, n_items, s);
-  }
+  if (nt)
+    return causal ? launch_w<P, D, true, NewTokens>(tiles, waves, args, *nt, n_items, s)
+                  : launch_w<P, D, false, NewTokens>(tiles, waves, args, *nt, n_items, s);
   return causal ? launch_w<P, D, true, NoNewTokens>(tiles, waves, args, NoNewTokens{}, n_items, s)
                 : launch_w<P, D, false, NoNewTokens>(tiles, waves, args, NoNewTokens{}, n_items, s);
 }

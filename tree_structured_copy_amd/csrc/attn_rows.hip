@@ -425,10 +425,9 @@ hipError_t launch_shape(int tiles, const AttnArgs& args, const X& x, int32_t n_i
 template <class P, int D>
 hipError_t launch_c(int tiles, bool causal, const AttnArgs& args, const NewTokens* nt, int32_t n_items, hipStream_t s,
                     int cus) {
-  if (nt) {
-    if (causal) return hipErrorInvalidValue;
-    return launch_shape<P, D, false, NewTokens>(tiles, args, *nt, n_items, s, cus);
-  }
+  if (nt)
+    return causal ? launch_shape<P, D, true, NewTokens>(tiles, args, *nt, n_items, s, cus)
+                  : launch_shape<P, D, false, NewTokens>(tiles, args, *nt, n_items, s, cus);
   return causal ? launch_shape<P, D, true, NoNewTokens>(tiles, args, NoNewTokens{}, n_items, s, cus)
                 : launch_shape<P, D, false, NoNewTokens>(tiles, args, NoNewTokens{}, n_items, s, cus);
 }

@@ -1043,6 +1043,14 @@ int tkv_attend_decode_new_tokens(tkv_cache* c, int32_t layer, const tkv_seq* seq
   return attend(c, layer, seqs, nullptr, nseq, q, out, ws, ws_bytes, stream, k_new, v_new, false, ntok);
 }
 
+int tkv_attend_verify_new_tokens(tkv_cache* c, int32_t layer, const tkv_seq* seqs, const int32_t* nq, int32_t nseq,
+                                 const void* k_new, const void* v_new, const void* q, float* out, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!k_new || !v_new || !nq) return TKV_E_INVAL;
+  // the verified tokens are the new ones: handle i's last nq[i]
+  return attend(c, layer, seqs, nq, nseq, q, out, ws, ws_bytes, stream, k_new, v_new, false, nq);
+}
+
 int tkv_attend_decode_noalloc(tkv_cache* c, int32_t layer, const tkv_seq* seqs, int32_t nseq, const void* q,
                               float* out, void* stream) {
   return attend(c, layer, seqs, nullptr, nseq, q, out, nullptr, 0, stream, nullptr, nullptr, true);

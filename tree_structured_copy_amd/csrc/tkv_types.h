@@ -137,7 +137,7 @@ struct IdPatch {
 };
 // Up to this many new tokens and id patches travel in an attention launch's
 // arguments (with AttnArgs, within the 4 KiB kernel-argument limit).
-constexpr int kFusedMaxTokens = 160;
+constexpr int kFusedMaxTokens = 192;
 constexpr int kMaxIdPatches = 64;
 struct NewTokens {
   static constexpr bool kActive = true;

@@ -84,7 +84,7 @@ class LibReplay:
         elif kind == "truncate":
             _, h, L = op
             tkv.tkv_truncate(self.c, self.h[h], L)
-        elif kind in ("decode", "decode_new", "verify", "time_begin"):
+        elif kind in ("decode", "decode_new", "verify", "verify_new", "time_begin"):
             pass
         else:
             raise ValueError(kind)
@@ -92,7 +92,7 @@ class LibReplay:
     def build(self, stop_at_attend: bool = True):
         """Apply ops up to (not including) the first decode/verify; returns its index."""
         for i, op in enumerate(self.wl.ops):
-            if stop_at_attend and op[0] in ("decode", "decode_new", "verify"):
+            if stop_at_attend and op[0] in ("decode", "decode_new", "verify", "verify_new"):
                 return i
             self.apply(op)
         return len(self.wl.ops)
@@ -102,12 +102,12 @@ class LibReplay:
         return [self.h[x] for x in op[2]]
 
     def nrows(self, op) -> int:
-        return sum(op[3]) if op[0] == "verify" else len(op[2])
+        return sum(op[3]) if op[0] in ("verify", "verify_new") else len(op[2])
 
     def workspace(self, op):
         import torch
         seqs = self.handles(op)
-        nq = op[3] if op[0] == "verify" else None
+        nq = op[3] if op[0] in ("verify", "verify_new") else None
         need = tkv.tkv_workspace_size(self.c, seqs, nq)
         if need and (self._ws is None or self._ws.numel() < need):
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
@@ -138,6 +138,14 @@ class LibReplay:
                 tkv.tkv_attend_decode_new_tokens(self.c, op[1], self.handles(op), ns, k, v, q, out, ws, need, stream)
             else:
                 tkv.tkv_attend_decode_new_token(self.c, op[1], self.handles(op), k, v, q, out, ws, need, stream)
+        elif op[0] == "verify_new":
+            # the verified tokens are the reserved ones: their K/V of this layer
+            # are rows of batched append call op[4], in batch order
+            from workloads import gen
+            total = sum(op[3])
+            k = wdev.kv_tensor(wl, op[4], total, gen.KIND_K, self.device)[op[1]].contiguous()
+            v = wdev.kv_tensor(wl, op[4], total, gen.KIND_V, self.device)[op[1]].contiguous()
+            tkv.tkv_attend_verify_new_tokens(self.c, op[1], self.handles(op), op[3], k, v, q, out, ws, need, stream)
         else:
             tkv.tkv_attend_verify(self.c, op[1], self.handles(op), op[3], q, out, ws, need, stream)
         return out

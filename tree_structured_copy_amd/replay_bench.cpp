@@ -93,7 +93,7 @@ class Replayer {
         max_src = std::max(max_src, t);
       }
       if (op.kind == "decode" || op.kind == "decode_new") max_rows = std::max(max_rows, op.a[1]);
-      if (op.kind == "verify") {
+      if (op.kind == "verify" || op.kind == "verify_new") {
         int64_t t = 0;
         for (int64_t i = 0; i < op.a[1]; ++i) t += op.a[3 + 2 * i];
         max_rows = std::max(max_rows, t);
@@ -216,6 +216,32 @@ class Replayer {
         check(tkv_attend_decode_new_tokens(cache, static_cast<int32_t>(a[0]), seqs.data(), counts.data(), n, ksrc_,
                                            vsrc_, q_, static_cast<float*>(out_), ws_, ws_cap_, stream_),
               "tkv_attend_decode_new_tokens");
+      } else if (op.kind == "verify_new") {
+        // the reserved drafts' K/V of this layer (the constant-filled source
+        // rows), written and verified in one call
+        seqs.clear();
+        counts.clear();
+        int64_t rows = 0;
+        for (int64_t i = 0; i < a[1]; ++i) {
+          seqs.push_back(h[a[2 + 2 * i]]);
+          counts.push_back(static_cast<int32_t>(a[3 + 2 * i]));
+          rows += a[3 + 2 * i];
+        }
+        const int32_t n = static_cast<int32_t>(seqs.size());
+        ++st.attend_calls;
+        st.verify_tokens += rows;
+        size_t need = 0;
+        check(tkv_workspace_size(cache, seqs.data(), counts.data(), n, &need), "tkv_workspace_size");
+        if (host_) continue;
+        if (need > ws_cap_) {
+          if (ws_) hip_check(hipStreamSynchronize(stream_), "hipStreamSynchronize");
+          if (ws_) (void)hipFree(ws_);
+          ws_cap_ = need + need / 4;
+          hip_check(hipMalloc(&ws_, ws_cap_), "hipMalloc");
+        }
+        check(tkv_attend_verify_new_tokens(cache, static_cast<int32_t>(a[0]), seqs.data(), counts.data(), n, ksrc_,
+                                           vsrc_, q_, static_cast<float*>(out_), ws_, ws_cap_, stream_),
+              "tkv_attend_verify_new_tokens");
       } else if (op.kind == "fork") {
         const int32_t n = static_cast<int32_t>(a[1]);
         int64_t len = 0;

@@ -116,6 +116,7 @@ _SIGS = {
     "tkv_attend_verify": [_P, _I32, _pU64, _pI32, _I32, _P, _P, _P, _SZ, _P],
     "tkv_attend_decode_new_token": [_P, _I32, _pU64, _I32, _P, _P, _P, _P, _P, _SZ, _P],
     "tkv_attend_decode_new_tokens": [_P, _I32, _pU64, ctypes.POINTER(_I32), _I32, _P, _P, _P, _P, _P, _SZ, _P],
+    "tkv_attend_verify_new_tokens": [_P, _I32, _pU64, ctypes.POINTER(_I32), _I32, _P, _P, _P, _P, _P, _SZ, _P],
     "tkv_attend_decode_noalloc": [_P, _I32, _pU64, _I32, _P, _P, _P],
     "tkv_gather": [_P, _U64, _I32, _P, _P, _P],
     "tkv_seq_len": [_P, _U64, ctypes.POINTER(_I64)],
@@ -270,6 +271,15 @@ def tkv_attend_verify(c, layer: int, seqs, nq, q, out, ws=None, ws_bytes: int = 
     na = i32_array(nq)
     _check(_lib.tkv_attend_verify(c, layer, sa, na, len(sa), _ptr(q), _ptr(out), _ptr(ws), ws_bytes,
                                   _stream(stream)), "tkv_attend_verify")
+
+
+def tkv_attend_verify_new_tokens(c, layer: int, seqs, nq, k_new, v_new, q, out, ws=None, ws_bytes: int = 0,
+                                 stream=None) -> None:
+    sa = seq_array(seqs)
+    na = i32_array(nq)
+    _check(_lib.tkv_attend_verify_new_tokens(c, layer, sa, na, len(sa), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                             _ptr(out), _ptr(ws), ws_bytes, _stream(stream)),
+           "tkv_attend_verify_new_tokens")
 
 
 def tkv_gather(c, s: int, layer: int, k_out, v_out, stream=None) -> None:

@@ -32,6 +32,10 @@ Operations:
   ``(KIND_Q, qcall)``, laid out ``[n][q_heads][head_dim]``
 * ``("verify", layer, [h...], [nq...], qcall)`` -- the last ``nq[i]`` positions of each
   handle are queries; Q laid out ``[sum nq][q_heads][head_dim]``
+* ``("verify_new", layer, [h...], [nq...], call, qcall)`` -- as ``verify``, where the
+  queried tokens are the ones ``reserve_batch`` ``call`` reserved with counts ``nq``:
+  the call writes layer ``layer`` of their K/V and verifies them
+  (``tkv_attend_verify_new_tokens``)
 
 The tree shapes follow the fork-based decoding strategies of the Dendrite
 article (ainews.cool, "technical deep dive" and its Table 1: width-4 fork
@@ -71,7 +75,7 @@ class Workload:
         return 4 if self.dtype == "f32" else 2
 
     def attend_ops(self):
-        return [op for op in self.ops if op[0] in ("decode", "decode_new", "verify")]
+        return [op for op in self.ops if op[0] in ("decode", "decode_new", "verify", "verify_new")]
 
 
 class _Names:
@@ -273,7 +277,8 @@ def decode_loop_workload(name: str, *, dtype: str = "bf16", layers: int = 1, q_h
 
 def spec_loop_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_heads: int = 8,
                        head_dim: int = 128, requests: int = 64, prefix: int = 2048, paths: int = 3,
-                       drafts: int = 8, rounds: int = 8, seed: int = 0, description: str = "") -> Workload:
+                       drafts: int = 8, rounds: int = 8, seed: int = 0, one_launch: bool = False,
+                       description: str = "") -> Workload:
     """The multi-round speculative loop: per request, P = new; append(P, prefix).
     Each round: every request forks P into ``paths`` draft paths and releases P;
     one append_batch gives every path ``drafts`` tokens; one verify covers every
@@ -284,7 +289,9 @@ def spec_loop_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_
     token the target model emits after its accepted drafts.  Path a is the next
     round's P.  From the second round on the forks fall at unaligned lengths,
     so a fork point's partial block is shared, frozen, and each path's drafts
-    start a fresh block."""
+    start a fresh block.  With ``one_launch`` the drafts are reserved instead
+    (``reserve_batch``) and written by the verify call itself (``verify_new``),
+    as a target model computes the drafts' K/V in the pass that verifies them."""
     nm = _Names()
     ops: List[tuple] = []
     call = 0
@@ -305,8 +312,12 @@ def spec_loop_workload(name: str, *, dtype: str = "bf16", q_heads: int = 32, kv_
             ops.append(("release", p))
             kids.append(ks)
         allk = [h for ks in kids for h in ks]
-        ops.append(("append_batch", allk, [drafts] * len(allk), call)); call += 1
-        ops.append(("verify", 0, allk, [drafts] * len(allk), qcall)); qcall += 1
+        if one_launch:
+            ops.append(("reserve_batch", allk, call, [drafts] * len(allk)))
+            ops.append(("verify_new", 0, allk, [drafts] * len(allk), call, qcall)); call += 1; qcall += 1
+        else:
+            ops.append(("append_batch", allk, [drafts] * len(allk), call)); call += 1
+            ops.append(("verify", 0, allk, [drafts] * len(allk), qcall)); qcall += 1
         nxt = []
         for r, ks in enumerate(kids):
             st = gen.stream_id(gen.KIND_ACCEPT, 100000 * (rnd + 1) + r)
@@ -390,7 +401,8 @@ def ops_text(wl: Workload) -> str:
     ``new h``, ``append h ntok``, ``append_batch n h1 n1 ... hn nn``,
     ``fork h n c1 ... cn``, ``release h``, ``truncate h len``, ``time_begin``,
     ``decode layer n h1 ... hn``, ``verify layer n h1 q1 ... hn qn``,
-    ``reserve_batch n h1 n1 ... hn nn``, ``decode_new layer n h1 n1 ... hn nn``.  K/V/Q
+    ``reserve_batch n h1 n1 ... hn nn``, ``decode_new layer n h1 n1 ... hn nn``,
+    ``verify_new layer n h1 q1 ... hn qn``.  K/V/Q
     values are not carried: the replayer measures time and memory, while the
     parity tests replay the same recipe against the oracle."""
     out = ["config %d %d %d %d %d %d" % (wl.layers, wl.q_heads, wl.kv_heads, wl.head_dim, wl.num_blocks,
@@ -421,6 +433,8 @@ def ops_text(wl: Workload) -> str:
         elif k == "decode_new":
             ns = op[4] if len(op) > 5 else [1] * len(op[2])
             out.append("decode_new %d %d %s" % (op[1], len(op[2]), " ".join("%d %d" % x for x in zip(op[2], ns))))
+        elif k == "verify_new":
+            out.append("verify_new %d %d %s" % (op[1], len(op[2]), " ".join("%d %d" % x for x in zip(op[2], op[3]))))
         else:
             raise ValueError(k)
     return "\n".join(out) + "\n"
