@@ -44,22 +44,22 @@ KERNEL_SOURCES = {
 }
 TRAFFIC_RECORDS = {
     "full_depth": {"kernel": "attn_rows_kernel<BF16, 128, 1, 4, 1, 2, false, 2, false>",
-                   "sources_sha256": "460763e2eda4bffef08b13ca6bbe8e00a01d89ceae545f17545ea4f667e59852",
-                   "fetch_kib_per_launch": 1581688.3125, "fetch_factor": 1.99992, "write_kib_per_launch": 16384.0,
-                   "write_factor": 1.0, "hbm_bytes_per_launch": 3255945308},
+                   "sources_sha256": "fd448e0d27bf219a33c1df2eab9b2eb0d33d0e73e319fa3a77d76179a5582f72",
+                   "fetch_kib_per_launch": 1581694.84375, "fetch_factor": 1.99992, "write_kib_per_launch": 16384.0,
+                   "write_factor": 1.0, "hbm_bytes_per_launch": 3255958684},
     "llama_fork": {"kernel": "attn_partial_kernel<BF16, 128, 1, 2, false>",
-                   "sources_sha256": "fbc7f38d714e710f48d26dfa0847ee8ef34298b0a8ffe11c720e1b9d881472bd",
-                   "fetch_kib_per_launch": 281850.03125, "fetch_factor": 1.99992, "write_kib_per_launch": 2048.0,
-                   "write_factor": 1.0, "hbm_bytes_per_launch": 579302927},
+                   "sources_sha256": "645721a831f3992a9adb5707111340e8a6e71f5cfe46b4e567453efa1005d5e7",
+                   "fetch_kib_per_launch": 281861.6875, "fetch_factor": 1.99992, "write_kib_per_launch": 2048.0,
+                   "write_factor": 1.0, "hbm_bytes_per_launch": 579326798},
     "spec_verify": {"kernel": "attn_rows_kernel<BF16, 128, 1, 6, 2, 2, false, 3, true>",
-                    "sources_sha256": "460763e2eda4bffef08b13ca6bbe8e00a01d89ceae545f17545ea4f667e59852",
-                    "fetch_kib_per_launch": 275007.84375, "fetch_factor": 1.99992, "write_kib_per_launch": 24576.0,
-                    "write_factor": 1.0, "hbm_bytes_per_launch": 588359359},
+                    "sources_sha256": "fd448e0d27bf219a33c1df2eab9b2eb0d33d0e73e319fa3a77d76179a5582f72",
+                    "fetch_kib_per_launch": 275004.96875, "fetch_factor": 1.99992, "write_kib_per_launch": 24576.0,
+                    "write_factor": 1.0, "hbm_bytes_per_launch": 588353472},
     # the attention kernel alone; its merge kernel adds 20.2 MB fetched and 4.2 MB written
     "mcts_tree": {"kernel": "attn_rows_kernel<BF16, 128, 1, 8, 1, 2, false, 4, false>",
-                  "sources_sha256": "460763e2eda4bffef08b13ca6bbe8e00a01d89ceae545f17545ea4f667e59852",
-                  "fetch_kib_per_launch": 87226.40625, "fetch_factor": 1.99992, "write_kib_per_launch": 18703.75,
-                  "write_factor": 1.0, "hbm_bytes_per_launch": 197785174},
+                  "sources_sha256": "fd448e0d27bf219a33c1df2eab9b2eb0d33d0e73e319fa3a77d76179a5582f72",
+                  "fetch_kib_per_launch": 87175.40625, "fetch_factor": 1.99992, "write_kib_per_launch": 18703.75,
+                  "write_factor": 1.0, "hbm_bytes_per_launch": 197680731},
 }
 
 
