@@ -44,22 +44,22 @@ KERNEL_SOURCES = {
 }
 TRAFFIC_RECORDS = {
     "full_depth": {"kernel": "attn_rows_kernel<BF16, 128, 1, 4, 1, 2, false, 2, false>",
-                   "sources_sha256": "fd448e0d27bf219a33c1df2eab9b2eb0d33d0e73e319fa3a77d76179a5582f72",
-                   "fetch_kib_per_launch": 1581694.84375, "fetch_factor": 1.99992, "write_kib_per_launch": 16384.0,
-                   "write_factor": 1.0, "hbm_bytes_per_launch": 3255958684},
+                   "sources_sha256": "f18ed1514ed7580fdce3c054154e9d295ea62dd48a184a0a25801d821996d62c",
+                   "fetch_kib_per_launch": 1581696.0625, "fetch_factor": 1.99992, "write_kib_per_launch": 16384.0,
+                   "write_factor": 1.0, "hbm_bytes_per_launch": 3255961179},
     "llama_fork": {"kernel": "attn_partial_kernel<BF16, 128, 1, 2, false>",
-                   "sources_sha256": "645721a831f3992a9adb5707111340e8a6e71f5cfe46b4e567453efa1005d5e7",
-                   "fetch_kib_per_launch": 281861.6875, "fetch_factor": 1.99992, "write_kib_per_launch": 2048.0,
-                   "write_factor": 1.0, "hbm_bytes_per_launch": 579326798},
+                   "sources_sha256": "18ada46400e7718bc79ffb2a2e66d895f5cc0184f81e2f84198b43b34822585e",
+                   "fetch_kib_per_launch": 281803.8125, "fetch_factor": 1.99992, "write_kib_per_launch": 2048.0,
+                   "write_factor": 1.0, "hbm_bytes_per_launch": 579208275},
     "spec_verify": {"kernel": "attn_rows_kernel<BF16, 128, 1, 6, 2, 2, false, 3, true>",
-                    "sources_sha256": "fd448e0d27bf219a33c1df2eab9b2eb0d33d0e73e319fa3a77d76179a5582f72",
-                    "fetch_kib_per_launch": 275004.96875, "fetch_factor": 1.99992, "write_kib_per_launch": 24576.0,
-                    "write_factor": 1.0, "hbm_bytes_per_launch": 588353472},
+                    "sources_sha256": "f18ed1514ed7580fdce3c054154e9d295ea62dd48a184a0a25801d821996d62c",
+                    "fetch_kib_per_launch": 275007.46875, "fetch_factor": 1.99992, "write_kib_per_launch": 24576.0,
+                    "write_factor": 1.0, "hbm_bytes_per_launch": 588358591},
     # the attention kernel alone; its merge kernel adds 20.2 MB fetched and 4.2 MB written
     "mcts_tree": {"kernel": "attn_rows_kernel<BF16, 128, 1, 8, 1, 2, false, 4, false>",
-                  "sources_sha256": "fd448e0d27bf219a33c1df2eab9b2eb0d33d0e73e319fa3a77d76179a5582f72",
-                  "fetch_kib_per_launch": 87175.40625, "fetch_factor": 1.99992, "write_kib_per_launch": 18703.75,
-                  "write_factor": 1.0, "hbm_bytes_per_launch": 197680731},
+                  "sources_sha256": "f18ed1514ed7580fdce3c054154e9d295ea62dd48a184a0a25801d821996d62c",
+                  "fetch_kib_per_launch": 86828.59375, "fetch_factor": 1.99992, "write_kib_per_launch": 18703.75,
+                  "write_factor": 1.0, "hbm_bytes_per_launch": 196970487},
 }
 
 

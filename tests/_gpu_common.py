@@ -93,4 +93,5 @@ def run_both(wl, sample=None, options=None, extra_blocks=0, check_tables=True, t
 
 def assert_close(results, dtype):
     for kind, err, n in results:
+        say("max abs error %.3e over %d outputs (%s, %s)" % (err, n, kind, dtype))
         assert err <= TOL[dtype], (kind, err)

@@ -6,6 +6,8 @@ truncations, block reuse and both dtypes.  Tolerances: max-abs 1e-5 (fp32) and
 2e-3 (bf16 inputs, fp32 accumulation).
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -34,6 +36,23 @@ def test_small_verify(dtype):
     wl = recipes.verify_workload("small_verify", dtype=dtype, q_heads=8, kv_heads=2, head_dim=128,
                                  requests=3, prefix=37, paths=3, drafts=5, seed=5)
     assert_close(run_both(wl), dtype)
+
+
+@pytest.mark.parametrize("q_scale", [2, 4])
+@pytest.mark.parametrize("kind,prefix", [("decode", 37), ("decode", 1100), ("verify", 300), ("verify", 1100)])
+def test_sharp_scores(kind, prefix, q_scale):
+    """Queries scaled by 2 and 4: score spreads 2 and 4 times wider, so weights
+    gather on a few keys, the case in which the P.V step must keep the low
+    parts of its bf16 weights; short and long contexts, every output against
+    the oracle."""
+    if kind == "decode":
+        wl = recipes.fork_workload("sharp_fork", dtype="bf16", layers=1, q_heads=16, kv_heads=4, head_dim=128,
+                                   requests=3, prefix=prefix, width=4, branch_tokens=21, seed=60 + q_scale)
+    else:
+        wl = recipes.verify_workload("sharp_verify", dtype="bf16", q_heads=16, kv_heads=4, head_dim=128,
+                                     requests=3, prefix=prefix, paths=3, drafts=8, seed=70 + q_scale)
+    wl = dataclasses.replace(wl, q_scale=q_scale)
+    assert_close(run_both(wl), "bf16")
 
 
 def test_small_mcts():

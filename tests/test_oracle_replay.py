@@ -16,6 +16,8 @@ keeps one token too many, a transposed generator index, a dropped last key)
 must each fail a pin.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -219,6 +221,17 @@ def pin_kv_slice():
                     t1 = int(r.integers(t0 + 1, ntok + 1))
                     np.testing.assert_array_equal(workloads.kv_slice(wl, call, ntok, kind, layer, kvh, t0, t1),
                                                   whole[layer, t0:t1, kvh, :])
+
+
+def test_query_scale_multiplies_every_query_value():
+    wl = recipes.verify_workload("qs", dtype="bf16", q_heads=4, kv_heads=2, head_dim=64, requests=1, prefix=5,
+                                 paths=2, drafts=3, seed=9)
+    base = workloads.q_values(wl, 3, 6)
+    for scale in (2, 4):
+        scaled = workloads.q_values(dataclasses.replace(wl, q_scale=scale), 3, 6)
+        assert np.array_equal(scaled, base * scale)
+    with pytest.raises(ValueError):
+        recipes.ops_text(dataclasses.replace(wl, q_scale=2))
 
 
 def test_kv_slice_is_a_slice_of_kv_values():

@@ -373,7 +373,8 @@ __global__ __launch_bounds__(64 * W) void attn_partial_kernel(AttnArgs a, X x) {
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = fast_exp2((sc[i] - mm) * sl2);
-      P::pv(v, p, acc[t], l[t]);
+      // the same expression on the lane's largest score: exactly its largest weight
+      P::pv(v, p, fast_exp2((bm - mm) * sl2), acc[t], l[t]);
     }
   };
 

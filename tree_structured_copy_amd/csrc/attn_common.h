@@ -56,6 +56,18 @@ __device__ inline void split_hi_lo(const float* p, bf16x8& hi, bf16x8& lo) {
   hi = bitcast<bf16x8>(h);
   lo = bitcast<bf16x8>(w);
 }
+// The hi part alone: bf16(p) for 8 fp32 weights, round to nearest even.
+__device__ inline void to_bf16(const float* p, bf16x8& hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  u32x4 h;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x2 pj = {p[2 * j], p[2 * j + 1]};
+    h[j] = bitcast<uint32_t>(__builtin_convertvector(pj, bf16x2));
+  }
+  hi = bitcast<bf16x8>(h);
+}
 
 // Wait states between an MFMA chain and the first VALU / accvgpr read of its
 // result.  For v_mfma_f32_16x16x4_f32 on gfx950 the compiler's hazard model
@@ -184,20 +196,31 @@ struct BF16 {
       v.av[dt] = u32x4{x.x, x.y, y.x, y.y};
     }
   }
-  // acc[dt] += V^T . P^T over the super-block's 8 tokens per lane group.  A
-  // weight p is split into bf16 hi + lo (split_hi_lo); one MFMA per d-tile
-  // takes the hi parts, one the lo parts, with the same A operand.
+  // acc[dt] += V^T . P^T over the super-block's 8 tokens per lane group.  Each
+  // weight p enters one MFMA per d-tile as bf16 hi = bf16(p) (relative error at
+  // most 2^-9).  While some lane of the wave holds a weight above kLoShare of
+  // its running sum l (the first super-blocks of a row, short contexts, weights
+  // gathered on a few keys), the remainder lo = bf16(p - hi) goes through a
+  // second MFMA per d-tile with the same A operand, carrying p to about 2^-17.
+  // Once every weight is a small share of its sum, the rounding errors of many
+  // comparable weights average out and hi alone stays far inside the output
+  // tolerance.  pmax is the largest of the lane's 8 weights.
+  static constexpr float kLoShare = 0.125f;
   template <int D>
-  __device__ static void pv(const VPair<D>& v, const float* p, f32x4* acc, float& l) {
+  __device__ static void pv(const VPair<D>& v, const float* p, float pmax, f32x4* acc, float& l) {
     l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     bf16x8 hi, lo;
-    split_hi_lo(p, hi, lo);
+    const bool with_lo = __any(pmax > kLoShare * l);
+    if (with_lo) split_hi_lo(p, hi, lo);
+    else to_bf16(p, hi);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(v.av[dt]), hi, acc[dt], 0, 0, 0);
+    if (with_lo) {
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(v.av[dt]), lo, acc[dt], 0, 0, 0);
+      for (int dt = 0; dt < D / 16; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(v.av[dt]), lo, acc[dt], 0, 0, 0);
+    }
   }
 };
 
@@ -255,8 +278,9 @@ struct F32 {
     load_tile_lds(v.a, va_addr, lane);
     load_tile_lds(v.b, va_addr + 16 * D * 4, lane);
   }
+  // full fp32 weights: pmax plays no part
   template <int D>
-  __device__ static void pv(const VPair<D>& v, const float* p, f32x4* acc, float& l) {
+  __device__ static void pv(const VPair<D>& v, const float* p, float pmax, f32x4* acc, float& l) {
     l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {

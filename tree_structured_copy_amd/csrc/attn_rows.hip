@@ -313,7 +313,8 @@ __global__ __launch_bounds__(64 * W * HPW, MINW) void attn_rows_kernel(AttnArgs 
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = fast_exp2((x[i] - mm) * sl2);
-      P::pv(vp, p, acc[t], l[t]);
+      // the same expression on the lane's largest score: exactly its largest weight
+      P::pv(vp, p, fast_exp2((bm - mm) * sl2), acc[t], l[t]);
       if constexpr (TPW > 1) __builtin_amdgcn_sched_barrier(0);  // one tile's weights live at a time
     }
   }

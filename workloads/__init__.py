@@ -31,5 +31,5 @@ def kv_slice(wl, call: int, ntok: int, kind: int, layer: int, kvh: int, t0: int,
 def q_values(wl, qcall: int, nrows: int) -> np.ndarray:
     """Query values of a decode/verify call: [nrows][q_heads][head_dim], float32."""
     n = nrows * wl.q_heads * wl.head_dim
-    v = gen.values_range(wl.seed, gen.stream_id(gen.KIND_Q, qcall), 0, n, wl.dtype)
+    v = gen.values_range(wl.seed, gen.stream_id(gen.KIND_Q, qcall), 0, n, wl.dtype) * np.float32(wl.q_scale)
     return v.reshape(nrows, wl.q_heads, wl.head_dim)

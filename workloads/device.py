@@ -65,4 +65,5 @@ def kv_tensor(wl, call: int, ntok: int, kind: int, device="cuda") -> torch.Tenso
 
 def q_tensor(wl, qcall: int, nrows: int, device="cuda") -> torch.Tensor:
     t = torch.empty((nrows, wl.q_heads, wl.head_dim), dtype=torch_dtype(wl.dtype), device=device)
-    return fill(t, wl.dtype, wl.seed, gen.stream_id(gen.KIND_Q, qcall))
+    t = fill(t, wl.dtype, wl.seed, gen.stream_id(gen.KIND_Q, qcall))
+    return t.mul_(wl.q_scale) if wl.q_scale != 1 else t

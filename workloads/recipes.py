@@ -67,6 +67,10 @@ class Workload:
     ops: List[tuple]
     seed: int = 0
     block_size: int = 16
+    # every query value is multiplied by this power of two (exact in bf16 and
+    # fp32): 2 or 4 give score spreads 2 or 4 times wider, weights gathered on
+    # fewer keys
+    q_scale: int = 1
     # descriptive fields (no effect on replay)
     description: str = ""
 
@@ -405,6 +409,8 @@ def ops_text(wl: Workload) -> str:
     ``verify_new layer n h1 q1 ... hn qn``.  K/V/Q
     values are not carried: the replayer measures time and memory, while the
     parity tests replay the same recipe against the oracle."""
+    if wl.q_scale != 1:
+        raise ValueError("the native replayer generates unscaled queries")
     out = ["config %d %d %d %d %d %d" % (wl.layers, wl.q_heads, wl.kv_heads, wl.head_dim, wl.num_blocks,
                                          1 if wl.dtype == "bf16" else 0)]
     for op in wl.ops:
