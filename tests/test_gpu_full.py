@@ -9,6 +9,8 @@ Loops and extreme shapes are sampled; the sample always includes the first and
 last rows.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -40,6 +42,17 @@ def test_standard_workload_every_output(name):
     op = wl.attend_ops()[0]
     rows = sum(op[3]) if op[0] == "verify" else len(op[2])
     assert [n for _, _, n in res] == [rows * wl.q_heads * wl.head_dim]
+    assert_close(res, wl.dtype)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,q_scale", [("spec_verify", 2), ("spec_verify", 4), ("llama_fork", 2), ("llama_fork", 4)])
+def test_standard_workload_sharp_scores_every_output(name, q_scale):
+    """The same at full size with the queries scaled by a power of two: wider
+    score spreads, weights gathered on fewer keys, so the P.V step keeps the
+    low parts of its bf16 weights on more of the super-blocks."""
+    wl = dataclasses.replace(recipes.STANDARD[name](), q_scale=q_scale)
+    res = run_both(wl, threads=oracle_threads())
     assert_close(res, wl.dtype)
 
 
